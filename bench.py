@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSpark per-step verify path on one MI355X.
+
+One step = dspark_plan (STS confidence -> survival -> budget sweep ->
+verify_lens) + dspark_pack (cu_seqlens, front-packed rows, tier) +
+dspark_accept (vocab-wide argmax over the packed target logits, leading-match
+count, bonus, commit, output tokens), on the B=256, gamma=8, V=129280 bf16
+workload. Every input, including the packed target logits a forward pass
+would have produced, is resident in HBM before the timed region. Three
+copies of the packed logits rotate, about 1 GB in all, so the 256 MB
+Infinity Cache cannot serve repeated reads.
+
+Prints one JSON line. ``value`` is steps/s (eager launches). ``roofline`` is
+the accept kernel's achieved HBM bandwidth: algorithmic bytes per launch over
+its mean duration, timed with HIP events on the stream it runs on.
+``cpu_baseline`` is the untouched CPU oracle on a bounded sample of the same
+step.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "plan+accept steps/s and logit-pass HBM GB/s (% peak) at B=256,γ=8,V=129280"
+TRAFFIC_FILE = ROOT / "profiles" / "accept_b256_g8_v129280_bf16_traffic.json"
+ACCEPT_SRC = ROOT / "dspark_verify_scheduling_amd" / "csrc" / "accept.hip"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def accept_bytes(total, B, gamma, V, esize):
+    """Algorithmic bytes of one accept launch: every packed logit once, plus
+    cu_seqlens, drafts, prefix lengths, and the outputs (row argmax, four
+    per-request ints, out_tokens, prefix_mask)."""
+    logits = total * V * esize
+    inputs = (B + 1) * 4 + B * gamma * 4 + B * 4
+    outputs = total * 4 + 4 * B * 4 + B * (gamma + 1) * 4 + B * gamma + 2 * 4
+    return logits + inputs + outputs
+
+
+def traffic_for(total_rows):
+    """HBM bytes per accept launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    rec = json.loads(TRAFFIC_FILE.read_text())
+    src_hash = hashlib.sha256(ACCEPT_SRC.read_bytes()).hexdigest()
+    if rec.get("accept_hip_sha256") != src_hash or rec.get("rows") != total_rows:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, lens_ref, packed_host, total, budget_s):
+    """The oracle as it stands, on one host core: full plan and pack, accept
+    on a 32-row sample of the packed logits, scaled to the step's rows."""
+    import oracle
+    from oracle.accept import as_f32_rows
+
+    sample_rows = 32
+    t_plan, t_pack, t_row = [], [], []
+    t_end = time.perf_counter() + budget_s
+    while time.perf_counter() < t_end or not t_plan:
+        t0 = time.perf_counter()
+        rp = oracle.plan(w.B, w.gamma, oracle.IN_CONF_LOGITS, w.conf, w.temps, w.min_len,
+                         w.max_len, w.eps, w.b_lo, w.b_hi, w.bias, w.alpha, w.theta)
+        t1 = time.perf_counter()
+        rk = oracle.pack(w.B, w.gamma, rp["verify_lens"], w.anchors, w.drafts, w.tiers,
+                         w.prefix_lens)
+        t2 = time.perf_counter()
+        rows = packed_host[:sample_rows]
+        oracle.row_argmax(as_f32_rows(rows, "bf16" if rows.dtype == np.uint16 else "f32"))
+        t3 = time.perf_counter()
+        assert np.array_equal(rp["verify_lens"], lens_ref)
+        t_plan.append(t1 - t0)
+        t_pack.append(t2 - t1)
+        t_row.append((t3 - t2) / sample_rows)
+    step = statistics.median(t_plan) + statistics.median(t_pack) + statistics.median(t_row) * total
+    return {
+        "value": 1.0 / step,
+        "unit": "steps/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{len(t_plan)} repetitions of the full plan + pack and of the row argmax on "
+                   f"{sample_rows} of the {total} packed bf16 rows; the per-row time is scaled to "
+                   f"{total} rows (median of repetitions)"),
+        "ms_plan": 1e3 * statistics.median(t_plan),
+        "ms_pack": 1e3 * statistics.median(t_pack),
+        "ms_accept_per_row": 1e3 * statistics.median(t_row),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the per-step verify path "
+                                   "shards by request across GPUs (see the design notes), but "
+                                   "no multi-GPU run is provided", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import dspark_verify_scheduling_amd as dv
+    from workloads import make
+
+    dev = "cuda"
+    dv.load()
+    log(f"generating workload {args.config}")
+    w = make(args.config)
+    B, G, V = w.B, w.gamma, w.V
+    dt = dv.BF16 if w.dtype == "bf16" else dv.F32
+    tdt = torch.bfloat16 if dt == dv.BF16 else torch.float32
+    esize = 2 if dt == dv.BF16 else 4
+    cap = int(w.tiers[-1])
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    conf_t, temps_t = t(w.conf), t(w.temps)
+    alpha_t, theta_t = t(w.alpha), t(w.theta)
+    anchors_t, drafts_t, prefix_t = t(w.anchors), t(w.drafts), t(w.prefix_lens)
+    tiers = [int(x) for x in w.tiers]
+    po = dv.alloc_plan_outputs(B, G, dev, survival=False, sweep=False)
+    ko = dv.alloc_pack_outputs(B, cap, dev)
+
+    # plan once to learn the packed layout; the stand-in for the target
+    # forward fills the packed logits for exactly those rows
+    dv.dspark_plan(B, G, dv.IN_CONF_LOGITS, conf_t, temps_t, w.min_len, w.max_len, w.eps,
+                   w.b_lo, w.b_hi, float(w.bias), alpha_t, theta_t, po)
+    dv.dspark_pack(B, G, po.verify_lens, anchors_t, drafts_t, tiers, prefix_t, ko)
+    torch.cuda.synchronize()
+    lens = po.verify_lens.cpu().numpy()
+    cu = ko.cu_seqlens.cpu().numpy()
+    total, tier = int(ko.pack_meta[0].item()), int(ko.pack_meta[1].item())
+    req = np.repeat(np.arange(B), lens)
+    jrow = np.arange(total) - np.repeat(cu[:-1], lens)
+    src = torch.from_numpy(req * (G + 1) + jrow).to(dev)
+    host_view = w.target.reshape(B * (G + 1), V)
+    strided = torch.from_numpy(host_view.view(np.int16) if dt == dv.BF16 else host_view).to(dev)
+    if dt == dv.BF16:
+        strided = strided.view(torch.bfloat16)
+    n_rot = 3
+    packed = []
+    for _ in range(n_rot):
+        buf = torch.zeros(tier, V, dtype=tdt, device=dev)
+        buf[:total] = strided.index_select(0, src)
+        packed.append(buf)
+    packed_host = w.target[req[:64], jrow[:64]]  # rows for the CPU sample
+    del strided
+    torch.cuda.empty_cache()
+    ao = dv.alloc_accept_outputs(B, G, tier, V, dt, dev)
+    log(f"B={B} gamma={G} V={V}: total={total} rows, tier={tier}, "
+        f"{n_rot} rotating buffers of {total * V * esize / 2**20:.1f} MiB")
+
+    stream = torch.cuda.current_stream()
+
+    def step(i):  # on the current stream (graph capture switches it)
+        dv.dspark_plan(B, G, dv.IN_CONF_LOGITS, conf_t, temps_t, w.min_len, w.max_len, w.eps,
+                       w.b_lo, w.b_hi, float(w.bias), alpha_t, theta_t, po)
+        dv.dspark_pack(B, G, po.verify_lens, anchors_t, drafts_t, tiers, prefix_t, ko)
+        dv.dspark_accept(B, G, V, dt, packed[i % n_rot], V, tier, ko.cu_seqlens, drafts_t,
+                         prefix_t, ao)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed: K eager steps (events around each accept on its stream)
+    ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        dv.dspark_plan(B, G, dv.IN_CONF_LOGITS, conf_t, temps_t, w.min_len, w.max_len, w.eps,
+                       w.b_lo, w.b_hi, float(w.bias), alpha_t, theta_t, po, stream)
+        dv.dspark_pack(B, G, po.verify_lens, anchors_t, drafts_t, tiers, prefix_t, ko, stream)
+        ev_a0[i].record(stream)
+        dv.dspark_accept(B, G, V, dt, packed[i % n_rot], V, tier, ko.cu_seqlens, drafts_t,
+                         prefix_t, ao, stream)
+        ev_a1[i].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / args.steps
+    acc_us = [1e3 * a.elapsed_time(b) for a, b in zip(ev_a0, ev_a1)]
+    acc_mean_us = statistics.mean(acc_us)
+
+    # results of the timed steps must be the planned ones
+    assert np.array_equal(po.verify_lens.cpu().numpy(), lens)
+    assert int(ao.accept_meta[1].item()) == 0
+
+    # ---- plan and pack alone (events), and one step as a HIP graph replay
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    reps = 50
+    ev[0].record(stream)
+    for _ in range(reps):
+        dv.dspark_plan(B, G, dv.IN_CONF_LOGITS, conf_t, temps_t, w.min_len, w.max_len, w.eps,
+                       w.b_lo, w.b_hi, float(w.bias), alpha_t, theta_t, po, stream)
+    ev[1].record(stream)
+    for _ in range(reps):
+        dv.dspark_pack(B, G, po.verify_lens, anchors_t, drafts_t, tiers, prefix_t, ko, stream)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    plan_us = 1e3 * ev[0].elapsed_time(ev[1]) / reps
+    pack_us = 1e3 * ev[1].elapsed_time(ev[2]) / reps
+
+    graphs = []
+    gs = torch.cuda.Stream()
+    gs.wait_stream(stream)
+    with torch.cuda.stream(gs):
+        step(0)
+    stream.wait_stream(gs)
+    torch.cuda.synchronize()
+    for i in range(n_rot):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % n_rot].replay()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        graphs[i % n_rot].replay()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step_graph = start.elapsed_time(stop) / args.steps
+    assert np.array_equal(po.verify_lens.cpu().numpy(), lens)
+
+    # ---- fixed-shape roofline: static mode, every request verifies gamma + 1 rows
+    static_rows = B * (G + 1)
+    cu_static = torch.arange(0, static_rows + 1, G + 1, dtype=torch.int32, device=dev)
+    stat_bufs = []
+    host_all = w.target.reshape(static_rows, V)
+    for _ in range(2):
+        tb = torch.from_numpy(host_all.view(np.int16) if dt == dv.BF16 else host_all).to(dev)
+        stat_bufs.append(tb.view(torch.bfloat16) if dt == dv.BF16 else tb)
+    ao_s = dv.alloc_accept_outputs(B, G, static_rows, V, dt, dev)
+    for i in range(5):
+        dv.dspark_accept(B, G, V, dt, stat_bufs[i % 2], V, static_rows, cu_static, drafts_t,
+                         prefix_t, ao_s, stream)
+    torch.cuda.synchronize()
+    start.record(stream)
+    n_static = 50
+    for i in range(n_static):
+        dv.dspark_accept(B, G, V, dt, stat_bufs[i % 2], V, static_rows, cu_static, drafts_t,
+                         prefix_t, ao_s, stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    static_us = 1e3 * start.elapsed_time(stop) / n_static
+    static_gbs = accept_bytes(static_rows, B, G, V, esize) / (static_us * 1e-6) / 1e9
+
+    acc_bytes = accept_bytes(total, B, G, V, esize)
+    achieved = acc_bytes / (acc_mean_us * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(w, lens, packed_host, total, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": 1e3 / ms_step,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.spec.name}: B={B} gamma={G} V={V} {w.dtype}, planned packed rows",
+                   "B": B, "gamma": G, "V": V, "rows": total, "tier": tier, "seed": w.seed,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_for(total),
+                     "kernel": "accept_kernel<bf16>", "bytes_per_launch": acc_bytes,
+                     "mean_us": acc_mean_us},
+        "cpu_baseline": cpu,
+        "steps_per_s_graph": 1e3 / ms_step_graph,
+        "ms_per_step_graph": ms_step_graph,
+        "plan_us": plan_us,
+        "pack_us": pack_us,
+        "accept_us_median": statistics.median(acc_us),
+        "accept_static": {"rows": static_rows, "us": static_us, "GB/s": static_gbs,
+                          "frac": static_gbs / PEAK_HBM_GBS},
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,243 @@
+"""MI355X (gfx950) DSpark per-step verify path: Python binding of libdspark.
+
+The functions below carry the names of the C entry points in
+``include/dspark.h`` and only marshal arguments. They check that each tensor
+is a contiguous CUDA tensor of the right dtype and size, pass raw pointers and
+the current HIP stream, and raise ``DsparkError`` on a non-OK status. Every
+step of the computation runs in the library's HIP kernels. PyTorch supplies
+device memory and streams.
+
+``alloc_*`` helpers allocate output tensors for convenience. The library
+itself never allocates.
+"""
+
+from __future__ import annotations
+
+from typing import NamedTuple, Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import (
+    BF16, DATA_BAD_CONF, DATA_BAD_COST, DATA_BAD_LENS, F32, IN_COND, IN_CONF_LOGITS,
+    IN_SURVIVAL, MAX_BATCH, MAX_CANDIDATES, MAX_GAMMA, MAX_TIERS, MAX_VOCAB, DsparkError,
+)
+
+__all__ = [
+    "load", "dspark_plan", "dspark_pack", "dspark_accept", "dspark_tv_accept",
+    "dspark_accept_workspace_size", "alloc_plan_outputs", "alloc_pack_outputs",
+    "alloc_accept_outputs", "DsparkError", "F32", "BF16", "IN_CONF_LOGITS", "IN_COND",
+    "IN_SURVIVAL", "DATA_BAD_COST", "DATA_BAD_CONF", "DATA_BAD_LENS",
+]
+
+
+def load():
+    """Load libdspark.so (raises if it is not built)."""
+    return _lib.lib()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype, numel: int, required: bool = True):
+    if t is None:
+        if required and numel > 0:
+            raise ValueError(f"{name} is required")
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _logit_dtype(dt: int):
+    if dt == BF16:
+        return torch.bfloat16
+    if dt == F32:
+        return torch.float32
+    raise ValueError(f"unknown dtype code {dt}")
+
+
+# ------------------------------------------------------------------ plan
+
+class PlanOutputs(NamedTuple):
+    verify_lens: torch.Tensor  # [B] int32
+    plan_meta: torch.Tensor  # [4] int32
+    plan_val: torch.Tensor  # [2] float64
+    survival_out: Optional[torch.Tensor]  # [B, gamma] float32
+    sweep_out: Optional[torch.Tensor]  # [B*gamma+1, 2] float64
+
+
+def alloc_plan_outputs(B: int, gamma: int, device, survival=True, sweep=False) -> PlanOutputs:
+    return PlanOutputs(
+        torch.empty(B, dtype=torch.int32, device=device),
+        torch.empty(4, dtype=torch.int32, device=device),
+        torch.empty(2, dtype=torch.float64, device=device),
+        torch.empty(B, gamma, dtype=torch.float32, device=device) if survival else None,
+        torch.empty(B * gamma + 1, 2, dtype=torch.float64, device=device) if sweep else None,
+    )
+
+
+def dspark_plan(B: int, gamma: int, kind: int, conf: torch.Tensor, sts_temp, min_verify_len: int,
+                max_verify_len: int, survival_eps: float, budget_lo: int, budget_hi: int,
+                cost_bias: float, cost_alpha: torch.Tensor, cost_theta: torch.Tensor,
+                out: PlanOutputs, stream=None) -> PlanOutputs:
+    f32, i32, f64 = torch.float32, torch.int32, torch.float64
+    args = (
+        B, gamma, kind,
+        _ptr(conf, "conf", f32, B * gamma),
+        _ptr(sts_temp, "sts_temp", f32, gamma, required=(kind == IN_CONF_LOGITS)),
+        min_verify_len, max_verify_len, survival_eps, budget_lo, budget_hi, cost_bias,
+        _ptr(cost_alpha, "cost_alpha", f32, 1), cost_alpha.numel(),
+        _ptr(cost_theta, "cost_theta", f32, 1), cost_theta.numel(),
+        _ptr(out.verify_lens, "verify_lens", i32, B),
+        _ptr(out.plan_meta, "plan_meta", i32, 4),
+        _ptr(out.plan_val, "plan_val", f64, 2),
+        _ptr(out.survival_out, "survival_out", f32, B * gamma, required=False),
+        _ptr(out.sweep_out, "sweep_out", f64, 2 * (B * gamma + 1), required=False),
+        _stream(stream),
+    )
+    _lib.check("dspark_plan", _lib.lib().dspark_plan(*args))
+    return out
+
+
+# ------------------------------------------------------------------ pack
+
+class PackOutputs(NamedTuple):
+    cu_seqlens: torch.Tensor  # [B+1] int32
+    packed_ids: torch.Tensor  # [capacity] int32
+    packed_req: Optional[torch.Tensor]
+    packed_pos: Optional[torch.Tensor]
+    pack_meta: torch.Tensor  # [3] int32
+
+
+def alloc_pack_outputs(B: int, capacity: int, device, req=True, pos=True) -> PackOutputs:
+    i32 = torch.int32
+    return PackOutputs(
+        torch.empty(B + 1, dtype=i32, device=device),
+        torch.empty(capacity, dtype=i32, device=device),
+        torch.empty(capacity, dtype=i32, device=device) if req else None,
+        torch.empty(capacity, dtype=i32, device=device) if pos else None,
+        torch.empty(3, dtype=i32, device=device),
+    )
+
+
+def dspark_pack(B: int, gamma: int, verify_lens: torch.Tensor, anchor_ids: torch.Tensor,
+                draft_tokens: torch.Tensor, tiers: Sequence[int], prefix_lens, out: PackOutputs,
+                stream=None) -> PackOutputs:
+    import ctypes
+
+    i32 = torch.int32
+    tiers = [int(t) for t in tiers]
+    if not tiers:
+        raise ValueError("tiers must not be empty")
+    cap = tiers[-1]
+    tiers_host = (ctypes.c_int32 * len(tiers))(*tiers)
+    args = (
+        B, gamma,
+        _ptr(verify_lens, "verify_lens", i32, B),
+        _ptr(anchor_ids, "anchor_ids", i32, B),
+        _ptr(draft_tokens, "draft_tokens", i32, B * gamma),
+        ctypes.cast(tiers_host, ctypes.c_void_p), len(tiers),
+        _ptr(prefix_lens, "prefix_lens", i32, B, required=False),
+        _ptr(out.cu_seqlens, "cu_seqlens", i32, B + 1),
+        _ptr(out.packed_ids, "packed_ids", i32, cap),
+        _ptr(out.packed_req, "packed_req", i32, cap, required=False),
+        _ptr(out.packed_pos, "packed_pos", i32, cap, required=False),
+        _ptr(out.pack_meta, "pack_meta", i32, 3),
+        _stream(stream),
+    )
+    _lib.check("dspark_pack", _lib.lib().dspark_pack(*args))
+    return out
+
+
+# ------------------------------------------------------------------ accept
+
+class AcceptOutputs(NamedTuple):
+    row_argmax: torch.Tensor  # [max_rows] int32
+    num_correct: torch.Tensor  # [B] int32
+    bonus: torch.Tensor
+    commit_lens: torch.Tensor
+    out_tokens: torch.Tensor  # [B, gamma+1] int32
+    new_seq_lens: Optional[torch.Tensor]
+    prefix_mask: Optional[torch.Tensor]  # [B, gamma] uint8
+    accept_meta: torch.Tensor  # [2] int32
+    workspace: torch.Tensor  # uint8, zero-filled
+
+
+def dspark_accept_workspace_size(max_rows: int, V: int, dt: int) -> int:
+    return int(_lib.lib().dspark_accept_workspace_size(max_rows, V, dt))
+
+
+def alloc_accept_outputs(B: int, gamma: int, max_rows: int, V: int, dt: int, device,
+                         new_seq=True, mask=True) -> AcceptOutputs:
+    i32 = torch.int32
+    ws = dspark_accept_workspace_size(max_rows, V, dt)
+    return AcceptOutputs(
+        torch.empty(max(max_rows, 1), dtype=i32, device=device),
+        torch.empty(B, dtype=i32, device=device),
+        torch.empty(B, dtype=i32, device=device),
+        torch.empty(B, dtype=i32, device=device),
+        torch.empty(B, gamma + 1, dtype=i32, device=device),
+        torch.empty(B, dtype=i32, device=device) if new_seq else None,
+        torch.empty(B, gamma, dtype=torch.uint8, device=device) if mask else None,
+        torch.empty(2, dtype=i32, device=device),
+        torch.zeros(max(ws, 256), dtype=torch.uint8, device=device),
+    )
+
+
+def dspark_accept(B: int, gamma: int, V: int, dt: int, packed_logits: torch.Tensor, ld: int,
+                  max_rows: int, cu_seqlens: torch.Tensor, draft_tokens: torch.Tensor,
+                  prefix_lens, out: AcceptOutputs, stream=None) -> AcceptOutputs:
+    i32 = torch.int32
+    args = (
+        B, gamma, V, dt,
+        _ptr(packed_logits, "packed_logits", _logit_dtype(dt), max_rows * ld if max_rows else 0),
+        ld, max_rows,
+        _ptr(cu_seqlens, "cu_seqlens", i32, B + 1),
+        _ptr(draft_tokens, "draft_tokens", i32, B * gamma),
+        _ptr(prefix_lens, "prefix_lens", i32, B, required=False),
+        _ptr(out.row_argmax, "row_argmax", i32, max_rows),
+        _ptr(out.num_correct, "num_correct", i32, B),
+        _ptr(out.bonus, "bonus", i32, B),
+        _ptr(out.commit_lens, "commit_lens", i32, B),
+        _ptr(out.out_tokens, "out_tokens", i32, B * (gamma + 1)),
+        _ptr(out.new_seq_lens, "new_seq_lens", i32, B, required=False),
+        _ptr(out.prefix_mask, "prefix_mask", torch.uint8, B * gamma, required=False),
+        _ptr(out.accept_meta, "accept_meta", i32, 2),
+        _ptr(out.workspace, "workspace", torch.uint8, 1), out.workspace.numel(),
+        _stream(stream),
+    )
+    _lib.check("dspark_accept", _lib.lib().dspark_accept(*args))
+    return out
+
+
+# ------------------------------------------------------------------ TV
+
+def dspark_tv_accept(B: int, gamma: int, V: int, dt: int, draft_logits: torch.Tensor, ld_q: int,
+                     target_logits: torch.Tensor, ld_p: int, target_rows_per_req: int,
+                     accept_rate: torch.Tensor, survival: torch.Tensor, stream=None):
+    ldt = _logit_dtype(dt)
+    f32 = torch.float32
+    args = (
+        B, gamma, V, dt,
+        _ptr(draft_logits, "draft_logits", ldt, (B * gamma - 1) * ld_q + V if B else 0), ld_q,
+        _ptr(target_logits, "target_logits", ldt,
+             ((B - 1) * target_rows_per_req + gamma - 1) * ld_p + V if B else 0), ld_p,
+        target_rows_per_req,
+        _ptr(accept_rate, "accept_rate", f32, B * gamma),
+        _ptr(survival, "survival", f32, B * gamma),
+        _stream(stream),
+    )
+    _lib.check("dspark_tv_accept", _lib.lib().dspark_tv_accept(*args))
+    return accept_rate, survival

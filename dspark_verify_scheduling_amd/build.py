@@ -1,0 +1,71 @@
+"""Build libdspark.so (the C-ABI library with its gfx950 kernels) in-tree.
+
+``python -m dspark_verify_scheduling_amd.build`` or ``build()`` compiles every
+HIP source under ``csrc/`` with hipcc for gfx950. A second, host-only library,
+``libdspark_hostcheck.so``, exposes the device sigmoid compiled for the CPU so
+that its rarely taken exact path can be tested without a GPU.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+INCLUDE = ROOT / "include"
+LIB = PKG / "libdspark.so"
+HOSTCHECK = PKG / "libdspark_hostcheck.so"
+ARCH = "gfx950"
+
+LIB_SOURCES = ["api.hip", "plan.hip", "pack.hip", "accept.hip", "tv.hip"]
+
+COMMON_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-Wall",
+    "-Wno-unused-function",
+    # no packed fp32 instructions: plain scalar fp32 code only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{INCLUDE}",
+    f"-I{CSRC}",
+]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and Path(cand).exists():
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libdspark)")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(str(c) for c in cmd), flush=True)
+    res = subprocess.run([str(c) for c in cmd], capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"build failed: {cmd[-1]}")
+
+
+def build(verbose: bool = False) -> Path:
+    """Compile libdspark.so and libdspark_hostcheck.so next to this file."""
+    hipcc = _hipcc()
+    tmp = LIB.with_suffix(".so.tmp")
+    _run([hipcc, *COMMON_FLAGS, "-o", tmp, *[CSRC / s for s in LIB_SOURCES]], verbose)
+    os.replace(tmp, LIB)
+    tmp = HOSTCHECK.with_suffix(".so.tmp")
+    _run([hipcc, *COMMON_FLAGS, "-o", tmp, CSRC / "hostcheck.hip"], verbose)
+    os.replace(tmp, HOSTCHECK)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

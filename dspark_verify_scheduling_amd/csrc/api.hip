@@ -1,0 +1,346 @@
+// C ABI of libdspark: argument validation on the host, then kernel launches
+// on the caller's stream. No allocation, no synchronization, no host reads of
+// device data.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+dspark_status fail(dspark_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+dspark_status ok() {
+  g_last_error[0] = '\0';
+  return DSPARK_OK;
+}
+
+dspark_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) {
+    return fail(DSPARK_E_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  }
+  return ok();
+}
+
+int next_pow2(int x) {
+  int n = 1;
+  while (n < x) n <<= 1;
+  return n;
+}
+
+// Compute units of the current device, cached per device id.
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0) {
+      n = 256;
+    }
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(dspark_dtype dt) { return dt == DSPARK_BF16 ? 2 : 4; }
+
+// Row geometry of the vocabulary pass: whole 16-byte vectors, tail elements,
+// units (chunks) per row and vectors per unit.
+struct RowGeom {
+  int nvec, tail, chunks, chunk_vecs;
+};
+
+RowGeom row_geom(int V, dspark_dtype dt) {
+  const int epv = (int)(16 / elem_size(dt));
+  RowGeom g;
+  g.nvec = V / epv;
+  g.tail = V - g.nvec * epv;
+  g.chunks = (g.nvec + dspark::kAccMaxChunkVecs - 1) / dspark::kAccMaxChunkVecs;
+  if (g.chunks < 1) g.chunks = 1;
+  g.chunk_vecs = (g.nvec + g.chunks - 1) / g.chunks;
+  return g;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t glob, rows, parts, total;
+};
+
+WsLayout ws_layout(int max_rows, int chunks) {
+  WsLayout w;
+  w.glob = 0;
+  w.rows = 256;
+  w.parts = w.rows + align256((size_t)max_rows * sizeof(unsigned int));
+  w.total = w.parts + align256((size_t)max_rows * chunks * sizeof(unsigned long long));
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dspark_version(void) { return (1 << 16) | 0; }
+
+const char* dspark_status_str(dspark_status s) {
+  switch (s) {
+    case DSPARK_OK: return "DSPARK_OK";
+    case DSPARK_E_INVALID: return "DSPARK_E_INVALID";
+    case DSPARK_E_UNSUPPORTED: return "DSPARK_E_UNSUPPORTED";
+    case DSPARK_E_WORKSPACE: return "DSPARK_E_WORKSPACE";
+    case DSPARK_E_LAUNCH: return "DSPARK_E_LAUNCH";
+  }
+  return "DSPARK_E_UNKNOWN";
+}
+
+const char* dspark_last_error(void) { return g_last_error; }
+
+dspark_status dspark_plan(int32_t B, int32_t gamma, dspark_input kind, const float* conf,
+                          const float* sts_temp, int32_t min_verify_len,
+                          int32_t max_verify_len, float survival_eps, int32_t budget_lo,
+                          int32_t budget_hi, float cost_bias, const float* cost_alpha,
+                          int32_t alpha_len, const float* cost_theta, int32_t theta_len,
+                          int32_t* verify_lens, int32_t* plan_meta, double* plan_val,
+                          float* survival_out, double* sweep_out, void* stream) {
+  if (B < 0) return fail(DSPARK_E_INVALID, "dspark_plan: B = %d < 0", B);
+  if (gamma < 1 || gamma > DSPARK_MAX_GAMMA)
+    return fail(DSPARK_E_INVALID, "dspark_plan: gamma = %d outside [1, %d]", gamma,
+                DSPARK_MAX_GAMMA);
+  if (kind != DSPARK_IN_CONF_LOGITS && kind != DSPARK_IN_COND && kind != DSPARK_IN_SURVIVAL)
+    return fail(DSPARK_E_INVALID, "dspark_plan: unknown input kind %d", (int)kind);
+  if (B > DSPARK_MAX_BATCH || (int64_t)B * gamma > DSPARK_MAX_CANDIDATES)
+    return fail(DSPARK_E_UNSUPPORTED, "dspark_plan: B * gamma = %lld exceeds %d",
+                (long long)B * gamma, DSPARK_MAX_CANDIDATES);
+  if (B > 0 && !conf) return fail(DSPARK_E_INVALID, "dspark_plan: conf is NULL");
+  if (kind == DSPARK_IN_CONF_LOGITS && !sts_temp)
+    return fail(DSPARK_E_INVALID, "dspark_plan: sts_temp is NULL for confidence logits");
+  if (!cost_alpha || !cost_theta)
+    return fail(DSPARK_E_INVALID, "dspark_plan: cost table pointer is NULL");
+  if (!plan_meta || !plan_val || (B > 0 && !verify_lens))
+    return fail(DSPARK_E_INVALID, "dspark_plan: an output pointer is NULL");
+  if (budget_lo < 0) return fail(DSPARK_E_INVALID, "dspark_plan: budget_lo = %d < 0", budget_lo);
+  if (budget_hi >= 0 && budget_lo > budget_hi)
+    return fail(DSPARK_E_INVALID, "dspark_plan: budget_lo %d > budget_hi %d", budget_lo,
+                budget_hi);
+  if (survival_eps != survival_eps)
+    return fail(DSPARK_E_INVALID, "dspark_plan: survival_eps is NaN");
+  const int lmin = std::min(std::max(min_verify_len, 1), gamma + 1);
+  const int lmax = std::min(std::max(max_verify_len, lmin), gamma + 1);
+  if (alpha_len <= B)
+    return fail(DSPARK_E_INVALID, "dspark_plan: alpha_len %d must exceed B = %d", alpha_len, B);
+  if ((int64_t)theta_len <= (int64_t)B * lmax)
+    return fail(DSPARK_E_INVALID, "dspark_plan: theta_len %d must exceed B * L_max = %lld",
+                theta_len, (long long)B * lmax);
+
+  dspark::PlanArgs a;
+  a.B = B;
+  a.gamma = gamma;
+  a.kind = (int)kind;
+  a.lmin = lmin;
+  a.lmax = lmax;
+  a.b_lo = budget_lo;
+  a.b_hi = budget_hi < 0 ? -1 : budget_hi;
+  a.n_sort = next_pow2(std::max(1, B * (lmax - lmin)));
+  a.eps = survival_eps;
+  a.bias = cost_bias;
+  a.conf = conf;
+  a.temps = sts_temp;
+  a.alpha = cost_alpha;
+  a.theta = cost_theta;
+  a.lens = verify_lens;
+  a.meta = plan_meta;
+  a.val = plan_val;
+  a.surv_out = survival_out;
+  a.sweep = sweep_out;
+  return launched(dspark::launch_plan(a, (hipStream_t)stream), "dspark_plan");
+}
+
+dspark_status dspark_pack(int32_t B, int32_t gamma, const int32_t* verify_lens,
+                          const int32_t* anchor_ids, const int32_t* draft_tokens,
+                          const int32_t* tiers_host, int32_t num_tiers,
+                          const int32_t* prefix_lens, int32_t* cu_seqlens,
+                          int32_t* packed_ids, int32_t* packed_req, int32_t* packed_pos,
+                          int32_t* pack_meta, void* stream) {
+  if (B < 0) return fail(DSPARK_E_INVALID, "dspark_pack: B = %d < 0", B);
+  if (gamma < 1 || gamma > DSPARK_MAX_GAMMA)
+    return fail(DSPARK_E_INVALID, "dspark_pack: gamma = %d outside [1, %d]", gamma,
+                DSPARK_MAX_GAMMA);
+  if (B > DSPARK_MAX_BATCH)
+    return fail(DSPARK_E_UNSUPPORTED, "dspark_pack: B = %d exceeds %d", B, DSPARK_MAX_BATCH);
+  if (B > 0 && (!verify_lens || !anchor_ids || !draft_tokens))
+    return fail(DSPARK_E_INVALID, "dspark_pack: an input pointer is NULL");
+  if (!cu_seqlens || !packed_ids || !pack_meta)
+    return fail(DSPARK_E_INVALID, "dspark_pack: an output pointer is NULL");
+  if (!tiers_host || num_tiers < 1 || num_tiers > DSPARK_MAX_TIERS)
+    return fail(DSPARK_E_INVALID, "dspark_pack: need 1..%d tiers, got %d", DSPARK_MAX_TIERS,
+                num_tiers);
+  if (tiers_host[0] < 1) return fail(DSPARK_E_INVALID, "dspark_pack: tiers must be >= 1");
+  for (int i = 1; i < num_tiers; ++i) {
+    if (tiers_host[i] <= tiers_host[i - 1])
+      return fail(DSPARK_E_INVALID, "dspark_pack: tiers not strictly ascending at %d", i);
+  }
+  if ((int64_t)tiers_host[num_tiers - 1] < (int64_t)B * (gamma + 1))
+    return fail(DSPARK_E_INVALID, "dspark_pack: last tier %d < B * (gamma + 1) = %lld",
+                tiers_host[num_tiers - 1], (long long)B * (gamma + 1));
+
+  dspark::PackArgs a;
+  a.B = B;
+  a.gamma = gamma;
+  a.ntiers = num_tiers;
+  a.lens = verify_lens;
+  a.anchors = anchor_ids;
+  a.drafts = draft_tokens;
+  a.prefix = prefix_lens;
+  a.cu = cu_seqlens;
+  a.ids = packed_ids;
+  a.req = packed_req;
+  a.pos = packed_pos;
+  a.meta = pack_meta;
+  for (int i = 0; i < DSPARK_MAX_TIERS; ++i) a.tiers[i] = i < num_tiers ? tiers_host[i] : 0;
+  return launched(dspark::launch_pack(a, (hipStream_t)stream), "dspark_pack");
+}
+
+size_t dspark_accept_workspace_size(int32_t max_rows, int32_t V, dspark_dtype dt) {
+  if (max_rows < 0 || V < 1 || V > DSPARK_MAX_VOCAB) return 0;
+  if (dt != DSPARK_F32 && dt != DSPARK_BF16) return 0;
+  return ws_layout(max_rows, row_geom(V, dt).chunks).total;
+}
+
+dspark_status dspark_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,
+                            const void* packed_logits, int64_t ld, int32_t max_rows,
+                            const int32_t* cu_seqlens, const int32_t* draft_tokens,
+                            const int32_t* prefix_lens, int32_t* row_argmax,
+                            int32_t* num_correct, int32_t* bonus, int32_t* commit_lens,
+                            int32_t* out_tokens, int32_t* new_seq_lens, uint8_t* prefix_mask,
+                            int32_t* accept_meta, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (B < 0) return fail(DSPARK_E_INVALID, "dspark_accept: B = %d < 0", B);
+  if (gamma < 1 || gamma > DSPARK_MAX_GAMMA)
+    return fail(DSPARK_E_INVALID, "dspark_accept: gamma = %d outside [1, %d]", gamma,
+                DSPARK_MAX_GAMMA);
+  if (dt != DSPARK_F32 && dt != DSPARK_BF16)
+    return fail(DSPARK_E_UNSUPPORTED, "dspark_accept: unsupported dtype %d", (int)dt);
+  if (V < 1 || V > DSPARK_MAX_VOCAB)
+    return fail(V < 1 ? DSPARK_E_INVALID : DSPARK_E_UNSUPPORTED,
+                "dspark_accept: V = %d outside [1, %d]", V, DSPARK_MAX_VOCAB);
+  if (max_rows < 0) return fail(DSPARK_E_INVALID, "dspark_accept: max_rows = %d < 0", max_rows);
+  if (ld < V) return fail(DSPARK_E_INVALID, "dspark_accept: ld = %lld < V = %d", (long long)ld, V);
+  const size_t es = elem_size(dt);
+  if ((ld * (int64_t)es) % 16 != 0)
+    return fail(DSPARK_E_INVALID, "dspark_accept: row stride %lld bytes is not a multiple of 16",
+                (long long)(ld * (int64_t)es));
+  if (max_rows > 0 && (!packed_logits || !aligned16(packed_logits)))
+    return fail(DSPARK_E_INVALID, "dspark_accept: packed_logits NULL or not 16-byte aligned");
+  if (!cu_seqlens || !accept_meta)
+    return fail(DSPARK_E_INVALID, "dspark_accept: cu_seqlens or accept_meta is NULL");
+  if (B > 0 && (!draft_tokens || !num_correct || !bonus || !commit_lens || !out_tokens))
+    return fail(DSPARK_E_INVALID, "dspark_accept: a required per-request pointer is NULL");
+  if (max_rows > 0 && !row_argmax)
+    return fail(DSPARK_E_INVALID, "dspark_accept: row_argmax is NULL");
+  if (new_seq_lens && !prefix_lens)
+    return fail(DSPARK_E_INVALID, "dspark_accept: new_seq_lens needs prefix_lens");
+  const RowGeom g = row_geom(V, dt);
+  if ((int64_t)max_rows * g.chunks > 0x7fffffffLL)
+    return fail(DSPARK_E_UNSUPPORTED, "dspark_accept: max_rows * chunks overflows int32");
+  const WsLayout wl = ws_layout(max_rows, g.chunks);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+      workspace_bytes < wl.total)
+    return fail(DSPARK_E_WORKSPACE, "dspark_accept: workspace needs %zu bytes, 256-byte aligned",
+                wl.total);
+
+  dspark::AcceptArgs a;
+  a.logits = static_cast<const unsigned char*>(packed_logits);
+  a.ld_bytes = ld * (int64_t)es;
+  a.V = V;
+  a.max_rows = max_rows;
+  a.B = B;
+  a.gamma = gamma;
+  a.chunks = g.chunks;
+  a.chunk_vecs = g.chunk_vecs;
+  a.nvec = g.nvec;
+  a.tail = g.tail;
+  a.cu = cu_seqlens;
+  a.drafts = draft_tokens;
+  a.prefix = prefix_lens;
+  a.row_am = row_argmax;
+  a.num_correct = num_correct;
+  a.bonus = bonus;
+  a.commit = commit_lens;
+  a.out_tokens = out_tokens;
+  a.new_seq = new_seq_lens;
+  a.mask = prefix_mask;
+  a.meta = accept_meta;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  a.glob_cnt = reinterpret_cast<unsigned int*>(ws + wl.glob);
+  a.row_cnt = reinterpret_cast<unsigned int*>(ws + wl.rows);
+  a.partials = reinterpret_cast<unsigned long long*>(ws + wl.parts);
+  const int64_t units_max = (int64_t)max_rows * g.chunks;
+  int64_t grid = (int64_t)device_cus() * 8;
+  if (units_max < grid) grid = units_max;
+  if (grid < 1) grid = 1;
+  return launched(dspark::launch_accept(a, dt, (int)grid, (hipStream_t)stream), "dspark_accept");
+}
+
+dspark_status dspark_tv_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,
+                               const void* draft_logits, int64_t ld_q,
+                               const void* target_logits, int64_t ld_p,
+                               int32_t target_rows_per_req, float* accept_rate,
+                               float* survival, void* stream) {
+  if (B < 0) return fail(DSPARK_E_INVALID, "dspark_tv_accept: B = %d < 0", B);
+  if (gamma < 1 || gamma > DSPARK_MAX_GAMMA)
+    return fail(DSPARK_E_INVALID, "dspark_tv_accept: gamma = %d outside [1, %d]", gamma,
+                DSPARK_MAX_GAMMA);
+  if (dt != DSPARK_F32 && dt != DSPARK_BF16)
+    return fail(DSPARK_E_UNSUPPORTED, "dspark_tv_accept: unsupported dtype %d", (int)dt);
+  if (V < 1 || V > DSPARK_MAX_VOCAB)
+    return fail(V < 1 ? DSPARK_E_INVALID : DSPARK_E_UNSUPPORTED,
+                "dspark_tv_accept: V = %d outside [1, %d]", V, DSPARK_MAX_VOCAB);
+  if ((int64_t)B * gamma > 0x7fffffffLL)
+    return fail(DSPARK_E_UNSUPPORTED, "dspark_tv_accept: B * gamma too large");
+  if (target_rows_per_req < gamma)
+    return fail(DSPARK_E_INVALID, "dspark_tv_accept: target_rows_per_req %d < gamma %d",
+                target_rows_per_req, gamma);
+  if (ld_q < V || ld_p < V)
+    return fail(DSPARK_E_INVALID, "dspark_tv_accept: row stride below V");
+  const size_t es = elem_size(dt);
+  if ((ld_q * (int64_t)es) % 16 != 0 || (ld_p * (int64_t)es) % 16 != 0)
+    return fail(DSPARK_E_INVALID, "dspark_tv_accept: row strides must be multiples of 16 bytes");
+  if (B > 0) {
+    if (!draft_logits || !target_logits || !aligned16(draft_logits) || !aligned16(target_logits))
+      return fail(DSPARK_E_INVALID, "dspark_tv_accept: logits NULL or not 16-byte aligned");
+    if (!accept_rate || !survival)
+      return fail(DSPARK_E_INVALID, "dspark_tv_accept: an output pointer is NULL");
+  }
+  const int epv = (int)(16 / es);
+  dspark::TvArgs a;
+  a.q = static_cast<const unsigned char*>(draft_logits);
+  a.ldq_bytes = ld_q * (int64_t)es;
+  a.p = static_cast<const unsigned char*>(target_logits);
+  a.ldp_bytes = ld_p * (int64_t)es;
+  a.V = V;
+  a.B = B;
+  a.gamma = gamma;
+  a.rows_per_req = target_rows_per_req;
+  a.nvec = V / epv;
+  a.tail = V - a.nvec * epv;
+  a.a_out = accept_rate;
+  a.s_out = survival;
+  return launched(dspark::launch_tv(a, dt, (hipStream_t)stream), "dspark_tv_accept");
+}
+
+}  // extern "C"

@@ -1,0 +1,286 @@
+/*
+ * dspark.h - C ABI of the DSpark per-step verify path for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * One decode step of confidence-scheduled speculative decoding, for B
+ * requests that each drafted gamma tokens:
+ *
+ *   dspark_plan      STS confidence -> prefix survival -> global top-b budget
+ *                    sweep -> verify_lens
+ *   dspark_pack      verify_lens -> cu_seqlens, front-packed verify rows,
+ *                    packed total rounded up to a captured tier
+ *   dspark_accept    packed target logits -> per-row argmax -> leading-match
+ *                    count, bonus token, commit lengths, output tokens
+ *   dspark_tv_accept (optional) soft accept-rate 1 - TV(softmax q, softmax p)
+ *                    and its per-request cumulative product, which can feed
+ *                    dspark_plan as survivals
+ *
+ * Page references used below:
+ *   [Budget] akiyangdev, "DSpark 自适应 Verify 怎样分配候选预算"
+ *   [Round]  akiyangdev, "DeepSeek-V4 DSpark 一轮 Draft、Verify、Accept 与 Commit"
+ *   [SGLang] yingzheng, "DSpark 接入 SGLang：用置信度驱动可变长度验证"
+ *   [CSSD]   charlestar, "DSpark confidence-scheduled speculative decoding"
+ *
+ * Conventions for every entry point:
+ *   - Array arguments are DEVICE pointers to caller-owned memory, except those
+ *     whose name ends in _host. The library never allocates, frees or
+ *     synchronizes. Each call enqueues its kernels on `stream` (a hipStream_t
+ *     passed as void*; NULL is the null stream) and returns at once, so a
+ *     step can be captured into a HIP graph.
+ *   - Integers are int32 and arrays are dense, request-major and row-major:
+ *     conf[r * gamma + (k - 1)] holds draft position k = 1..gamma of
+ *     request r. Verify row j = 0 of a request is its root (anchor) row;
+ *     row j >= 1 verifies draft j.
+ *   - Argument errors are found on the host before any launch and returned
+ *     synchronously; nothing is enqueued then. Data errors only visible on
+ *     the device (bad cost table, NaN confidence, malformed lengths) are
+ *     reported in the status word of the *_meta output, together with a
+ *     documented fallback. Kernels never trap.
+ *   - dspark_last_error() returns a thread-local description of the last
+ *     non-OK status returned on the calling thread.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dspark_status {
+  DSPARK_OK = 0,
+  DSPARK_E_INVALID = 1,     /* bad scalar argument or missing required pointer */
+  DSPARK_E_UNSUPPORTED = 2, /* sizes beyond what the kernels handle (see limits) */
+  DSPARK_E_WORKSPACE = 3,   /* workspace missing, misaligned or too small */
+  DSPARK_E_LAUNCH = 4       /* the HIP runtime refused a launch */
+} dspark_status;
+
+typedef enum dspark_dtype { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+/* What dspark_plan's `conf` holds. */
+typedef enum dspark_input {
+  DSPARK_IN_CONF_LOGITS = 0, /* confidence logits z; c = sigmoid(z / T[k]) */
+  DSPARK_IN_COND = 1,        /* conditional confidences c in [0, 1] */
+  DSPARK_IN_SURVIVAL = 2     /* prefix survivals s in [0, 1], non-increasing in k */
+} dspark_input;
+
+/* Bits of the device-side status word (plan_meta[2], pack_meta[2],
+ * accept_meta[1]). */
+#define DSPARK_DATA_BAD_COST 1 /* some T(B, M) <= 0 or non-finite in the sweep */
+#define DSPARK_DATA_BAD_CONF 2 /* confidence/survival/temperature out of domain */
+#define DSPARK_DATA_BAD_LENS 4 /* verify lengths or cu_seqlens malformed */
+
+/* Limits. */
+#define DSPARK_MAX_GAMMA 64
+#define DSPARK_MAX_CANDIDATES 8192 /* B * gamma for dspark_plan */
+#define DSPARK_MAX_BATCH 8192      /* B for dspark_plan and dspark_pack */
+#define DSPARK_MAX_TIERS 32
+#define DSPARK_MAX_VOCAB 262144
+
+/*
+ * dspark_plan - choose the extra verify budget and the per-request verify_lens.
+ *
+ * Defined by [Budget] §一 (tau(b) = B + sum of the b largest survivals;
+ * budget = argmax_b tau(b) / T(B, B + b); ties in survival go to the earlier
+ * position, then the lower request id; ScheduleVerifyLensTopk allocation
+ * with min/max_verify_len and survival_eps), [Budget] §二 (STS runtime
+ * c_k = sigmoid(z_k / T_k), S_k = prod_{i<=k} c_i), [Budget] §四 and [CSSD]
+ * (additive cost T(B, M) = bias + alpha(B) + theta(M), M = bs + K).
+ *
+ * Arithmetic (the same on every GPU and in the CPU reference):
+ *   x = RN32(z / T[k]); c = the float32 nearest to 1 / (1 + e^-x);
+ *   s_1 = c_1, s_k = RN32(s_{k-1} * c_k).
+ *   L_min = clamp(min_verify_len, 1, gamma + 1);
+ *   L_max = clamp(max_verify_len, L_min, gamma + 1).
+ *   Positions k < L_min are always verified and their survivals count in tau.
+ *   Candidates are positions L_min <= k < L_max with s >= survival_eps,
+ *   sorted by (s descending, k ascending, r ascending).
+ *   tau(b) = B + sum over forced + the first b candidates, each term taken
+ *   at a resolution of 2^-40 (nearest, ties to even): exact and
+ *   order-independent.
+ *   T(b) = (bias + alpha[B]) + theta[B * L_min + b], summed in fp64;
+ *   ratio(b) = tau(b) / T(b) in fp64.
+ *   b* = the smallest b in [budget_lo, budget_hi] (clipped to
+ *   [0, #candidates]) with the largest ratio.
+ *   verify_lens[r] = L_min + #{candidates of r among the first b*}.
+ *
+ * Arguments:
+ *   B                  requests, 0 <= B <= DSPARK_MAX_BATCH,
+ *                      B * gamma <= DSPARK_MAX_CANDIDATES
+ *   gamma              drafted positions per request, 1..DSPARK_MAX_GAMMA
+ *   kind, conf         [B, gamma] float32 as given by `kind`
+ *   sts_temp           [gamma] float32 STS temperatures (CONF_LOGITS only;
+ *                      otherwise ignored, may be NULL)
+ *   min_verify_len, max_verify_len   clamped as above
+ *   survival_eps       candidates below it are dropped (equal is kept)
+ *   budget_lo, budget_hi  extra-row budget range; budget_hi < 0 means no
+ *                      upper limit; budget_lo > budget_hi >= 0 is invalid
+ *   cost_bias          ms
+ *   cost_alpha         [alpha_len] float32, alpha(bs) in ms; alpha_len > B
+ *   cost_theta         [theta_len] float32, theta(M) in ms for M = 0..;
+ *                      theta_len > B * L_max
+ *   verify_lens        out [B] int32
+ *   plan_meta          out [4] int32: b*, #candidates, status bits,
+ *                      B * L_min + b* (total verify rows before tier rounding)
+ *   plan_val           out [2] double: tau(b*), ratio(b*) (tokens per ms)
+ *   survival_out       out [B, gamma] float32 survivals, or NULL
+ *   sweep_out          out [B * gamma + 1][2] double (tau(b), ratio(b)) for
+ *                      b = 0..#candidates and NaN beyond, or NULL
+ * Data errors: a bad cost value at a considered budget sets
+ *   DSPARK_DATA_BAD_COST. A NaN/out-of-range confidence or survival, an
+ *   increasing survival, or a non-positive/non-finite temperature sets
+ *   DSPARK_DATA_BAD_CONF. Either way verify_lens = L_max for every request
+ *   (the static window), plan_meta = {-1, -1, status, B * L_max},
+ *   plan_val = NaN and sweep_out = NaN.
+ */
+dspark_status dspark_plan(int32_t B, int32_t gamma, dspark_input kind, const float* conf,
+                          const float* sts_temp, int32_t min_verify_len,
+                          int32_t max_verify_len, float survival_eps, int32_t budget_lo,
+                          int32_t budget_hi, float cost_bias, const float* cost_alpha,
+                          int32_t alpha_len, const float* cost_theta, int32_t theta_len,
+                          int32_t* verify_lens, int32_t* plan_meta, double* plan_val,
+                          float* survival_out, double* sweep_out, void* stream);
+
+/*
+ * dspark_pack - compact ragged verify layout.
+ *
+ * Defined by [Budget] §五 and §六 (compact RaggedVerifyLayout; cu_seqlens_q
+ * is the exclusive prefix sum of verify_lens with a leading 0, e.g.
+ * [2,1,4] -> [0,2,3,7]), [Round] §三 (verify ids are the anchor followed by
+ * the drafts; compact mode front-packs the anchor plus the selected draft
+ * prefix), [SGLang] and [CSSD] (the packed total is rounded up to the
+ * smallest captured tier that holds it).
+ *
+ *   cu_seqlens[0] = 0, cu_seqlens[r+1] = cu_seqlens[r] + verify_lens[r]
+ *   row cu[r] + j (j < verify_lens[r]): packed_ids = j ? draft_tokens[r, j-1]
+ *     : anchor_ids[r]; packed_req = r; packed_pos = prefix_lens[r] + j
+ *     (just j if prefix_lens is NULL)
+ *   pad rows [total, tier): packed_ids = 0, packed_req = -1, packed_pos = 0
+ *
+ * Arguments:
+ *   B, gamma           as for dspark_plan (B <= DSPARK_MAX_BATCH)
+ *   verify_lens        [B] int32, each in [1, gamma + 1]
+ *   anchor_ids         [B] int32 root-row token per request
+ *   draft_tokens       [B, gamma] int32
+ *   tiers_host         HOST array of num_tiers int32, strictly ascending,
+ *                      1 <= num_tiers <= DSPARK_MAX_TIERS, first >= 1,
+ *                      last >= B * (gamma + 1); read during the call only
+ *   prefix_lens        [B] int32 or NULL
+ *   cu_seqlens         out [B + 1] int32
+ *   packed_ids         out, capacity tiers_host[num_tiers - 1] int32
+ *   packed_req, packed_pos  out, same capacity, or NULL
+ *   pack_meta          out [3] int32: total, tier, status bits
+ * Only rows [0, tier) are written.
+ * Data errors: a length outside [1, gamma + 1] sets DSPARK_DATA_BAD_LENS and
+ * is clamped into that range before packing.
+ */
+dspark_status dspark_pack(int32_t B, int32_t gamma, const int32_t* verify_lens,
+                          const int32_t* anchor_ids, const int32_t* draft_tokens,
+                          const int32_t* tiers_host, int32_t num_tiers,
+                          const int32_t* prefix_lens, int32_t* cu_seqlens,
+                          int32_t* packed_ids, int32_t* packed_req, int32_t* packed_pos,
+                          int32_t* pack_meta, void* stream);
+
+/*
+ * dspark_accept - greedy accept over packed target logits.
+ *
+ * Defined by [Round] §四 and §五 (AcceptGreedy: target_predict =
+ * argmax(target_logits); draft k is checked against the prediction of verify
+ * row k-1; correct_len counts the leading matches and stops at the first
+ * mismatch; bonus is the prediction of the last valid input row;
+ * FinalizeAcceptLens commit_lens = correct_len + 1 and new_seq_lens =
+ * prefix_lens + commit_lens; BuildOutTokens out[:, :gamma] = drafts, then
+ * out[r, correct_len] = bonus), [Budget] §二 (prefix_mask = positions <
+ * num_correct_drafts) and [Budget] §三 (the cap: at most verify_len - 1
+ * drafts can be accepted).
+ *
+ * The argmax compares values as float32 (bfloat16 widens exactly). -0 equals
+ * +0, NaN ranks above every number, and the lowest index wins ties.
+ * out_tokens[r, gamma] starts at -1.
+ *
+ * Arguments:
+ *   B, gamma, V        requests, drafted positions, vocabulary
+ *                      (1 <= V <= DSPARK_MAX_VOCAB)
+ *   dt                 element type of packed_logits
+ *   packed_logits      [max_rows, ld] rows; 16-byte aligned; ld * element
+ *                      size a multiple of 16 bytes; ld >= V
+ *   max_rows           rows the logits buffer holds (>= the packed total;
+ *                      rows at or beyond it are never read)
+ *   cu_seqlens         [B + 1] int32 as written by dspark_pack; the total
+ *                      cu_seqlens[B] is read on the device
+ *   draft_tokens       [B, gamma] int32
+ *   prefix_lens        [B] int32 or NULL (then new_seq_lens must be NULL)
+ *   row_argmax         out [max_rows] int32; rows < total are written
+ *   num_correct, bonus, commit_lens   out [B] int32
+ *   out_tokens         out [B, gamma + 1] int32
+ *   new_seq_lens       out [B] int32 or NULL
+ *   prefix_mask        out [B, gamma] uint8 or NULL
+ *   accept_meta        out [2] int32: cu_seqlens[B], status bits
+ *   workspace          device scratch of dspark_accept_workspace_size() bytes,
+ *                      256-byte aligned, ZERO-FILLED before its first use;
+ *                      every call leaves it zero-filled again. Calls that
+ *                      share a workspace must not overlap in time.
+ * Data errors: a request whose rows are not 1..gamma+1 rows inside
+ *   [0, min(cu_seqlens[B], max_rows)) sets DSPARK_DATA_BAD_LENS and gets
+ *   num_correct 0, bonus -1, commit 0, out_tokens -1, prefix_mask 0,
+ *   new_seq = prefix.
+ */
+dspark_status dspark_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,
+                            const void* packed_logits, int64_t ld, int32_t max_rows,
+                            const int32_t* cu_seqlens, const int32_t* draft_tokens,
+                            const int32_t* prefix_lens, int32_t* row_argmax,
+                            int32_t* num_correct, int32_t* bonus, int32_t* commit_lens,
+                            int32_t* out_tokens, int32_t* new_seq_lens, uint8_t* prefix_mask,
+                            int32_t* accept_meta, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Bytes of workspace dspark_accept needs for `max_rows` rows of V elements of
+ * type dt (0 for invalid sizes). */
+size_t dspark_accept_workspace_size(int32_t max_rows, int32_t V, dspark_dtype dt);
+
+/*
+ * dspark_tv_accept - soft accept-rate and its cumulative product.
+ *
+ * Defined by [Budget] §二 (DeepSpec target: accept_rate = 1 - 0.5 *
+ * sum |softmax(draft_logits) - softmax(target_logits)|, equal to
+ * sum_x min(p, q) under rejection sampling; confidence_prefix_targets =
+ * accept_rate.cumprod).
+ *
+ *   a[r, k] = sum_x min(softmax(q_{r,k})_x, softmax(p_{r,k-1})_x), clamped to
+ *   [0, 1]; S[r, k] = RN32(S[r, k-1] * a[r, k]).
+ * The draft row that proposed draft k pairs with target row k-1, the row that
+ * predicts position k.
+ *
+ * Arguments:
+ *   B, gamma, V, dt    as for dspark_accept
+ *   draft_logits       q rows: row r * gamma + (k - 1); stride ld_q elements
+ *   target_logits      p rows: row r * target_rows_per_req + (k - 1); stride ld_p
+ *   target_rows_per_req >= gamma (gamma + 1 for the strided verify layout)
+ *   Both logit buffers: 16-byte aligned, ld * element size multiple of 16.
+ *   accept_rate        out [B, gamma] float32
+ *   survival           out [B, gamma] float32 (usable as DSPARK_IN_SURVIVAL)
+ * Accuracy: float32 with exp2/log2 hardware approximations; within 1e-5
+ * absolute of an fp64 evaluation for the vocabularies above.
+ */
+dspark_status dspark_tv_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,
+                               const void* draft_logits, int64_t ld_q,
+                               const void* target_logits, int64_t ld_p,
+                               int32_t target_rows_per_req, float* accept_rate,
+                               float* survival, void* stream);
+
+/* Name of a status code (static string). */
+const char* dspark_status_str(dspark_status s);
+
+/* Thread-local detail of the last non-OK status on this thread ("" if none). */
+const char* dspark_last_error(void);
+
+/* ABI version: (major << 16) | minor. */
+int32_t dspark_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

@@ -1,0 +1,202 @@
+"""C-ABI checks that need no GPU.
+
+* libdspark.so loads and exports every function include/dspark.h declares.
+* Argument errors are caught on the host, before any launch, with the
+  documented status codes. No call here reaches a kernel launch.
+* The device sigmoid, compiled for the host, equals the oracle's correctly
+  rounded sigmoid bit for bit on both of its paths (the fp64 fast path and
+  the double-double path that real inputs reach about once per million).
+"""
+
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+from dspark_verify_scheduling_amd import _lib
+from oracle.sigmoid import nearest_f32, sigmoid32, sigmoid_decimal
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "dspark.h"
+
+NULL = None
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def _declared():
+    text = HEADER.read_text(encoding="utf-8")
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("dspark_plan", "dspark_pack", "dspark_accept", "dspark_tv_accept",
+              "dspark_accept_workspace_size", "dspark_status_str", "dspark_last_error",
+              "dspark_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert set(_lib.SIGNATURES) == set(_declared())
+    assert lib.dspark_version() >> 16 == 1
+
+
+def test_status_strings():
+    assert _lib.status_str(0) == "DSPARK_OK"
+    assert _lib.status_str(2) == "DSPARK_E_UNSUPPORTED"
+
+
+def _plan(**kw):
+    a = dict(B=4, gamma=4, kind=0, conf=FAKE, temp=FAKE, mn=1, mx=5, eps=1e-3, lo=0, hi=-1,
+             bias=0.5, alpha=FAKE, alen=5, theta=FAKE, tlen=21, lens=FAKE, meta=FAKE, val=FAKE,
+             surv=NULL, sweep=NULL, stream=NULL)
+    a.update(kw)
+    return _lib.lib().dspark_plan(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), _lib.E_INVALID),
+    (dict(gamma=0), _lib.E_INVALID),
+    (dict(gamma=65), _lib.E_INVALID),
+    (dict(kind=7), _lib.E_INVALID),
+    (dict(B=1025, gamma=8), _lib.E_UNSUPPORTED),
+    (dict(B=8193, gamma=1, alen=9000, tlen=20000), _lib.E_UNSUPPORTED),
+    (dict(conf=NULL), _lib.E_INVALID),
+    (dict(temp=NULL), _lib.E_INVALID),
+    (dict(alpha=NULL), _lib.E_INVALID),
+    (dict(lens=NULL), _lib.E_INVALID),
+    (dict(lo=-1), _lib.E_INVALID),
+    (dict(lo=3, hi=2), _lib.E_INVALID),
+    (dict(eps=float("nan")), _lib.E_INVALID),
+    (dict(alen=4), _lib.E_INVALID),
+    (dict(tlen=20), _lib.E_INVALID),  # needs > B * L_max = 20
+])
+def test_plan_argument_errors(kw, code):
+    assert _plan(**kw) == code
+    assert _lib.last_error() != ""
+
+
+def _pack(tiers, **kw):
+    arr = (ctypes.c_int32 * len(tiers))(*tiers)
+    a = dict(B=3, gamma=3, lens=FAKE, anchors=FAKE, drafts=FAKE,
+             tiers=ctypes.cast(arr, ctypes.c_void_p), ntiers=len(tiers), prefix=NULL, cu=FAKE,
+             ids=FAKE, req=NULL, pos=NULL, meta=FAKE, stream=NULL)
+    a.update(kw)
+    return _lib.lib().dspark_pack(*a.values())
+
+
+def test_pack_argument_errors():
+    assert _pack([4, 8, 12], B=-1) == _lib.E_INVALID
+    assert _pack([4, 8, 8]) == _lib.E_INVALID  # not strictly ascending
+    assert _pack([4, 8, 11]) == _lib.E_INVALID  # last tier < B * (gamma + 1)
+    assert _pack([0, 12]) == _lib.E_INVALID
+    assert _pack([12], ntiers=0) == _lib.E_INVALID
+    assert _pack(list(range(1, 34))) == _lib.E_INVALID  # more than 32 tiers
+    assert _pack([12], ids=NULL) == _lib.E_INVALID
+    assert _pack([12], lens=NULL) == _lib.E_INVALID
+    assert _pack([12], B=8193, gamma=1) == _lib.E_UNSUPPORTED
+
+
+def _accept(**kw):
+    a = dict(B=2, gamma=4, V=1024, dt=_lib.BF16, logits=FAKE, ld=1024, max_rows=10, cu=FAKE,
+             drafts=FAKE, prefix=FAKE, am=FAKE, nc=FAKE, bonus=FAKE, commit=FAKE, out=FAKE,
+             newseq=FAKE, mask=NULL, meta=FAKE, ws=ctypes.c_void_p(0x10000), wsb=1 << 20,
+             stream=NULL)
+    a.update(kw)
+    return _lib.lib().dspark_accept(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(V=0), _lib.E_INVALID),
+    (dict(V=262145, ld=262152), _lib.E_UNSUPPORTED),
+    (dict(dt=5), _lib.E_UNSUPPORTED),
+    (dict(ld=1000), _lib.E_INVALID),  # ld < V
+    (dict(V=1001, ld=1001), _lib.E_INVALID),  # 2002-byte rows: not a multiple of 16
+    (dict(logits=ctypes.c_void_p(0x1008)), _lib.E_INVALID),  # misaligned
+    (dict(cu=NULL), _lib.E_INVALID),
+    (dict(out=NULL), _lib.E_INVALID),
+    (dict(prefix=NULL), _lib.E_INVALID),  # new_seq_lens needs prefix_lens
+    (dict(ws=NULL), _lib.E_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x10010)), _lib.E_WORKSPACE),  # not 256-byte aligned
+    (dict(wsb=64), _lib.E_WORKSPACE),
+    (dict(gamma=65), _lib.E_INVALID),
+    (dict(max_rows=-1), _lib.E_INVALID),
+])
+def test_accept_argument_errors(kw, code):
+    assert _accept(**kw) == code
+
+
+def test_accept_workspace_size():
+    f = _lib.lib().dspark_accept_workspace_size
+    # 129280 bf16 = 16160 16-byte vectors -> 8 units per row
+    assert f(2304, 129280, _lib.BF16) == 256 + 9216 + 2304 * 8 * 8
+    assert f(10, 0, _lib.BF16) == 0 and f(-1, 10, _lib.F32) == 0
+    assert f(1, 1, _lib.F32) >= 256 + 8
+
+
+def test_tv_argument_errors():
+    call = _lib.lib().dspark_tv_accept
+    ok = dict(B=2, gamma=3, V=1024, dt=_lib.BF16, q=FAKE, ldq=1024, p=FAKE, ldp=1024, rpr=4,
+              a=FAKE, s=FAKE, stream=NULL)
+
+    def run(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return call(*d.values())
+
+    assert run(rpr=2) == _lib.E_INVALID
+    assert run(ldq=1000) == _lib.E_INVALID
+    assert run(q=ctypes.c_void_p(0x1004)) == _lib.E_INVALID
+    assert run(a=NULL) == _lib.E_INVALID
+    assert run(V=300000, ldq=300000, ldp=300000) == _lib.E_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- sigmoid logic on the CPU
+
+def _host_sigmoid(x, force_slow=False):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty_like(x)
+    slow = np.zeros(x.shape, dtype=np.uint8)
+    _lib.hostcheck().dspark_hostcheck_sigmoid(x.ctypes.data, y.ctypes.data, slow.ctypes.data,
+                                              x.size, 1 if force_slow else 0)
+    return y, slow
+
+
+def test_device_sigmoid_fast_path_matches_oracle():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([
+        rng.normal(0, 4, 200000), rng.uniform(-104, 18, 50000),
+        [0.0, -0.0, 17.3, 17.33, 17.34, 17.5, -87.3, -90.0, -103.9, -104.0, np.inf, -np.inf],
+    ]).astype(np.float32)
+    y, _ = _host_sigmoid(x)
+    assert np.array_equal(y.view(np.uint32), sigmoid32(x).view(np.uint32))
+
+
+def test_device_sigmoid_exact_path_matches_oracle():
+    rng = np.random.default_rng(6)
+    x = np.concatenate([rng.normal(0, 5, 3000), rng.uniform(-103.9, 17.4, 1000)]).astype(np.float32)
+    y, slow = _host_sigmoid(x, force_slow=True)
+    assert slow[(x > -104) & (x < 17.5)].all()
+    assert np.array_equal(y.view(np.uint32), sigmoid32(x).view(np.uint32))
+
+
+def test_inputs_that_reach_the_exact_path():
+    # scan random inputs until the fast path declines some; those must still be exact
+    rng = np.random.default_rng(7)
+    hits = []
+    for _ in range(40):
+        x = rng.uniform(-30, 18, 1_000_000).astype(np.float32)
+        y, slow = _host_sigmoid(x)
+        idx = np.flatnonzero(slow)
+        hits.extend((x[i], y[i]) for i in idx)
+        if len(hits) >= 8:
+            break
+    assert len(hits) >= 1
+    for xv, yv in hits:
+        assert np.float32(yv).view(np.uint32) == nearest_f32(sigmoid_decimal(float(xv))).view(np.uint32)

@@ -1,0 +1,164 @@
+"""GPU parity for the soft accept-rate stage and the config-4 chain.
+
+Tolerances: the accept rate a within 1e-5 absolute of the fp64 oracle, and the
+cumulative product S_k within 1e-5 * k. Downstream of TV the planner is
+checked stage-isolated: both sides get the oracle's survivals, rounded to
+float32, and must agree bit for bit. In the chained run the GPU planner
+consumes the GPU's own survivals. Its integer decisions may then differ from
+the oracle's only at a near-tie, which the test verifies from the oracle's
+numbers.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.tv import tv_pair
+from workloads import f32_to_bf16_bits, make
+from _gpu import accept, gather_packed, logits_up, pack, plan, say, tv
+
+pytestmark = pytest.mark.gpu
+
+A_TOL = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu(hip):
+    return hip
+
+
+def _rand_logits(rng, shape, sigma, dt):
+    x = rng.normal(0, sigma, shape).astype(np.float32)
+    return f32_to_bf16_bits(x) if dt == 1 else x
+
+
+@pytest.mark.parametrize("V,pad,dt", [(257, 0, 1), (257, 7, 1), (1000, 0, 0), (1001, 3, 0),
+                                      (4096, 8, 1), (32000, 0, 1), (3, 1, 0)])
+def test_tv_small(V, pad, dt):
+    rng = np.random.default_rng(V * 7 + pad + dt)
+    B, G = 3, 4
+    epv = 8 if dt == 1 else 4
+    ld = V + pad
+    ld += (-ld) % epv  # rows must start on 16-byte boundaries
+    q = _rand_logits(rng, (B, G, V), 2.0, dt)
+    p = _rand_logits(rng, (B, G + 1, V), 2.0, dt)
+    q[0, 1] = p[0, 1]  # one identical pair -> a = 1
+    nan = np.uint16(0x7FC1) if dt == 1 else np.float32(np.nan)
+    qs = np.full((B * G, ld), nan, dtype=q.dtype)
+    ps = np.full((B * (G + 1), ld), nan, dtype=p.dtype)  # stride padding: never read
+    qs[:, :V] = q.reshape(B * G, V)
+    ps[:, :V] = p.reshape(B * (G + 1), V)
+    a, S = tv(B, G, V, dt, logits_up(qs, dt), ld, logits_up(ps, dt), ld, G + 1, tag=f"V={V}")
+    ref_a, ref_S = oracle.tv_accept(B, G, q, p, "bf16" if dt == 1 else "f32")
+    assert np.all(np.abs(a - ref_a) <= A_TOL), np.abs(a - ref_a).max()
+    k = np.arange(1, G + 1)
+    assert np.all(np.abs(S - ref_S) <= A_TOL * k)
+    assert abs(a[0, 1] - 1.0) <= 1e-6
+    assert np.all((a >= 0) & (a <= 1))
+    # S is the float32 running product of a
+    for r in range(B):
+        acc = np.float32(1)
+        for kk in range(G):
+            acc = a[r, kk] if kk == 0 else np.float32(acc * a[r, kk])
+            assert S[r, kk] == acc
+
+
+def test_tv_closed_forms():
+    # uniform q against one spike in p: a = 1/V + (V-1)/(e^L + V - 1)
+    V, L = 4096, 6.0
+    B, G = 1, 2
+    q = np.zeros((B, G, V), np.float32)
+    p = np.zeros((B, G + 1, V), np.float32)
+    p[0, 0, 17] = L
+    p[0, 1, 4000] = L
+    q[0, 1, 4000] = L  # identical pair
+    a, _ = tv(B, G, V, 0, logits_up(q.reshape(-1, V), 0), V, logits_up(p.reshape(-1, V), 0), V,
+              G + 1, tag="closed form")
+    expect = 1.0 / V + (V - 1) / (np.exp(L) + V - 1)
+    assert abs(a[0, 0] - expect) <= A_TOL
+    assert abs(a[0, 1] - 1.0) <= 1e-6
+
+
+@pytest.fixture(scope="module")
+def cfg4():
+    say("generating config 4 (q and p logits)")
+    w = make(4)
+    say("oracle TV over all pairs of config 4")
+    a, S = oracle.tv_accept(w.B, w.gamma, w.draft_logits, w.target, "bf16")
+    return w, a, S
+
+
+def _gpu_tv_full(w):
+    q_t = logits_up(w.draft_logits.reshape(w.B * w.gamma, w.V), 1)
+    p_t = logits_up(w.target.reshape(w.B * (w.gamma + 1), w.V), 1)
+    out = tv(w.B, w.gamma, w.V, 1, q_t, w.V, p_t, w.V, w.gamma + 1, tag="cfg4")
+    del q_t, p_t
+    torch.cuda.empty_cache()
+    return out
+
+
+def test_tv_config4_full(cfg4):
+    w, ref_a, ref_S = cfg4
+    a, S = _gpu_tv_full(w)
+    err = np.abs(a - ref_a)
+    say(f"cfg4 TV: max |a - oracle| = {err.max():.3e}")
+    assert err.max() <= A_TOL
+    k = np.arange(1, w.gamma + 1)
+    assert np.all(np.abs(S - ref_S) <= A_TOL * k)
+    assert np.all(S[:, 1:] <= S[:, :-1])
+
+
+def _plan_survival(w, S32, gpu: bool):
+    args = (w.B, w.gamma, oracle.IN_SURVIVAL, S32, None, w.min_len, w.max_len, w.eps, w.b_lo,
+            w.b_hi, w.bias, w.alpha, w.theta)
+    return plan(*args, tag="cfg4 survival") if gpu else oracle.plan(*args)
+
+
+def test_config4_planner_stage_isolated(cfg4):
+    w, _, ref_S = cfg4
+    S32 = ref_S.astype(np.float32)
+    got = _plan_survival(w, S32, True)
+    ref = _plan_survival(w, S32, False)
+    for k in ("verify_lens", "meta", "val", "survival", "sweep"):
+        assert np.array_equal(got[k], ref[k], equal_nan=True), k
+
+
+def test_config4_pack_accept_stage_isolated(cfg4):
+    w, _, ref_S = cfg4
+    lens = _plan_survival(w, ref_S.astype(np.float32), False)["verify_lens"]
+    ref_pack = oracle.pack(w.B, w.gamma, lens, w.anchors, w.drafts, w.tiers, w.prefix_lens)
+    got_pack = pack(w.B, w.gamma, lens, w.anchors, w.drafts, w.tiers, w.prefix_lens, tag="cfg4")
+    tier = int(ref_pack["meta"][1])
+    assert np.array_equal(got_pack["meta"], ref_pack["meta"])
+    assert np.array_equal(got_pack["cu_seqlens"], ref_pack["cu_seqlens"])
+    assert np.array_equal(got_pack["ids"][:tier], ref_pack["ids"])
+    cu = ref_pack["cu_seqlens"]
+    rows = gather_packed(w.target, cu, lens, tier)
+    got = accept(w.B, w.gamma, w.V, 1, rows, w.V, cu, w.drafts, w.prefix_lens, tag="cfg4")
+    ref = oracle.accept(w.B, w.gamma, rows, "bf16", cu, w.drafts, w.prefix_lens)
+    total = int(cu[-1])
+    assert np.array_equal(got["row_argmax"][:total], ref["row_argmax"])
+    for k in ("num_correct", "bonus", "commit", "out_tokens", "prefix_mask", "new_seq", "meta"):
+        assert np.array_equal(got[k], ref[k]), k
+
+
+def test_config4_chained(cfg4):
+    w, ref_a, ref_S = cfg4
+    a, S = _gpu_tv_full(w)
+    got = _plan_survival(w, S, True)
+    ref = _plan_survival(w, ref_S.astype(np.float32), False)
+    if np.array_equal(got["verify_lens"], ref["verify_lens"]):
+        return
+    # a disagreement must come from a near-tie the survival error can flip:
+    # either two survivals straddling the cut, or two budgets with ratios
+    # equal to within the propagated error
+    n_diff = int(np.sum(got["verify_lens"] != ref["verify_lens"]))
+    say(f"cfg4 chained: {n_diff} requests differ; checking for a near-tie")
+    b_star = int(ref["meta"][0])
+    s = np.sort(ref["survival"].reshape(-1))[::-1]
+    gap = abs(float(s[b_star - 1]) - float(s[b_star])) if 0 < b_star < s.size else np.inf
+    sw = ref["sweep"][:, 1]
+    gb = int(got["meta"][0])
+    ratio_gap = abs(sw[gb] - sw[b_star]) / sw[b_star] if 0 <= gb < sw.size else np.inf
+    assert gap <= 2e-5 or ratio_gap <= 2e-5, (gap, ratio_gap)
