@@ -172,7 +172,7 @@ class AcceptOutputs(NamedTuple):
     new_seq_lens: Optional[torch.Tensor]
     prefix_mask: Optional[torch.Tensor]  # [B, gamma] uint8
     accept_meta: torch.Tensor  # [2] int32
-    workspace: torch.Tensor  # uint8, zero-filled
+    workspace: torch.Tensor  # uint8 scratch (no initialization needed)
 
 
 def dspark_accept_workspace_size(max_rows: int, V: int, dt: int) -> int:
@@ -192,7 +192,7 @@ def alloc_accept_outputs(B: int, gamma: int, max_rows: int, V: int, dt: int, dev
         torch.empty(B, dtype=i32, device=device) if new_seq else None,
         torch.empty(B, gamma, dtype=torch.uint8, device=device) if mask else None,
         torch.empty(2, dtype=i32, device=device),
-        torch.zeros(max(ws, 256), dtype=torch.uint8, device=device),
+        torch.empty(max(ws, 256), dtype=torch.uint8, device=device),
     )
 
 

@@ -12,23 +12,26 @@
 //     positions < num_correct_drafts; a match after the first mismatch is
 //     not accepted.
 //
-// The vocabulary pass is a pure stream of total*V elements (about 596 MB at
-// 2304 rows x 129280 bf16) read once, so the kernel is built for HBM
-// bandwidth, not for matrix cores:
-//   * a persistent grid of 256-thread workgroups walks (row, chunk) units of
-//     up to 2048 16-byte vectors (32 KB); eight vectors per thread are in
-//     flight per unit, and eight resident workgroups per CU keep about
-//     256 KB of loads outstanding per CU;
-//   * loads are 16-byte nontemporal (the logits are read exactly once);
-//   * bf16 elements become 16-bit order keys with packed 16-bit integer ops
-//     (two elements per instruction). NaN maps to the top, -0 and +0 to the
-//     same key. Each key carries its in-thread position in the low half of a
-//     32-bit word, so one v_max3_u32 folds two elements into the running
-//     (value, lowest index) maximum;
-//   * a unit's maximum goes to a workspace slot. The last unit of a row
-//     (atomic counter) merges the row; the last row overall finalizes every
-//     request. No workgroup ever waits for another, and the counters return
-//     to zero before the kernel ends.
+// Two kernels on the caller's stream:
+//
+// 1. accept_argmax_kernel streams the total * V logits once. One
+//    256-thread workgroup per (row, unit) of up to 2048 16-byte vectors
+//    (32 KB); eight nontemporal 16-byte loads per thread are in flight before
+//    any arithmetic. For bf16 the common case costs two packed 16-bit
+//    instructions per pair of elements: a signed max of the raw bits (the
+//    order of non-negative bf16 values) and an unsigned max that detects
+//    negative NaNs. When the unit's maximum is positive and it holds no NaN,
+//    only the lanes that hold the maximum search their registers for its
+//    first position. Otherwise the unit is redone exactly from the same
+//    registers with a total-order key (NaN highest, -0 == +0, lowest index
+//    wins). Each unit writes one 64-bit (key, index) partial. The kernel has
+//    no atomics and no cross-workgroup waits.
+// 2. accept_finalize_kernel: one wave per request merges its rows' partials,
+//    counts the leading matches with a ballot, and writes the outputs; a
+//    grid-stride pass writes the row argmax of every packed row.
+//
+// The partials are fully rewritten by every call, so the workspace needs no
+// initialization and holds no state between calls.
 #include "common.h"
 
 namespace dspark {
@@ -39,12 +42,21 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 
+constexpr int kWaves = kAccThreads / kWave;
+
+// Reinterpret a dword as two 16-bit lanes. The dword is taken by value: with
+// this toolchain, __builtin_bit_cast applied directly to an ext_vector element
+// (d[j][w]) reads element 0 of the vector whatever the subscript.
+__device__ inline i16x2 as_i16x2(unsigned int x) { return __builtin_bit_cast(i16x2, x); }
+__device__ inline u16x2 as_u16x2(unsigned int x) { return __builtin_bit_cast(u16x2, x); }
+
 // 16-bit order key of two bf16 values packed in one dword (each half
 // independently): larger value -> larger key; -0 == +0; NaN above +inf.
-//   m = sign mask (0xFFFF for negatives); key = (h ^ (m | 0x8000)) - m maps
-//   the sign-magnitude bits to an order-preserving integer (-0 and +0 both to
+//   m = sign mask (0xFFFF for negatives); (h ^ (m | 0x8000)) - m maps the
+//   sign-magnitude bits to an order-preserving integer (-0 and +0 both to
 //   0x8000, -inf to 0x0080). Subtracting 0x80 moves -inf to 0 and every NaN to
-//   0xFF01..0xFFFF (wrapping), and the final min folds all NaNs onto 0xFF01.
+//   0xFF01..0xFFFF (wrapping); the final min folds all NaNs onto 0xFF01.
+//   A positive non-NaN h maps to h + 0x7F80.
 __device__ inline unsigned int bf16x2_keys(unsigned int w) {
   const i16x2 v = __builtin_bit_cast(i16x2, w);
   const i16x2 m = v >> (i16x2){15, 15};
@@ -64,37 +76,38 @@ __device__ inline unsigned int f32_key(unsigned int b) {
   return k < 0xFF000001u ? k : 0xFF000001u;
 }
 
+// Partial of a unit: key in the high word, 0xFFFFFFFF - index in the low word,
+// so the maximum is the largest value at the lowest index. 0 = no element.
 __device__ inline unsigned long long pack_best(unsigned int key, unsigned int gidx) {
   return ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - gidx);
 }
 
-__device__ inline unsigned long long wave_max_u64(unsigned long long v) {
+template <typename T>
+__device__ inline T wave_max(T v) {
   for (int off = kWave / 2; off > 0; off >>= 1) {
-    const unsigned long long o = __shfl_xor(v, off, kWave);
+    const T o = __shfl_xor(v, off, kWave);
     v = o > v ? o : v;
   }
   return v;
 }
 
-// Best (key, lowest index) of one unit for this thread, as a packed u64
-// (0 if the thread owns no element of the unit).
-template <dspark_dtype DT>
-__device__ inline unsigned long long unit_scan(const AcceptArgs& a, int row, int chunk) {
-  const int tid = threadIdx.x;
-  const u32x4* rp = reinterpret_cast<const u32x4*>(a.logits + (size_t)row * a.ld_bytes);
-  const int v0 = chunk * a.chunk_vecs;
-  const int v1 = min(v0 + a.chunk_vecs, a.nvec);
-  u32x4 d[kAccVecsPerThread];
-#pragma unroll
-  for (int j = 0; j < kAccVecsPerThread; ++j) {
-    const int v = v0 + j * kAccThreads + tid;
-    if (v < v1) d[j] = __builtin_nontemporal_load(rp + v);
+template <typename T>
+__device__ inline T wave_min(T v) {
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const T o = __shfl_xor(v, off, kWave);
+    v = o < v ? o : v;
   }
-  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;  // elements per 16-byte vector
+  return v;
+}
+
+// Exact per-thread (key, lowest index) over this thread's elements of a unit.
+template <dspark_dtype DT>
+__device__ inline unsigned long long exact_thread_best(const u32x4* d, int v0, int v1) {
+  const int tid = threadIdx.x;
+  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
   unsigned long long best = 0;
   if constexpr (DT == DSPARK_BF16) {
-    // packed: key << 16 | (0xFFFF - p), p = j * 8 + element (in-thread order)
-    const unsigned int hi_mask = 0xFFFF0000u;
+    // key << 16 | (0xFFFF - p) with p = j * 8 + element: the in-thread order
     unsigned int b32 = 0;
 #pragma unroll
     for (int j = 0; j < kAccVecsPerThread; ++j) {
@@ -104,7 +117,7 @@ __device__ inline unsigned long long unit_scan(const AcceptArgs& a, int row, int
           const unsigned int k = bf16x2_keys(d[j][w]);
           const unsigned int p = (unsigned int)(j * 8 + w * 2);
           const unsigned int lo = (k << 16) | (0xFFFFu - p);
-          const unsigned int hi = (k & hi_mask) | (0xFFFFu - (p + 1));
+          const unsigned int hi = (k & 0xFFFF0000u) | (0xFFFFu - (p + 1));
           b32 = max(b32, max(lo, hi));
         }
       }
@@ -134,142 +147,193 @@ __device__ inline unsigned long long unit_scan(const AcceptArgs& a, int row, int
       best = pack_best((unsigned int)(b64 >> 32), v * kEpv + (p & 3u));
     }
   }
-  // elements after the last whole vector (V * size not a multiple of 16)
-  if (a.tail && chunk == a.chunks - 1 && tid == 0) {
-    const unsigned char* row_p = a.logits + (size_t)row * a.ld_bytes;
-    for (int t = 0; t < a.tail; ++t) {
-      const unsigned int gi = (unsigned int)(a.nvec * kEpv + t);
-      unsigned int key;
-      if constexpr (DT == DSPARK_BF16) {
-        const unsigned short h = reinterpret_cast<const unsigned short*>(row_p)[gi];
-        key = bf16x2_keys((unsigned int)h) & 0xFFFFu;
-      } else {
-        key = f32_key(reinterpret_cast<const unsigned int*>(row_p)[gi]);
-      }
-      const unsigned long long c = pack_best(key, gi);
-      best = c > best ? c : best;
-    }
-  }
   return best;
 }
 
-__device__ inline int load_am(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+template <dspark_dtype DT>
+__global__ __launch_bounds__(kAccThreads) void accept_argmax_kernel(AcceptArgs a) {
+  __shared__ int s_max[kWaves];
+  __shared__ unsigned int s_idx[kWaves];
+  __shared__ unsigned long long s_best[kWaves];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int total = a.cu[a.B];
+  const int total_eff = min(max(total, 0), a.max_rows);
+  if (blockIdx.x == 0 && tid == 0) {
+    a.meta[0] = total;
+    a.meta[1] = total != total_eff ? DSPARK_DATA_BAD_LENS : 0;
+  }
+  const int u = blockIdx.x;
+  if (u >= total_eff * a.chunks) return;
+  const int row = u / a.chunks;
+  const int chunk = u - row * a.chunks;
+  const u32x4* rp = reinterpret_cast<const u32x4*>(a.logits + (size_t)row * a.ld_bytes);
+  const int v0 = chunk * a.chunk_vecs;
+  const int v1 = min(v0 + a.chunk_vecs, a.nvec);
+  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
+
+  u32x4 d[kAccVecsPerThread];
+#pragma unroll
+  for (int j = 0; j < kAccVecsPerThread; ++j) {
+    const int v = v0 + j * kAccThreads + tid;
+    // -0.0 fill: below any positive value, never a NaN
+    d[j] = (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    if (v < v1) d[j] = __builtin_nontemporal_load(rp + v);
+  }
+
+  unsigned long long best = 0;
+  bool exact = true;
+  if constexpr (DT == DSPARK_BF16) {
+    // fast path: raw signed-16 max and NaN detection
+    i16x2 mi = (i16x2){(short)0x8000, (short)0x8000};
+    u16x2 mu = (u16x2){0, 0};
+#pragma unroll
+    for (int j = 0; j < kAccVecsPerThread; ++j) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const unsigned int x = d[j][w];
+        mi = __builtin_elementwise_max(mi, as_i16x2(x));
+        mu = __builtin_elementwise_max(mu, as_u16x2(x));
+      }
+    }
+    const int lm = max((int)mi[0], (int)mi[1]);
+    const int lu = max((int)mu[0], (int)mu[1]);
+    // positive NaN: raw value above +inf (0x7F80); negative NaN: above 0xFF80 unsigned
+    int v = (lm > 0x7F80 || lu > 0xFF80) ? 0x7FFFFFFF : lm;
+    v = wave_max(v);
+    if (lane == 0) s_max[wave] = v;
+    __syncthreads();
+    int M = s_max[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = max(M, s_max[w]);
+    if (M > 0 && M <= 0x7F80) {  // uniform over the workgroup
+      exact = false;
+      unsigned int cand = 0xFFFFFFFFu;
+      if (lm == M) {
+        // this lane holds the maximum: its first position (lowest j, w, half)
+#pragma unroll
+        for (int j = kAccVecsPerThread - 1; j >= 0; --j) {
+#pragma unroll
+          for (int w = 3; w >= 0; --w) {
+            const unsigned int x = d[j][w];
+            const unsigned int base = (unsigned int)(v0 + j * kAccThreads + tid) * 8u + 2u * w;
+            if ((int)(short)(x >> 16) == M) cand = base + 1u;
+            if ((int)(short)(x & 0xFFFFu) == M) cand = base;
+          }
+        }
+      }
+      cand = wave_min(cand);
+      if (lane == 0) s_idx[wave] = cand;
+      __syncthreads();
+      if (tid == 0) {
+        unsigned int c = s_idx[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) c = min(c, s_idx[w]);
+        best = pack_best((unsigned int)M + 0x7F80u, c);
+      }
+    }
+  }
+  if (exact) {  // uniform over the workgroup
+    unsigned long long b = exact_thread_best<DT>(d, v0, v1);
+    b = wave_max(b);
+    if (lane == 0) s_best[wave] = b;
+    __syncthreads();
+    if (tid == 0) {
+      best = s_best[0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) best = s_best[w] > best ? s_best[w] : best;
+    }
+  }
+  if (tid == 0) {
+    // elements after the last whole vector (V * size not a multiple of 16)
+    if (a.tail && chunk == a.chunks - 1) {
+      const unsigned char* row_p = a.logits + (size_t)row * a.ld_bytes;
+      for (int t = 0; t < a.tail; ++t) {
+        const unsigned int gi = (unsigned int)(a.nvec * kEpv + t);
+        unsigned int key;
+        if constexpr (DT == DSPARK_BF16) {
+          key = bf16x2_keys((unsigned int)reinterpret_cast<const unsigned short*>(row_p)[gi]) &
+                0xFFFFu;
+        } else {
+          key = f32_key(reinterpret_cast<const unsigned int*>(row_p)[gi]);
+        }
+        const unsigned long long c = pack_best(key, gi);
+        best = c > best ? c : best;
+      }
+    }
+    a.partials[u] = best;
+  }
 }
 
-// Finalize every request (one workgroup). Row argmaxes come from other
-// workgroups, so they are read with agent-scope atomic loads after an
-// acquire fence.
-__device__ void finalize(const AcceptArgs& a, int total, int total_eff) {
-  __shared__ int s_status;
-  const int tid = threadIdx.x;
-  if (tid == 0) s_status = total != total_eff ? DSPARK_DATA_BAD_LENS : 0;
-  __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+__device__ inline int merge_row(const AcceptArgs& a, int row) {
+  const unsigned long long* p = a.partials + (size_t)row * a.chunks;
+  unsigned long long m = 0;
+  for (int c = 0; c < a.chunks; ++c) m = p[c] > m ? p[c] : m;
+  return (int)(0xFFFFFFFFu - (unsigned int)(m & 0xFFFFFFFFu));
+}
+
+// One wave per request (blockIdx.x = r), plus a grid-stride pass that writes
+// the argmax of every packed row.
+__global__ __launch_bounds__(kWave) void accept_finalize_kernel(AcceptArgs a) {
+  __shared__ int am[DSPARK_MAX_GAMMA + 1];
+  const int lane = threadIdx.x;
+  const int total = a.cu[a.B];
+  const int total_eff = min(max(total, 0), a.max_rows);
+  for (int i = blockIdx.x * kWave + lane; i < total_eff; i += gridDim.x * kWave) {
+    a.row_am[i] = merge_row(a, i);
+  }
+  const int r = blockIdx.x;
+  if (r >= a.B) return;
   const int G = a.gamma;
-  int bad = 0;
-  for (int r = tid; r < a.B; r += kAccThreads) {
-    const int c0 = a.cu[r], c1 = a.cu[r + 1];
-    const int len = c1 - c0;
-    const int prefix = a.prefix ? a.prefix[r] : 0;
-    const int32_t* dr = a.drafts + (size_t)r * G;
-    int32_t* out = a.out_tokens + (size_t)r * (G + 1);
-    if (!(c0 >= 0 && len >= 1 && len <= G + 1 && c1 <= total_eff)) {
-      bad = 1;
+  const int c0 = a.cu[r], c1 = a.cu[r + 1];
+  const int len = c1 - c0;
+  const int prefix = a.prefix ? a.prefix[r] : 0;
+  const int32_t* dr = a.drafts + (size_t)r * G;
+  int32_t* out = a.out_tokens + (size_t)r * (G + 1);
+  if (!(c0 >= 0 && len >= 1 && len <= G + 1 && c1 <= total_eff)) {
+    for (int j = lane; j <= G; j += kWave) out[j] = -1;
+    if (a.mask) {
+      for (int k = lane; k < G; k += kWave) a.mask[(size_t)r * G + k] = 0;
+    }
+    if (lane == 0) {
       a.num_correct[r] = 0;
       a.bonus[r] = -1;
       a.commit[r] = 0;
       if (a.new_seq) a.new_seq[r] = prefix;
-      for (int j = 0; j <= G; ++j) out[j] = -1;
-      if (a.mask) {
-        for (int k = 0; k < G; ++k) a.mask[(size_t)r * G + k] = 0;
-      }
-      continue;
+      atomicOr(a.meta + 1, DSPARK_DATA_BAD_LENS);
     }
-    int c = 0;
-    bool run = true;
-    for (int k = 0; k < len - 1; ++k) {
-      const bool m = dr[k] == load_am(a.row_am + c0 + k);
-      run = run && m;
-      c += run ? 1 : 0;
-    }
-    const int bon = load_am(a.row_am + c0 + c);
+    return;
+  }
+  for (int j = lane; j < len; j += kWave) am[j] = merge_row(a, c0 + j);
+  __syncthreads();
+  // draft k (0-based, k < len - 1 <= 64) against the prediction of row k
+  const bool mismatch = lane < len - 1 && dr[lane] != am[lane];
+  const unsigned long long mm = __ballot(mismatch);
+  const int c = mm ? (int)__builtin_ctzll(mm) : len - 1;
+  const int bon = am[c];
+  for (int j = lane; j <= G; j += kWave) out[j] = j == c ? bon : (j < G ? dr[j] : -1);
+  if (a.mask) {
+    for (int k = lane; k < G; k += kWave) a.mask[(size_t)r * G + k] = k < c ? 1 : 0;
+  }
+  if (lane == 0) {
     a.num_correct[r] = c;
     a.bonus[r] = bon;
     a.commit[r] = c + 1;
     if (a.new_seq) a.new_seq[r] = prefix + c + 1;
-    for (int j = 0; j < G; ++j) out[j] = j == c ? bon : dr[j];
-    out[G] = c == G ? bon : -1;
-    if (a.mask) {
-      for (int k = 0; k < G; ++k) a.mask[(size_t)r * G + k] = k < c ? 1 : 0;
-    }
   }
-  if (bad) atomicOr(&s_status, DSPARK_DATA_BAD_LENS);
-  __syncthreads();
-  if (tid == 0) {
-    a.meta[0] = total;
-    a.meta[1] = s_status;
-  }
-}
-
-template <dspark_dtype DT>
-__global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
-  __shared__ unsigned long long s_best[2][kAccThreads / kWave];
-  __shared__ int s_final;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-
-  const int total = a.cu[a.B];
-  const int total_eff = min(max(total, 0), a.max_rows);
-  const int units = total_eff * a.chunks;
-  bool is_final = false;
-  int par = 0;
-  for (int u = blockIdx.x; u < units; u += gridDim.x, par ^= 1) {
-    const int row = u / a.chunks;
-    const int chunk = u - row * a.chunks;
-    unsigned long long best = unit_scan<DT>(a, row, chunk);
-    best = wave_max_u64(best);
-    if (lane == 0) s_best[par][wave] = best;
-    __syncthreads();
-    if (tid == 0) {
-      unsigned long long m = s_best[par][0];
-      for (int w = 1; w < kAccThreads / kWave; ++w) m = s_best[par][w] > m ? s_best[par][w] : m;
-      a.partials[u] = m;
-      const unsigned int old = __hip_atomic_fetch_add(a.row_cnt + row, 1u, __ATOMIC_RELEASE,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-      if (old == (unsigned int)(a.chunks - 1)) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        unsigned long long rm = 0;
-        for (int c = 0; c < a.chunks; ++c) {
-          const unsigned long long pc = __hip_atomic_load(
-              a.partials + (size_t)row * a.chunks + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          rm = pc > rm ? pc : rm;
-        }
-        a.row_am[row] = (int32_t)(0xFFFFFFFFu - (unsigned int)(rm & 0xFFFFFFFFu));
-        __hip_atomic_store(a.row_cnt + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned int done = __hip_atomic_fetch_add(a.glob_cnt, 1u, __ATOMIC_ACQ_REL,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-        if (done == (unsigned int)(total_eff - 1)) {
-          __hip_atomic_store(a.glob_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          is_final = true;
-        }
-      }
-    }
-  }
-  // The finalizing workgroup is the one that completed the last row; with no
-  // rows at all, workgroup 0 finalizes.
-  if (tid == 0) s_final = (is_final || (units == 0 && blockIdx.x == 0)) ? 1 : 0;
-  __syncthreads();
-  if (s_final) finalize(a, total, total_eff);
 }
 
 }  // namespace
 
 hipError_t launch_accept(const AcceptArgs& a, dspark_dtype dt, int grid, hipStream_t s) {
   if (dt == DSPARK_BF16) {
-    hipLaunchKernelGGL(accept_kernel<DSPARK_BF16>, dim3(grid), dim3(kAccThreads), 0, s, a);
+    hipLaunchKernelGGL(accept_argmax_kernel<DSPARK_BF16>, dim3(grid), dim3(kAccThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL(accept_kernel<DSPARK_F32>, dim3(grid), dim3(kAccThreads), 0, s, a);
+    hipLaunchKernelGGL(accept_argmax_kernel<DSPARK_F32>, dim3(grid), dim3(kAccThreads), 0, s, a);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int fgrid = a.B > 0 ? a.B : 1;
+  hipLaunchKernelGGL(accept_finalize_kernel, dim3(fgrid), dim3(kWave), 0, s, a);
   return hipGetLastError();
 }
 

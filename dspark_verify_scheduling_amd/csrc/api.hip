@@ -39,22 +39,6 @@ int next_pow2(int x) {
   return n;
 }
 
-// Compute units of the current device, cached per device id.
-int device_cus() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0) {
-      n = 256;
-    }
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 size_t elem_size(dspark_dtype dt) { return dt == DSPARK_BF16 ? 2 : 4; }
@@ -78,17 +62,10 @@ RowGeom row_geom(int V, dspark_dtype dt) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-struct WsLayout {
-  size_t glob, rows, parts, total;
-};
-
-WsLayout ws_layout(int max_rows, int chunks) {
-  WsLayout w;
-  w.glob = 0;
-  w.rows = 256;
-  w.parts = w.rows + align256((size_t)max_rows * sizeof(unsigned int));
-  w.total = w.parts + align256((size_t)max_rows * chunks * sizeof(unsigned long long));
-  return w;
+// Workspace of dspark_accept: one 64-bit (key, index) partial per unit.
+size_t ws_bytes(int max_rows, int chunks) {
+  const size_t b = align256((size_t)max_rows * chunks * sizeof(unsigned long long));
+  return b > 256 ? b : 256;
 }
 
 }  // namespace
@@ -218,7 +195,7 @@ dspark_status dspark_pack(int32_t B, int32_t gamma, const int32_t* verify_lens,
 size_t dspark_accept_workspace_size(int32_t max_rows, int32_t V, dspark_dtype dt) {
   if (max_rows < 0 || V < 1 || V > DSPARK_MAX_VOCAB) return 0;
   if (dt != DSPARK_F32 && dt != DSPARK_BF16) return 0;
-  return ws_layout(max_rows, row_geom(V, dt).chunks).total;
+  return ws_bytes(max_rows, row_geom(V, dt).chunks);
 }
 
 dspark_status dspark_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,
@@ -257,11 +234,10 @@ dspark_status dspark_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt
   const RowGeom g = row_geom(V, dt);
   if ((int64_t)max_rows * g.chunks > 0x7fffffffLL)
     return fail(DSPARK_E_UNSUPPORTED, "dspark_accept: max_rows * chunks overflows int32");
-  const WsLayout wl = ws_layout(max_rows, g.chunks);
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
-      workspace_bytes < wl.total)
+  const size_t need = ws_bytes(max_rows, g.chunks);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
     return fail(DSPARK_E_WORKSPACE, "dspark_accept: workspace needs %zu bytes, 256-byte aligned",
-                wl.total);
+                need);
 
   dspark::AcceptArgs a;
   a.logits = static_cast<const unsigned char*>(packed_logits);
@@ -285,15 +261,12 @@ dspark_status dspark_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt
   a.new_seq = new_seq_lens;
   a.mask = prefix_mask;
   a.meta = accept_meta;
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  a.glob_cnt = reinterpret_cast<unsigned int*>(ws + wl.glob);
-  a.row_cnt = reinterpret_cast<unsigned int*>(ws + wl.rows);
-  a.partials = reinterpret_cast<unsigned long long*>(ws + wl.parts);
+  a.partials = static_cast<unsigned long long*>(workspace);
+  // one workgroup per (row, unit) of the largest possible packed total; the
+  // kernel reads the actual total on the device and idle workgroups exit
   const int64_t units_max = (int64_t)max_rows * g.chunks;
-  int64_t grid = (int64_t)device_cus() * 8;
-  if (units_max < grid) grid = units_max;
-  if (grid < 1) grid = 1;
-  return launched(dspark::launch_accept(a, dt, (int)grid, (hipStream_t)stream), "dspark_accept");
+  const int grid = units_max > 0 ? (int)units_max : 1;
+  return launched(dspark::launch_accept(a, dt, grid, (hipStream_t)stream), "dspark_accept");
 }
 
 dspark_status dspark_tv_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,

@@ -65,9 +65,7 @@ struct AcceptArgs {
   int32_t* new_seq;
   uint8_t* mask;
   int32_t* meta;
-  unsigned long long* partials;
-  unsigned int* row_cnt;
-  unsigned int* glob_cnt;
+  unsigned long long* partials;  // [max_rows * chunks] (key, index) per unit
 };
 constexpr int kAccThreads = 256;
 constexpr int kAccVecsPerThread = 8;

@@ -219,8 +219,8 @@ dspark_status dspark_pack(int32_t B, int32_t gamma, const int32_t* verify_lens,
  *   prefix_mask        out [B, gamma] uint8 or NULL
  *   accept_meta        out [2] int32: cu_seqlens[B], status bits
  *   workspace          device scratch of dspark_accept_workspace_size() bytes,
- *                      256-byte aligned, ZERO-FILLED before its first use;
- *                      every call leaves it zero-filled again. Calls that
+ *                      256-byte aligned; its contents on entry do not matter
+ *                      and it carries no state between calls. Calls that
  *                      share a workspace must not overlap in time.
  * Data errors: a request whose rows are not 1..gamma+1 rows inside
  *   [0, min(cu_seqlens[B], max_rows)) sets DSPARK_DATA_BAD_LENS and gets
