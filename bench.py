@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the DSpark per-step verify path on one MI355X.
 
-One step = dspark_plan (STS confidence -> survival -> budget sweep ->
-verify_lens) + dspark_pack (cu_seqlens, front-packed rows, tier) +
+One step = dspark_plan_pack (STS confidence -> survival -> budget sweep ->
+verify_lens -> cu_seqlens, front-packed rows, tier; one launch) +
 dspark_accept (vocab-wide argmax over the packed target logits, leading-match
 count, bonus, commit, output tokens), on the B=256, gamma=8, V=129280 bf16
 workload. Every input, including the packed target logits a forward pass
@@ -179,10 +179,13 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    def plan_pack(stream=None):
+        dv.dspark_plan_pack(B, G, dv.IN_CONF_LOGITS, conf_t, temps_t, w.min_len, w.max_len,
+                            w.eps, w.b_lo, w.b_hi, float(w.bias), alpha_t, theta_t, po,
+                            anchors_t, drafts_t, tiers, prefix_t, ko, stream)
+
     def step(i):  # on the current stream (graph capture switches it)
-        dv.dspark_plan(B, G, dv.IN_CONF_LOGITS, conf_t, temps_t, w.min_len, w.max_len, w.eps,
-                       w.b_lo, w.b_hi, float(w.bias), alpha_t, theta_t, po)
-        dv.dspark_pack(B, G, po.verify_lens, anchors_t, drafts_t, tiers, prefix_t, ko)
+        plan_pack()
         dv.dspark_accept(B, G, V, dt, packed[i % n_rot], V, tier, ko.cu_seqlens, drafts_t,
                          prefix_t, ao)
 
@@ -198,9 +201,7 @@ def main():
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        dv.dspark_plan(B, G, dv.IN_CONF_LOGITS, conf_t, temps_t, w.min_len, w.max_len, w.eps,
-                       w.b_lo, w.b_hi, float(w.bias), alpha_t, theta_t, po, stream)
-        dv.dspark_pack(B, G, po.verify_lens, anchors_t, drafts_t, tiers, prefix_t, ko, stream)
+        plan_pack(stream)
         ev_a0[i].record(stream)
         dv.dspark_accept(B, G, V, dt, packed[i % n_rot], V, tier, ko.cu_seqlens, drafts_t,
                          prefix_t, ao, stream)
@@ -216,9 +217,12 @@ def main():
     assert np.array_equal(po.verify_lens.cpu().numpy(), lens)
     assert int(ao.accept_meta[1].item()) == 0
 
-    # ---- plan and pack alone (events), and one step as a HIP graph replay
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    # ---- plan+pack, plan and pack alone (events), and one step as a HIP graph replay
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     reps = 50
+    ev[3].record(stream)
+    for _ in range(reps):
+        plan_pack(stream)
     ev[0].record(stream)
     for _ in range(reps):
         dv.dspark_plan(B, G, dv.IN_CONF_LOGITS, conf_t, temps_t, w.min_len, w.max_len, w.eps,
@@ -228,6 +232,7 @@ def main():
         dv.dspark_pack(B, G, po.verify_lens, anchors_t, drafts_t, tiers, prefix_t, ko, stream)
     ev[2].record(stream)
     torch.cuda.synchronize()
+    plan_pack_us = 1e3 * ev[3].elapsed_time(ev[0]) / reps
     plan_us = 1e3 * ev[0].elapsed_time(ev[1]) / reps
     pack_us = 1e3 * ev[1].elapsed_time(ev[2]) / reps
 
@@ -308,6 +313,7 @@ def main():
         "cpu_baseline": cpu,
         "steps_per_s_graph": 1e3 / ms_step_graph,
         "ms_per_step_graph": ms_step_graph,
+        "plan_pack_us": plan_pack_us,
         "plan_us": plan_us,
         "pack_us": pack_us,
         "accept_us_median": statistics.median(acc_us),

@@ -24,7 +24,7 @@ from ._lib import (
 )
 
 __all__ = [
-    "load", "dspark_plan", "dspark_pack", "dspark_accept", "dspark_tv_accept",
+    "load", "dspark_plan", "dspark_pack", "dspark_plan_pack", "dspark_accept", "dspark_tv_accept",
     "dspark_accept_workspace_size", "alloc_plan_outputs", "alloc_pack_outputs",
     "alloc_accept_outputs", "DsparkError", "F32", "BF16", "IN_CONF_LOGITS", "IN_COND",
     "IN_SURVIVAL", "DATA_BAD_COST", "DATA_BAD_CONF", "DATA_BAD_LENS",
@@ -159,6 +159,47 @@ def dspark_pack(B: int, gamma: int, verify_lens: torch.Tensor, anchor_ids: torch
     )
     _lib.check("dspark_pack", _lib.lib().dspark_pack(*args))
     return out
+
+
+def dspark_plan_pack(B: int, gamma: int, kind: int, conf: torch.Tensor, sts_temp,
+                     min_verify_len: int, max_verify_len: int, survival_eps: float,
+                     budget_lo: int, budget_hi: int, cost_bias: float, cost_alpha: torch.Tensor,
+                     cost_theta: torch.Tensor, plan_out: PlanOutputs, anchor_ids: torch.Tensor,
+                     draft_tokens: torch.Tensor, tiers: Sequence[int], prefix_lens,
+                     pack_out: PackOutputs, stream=None):
+    import ctypes
+
+    f32, i32, f64 = torch.float32, torch.int32, torch.float64
+    tiers = [int(t) for t in tiers]
+    if not tiers:
+        raise ValueError("tiers must not be empty")
+    cap = tiers[-1]
+    tiers_host = (ctypes.c_int32 * len(tiers))(*tiers)
+    args = (
+        B, gamma, kind,
+        _ptr(conf, "conf", f32, B * gamma),
+        _ptr(sts_temp, "sts_temp", f32, gamma, required=(kind == IN_CONF_LOGITS)),
+        min_verify_len, max_verify_len, survival_eps, budget_lo, budget_hi, cost_bias,
+        _ptr(cost_alpha, "cost_alpha", f32, 1), cost_alpha.numel(),
+        _ptr(cost_theta, "cost_theta", f32, 1), cost_theta.numel(),
+        _ptr(plan_out.verify_lens, "verify_lens", i32, B),
+        _ptr(plan_out.plan_meta, "plan_meta", i32, 4),
+        _ptr(plan_out.plan_val, "plan_val", f64, 2),
+        _ptr(plan_out.survival_out, "survival_out", f32, B * gamma, required=False),
+        _ptr(plan_out.sweep_out, "sweep_out", f64, 2 * (B * gamma + 1), required=False),
+        _ptr(anchor_ids, "anchor_ids", i32, B),
+        _ptr(draft_tokens, "draft_tokens", i32, B * gamma),
+        ctypes.cast(tiers_host, ctypes.c_void_p), len(tiers),
+        _ptr(prefix_lens, "prefix_lens", i32, B, required=False),
+        _ptr(pack_out.cu_seqlens, "cu_seqlens", i32, B + 1),
+        _ptr(pack_out.packed_ids, "packed_ids", i32, cap),
+        _ptr(pack_out.packed_req, "packed_req", i32, cap, required=False),
+        _ptr(pack_out.packed_pos, "packed_pos", i32, cap, required=False),
+        _ptr(pack_out.pack_meta, "pack_meta", i32, 3),
+        _stream(stream),
+    )
+    _lib.check("dspark_plan_pack", _lib.lib().dspark_plan_pack(*args))
+    return plan_out, pack_out
 
 
 # ------------------------------------------------------------------ accept

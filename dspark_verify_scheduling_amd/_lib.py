@@ -27,6 +27,11 @@ SIGNATURES = {
         c_int32, c_int32, c_int, c_void_p, c_void_p, c_int32, c_int32, c_float, c_int32,
         c_int32, c_float, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
         c_void_p, c_void_p, c_void_p]),
+    "dspark_plan_pack": (c_int, [
+        c_int32, c_int32, c_int, c_void_p, c_void_p, c_int32, c_int32, c_float, c_int32,
+        c_int32, c_float, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dspark_pack": (c_int, [
         c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),

@@ -33,12 +33,6 @@ dspark_status launched(hipError_t e, const char* what) {
   return ok();
 }
 
-int next_pow2(int x) {
-  int n = 1;
-  while (n < x) n <<= 1;
-  return n;
-}
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 size_t elem_size(dspark_dtype dt) { return dt == DSPARK_BF16 ? 2 : 4; }
@@ -72,7 +66,7 @@ size_t ws_bytes(int max_rows, int chunks) {
 
 extern "C" {
 
-int32_t dspark_version(void) { return (1 << 16) | 0; }
+int32_t dspark_version(void) { return (1 << 16) | 1; }
 
 const char* dspark_status_str(dspark_status s) {
   switch (s) {
@@ -87,6 +81,109 @@ const char* dspark_status_str(dspark_status s) {
 
 const char* dspark_last_error(void) { return g_last_error; }
 
+}  // extern "C"
+
+// Validation shared by dspark_plan and dspark_plan_pack; fills `a`.
+static dspark_status check_plan(const char* fn, int32_t B, int32_t gamma, dspark_input kind,
+                                const float* conf, const float* sts_temp, int32_t min_verify_len,
+                                int32_t max_verify_len, float survival_eps, int32_t budget_lo,
+                                int32_t budget_hi, float cost_bias, const float* cost_alpha,
+                                int32_t alpha_len, const float* cost_theta, int32_t theta_len,
+                                int32_t* verify_lens, int32_t* plan_meta, double* plan_val,
+                                float* survival_out, double* sweep_out, dspark::PlanArgs* a) {
+  if (B < 0) return fail(DSPARK_E_INVALID, "%s: B = %d < 0", fn, B);
+  if (gamma < 1 || gamma > DSPARK_MAX_GAMMA)
+    return fail(DSPARK_E_INVALID, "%s: gamma = %d outside [1, %d]", fn, gamma, DSPARK_MAX_GAMMA);
+  if (kind != DSPARK_IN_CONF_LOGITS && kind != DSPARK_IN_COND && kind != DSPARK_IN_SURVIVAL)
+    return fail(DSPARK_E_INVALID, "%s: unknown input kind %d", fn, (int)kind);
+  if (B > DSPARK_MAX_BATCH || (int64_t)B * gamma > DSPARK_MAX_CANDIDATES)
+    return fail(DSPARK_E_UNSUPPORTED, "%s: B * gamma = %lld exceeds %d", fn, (long long)B * gamma,
+                DSPARK_MAX_CANDIDATES);
+  if (B > 0 && !conf) return fail(DSPARK_E_INVALID, "%s: conf is NULL", fn);
+  if (kind == DSPARK_IN_CONF_LOGITS && !sts_temp)
+    return fail(DSPARK_E_INVALID, "%s: sts_temp is NULL for confidence logits", fn);
+  if (!cost_alpha || !cost_theta)
+    return fail(DSPARK_E_INVALID, "%s: cost table pointer is NULL", fn);
+  if (!plan_meta || !plan_val || (B > 0 && !verify_lens))
+    return fail(DSPARK_E_INVALID, "%s: an output pointer is NULL", fn);
+  if (budget_lo < 0) return fail(DSPARK_E_INVALID, "%s: budget_lo = %d < 0", fn, budget_lo);
+  if (budget_hi >= 0 && budget_lo > budget_hi)
+    return fail(DSPARK_E_INVALID, "%s: budget_lo %d > budget_hi %d", fn, budget_lo, budget_hi);
+  if (survival_eps != survival_eps) return fail(DSPARK_E_INVALID, "%s: survival_eps is NaN", fn);
+  const int lmin = std::min(std::max(min_verify_len, 1), gamma + 1);
+  const int lmax = std::min(std::max(max_verify_len, lmin), gamma + 1);
+  if (alpha_len <= B)
+    return fail(DSPARK_E_INVALID, "%s: alpha_len %d must exceed B = %d", fn, alpha_len, B);
+  if ((int64_t)theta_len <= (int64_t)B * lmax)
+    return fail(DSPARK_E_INVALID, "%s: theta_len %d must exceed B * L_max = %lld", fn, theta_len,
+                (long long)B * lmax);
+  a->B = B;
+  a->gamma = gamma;
+  a->kind = (int)kind;
+  a->lmin = lmin;
+  a->lmax = lmax;
+  a->b_lo = budget_lo;
+  a->b_hi = budget_hi < 0 ? -1 : budget_hi;
+  a->theta_len = theta_len;
+  a->eps = survival_eps;
+  a->bias = cost_bias;
+  a->conf = conf;
+  a->temps = sts_temp;
+  a->alpha = cost_alpha;
+  a->theta = cost_theta;
+  a->lens = verify_lens;
+  a->meta = plan_meta;
+  a->val = plan_val;
+  a->surv_out = survival_out;
+  a->sweep = sweep_out;
+  return DSPARK_OK;
+}
+
+// Validation shared by dspark_pack and dspark_plan_pack; fills `a`.
+static dspark_status check_pack(const char* fn, int32_t B, int32_t gamma,
+                                const int32_t* verify_lens, bool need_lens,
+                                const int32_t* anchor_ids, const int32_t* draft_tokens,
+                                const int32_t* tiers_host, int32_t num_tiers,
+                                const int32_t* prefix_lens, int32_t* cu_seqlens,
+                                int32_t* packed_ids, int32_t* packed_req, int32_t* packed_pos,
+                                int32_t* pack_meta, dspark::PackArgs* a) {
+  if (B < 0) return fail(DSPARK_E_INVALID, "%s: B = %d < 0", fn, B);
+  if (gamma < 1 || gamma > DSPARK_MAX_GAMMA)
+    return fail(DSPARK_E_INVALID, "%s: gamma = %d outside [1, %d]", fn, gamma, DSPARK_MAX_GAMMA);
+  if (B > DSPARK_MAX_BATCH)
+    return fail(DSPARK_E_UNSUPPORTED, "%s: B = %d exceeds %d", fn, B, DSPARK_MAX_BATCH);
+  if (B > 0 && ((need_lens && !verify_lens) || !anchor_ids || !draft_tokens))
+    return fail(DSPARK_E_INVALID, "%s: an input pointer is NULL", fn);
+  if (!cu_seqlens || !packed_ids || !pack_meta)
+    return fail(DSPARK_E_INVALID, "%s: an output pointer is NULL", fn);
+  if (!tiers_host || num_tiers < 1 || num_tiers > DSPARK_MAX_TIERS)
+    return fail(DSPARK_E_INVALID, "%s: need 1..%d tiers, got %d", fn, DSPARK_MAX_TIERS, num_tiers);
+  if (tiers_host[0] < 1) return fail(DSPARK_E_INVALID, "%s: tiers must be >= 1", fn);
+  for (int i = 1; i < num_tiers; ++i) {
+    if (tiers_host[i] <= tiers_host[i - 1])
+      return fail(DSPARK_E_INVALID, "%s: tiers not strictly ascending at %d", fn, i);
+  }
+  if ((int64_t)tiers_host[num_tiers - 1] < (int64_t)B * (gamma + 1))
+    return fail(DSPARK_E_INVALID, "%s: last tier %d < B * (gamma + 1) = %lld", fn,
+                tiers_host[num_tiers - 1], (long long)B * (gamma + 1));
+  a->B = B;
+  a->gamma = gamma;
+  a->ntiers = num_tiers;
+  a->lens = verify_lens;
+  a->anchors = anchor_ids;
+  a->drafts = draft_tokens;
+  a->prefix = prefix_lens;
+  a->cu = cu_seqlens;
+  a->ids = packed_ids;
+  a->req = packed_req;
+  a->pos = packed_pos;
+  a->meta = pack_meta;
+  for (int i = 0; i < DSPARK_MAX_TIERS; ++i) a->tiers[i] = i < num_tiers ? tiers_host[i] : 0;
+  return DSPARK_OK;
+}
+
+extern "C" {
+
 dspark_status dspark_plan(int32_t B, int32_t gamma, dspark_input kind, const float* conf,
                           const float* sts_temp, int32_t min_verify_len,
                           int32_t max_verify_len, float survival_eps, int32_t budget_lo,
@@ -94,57 +191,39 @@ dspark_status dspark_plan(int32_t B, int32_t gamma, dspark_input kind, const flo
                           int32_t alpha_len, const float* cost_theta, int32_t theta_len,
                           int32_t* verify_lens, int32_t* plan_meta, double* plan_val,
                           float* survival_out, double* sweep_out, void* stream) {
-  if (B < 0) return fail(DSPARK_E_INVALID, "dspark_plan: B = %d < 0", B);
-  if (gamma < 1 || gamma > DSPARK_MAX_GAMMA)
-    return fail(DSPARK_E_INVALID, "dspark_plan: gamma = %d outside [1, %d]", gamma,
-                DSPARK_MAX_GAMMA);
-  if (kind != DSPARK_IN_CONF_LOGITS && kind != DSPARK_IN_COND && kind != DSPARK_IN_SURVIVAL)
-    return fail(DSPARK_E_INVALID, "dspark_plan: unknown input kind %d", (int)kind);
-  if (B > DSPARK_MAX_BATCH || (int64_t)B * gamma > DSPARK_MAX_CANDIDATES)
-    return fail(DSPARK_E_UNSUPPORTED, "dspark_plan: B * gamma = %lld exceeds %d",
-                (long long)B * gamma, DSPARK_MAX_CANDIDATES);
-  if (B > 0 && !conf) return fail(DSPARK_E_INVALID, "dspark_plan: conf is NULL");
-  if (kind == DSPARK_IN_CONF_LOGITS && !sts_temp)
-    return fail(DSPARK_E_INVALID, "dspark_plan: sts_temp is NULL for confidence logits");
-  if (!cost_alpha || !cost_theta)
-    return fail(DSPARK_E_INVALID, "dspark_plan: cost table pointer is NULL");
-  if (!plan_meta || !plan_val || (B > 0 && !verify_lens))
-    return fail(DSPARK_E_INVALID, "dspark_plan: an output pointer is NULL");
-  if (budget_lo < 0) return fail(DSPARK_E_INVALID, "dspark_plan: budget_lo = %d < 0", budget_lo);
-  if (budget_hi >= 0 && budget_lo > budget_hi)
-    return fail(DSPARK_E_INVALID, "dspark_plan: budget_lo %d > budget_hi %d", budget_lo,
-                budget_hi);
-  if (survival_eps != survival_eps)
-    return fail(DSPARK_E_INVALID, "dspark_plan: survival_eps is NaN");
-  const int lmin = std::min(std::max(min_verify_len, 1), gamma + 1);
-  const int lmax = std::min(std::max(max_verify_len, lmin), gamma + 1);
-  if (alpha_len <= B)
-    return fail(DSPARK_E_INVALID, "dspark_plan: alpha_len %d must exceed B = %d", alpha_len, B);
-  if ((int64_t)theta_len <= (int64_t)B * lmax)
-    return fail(DSPARK_E_INVALID, "dspark_plan: theta_len %d must exceed B * L_max = %lld",
-                theta_len, (long long)B * lmax);
-
   dspark::PlanArgs a;
-  a.B = B;
-  a.gamma = gamma;
-  a.kind = (int)kind;
-  a.lmin = lmin;
-  a.lmax = lmax;
-  a.b_lo = budget_lo;
-  a.b_hi = budget_hi < 0 ? -1 : budget_hi;
-  a.n_sort = next_pow2(std::max(1, B * (lmax - lmin)));
-  a.eps = survival_eps;
-  a.bias = cost_bias;
-  a.conf = conf;
-  a.temps = sts_temp;
-  a.alpha = cost_alpha;
-  a.theta = cost_theta;
-  a.lens = verify_lens;
-  a.meta = plan_meta;
-  a.val = plan_val;
-  a.surv_out = survival_out;
-  a.sweep = sweep_out;
-  return launched(dspark::launch_plan(a, (hipStream_t)stream), "dspark_plan");
+  dspark_status st = check_plan("dspark_plan", B, gamma, kind, conf, sts_temp, min_verify_len,
+                                max_verify_len, survival_eps, budget_lo, budget_hi, cost_bias,
+                                cost_alpha, alpha_len, cost_theta, theta_len, verify_lens,
+                                plan_meta, plan_val, survival_out, sweep_out, &a);
+  if (st != DSPARK_OK) return st;
+  return launched(dspark::launch_plan(a, nullptr, (hipStream_t)stream), "dspark_plan");
+}
+
+dspark_status dspark_plan_pack(int32_t B, int32_t gamma, dspark_input kind, const float* conf,
+                               const float* sts_temp, int32_t min_verify_len,
+                               int32_t max_verify_len, float survival_eps, int32_t budget_lo,
+                               int32_t budget_hi, float cost_bias, const float* cost_alpha,
+                               int32_t alpha_len, const float* cost_theta, int32_t theta_len,
+                               int32_t* verify_lens, int32_t* plan_meta, double* plan_val,
+                               float* survival_out, double* sweep_out, const int32_t* anchor_ids,
+                               const int32_t* draft_tokens, const int32_t* tiers_host,
+                               int32_t num_tiers, const int32_t* prefix_lens, int32_t* cu_seqlens,
+                               int32_t* packed_ids, int32_t* packed_req, int32_t* packed_pos,
+                               int32_t* pack_meta, void* stream) {
+  dspark::PlanArgs a;
+  dspark_status st = check_plan("dspark_plan_pack", B, gamma, kind, conf, sts_temp,
+                                min_verify_len, max_verify_len, survival_eps, budget_lo,
+                                budget_hi, cost_bias, cost_alpha, alpha_len, cost_theta,
+                                theta_len, verify_lens, plan_meta, plan_val, survival_out,
+                                sweep_out, &a);
+  if (st != DSPARK_OK) return st;
+  dspark::PackArgs p;
+  st = check_pack("dspark_plan_pack", B, gamma, verify_lens, false, anchor_ids, draft_tokens,
+                  tiers_host, num_tiers, prefix_lens, cu_seqlens, packed_ids, packed_req,
+                  packed_pos, pack_meta, &p);
+  if (st != DSPARK_OK) return st;
+  return launched(dspark::launch_plan(a, &p, (hipStream_t)stream), "dspark_plan_pack");
 }
 
 dspark_status dspark_pack(int32_t B, int32_t gamma, const int32_t* verify_lens,
@@ -153,42 +232,11 @@ dspark_status dspark_pack(int32_t B, int32_t gamma, const int32_t* verify_lens,
                           const int32_t* prefix_lens, int32_t* cu_seqlens,
                           int32_t* packed_ids, int32_t* packed_req, int32_t* packed_pos,
                           int32_t* pack_meta, void* stream) {
-  if (B < 0) return fail(DSPARK_E_INVALID, "dspark_pack: B = %d < 0", B);
-  if (gamma < 1 || gamma > DSPARK_MAX_GAMMA)
-    return fail(DSPARK_E_INVALID, "dspark_pack: gamma = %d outside [1, %d]", gamma,
-                DSPARK_MAX_GAMMA);
-  if (B > DSPARK_MAX_BATCH)
-    return fail(DSPARK_E_UNSUPPORTED, "dspark_pack: B = %d exceeds %d", B, DSPARK_MAX_BATCH);
-  if (B > 0 && (!verify_lens || !anchor_ids || !draft_tokens))
-    return fail(DSPARK_E_INVALID, "dspark_pack: an input pointer is NULL");
-  if (!cu_seqlens || !packed_ids || !pack_meta)
-    return fail(DSPARK_E_INVALID, "dspark_pack: an output pointer is NULL");
-  if (!tiers_host || num_tiers < 1 || num_tiers > DSPARK_MAX_TIERS)
-    return fail(DSPARK_E_INVALID, "dspark_pack: need 1..%d tiers, got %d", DSPARK_MAX_TIERS,
-                num_tiers);
-  if (tiers_host[0] < 1) return fail(DSPARK_E_INVALID, "dspark_pack: tiers must be >= 1");
-  for (int i = 1; i < num_tiers; ++i) {
-    if (tiers_host[i] <= tiers_host[i - 1])
-      return fail(DSPARK_E_INVALID, "dspark_pack: tiers not strictly ascending at %d", i);
-  }
-  if ((int64_t)tiers_host[num_tiers - 1] < (int64_t)B * (gamma + 1))
-    return fail(DSPARK_E_INVALID, "dspark_pack: last tier %d < B * (gamma + 1) = %lld",
-                tiers_host[num_tiers - 1], (long long)B * (gamma + 1));
-
   dspark::PackArgs a;
-  a.B = B;
-  a.gamma = gamma;
-  a.ntiers = num_tiers;
-  a.lens = verify_lens;
-  a.anchors = anchor_ids;
-  a.drafts = draft_tokens;
-  a.prefix = prefix_lens;
-  a.cu = cu_seqlens;
-  a.ids = packed_ids;
-  a.req = packed_req;
-  a.pos = packed_pos;
-  a.meta = pack_meta;
-  for (int i = 0; i < DSPARK_MAX_TIERS; ++i) a.tiers[i] = i < num_tiers ? tiers_host[i] : 0;
+  dspark_status st = check_pack("dspark_pack", B, gamma, verify_lens, true, anchor_ids,
+                                draft_tokens, tiers_host, num_tiers, prefix_lens, cu_seqlens,
+                                packed_ids, packed_req, packed_pos, pack_meta, &a);
+  if (st != DSPARK_OK) return st;
   return launched(dspark::launch_pack(a, (hipStream_t)stream), "dspark_pack");
 }
 

@@ -14,7 +14,7 @@ constexpr int kWave = 64;
 // ---------------------------------------------------------------- kernels
 
 struct PlanArgs {
-  int B, gamma, kind, lmin, lmax, b_lo, b_hi, n_sort;
+  int B, gamma, kind, lmin, lmax, b_lo, b_hi, theta_len;
   float eps, bias;
   const float* conf;
   const float* temps;
@@ -27,8 +27,7 @@ struct PlanArgs {
   double* sweep;
 };
 constexpr int kPlanThreads = 1024;
-hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-size_t plan_lds_bytes(int B, int n_sort);
+size_t plan_lds_bytes(int B, int gamma, int n_keys);
 
 struct PackArgs {
   int B, gamma, ntiers;
@@ -45,6 +44,8 @@ struct PackArgs {
 };
 constexpr int kPackThreads = 1024;
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
+// plan, then (p != nullptr) pack in the same workgroup
+hipError_t launch_plan(const PlanArgs& a, const PackArgs* p, hipStream_t s);
 
 struct AcceptArgs {
   const unsigned char* logits;
@@ -95,49 +96,103 @@ __device__ inline T wave_sum(T v) {
   return v;
 }
 
-template <typename T>
-__device__ inline T wave_incl_scan(T v) {
-  const int lane = lane_id();
-  for (int d = 1; d < kWave; d <<= 1) {
-    T n = __shfl_up(v, d, kWave);
-    if (lane >= d) v += n;
-  }
-  return v;
+// ---- wave primitives on DPP (data-parallel primitives): lane exchanges
+// inside the VALU, no LDS round trip. Encodings of the gfx9-family DPP
+// controls used here: row_shr:n = 0x110 + n, row_bcast:15 = 0x142,
+// row_bcast:31 = 0x143. A lane whose source lies outside its 16-lane row,
+// or whose row is masked off, receives `ident`.
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ inline uint32_t dpp32(uint32_t x, uint32_t ident) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)x, CTRL, ROW_MASK, 0xF, false);
 }
 
-// Exclusive scan over the block. `wsum` needs (waves + 1) slots. Returns the
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ inline uint64_t dpp64(uint64_t x, uint64_t ident) {
+  const uint32_t lo = dpp32<CTRL, ROW_MASK>((uint32_t)x, (uint32_t)ident);
+  const uint32_t hi = dpp32<CTRL, ROW_MASK>((uint32_t)(x >> 32), (uint32_t)(ident >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int CTRL, int ROW_MASK = 0xF, typename T>
+__device__ inline T dpp_t(T x, T ident) {
+  if constexpr (sizeof(T) == 8) {
+    return __builtin_bit_cast(T, dpp64<CTRL, ROW_MASK>(__builtin_bit_cast(uint64_t, x),
+                                                       __builtin_bit_cast(uint64_t, ident)));
+  } else {
+    return __builtin_bit_cast(T, dpp32<CTRL, ROW_MASK>(__builtin_bit_cast(uint32_t, x),
+                                                       __builtin_bit_cast(uint32_t, ident)));
+  }
+}
+
+// Inclusive scan over the 64 lanes of a wave for an associative `op` with
+// identity `ident` (Hillis-Steele inside each 16-lane row, then the row
+// totals carried to the later rows).
+template <typename T, typename Op>
+__device__ inline T wave_incl_scan_op(T x, T ident, Op op) {
+  x = op(x, dpp_t<0x111>(x, ident));
+  x = op(x, dpp_t<0x112>(x, ident));
+  x = op(x, dpp_t<0x114>(x, ident));
+  x = op(x, dpp_t<0x118>(x, ident));
+  x = op(x, dpp_t<0x142, 0xA>(x, ident));
+  x = op(x, dpp_t<0x143, 0xC>(x, ident));
+  return x;
+}
+
+template <typename T>
+__device__ inline T read_lane(T x, int lane) {
+  if constexpr (sizeof(T) == 8) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  } else {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+  }
+}
+
+struct OpAdd {
+  template <typename T>
+  __device__ T operator()(T a, T b) const { return a + b; }
+};
+
+// Exclusive scan over the block. `wsum` needs one slot per wave. Returns the
 // exclusive prefix of this thread's value; *total receives the block total.
+// Lane w of every wave reads wave w's total (one LDS read per lane), and the
+// wave offsets come from a DPP scan over those lanes.
 template <typename T, int NTHREADS>
 __device__ inline T block_excl_scan(T v, T* wsum, T* total) {
   constexpr int kWaves = NTHREADS / kWave;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
-  T incl = wave_incl_scan(v);
+  const T incl = wave_incl_scan_op(v, T(0), OpAdd{});
   if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
-  if (wave == 0) {
-    T w = lane < kWaves ? wsum[lane] : T(0);
-    T wi = wave_incl_scan(w);
-    if (lane < kWaves) wsum[lane] = wi - w;  // exclusive wave offsets
-    if (lane == kWaves - 1) wsum[kWaves] = wi;
-  }
+  const T t = lane < kWaves ? wsum[lane] : T(0);
+  const T tincl = wave_incl_scan_op(t, T(0), OpAdd{});
+  const T before = wave > 0 ? read_lane(tincl, wave - 1) : T(0);
+  *total = read_lane(tincl, kWaves - 1);
+  __syncthreads();  // wsum may be reused right after
+  return before + incl - v;
+}
+
+// Reduction over the block with `op` (identity `ident`), result in every
+// thread. `wsum` needs one slot per wave.
+template <typename T, int NTHREADS, typename Op>
+__device__ inline T block_reduce(T v, T ident, Op op, T* wsum) {
+  constexpr int kWaves = NTHREADS / kWave;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  v = wave_incl_scan_op(v, ident, op);
+  if (lane == kWave - 1) wsum[wave] = v;
   __syncthreads();
-  T res = wsum[wave] + incl - v;
-  *total = wsum[kWaves];
+  T t = lane < kWaves ? wsum[lane] : ident;
+  t = read_lane(wave_incl_scan_op(t, ident, op), kWave - 1);
   __syncthreads();
-  return res;
+  return t;
 }
 
 template <typename T, int NTHREADS>
 __device__ inline T block_sum(T v, T* wsum) {
-  constexpr int kWaves = NTHREADS / kWave;
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  v = wave_sum(v);
-  if (lane == 0) wsum[wave] = v;
-  __syncthreads();
-  T t = T(0);
-  for (int i = 0; i < kWaves; ++i) t += wsum[i];
-  __syncthreads();
-  return t;
+  return block_reduce<T, NTHREADS>(v, T(0), OpAdd{}, wsum);
 }
 
 }  // namespace dspark

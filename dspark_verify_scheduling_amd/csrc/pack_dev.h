@@ -1,0 +1,82 @@
+// Device side of the compact ragged layout, shared by the pack kernel and
+// the fused plan+pack kernel.
+//
+// Method sources:
+//   "DSpark 自适应 Verify 怎样分配候选预算" (akiyangdev) §五 (compact mode
+//     packs only the selected rows, e.g. A0 A1 | B0 | C0 C1 C2 C3) and §六
+//     (cu_seqlens_q = [0,2,3,7] for verify_lens [2,1,4]).
+//   "DeepSeek-V4 DSpark 一轮 Draft、Verify、Accept 与 Commit" (akiyangdev) §三
+//     (verify ids = anchor followed by the drafts; the anchor plus the
+//     selected draft prefix is front-packed).
+//   "DSpark 接入 SGLang" (yingzheng), ragged verify, and "DSpark
+//     confidence-scheduled speculative decoding" (charlestar), graph tiers:
+//     the packed total is rounded up to the smallest captured tier.
+#pragma once
+
+#include "common.h"
+
+namespace dspark {
+
+// Packs B requests whose (already clamped) lengths sit in LDS `lens`,
+// writing cu_seqlens into LDS `cu` (B + 1 entries) and to global memory.
+// Block-wide: every thread of the NTHREADS-thread workgroup must call it.
+// `status` is OR-ed into meta[2] by thread 0 at the end.
+template <int NTHREADS>
+__device__ void pack_block(const PackArgs& a, const int32_t* lens, int32_t* cu, int* wsum,
+                           int* s_tier, int status) {
+  const int tid = threadIdx.x;
+  const int B = a.B, G = a.gamma;
+  const int ipt = (B + NTHREADS - 1) / NTHREADS;
+  const int r0 = tid * ipt;
+  int local = 0;
+  for (int t = 0; t < ipt; ++t) {
+    if (r0 + t < B) local += lens[r0 + t];
+  }
+  int total;
+  int run = block_excl_scan<int, NTHREADS>(local, wsum, &total);
+  for (int t = 0; t < ipt; ++t) {
+    const int r = r0 + t;
+    if (r < B) {
+      cu[r] = run;
+      a.cu[r] = run;
+      run += lens[r];
+    }
+  }
+  if (tid == 0) {
+    cu[B] = total;
+    a.cu[B] = total;
+    int tier = a.tiers[a.ntiers - 1];
+    for (int i = 0; i < a.ntiers; ++i) {
+      if (a.tiers[i] >= total) {
+        tier = a.tiers[i];
+        break;
+      }
+    }
+    *s_tier = tier;
+  }
+  __syncthreads();
+  const int rows = B * (G + 1);
+  for (int f = tid; f < rows; f += NTHREADS) {
+    const int r = f / (G + 1);
+    const int j = f - r * (G + 1);
+    if (j < lens[r]) {
+      const int i = cu[r] + j;
+      a.ids[i] = j ? a.drafts[(size_t)r * G + (j - 1)] : a.anchors[r];
+      if (a.req) a.req[i] = r;
+      if (a.pos) a.pos[i] = (a.prefix ? a.prefix[r] : 0) + j;
+    }
+  }
+  const int tier = *s_tier;
+  for (int i = total + tid; i < tier; i += NTHREADS) {
+    a.ids[i] = 0;
+    if (a.req) a.req[i] = -1;
+    if (a.pos) a.pos[i] = 0;
+  }
+  if (tid == 0) {
+    a.meta[0] = total;
+    a.meta[1] = tier;
+    a.meta[2] = status;
+  }
+}
+
+}  // namespace dspark

@@ -1,5 +1,6 @@
 // Planner kernel: STS confidence -> prefix survival -> global top-b budget
-// sweep -> verify_lens, in one workgroup of 1024 threads.
+// sweep -> verify_lens, in one workgroup of 1024 threads; optionally followed
+// in the same workgroup by the compact layout (cu_seqlens, packed rows, tier).
 //
 // Method sources:
 //   "DSpark 自适应 Verify 怎样分配候选预算" (akiyangdev)
@@ -13,22 +14,32 @@
 //     prefix-event survival table and the cost model with M = bs + K.
 //
 // Design for one CU. The whole problem (B*gamma <= 8192 candidates, 64 KB
-// of 64-bit keys) fits in LDS, and the step is latency-bound, not
-// bandwidth-bound, so one workgroup does it without any global-memory
-// round trip:
-//   1. thread r walks request r: calibrated confidence, survival (fp32, in
-//      order), forced-row tau terms, and one 64-bit key per candidate slot
-//      (survival bits | 255-k | 2^24-1-r; 0 for a dropped slot);
-//   2. bitonic sort of the keys in LDS, descending, which is exactly
-//      (s desc, k asc, r asc) because the keys are unique;
-//   3. exact tau by an int64 block scan of survival * 2^40 (nearest), then
-//      the fp64 ratio for every b and a (ratio desc, b asc) argmax reduction;
-//   4. per-request counts of the first b* keys give verify_lens.
-// The arithmetic is written with explicit round-to-nearest intrinsics and
-// contraction disabled, so every step has one defined IEEE result.
+// of 64-bit keys) fits in LDS and the step is latency-bound, so one
+// workgroup does it without any global-memory round trip:
+//   1. every (request, position) confidence is calibrated in parallel; then
+//      thread r walks request r for the survival product (fp32, in order),
+//      the forced-row tau terms, and one 64-bit key per candidate slot
+//      (survival bits | 255-k | 2^24-1-r; 0 for a dropped slot). The cost
+//      entries the sweep will need are loaded at kernel start.
+//   2. the global order (s desc, k asc, r asc) is the descending order of
+//      the unique keys. A bucket sort on the survival bits over the observed
+//      range [min, max] (about one key per bucket) places every key with one
+//      LDS atomic, a scan of the bucket counts and an exact rank among its
+//      bucket's few members: four barriers and O(n) work. If a bucket holds
+//      more than 32 keys (many equal survivals), the keys are instead merged
+//      from the per-request runs, which are already descending, pairwise in
+//      ceil(log2 B) rounds of merge path. Both give the same order.
+//   3. (sorted positions spread over all 16 waves)
+//      exact tau by an int64 block scan of survival * 2^40 (nearest), the
+//      fp64 ratio for every b, and a (ratio desc, b asc) argmax reduction;
+//   4. per-request counts of the first b* keys give verify_lens;
+//   5. (fused variant) the exclusive scan, tier and front-packed rows.
+// The arithmetic uses explicit round-to-nearest intrinsics with contraction
+// disabled, so every step has one defined IEEE result.
 #include <float.h>
 
 #include "common.h"
+#include "pack_dev.h"
 #include "sigmoid_cr.h"
 
 #pragma clang fp contract(off)
@@ -38,7 +49,10 @@ namespace dspark {
 namespace {
 
 constexpr int kWaves = kPlanThreads / kWave;
-constexpr int kMaxItems = DSPARK_MAX_CANDIDATES / kPlanThreads;  // sorted keys per thread
+constexpr int kMaxItems = DSPARK_MAX_CANDIDATES / kPlanThreads;  // keys per thread, at most
+constexpr int kMinBuckets = 64;
+constexpr int kMaxBuckets = 4096;
+constexpr int kMaxBucketFill = 32;  // beyond this the bucket rank loop gives way to merging
 
 __device__ inline uint64_t make_key(float s, int k, int r) {
   return ((uint64_t)__float_as_uint(s) << 32) | ((uint64_t)(255 - k) << 24) |
@@ -52,6 +66,73 @@ __device__ inline long long fx40(float s) { return __double2ll_rn((double)s * 0x
 
 __device__ inline bool better(double r1, int b1, double r2, int b2) {
   return r1 > r2 || (r1 == r2 && b1 < b2);
+}
+
+// (ratio desc, b asc) maximum over the wave, left in lane 63. "None" is
+// (-1, INT_MAX): every real ratio is >= 0.
+__device__ inline void wave_argmax(double& r, int& b) {
+  struct RB {
+    double r;
+    int b;
+  };
+  auto step = [&](RB o) {
+    if (better(o.r, o.b, r, b)) {
+      r = o.r;
+      b = o.b;
+    }
+  };
+  step({dpp_t<0x111>(r, -1.0), dpp_t<0x111>(b, 0x7fffffff)});
+  step({dpp_t<0x112>(r, -1.0), dpp_t<0x112>(b, 0x7fffffff)});
+  step({dpp_t<0x114>(r, -1.0), dpp_t<0x114>(b, 0x7fffffff)});
+  step({dpp_t<0x118>(r, -1.0), dpp_t<0x118>(b, 0x7fffffff)});
+  step({dpp_t<0x142, 0xA>(r, -1.0), dpp_t<0x142, 0xA>(b, 0x7fffffff)});
+  step({dpp_t<0x143, 0xC>(r, -1.0), dpp_t<0x143, 0xC>(b, 0x7fffffff)});
+}
+
+
+// Number of keys in the descending run d[0, len) greater than `key`
+// (strict = true) or greater than or equal to it (strict = false).
+template <bool STRICT>
+__device__ inline int count_above(const uint64_t* d, int len, uint64_t key) {
+  int lo = 0, hi = len;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const bool above = STRICT ? d[mid] > key : d[mid] >= key;
+    if (above) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Merges the descending runs src[i*L, (i+1)*L) (the last one may be
+// shorter) pairwise until one run remains, ping-ponging between src and dst.
+// Each key finds its place by one binary search in the partner run: a key of
+// the first run of a pair goes after the partner's strictly greater keys, a
+// key of the second run after the partner's greater-or-equal keys, so equal
+// keys (the zero padding) keep a consistent order and every position is
+// written once. Returns the buffer that holds the merged run. Block-wide.
+__device__ uint64_t* merge_runs(uint64_t* src, uint64_t* dst, int n, int L) {
+  for (int runs = (n + L - 1) / L; runs > 1; runs = (runs + 1) >> 1, L <<= 1) {
+    for (int g = threadIdx.x; g < n; g += kPlanThreads) {
+      const uint64_t key = src[g];
+      const int i = g / L;
+      const int off = g - i * L;
+      int pos;
+      if (i & 1) {
+        pos = (i - 1) * L + off + count_above<false>(src + (i - 1) * L, L, key);
+      } else {
+        const int b0 = (i + 1) * L;
+        const int blen = min(L, max(0, n - b0));
+        pos = i * L + off + count_above<true>(src + b0, blen, key);
+      }
+      dst[pos] = key;
+    }
+    __syncthreads();
+    uint64_t* t = src;
+    src = dst;
+    dst = t;
+  }
+  return src;
 }
 
 __device__ void write_fallback(const PlanArgs& a, int flags) {
@@ -70,72 +151,217 @@ __device__ void write_fallback(const PlanArgs& a, int flags) {
   }
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-  extern __shared__ uint64_t keys[];  // n_sort keys; later reused as B int counters
+// Static window for every request: the fallback for bad data (and, in the
+// fused variant, its packed layout).
+template <bool PACK>
+__device__ void fallback(const PlanArgs& a, const PackArgs& p, int flags, uint64_t* lds, int* w32,
+                         int* s_tier) {
+  write_fallback(a, flags);
+  if (PACK) {
+    int32_t* lens = reinterpret_cast<int32_t*>(lds);
+    for (int r = threadIdx.x; r < a.B; r += kPlanThreads) lens[r] = a.lmax;
+    __syncthreads();
+    pack_block<kPlanThreads>(p, lens, lens + a.B, w32, s_tier, 0);
+  }
+}
+
+// LDS layout of the planner, in bytes (all offsets 8-byte aligned):
+//   [0, K)        keys: one 64-bit key per candidate slot (n_keys slots)
+//   [K, K + X)    phase 1: calibrated confidences (B * gamma floats);
+//                 then the second key buffer (n_keys) followed by the bucket
+//                 counts (kMaxBuckets + 1 ints)
+// The fused pack reuses [0, (2B + 1) * 4) at the end.
+__host__ __device__ inline size_t plan_x_bytes(int B, int gamma, int n_keys) {
+  const size_t c = (size_t)B * gamma * sizeof(float);
+  const size_t k = (size_t)n_keys * sizeof(uint64_t) + (size_t)(kMaxBuckets + 1) * sizeof(int);
+  return c > k ? c : k;
+}
+
+template <bool PACK>
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs p) {
+  extern __shared__ uint64_t lds[];
   __shared__ long long w64[kWaves + 1];
   __shared__ int w32[kWaves + 1];
   __shared__ double wratio[kWaves];
   __shared__ int wb[kWaves];
   __shared__ int s_flags;
+  __shared__ int s_tier;
+  __shared__ unsigned int wmin[kWaves], wmax[kWaves];
+  __shared__ int wbad[kWaves];
+  __shared__ int s_maxb;
 
   const int tid = threadIdx.x;
   const int B = a.B, G = a.gamma, lmin = a.lmin, lmax = a.lmax, span = lmax - lmin;
-  if (tid == 0) s_flags = 0;
+  const int n_keys = B * span;
+  const int ipt = (n_keys + kPlanThreads - 1) / kPlanThreads;  // sorted positions per thread
+  const int base_i = tid * ipt;
+  const int m0 = B * lmin;
+  uint64_t* keys = lds;
+  unsigned char* xreg = reinterpret_cast<unsigned char*>(lds + n_keys);
+  float* conf_c = reinterpret_cast<float*>(xreg);
+  uint64_t* aux = reinterpret_cast<uint64_t*>(xreg);
+  int* bucket = reinterpret_cast<int*>(xreg + (size_t)n_keys * sizeof(uint64_t));
+  if (tid == 0) {
+    s_flags = 0;
+    s_maxb = 0;
+  }
+
+  // cost entries of the budgets this thread will evaluate: b = base_i + e + 1
+  float th[kMaxItems];
+#pragma unroll
+  for (int e = 0; e < kMaxItems; ++e) {
+    const int m = m0 + base_i + e + 1;
+    th[e] = (e < ipt && base_i + e < n_keys && m < a.theta_len) ? a.theta[m] : 0.0f;
+  }
+  const float th0 = a.theta[m0];
+  const float alpha_b = a.alpha[B];
+
+  // ---- 1a. calibrated confidence of every (request, position), in parallel
+  int bad = 0;
+  for (int idx = tid; idx < B * G; idx += kPlanThreads) {
+    const float v = a.conf[idx];
+    float c = v;
+    if (a.kind == DSPARK_IN_CONF_LOGITS) {
+      const float T = a.temps[idx % G];
+      if (!(T > 0.0f && T <= FLT_MAX)) bad = 1;
+      c = sigmoid_cr(__fdiv_rn(v, T));
+    }
+    if (!(c >= 0.0f && c <= 1.0f)) bad = 1;
+    conf_c[idx] = c;
+  }
   __syncthreads();
 
-  // ---- 1. survival, forced terms, candidate keys
+  // ---- 1b. survival, forced terms, candidate keys: one thread per
+  // (request, position). Thread (r, k) forms c_1 * ... * c_k itself, left to
+  // right in fp32: the same operations in the same order as a running
+  // product, so the same bits, without a serial walk along each request.
   long long forced = 0;
-  int n_el = 0, bad = 0;
-  for (int r = tid; r < B; r += kPlanThreads) {
-    float sp = 1.0f;
-    for (int k = 1; k <= G; ++k) {
-      const float v = a.conf[(size_t)r * G + (k - 1)];
-      float s;
-      if (a.kind == DSPARK_IN_SURVIVAL) {
-        s = v;
-        if (!(s >= 0.0f && s <= 1.0f) || (k > 1 && s > sp)) bad = 1;
-      } else {
-        float c = v;
-        if (a.kind == DSPARK_IN_CONF_LOGITS) {
-          const float T = a.temps[k - 1];
-          if (!(T > 0.0f && T <= FLT_MAX)) bad = 1;
-          c = sigmoid_cr(__fdiv_rn(v, T));
-        }
-        if (!(c >= 0.0f && c <= 1.0f)) bad = 1;
-        s = (k == 1) ? c : __fmul_rn(sp, c);
+  int n_el = 0;
+  unsigned int smin = 0xFFFFFFFFu, smax = 0u;
+  for (int idx = tid; idx < B * G; idx += kPlanThreads) {
+    const int r = idx / G;
+    const int k = idx - r * G + 1;
+    const float* cr = conf_c + r * G;
+    float s = cr[0];
+    if (a.kind == DSPARK_IN_SURVIVAL) {
+      s = cr[k - 1];
+      if (k > 1 && s > cr[k - 2]) bad = 1;
+    } else {
+      for (int i = 1; i < k; ++i) s = __fmul_rn(s, cr[i]);
+    }
+    if (a.surv_out) a.surv_out[idx] = s;
+    if (k < lmin) {
+      forced += fx40(s);
+    } else if (k < lmax) {
+      const bool el = s >= a.eps;
+      keys[r * span + (k - lmin)] = el ? make_key(s, k, r) : 0ull;
+      if (el) {
+        ++n_el;
+        const unsigned int sb = __float_as_uint(s);
+        smin = min(smin, sb);
+        smax = max(smax, sb);
       }
-      if (a.surv_out) a.surv_out[(size_t)r * G + (k - 1)] = s;
-      if (k < lmin) {
-        forced += fx40(s);
-      } else if (k < lmax) {
-        const bool el = s >= a.eps;
-        keys[r * span + (k - lmin)] = el ? make_key(s, k, r) : 0ull;
-        n_el += el ? 1 : 0;
-      }
-      sp = s;
     }
   }
-  for (int i = B * span + tid; i < a.n_sort; i += kPlanThreads) keys[i] = 0ull;
-  if (bad) atomicOr(&s_flags, DSPARK_DATA_BAD_CONF);
-  forced = block_sum<long long, kPlanThreads>(forced, w64);
-  n_el = block_sum<int, kPlanThreads>(n_el, w32);
-  if (s_flags) {
-    write_fallback(a, s_flags);
+  // one block reduction for the five quantities: per-wave DPP reductions,
+  // then lane w of every wave combines wave w's partials
+  {
+    const int lane = lane_id(), wave = tid / kWave;
+    auto umin = [](unsigned int x, unsigned int y) { return min(x, y); };
+    auto umax = [](unsigned int x, unsigned int y) { return max(x, y); };
+    auto ior = [](int x, int y) { return x | y; };
+    forced = wave_incl_scan_op(forced, 0ll, OpAdd{});
+    n_el = wave_incl_scan_op(n_el, 0, OpAdd{});
+    smin = wave_incl_scan_op(smin, 0xFFFFFFFFu, umin);
+    smax = wave_incl_scan_op(smax, 0u, umax);
+    bad = wave_incl_scan_op(bad, 0, ior);
+    if (lane == kWave - 1) {
+      w64[wave] = forced;
+      w32[wave] = n_el;
+      wmin[wave] = smin;
+      wmax[wave] = smax;
+      wbad[wave] = bad;
+    }
+    __syncthreads();
+    const bool mine = lane < kWaves;
+    forced = read_lane(wave_incl_scan_op(mine ? w64[lane] : 0ll, 0ll, OpAdd{}), kWave - 1);
+    n_el = read_lane(wave_incl_scan_op(mine ? w32[lane] : 0, 0, OpAdd{}), kWave - 1);
+    smin = read_lane(wave_incl_scan_op(mine ? wmin[lane] : 0xFFFFFFFFu, 0xFFFFFFFFu, umin),
+                     kWave - 1);
+    smax = read_lane(wave_incl_scan_op(mine ? wmax[lane] : 0u, 0u, umax), kWave - 1);
+    bad = read_lane(wave_incl_scan_op(mine ? wbad[lane] : 0, 0, ior), kWave - 1);
+    __syncthreads();
+  }
+  if (bad) {
+    fallback<PACK>(a, p, DSPARK_DATA_BAD_CONF, lds, w32, &s_tier);
     return;
   }
 
-  // ---- 2. bitonic sort, descending
-  const int n = a.n_sort;
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < (n >> 1); i += kPlanThreads) {
-        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-        const int hi = lo + j;
-        const uint64_t x = keys[lo], y = keys[hi];
-        const bool desc = (lo & k) == 0;
-        if (desc ? (x < y) : (x > y)) {
-          keys[lo] = y;
-          keys[hi] = x;
+  // ---- 2. order the candidates by key, descending: bucket sort on the
+  // survival bits over [smin, smax], exact rank inside each bucket
+  const uint64_t* sorted = keys;
+  if (n_el > 0) {
+    const unsigned int hi = smax, range = smax - smin;
+    int nb = kMinBuckets;
+    while (nb < n_el && nb < kMaxBuckets) nb <<= 1;
+    int shift = 0;
+    while ((range >> shift) >= (unsigned int)nb) ++shift;
+    for (int i = tid; i <= nb; i += kPlanThreads) bucket[i] = 0;
+    __syncthreads();
+    uint64_t mk[kMaxItems];
+    int mb[kMaxItems], ms[kMaxItems];
+#pragma unroll
+    for (int e = 0; e < kMaxItems; ++e) {
+      const int g = tid + e * kPlanThreads;
+      mk[e] = (g < n_keys) ? keys[g] : 0ull;
+      mb[e] = 0;
+      ms[e] = 0;
+      if (mk[e]) {
+        mb[e] = (int)((hi - (unsigned int)(mk[e] >> 32)) >> shift);
+        ms[e] = atomicAdd(&bucket[mb[e]], 1);
+      }
+    }
+    __syncthreads();
+    // exclusive scan of the bucket counts (nb <= 4096: up to 4 per thread)
+    const int per = (nb + kPlanThreads - 1) / kPlanThreads;
+    int cnt_local = 0, big = 0;
+    for (int q = 0; q < per; ++q) {
+      const int i = tid * per + q;
+      if (i < nb) {
+        cnt_local += bucket[i];
+        big = max(big, bucket[i]);
+      }
+    }
+    if (big > kMaxBucketFill) atomicMax(&s_maxb, big);
+    int total_cnt;
+    int run = block_excl_scan<int, kPlanThreads>(cnt_local, w32, &total_cnt);
+    for (int q = 0; q < per; ++q) {
+      const int i = tid * per + q;
+      if (i < nb) {
+        const int c = bucket[i];
+        bucket[i] = run;
+        run += c;
+      }
+    }
+    if (tid == 0) bucket[nb] = total_cnt;
+    __syncthreads();
+    if (s_maxb) {
+      // a crowded bucket (many equal or nearly equal survivals): merge the
+      // per-request runs instead, O(n log B) whatever the values
+      sorted = merge_runs(keys, aux, n_keys, span);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kMaxItems; ++e) {
+        if (mk[e]) aux[bucket[mb[e]] + ms[e]] = mk[e];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < kMaxItems; ++e) {
+        if (mk[e]) {
+          const int b0 = bucket[mb[e]], b1 = bucket[mb[e] + 1];
+          int rank = 0;
+          for (int j = b0; j < b1; ++j) rank += aux[j] > mk[e] ? 1 : 0;
+          keys[b0 + rank] = mk[e];
         }
       }
       __syncthreads();
@@ -143,15 +369,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
 
   // ---- 3. exact tau scan, ratio sweep, argmax
-  const int ipt = n >= kPlanThreads ? n / kPlanThreads : 1;
-  const int i0 = tid * ipt;
+  uint64_t x[kMaxItems];
   long long fxv[kMaxItems];
   long long local = 0;
 #pragma unroll
-  for (int t = 0; t < kMaxItems; ++t) {
-    fxv[t] = 0;
-    if (t < ipt && i0 + t < n_el) fxv[t] = fx40(key_s(keys[i0 + t]));
-    local += fxv[t];
+  for (int e = 0; e < kMaxItems; ++e) {
+    const bool in = e < ipt && base_i + e < n_el;
+    x[e] = in ? sorted[base_i + e] : 0ull;
+    fxv[e] = in ? fx40(key_s(x[e])) : 0;
+    local += fxv[e];
   }
   long long total_fx;
   const long long offset = block_excl_scan<long long, kPlanThreads>(local, w64, &total_fx);
@@ -159,30 +385,29 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
   const int lo_b = min(max(a.b_lo, 0), n_el);
   const int hi_b = a.b_hi < 0 ? n_el : min(a.b_hi, n_el);
-  const double t_fixed = __dadd_rn((double)a.bias, (double)a.alpha[B]);
-  const int m0 = B * lmin;
+  const double t_fixed = __dadd_rn((double)a.bias, (double)alpha_b);
 
   double tau_v[kMaxItems + 1], ratio_v[kMaxItems + 1];
   double best_r = -1.0;
   int best_b = 0x7fffffff;
   int cost_bad = 0;
-  long long run = base + offset;
-  // slot 0 of thread 0 is b = 0; slot t + 1 is b = i0 + t + 1
+  long long run_fx = base + offset;
+  // slot 0 of thread 0 is b = 0; slot t >= 1 is b = base_i + t
 #pragma unroll
   for (int t = 0; t <= kMaxItems; ++t) {
     int b;
     if (t == 0) {
       b = (tid == 0) ? 0 : -1;
     } else {
-      run += fxv[t - 1];
-      b = (t - 1 < ipt && i0 + t <= n_el) ? i0 + t : -1;
+      run_fx += fxv[t - 1];
+      b = (t <= ipt && base_i + t <= n_el) ? base_i + t : -1;
     }
     tau_v[t] = 0.0;
     ratio_v[t] = 0.0;
     if (b < 0) continue;
-    const long long tfx = (t == 0) ? base : run;
+    const long long tfx = (t == 0) ? base : run_fx;
     const double tau = __ll2double_rn(tfx) * 0x1p-40;
-    const double T = __dadd_rn(t_fixed, (double)a.theta[m0 + b]);
+    const double T = __dadd_rn(t_fixed, (double)(t == 0 ? th0 : th[t - 1]));
     const double ratio = __ddiv_rn(tau, T);
     tau_v[t] = tau;
     ratio_v[t] = ratio;
@@ -195,94 +420,78 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     }
   }
   if (cost_bad) atomicOr(&s_flags, DSPARK_DATA_BAD_COST);
-  // argmax over the block: (ratio desc, b asc)
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const double orat = __shfl_xor(best_r, off, kWave);
-    const int ob = __shfl_xor(best_b, off, kWave);
-    if (better(orat, ob, best_r, best_b)) {
-      best_r = orat;
-      best_b = ob;
-    }
-  }
+  wave_argmax(best_r, best_b);
   const int lane = lane_id(), wave = tid / kWave;
-  if (lane == 0) {
+  if (lane == kWave - 1) {
     wratio[wave] = best_r;
     wb[wave] = best_b;
   }
   __syncthreads();
   if (s_flags) {
-    write_fallback(a, s_flags);
+    fallback<PACK>(a, p, s_flags, lds, w32, &s_tier);
     return;
   }
-  double br = wratio[0];
-  int bstar = wb[0];
-  for (int w = 1; w < kWaves; ++w) {
-    if (better(wratio[w], wb[w], br, bstar)) {
-      br = wratio[w];
-      bstar = wb[w];
+  double br = lane < kWaves ? wratio[lane] : -1.0;
+  int bstar = lane < kWaves ? wb[lane] : 0x7fffffff;
+  wave_argmax(br, bstar);
+  br = read_lane(br, kWave - 1);
+  bstar = read_lane(bstar, kWave - 1);
+
+#pragma unroll
+  for (int t = 0; t <= kMaxItems; ++t) {
+    const int b = (t == 0) ? (tid == 0 ? 0 : -1) : ((t <= ipt && base_i + t <= n_el) ? base_i + t : -1);
+    if (b < 0) continue;
+    if (a.sweep) {
+      a.sweep[2 * b] = tau_v[t];
+      a.sweep[2 * b + 1] = ratio_v[t];
+    }
+    if (b == bstar) {
+      a.val[0] = tau_v[t];
+      a.val[1] = ratio_v[t];
     }
   }
-
   if (a.sweep) {
-    const int nb = B * G + 1;
-#pragma unroll
-    for (int t = 0; t <= kMaxItems; ++t) {
-      const int b = (t == 0) ? (tid == 0 ? 0 : -1) : ((t - 1 < ipt && i0 + t <= n_el) ? i0 + t : -1);
-      if (b >= 0) {
-        a.sweep[2 * b] = tau_v[t];
-        a.sweep[2 * b + 1] = ratio_v[t];
-      }
-    }
-    for (int b = n_el + 1 + tid; b < nb; b += kPlanThreads) {
+    for (int b = n_el + 1 + tid; b < B * G + 1; b += kPlanThreads) {
       a.sweep[2 * b] = __builtin_nan("");
       a.sweep[2 * b + 1] = __builtin_nan("");
     }
   }
 
   // ---- 4. verify_lens = L_min + #(first b* keys of each request)
-  int my_r[kMaxItems];
-#pragma unroll
-  for (int t = 0; t < kMaxItems; ++t) {
-    my_r[t] = (t < ipt && i0 + t < bstar) ? key_r(keys[i0 + t]) : -1;
-  }
-  __syncthreads();
-  int* cnt = reinterpret_cast<int*>(keys);
-  for (int r = tid; r < B; r += kPlanThreads) cnt[r] = 0;
+  int32_t* cnt = reinterpret_cast<int32_t*>(lds);  // the keys now live in registers
+  for (int r = tid; r < B; r += kPlanThreads) cnt[r] = lmin;
   __syncthreads();
 #pragma unroll
-  for (int t = 0; t < kMaxItems; ++t) {
-    if (my_r[t] >= 0) atomicAdd(&cnt[my_r[t]], 1);
+  for (int e = 0; e < kMaxItems; ++e) {
+    if (e < ipt && base_i + e < bstar) atomicAdd(&cnt[key_r(x[e])], 1);
   }
   __syncthreads();
-  for (int r = tid; r < B; r += kPlanThreads) a.lens[r] = lmin + cnt[r];
+  for (int r = tid; r < B; r += kPlanThreads) a.lens[r] = cnt[r];
   if (tid == 0) {
     a.meta[0] = bstar;
     a.meta[1] = n_el;
     a.meta[2] = 0;
     a.meta[3] = m0 + bstar;
   }
-  // tau(b*) and ratio(b*) from the thread that owns b*
-#pragma unroll
-  for (int t = 0; t <= kMaxItems; ++t) {
-    const int b = (t == 0) ? (tid == 0 ? 0 : -1) : ((t - 1 < ipt && i0 + t <= n_el) ? i0 + t : -1);
-    if (b == bstar) {
-      a.val[0] = tau_v[t];
-      a.val[1] = ratio_v[t];
-    }
-  }
+  if (PACK) pack_block<kPlanThreads>(p, cnt, cnt + B, w32, &s_tier, 0);
 }
 
 }  // namespace
 
-size_t plan_lds_bytes(int B, int n_sort) {
-  size_t k = (size_t)n_sort * sizeof(uint64_t);
-  size_t c = (size_t)B * sizeof(int);
-  return k > c ? k : c;
+size_t plan_lds_bytes(int B, int gamma, int n_keys) {
+  const size_t main = (size_t)n_keys * sizeof(uint64_t) + plan_x_bytes(B, gamma, n_keys);
+  const size_t pk = (size_t)(2 * B + 1) * sizeof(int32_t);  // lens + cu for the fused pack
+  return main > pk ? main : pk;
 }
 
-hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
-  const size_t lds = plan_lds_bytes(a.B, a.n_sort);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), lds, s, a);
+hipError_t launch_plan(const PlanArgs& a, const PackArgs* p, hipStream_t s) {
+  const size_t lds = plan_lds_bytes(a.B, a.gamma, a.B * (a.lmax - a.lmin));
+  if (p) {
+    hipLaunchKernelGGL(plan_kernel<true>, dim3(1), dim3(kPlanThreads), lds, s, a, *p);
+  } else {
+    PackArgs none{};
+    hipLaunchKernelGGL(plan_kernel<false>, dim3(1), dim3(kPlanThreads), lds, s, a, none);
+  }
   return hipGetLastError();
 }
 

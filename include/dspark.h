@@ -9,6 +9,7 @@
  *                    sweep -> verify_lens
  *   dspark_pack      verify_lens -> cu_seqlens, front-packed verify rows,
  *                    packed total rounded up to a captured tier
+ *   dspark_plan_pack both of the above in one launch
  *   dspark_accept    packed target logits -> per-row argmax -> leading-match
  *                    count, bonus token, commit lengths, output tokens
  *   dspark_tv_accept (optional) soft accept-rate 1 - TV(softmax q, softmax p)
@@ -182,6 +183,29 @@ dspark_status dspark_pack(int32_t B, int32_t gamma, const int32_t* verify_lens,
                           const int32_t* prefix_lens, int32_t* cu_seqlens,
                           int32_t* packed_ids, int32_t* packed_req, int32_t* packed_pos,
                           int32_t* pack_meta, void* stream);
+
+/*
+ * dspark_plan_pack - dspark_plan followed by dspark_pack in one launch.
+ *
+ * Same arithmetic, arguments and outputs as dspark_plan, then dspark_pack
+ * on the verify_lens just computed (their ragged layout, tier and packed
+ * rows), in the same workgroup. This saves one kernel launch per step.
+ * verify_lens is written as by dspark_plan and packed from the same values.
+ * In the bad-data fallback the static window L_max is packed.
+ * Argument rules are the union of both calls. Pack's own status bit is
+ * never set here, because planned lengths are always in range.
+ */
+dspark_status dspark_plan_pack(int32_t B, int32_t gamma, dspark_input kind, const float* conf,
+                               const float* sts_temp, int32_t min_verify_len,
+                               int32_t max_verify_len, float survival_eps, int32_t budget_lo,
+                               int32_t budget_hi, float cost_bias, const float* cost_alpha,
+                               int32_t alpha_len, const float* cost_theta, int32_t theta_len,
+                               int32_t* verify_lens, int32_t* plan_meta, double* plan_val,
+                               float* survival_out, double* sweep_out, const int32_t* anchor_ids,
+                               const int32_t* draft_tokens, const int32_t* tiers_host,
+                               int32_t num_tiers, const int32_t* prefix_lens, int32_t* cu_seqlens,
+                               int32_t* packed_ids, int32_t* packed_req, int32_t* packed_pos,
+                               int32_t* pack_meta, void* stream);
 
 /*
  * dspark_accept - greedy accept over packed target logits.

@@ -33,7 +33,7 @@ def _declared():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for n in ("dspark_plan", "dspark_pack", "dspark_accept", "dspark_tv_accept",
+    for n in ("dspark_plan", "dspark_pack", "dspark_plan_pack", "dspark_accept", "dspark_tv_accept",
               "dspark_accept_workspace_size", "dspark_status_str", "dspark_last_error",
               "dspark_version"):
         assert n in names
@@ -80,6 +80,27 @@ def _plan(**kw):
 def test_plan_argument_errors(kw, code):
     assert _plan(**kw) == code
     assert _lib.last_error() != ""
+
+
+def test_plan_pack_argument_errors():
+    tiers = (ctypes.c_int32 * 2)(8, 20)
+    base = dict(B=4, gamma=4, kind=0, conf=FAKE, temp=FAKE, mn=1, mx=5, eps=1e-3, lo=0, hi=-1,
+                bias=0.5, alpha=FAKE, alen=5, theta=FAKE, tlen=21, lens=FAKE, meta=FAKE, val=FAKE,
+                surv=NULL, sweep=NULL, anchors=FAKE, drafts=FAKE,
+                tiers=ctypes.cast(tiers, ctypes.c_void_p), ntiers=2, prefix=NULL, cu=FAKE,
+                ids=FAKE, req=NULL, pos=NULL, pmeta=FAKE, stream=NULL)
+
+    def run(**kw):
+        d = dict(base)
+        d.update(kw)
+        return _lib.lib().dspark_plan_pack(*d.values())
+
+    assert run(gamma=0) == _lib.E_INVALID  # plan rule
+    assert run(tlen=20) == _lib.E_INVALID  # plan rule
+    assert run(ntiers=1) == _lib.E_INVALID  # last tier 8 < B * (gamma + 1) = 20
+    assert run(anchors=NULL) == _lib.E_INVALID  # pack rule
+    assert run(cu=NULL) == _lib.E_INVALID
+    assert "dspark_plan_pack" in _lib.last_error()
 
 
 def _pack(tiers, **kw):

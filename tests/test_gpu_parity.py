@@ -18,7 +18,7 @@ import torch
 import oracle
 from oracle.accept import as_f32_rows
 from workloads import make
-from _gpu import accept, gather_packed, logits_up, pack, plan, say, tv
+from _gpu import accept, gather_packed, logits_up, pack, plan, plan_pack, say, tv
 
 pytestmark = pytest.mark.gpu
 
@@ -101,6 +101,14 @@ def test_plan_edge_cases():
     cases.append((6, 3, oracle.IN_COND, c, None, 0, 99, 0.5, 1, 3))
     c2 = np.array([[1.0, 0.5], [0.5, 1.0]], np.float32)
     cases.append((2, 2, oracle.IN_COND, c2, None, 1, 3, 0.0, 2, 2))
+    # exactly one eligible candidate, sitting in the last request's slots
+    c1 = np.array([[0.01, 0.5], [0.02, 0.5], [0.9, 0.01]], np.float32)
+    cases.append((3, 2, oracle.IN_COND, c1, None, 1, 3, 0.5, 0, -1))
+    # many identical survivals (crowded buckets -> merge fallback), B not a power of two
+    c3 = np.ones((300, 6), np.float32)
+    c3[::7] = 0.5
+    cases.append((300, 6, oracle.IN_COND, c3, None, 1, 7, 0.0, 0, -1))
+    cases.append((300, 6, oracle.IN_COND, c3, None, 2, 5, 0.0, 10, 700))
     s = np.sort(rng.random((40, 5)).astype(np.float32), axis=1)[:, ::-1].copy()
     cases.append((40, 5, oracle.IN_SURVIVAL, s, None, 1, 6, 0.05, 0, -1))
     z = rng.normal(0, 30, (50, 7)).astype(np.float32)  # saturating confidences, subnormal survivals
@@ -215,6 +223,67 @@ def test_pack_edge_cases():
     got = pack(0, 3, np.zeros(0, np.int32), np.zeros(0, np.int32), np.zeros((0, 3), np.int32),
                [4], tag="B=0")
     assert got["meta"].tolist() == [0, 4, 0] and got["cu_seqlens"].tolist() == [0]
+
+
+# ---------------------------------------------------------------- fused plan + pack
+
+def _check_plan_pack(w, args, got_plan, got_pack):
+    ref_plan = oracle.plan(*args)
+    _check_plan(got_plan, ref_plan)
+    ref_pack = oracle.pack(w.B, w.gamma, ref_plan["verify_lens"], w.anchors, w.drafts, w.tiers,
+                           w.prefix_lens)
+    tier = int(ref_pack["meta"][1])
+    _eq(got_pack["meta"], ref_pack["meta"], "pack_meta")
+    _eq(got_pack["cu_seqlens"], ref_pack["cu_seqlens"], "cu_seqlens")
+    for k in ("ids", "req", "pos"):
+        _eq(got_pack[k][:tier], ref_pack[k], k)
+        assert np.all(got_pack[k][tier:] == -7), f"{k} written past the tier"
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+@pytest.mark.parametrize("seed", [None, 401, 402])
+def test_plan_pack_parity(cfg, seed):
+    w = make(cfg, seed=seed, logits=False)
+    args = (w.B, w.gamma, oracle.IN_CONF_LOGITS, w.conf, w.temps, w.min_len, w.max_len, w.eps,
+            w.b_lo, w.b_hi, w.bias, w.alpha, w.theta)
+    gp, gk = plan_pack(*args, w.anchors, w.drafts, w.tiers, w.prefix_lens, tag=f"cfg{cfg}")
+    _check_plan_pack(w, args, gp, gk)
+
+
+def test_plan_pack_fallback_and_limits():
+    w = make(1, logits=False)
+    theta = w.theta.copy()
+    theta[w.B + 2] = -1.0  # bad cost: static window, packed
+    args = (w.B, w.gamma, oracle.IN_CONF_LOGITS, w.conf, w.temps, w.min_len, w.max_len, w.eps,
+            w.b_lo, w.b_hi, w.bias, w.alpha, theta)
+    gp, gk = plan_pack(*args, w.anchors, w.drafts, w.tiers, w.prefix_lens, tag="bad cost")
+    _check_plan_pack(w, args, gp, gk)
+    assert gk["meta"][0] == w.B * (w.gamma + 1)
+    conf = w.conf.copy()
+    conf[0, 0] = np.nan  # bad confidence
+    args = args[:3] + (conf,) + args[4:12] + (w.theta,)
+    gp, gk = plan_pack(*args, w.anchors, w.drafts, w.tiers, w.prefix_lens, tag="bad conf")
+    _check_plan_pack(w, args, gp, gk)
+    # largest candidate count: B * gamma = 8192, cfg-3-like inputs
+    rng = np.random.default_rng(17)
+    B, G = 1024, 8
+    conf = (rng.normal(1.2, 1.2, (B, G)) - 0.3 * np.arange(1, G + 1)).astype(np.float32)
+    temps = rng.uniform(0.7, 2.0, G).astype(np.float32)
+    alpha = (0.005 * np.arange(B + 1)).astype(np.float32)
+    theta = (0.5 + 0.002 * np.arange(B * (G + 1) + 1)).astype(np.float32)
+    anchors = rng.integers(0, 1000, B).astype(np.int32)
+    drafts = rng.integers(0, 1000, (B, G)).astype(np.int32)
+    tiers = np.array([1024, 2048, 4096, 8192, 9216], np.int32)
+
+    class W:
+        pass
+
+    wl = W()
+    wl.B, wl.gamma, wl.anchors, wl.drafts, wl.tiers, wl.prefix_lens = B, G, anchors, drafts, tiers, None
+    args = (B, G, oracle.IN_CONF_LOGITS, conf, temps, 1, G + 1, 1e-3, 0, -1, np.float32(0.5),
+            alpha, theta)
+    gp, gk = plan_pack(*args, anchors, drafts, tiers, None, tag="B*gamma=8192")
+    _check_plan_pack(wl, args, gp, gk)
 
 
 # ---------------------------------------------------------------- accept
