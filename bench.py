@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-tv", action="store_true",
+                    help="skip the soft accept-rate pass (B=256, gamma=16, V=129280 bf16)")
     return ap.parse_args()
 
 
@@ -74,6 +76,95 @@ def traffic_for(total_rows):
     if rec.get("accept_hip_sha256") != src_hash or rec.get("rows") != total_rows:
         return None
     return rec.get("bytes_per_launch")
+
+
+def tv_bytes(B, gamma, V, esize):
+    """Algorithmic bytes of one soft accept-rate call: both logit rows of every
+    (draft, target) pair once, plus the accept rates and survivals written."""
+    return 2 * B * gamma * V * esize + 2 * B * gamma * 4
+
+
+def tv_section(dv, torch, dev, stream, reps):
+    """The soft accept-rate pass and the chained step that uses it (TV
+    accept-rate -> cumprod -> plan in survival mode -> pack -> accept) at
+    B=256, gamma=16, V=129280 bf16."""
+    from workloads import make
+
+    w = make(4)
+    B, G, V = w.B, w.gamma, w.V
+    f32 = torch.float32
+    q = torch.from_numpy(w.draft_logits.reshape(B * G, V).view(np.int16)).to(dev)
+    p = torch.from_numpy(w.target.reshape(B * (G + 1), V).view(np.int16)).to(dev)
+    q, p = q.view(torch.bfloat16), p.view(torch.bfloat16)
+    a = torch.empty(B * G, dtype=f32, device=dev)
+    S = torch.empty(B * G, dtype=f32, device=dev)
+
+    def tv():
+        dv.dspark_tv_accept(B, G, V, dv.BF16, q, V, p, V, G + 1, a, S, stream)
+
+    for _ in range(3):
+        tv()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(reps):
+        tv()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    tv_us = 1e3 * ev0.elapsed_time(ev1) / reps
+    gbs = tv_bytes(B, G, V, 2) / (tv_us * 1e-6) / 1e9
+
+    # chained step on the TV survivals
+    def t(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    alpha_t, theta_t = t(w.alpha), t(w.theta)
+    anchors_t, drafts_t, prefix_t = t(w.anchors), t(w.drafts), t(w.prefix_lens)
+    tiers = [int(x) for x in w.tiers]
+    po = dv.alloc_plan_outputs(B, G, dev, survival=False, sweep=False)
+    ko = dv.alloc_pack_outputs(B, tiers[-1], dev)
+
+    def plan_pack():
+        dv.dspark_plan_pack(B, G, dv.IN_SURVIVAL, S, None, w.min_len, w.max_len, w.eps,
+                            w.b_lo, w.b_hi, float(w.bias), alpha_t, theta_t, po,
+                            anchors_t, drafts_t, tiers, prefix_t, ko, stream)
+
+    tv()
+    plan_pack()
+    torch.cuda.synchronize()
+    lens = po.verify_lens.cpu().numpy()
+    cu = ko.cu_seqlens.cpu().numpy()
+    total, tier = int(ko.pack_meta[0].item()), int(ko.pack_meta[1].item())
+    req = np.repeat(np.arange(B), lens)
+    src = torch.from_numpy(req * (G + 1) + np.arange(total) - np.repeat(cu[:-1], lens)).to(dev)
+    packed = torch.zeros(tier, V, dtype=torch.int16, device=dev)
+    packed[:total] = p.view(torch.int16).index_select(0, src)
+    packed = packed.view(torch.bfloat16)
+    ao = dv.alloc_accept_outputs(B, G, tier, V, dv.BF16, dev)
+
+    def chain():
+        tv()
+        plan_pack()
+        dv.dspark_accept(B, G, V, dv.BF16, packed, V, tier, ko.cu_seqlens, drafts_t, prefix_t,
+                         ao, stream)
+
+    for _ in range(3):
+        chain()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(reps):
+        chain()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    chain_us = 1e3 * ev0.elapsed_time(ev1) / reps
+    assert np.array_equal(po.verify_lens.cpu().numpy(), lens)
+    assert int(ao.accept_meta[1].item()) == 0
+    return {
+        "workload": f"{w.spec.name}: B={B} gamma={G} V={V} bf16",
+        "tv_us": tv_us, "GB/s": gbs, "frac": gbs / PEAK_HBM_GBS,
+        "bytes_per_launch": tv_bytes(B, G, V, 2),
+        "chained_step_us": chain_us, "rows": total, "tier": tier,
+    }
 
 
 def cpu_baseline(w, lens_ref, packed_host, total, budget_s):
@@ -284,6 +375,13 @@ def main():
 
     acc_bytes = accept_bytes(total, B, G, V, esize)
     achieved = acc_bytes / (acc_mean_us * 1e-6) / 1e9
+    del stat_bufs
+    torch.cuda.empty_cache()
+
+    tv_res = None
+    if not args.no_tv:
+        log("soft accept-rate pass at B=256, gamma=16, V=129280 bf16")
+        tv_res = tv_section(dv, torch, dev, stream, 20)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -308,7 +406,8 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_for(total),
-                     "kernel": "accept_kernel<bf16>", "bytes_per_launch": acc_bytes,
+                     "kernel": "dspark_accept: accept_argmax_kernel<bf16> then accept_finalize_kernel",
+                     "bytes_per_launch": acc_bytes,
                      "mean_us": acc_mean_us},
         "cpu_baseline": cpu,
         "steps_per_s_graph": 1e3 / ms_step_graph,
@@ -319,6 +418,7 @@ def main():
         "accept_us_median": statistics.median(acc_us),
         "accept_static": {"rows": static_rows, "us": static_us, "GB/s": static_gbs,
                           "frac": static_gbs / PEAK_HBM_GBS},
+        "tv_pass": tv_res,
         "wall_s_timed": wall,
     }
     print(json.dumps(out), flush=True)
