@@ -7,8 +7,8 @@ dspark_accept (vocab-wide argmax over the packed target logits, leading-match
 count, bonus, commit, output tokens), on the B=256, gamma=8, V=129280 bf16
 workload. Every input, including the packed target logits a forward pass
 would have produced, is resident in HBM before the timed region. Three
-copies of the packed logits rotate, about 1 GB in all, so the 256 MB
-Infinity Cache cannot serve repeated reads.
+copies of the packed logits rotate (about 0.56 GB of live rows), so the
+256 MB Infinity Cache cannot serve repeated reads.
 
 Prints one JSON line. ``value`` is steps/s (eager launches). ``roofline`` is
 the accept kernel's achieved HBM bandwidth: algorithmic bytes per launch over
