@@ -83,7 +83,7 @@ struct TvArgs {
   float* a_out;
   float* s_out;
 };
-constexpr int kTvThreads = 256;
+constexpr int kTvThreads = 1024;
 hipError_t launch_tv(const TvArgs& a, dspark_dtype dt, hipStream_t s);
 
 // ---------------------------------------------------------------- helpers

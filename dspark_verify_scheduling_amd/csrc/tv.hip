@@ -6,17 +6,23 @@
 // equals sum_x min(p(x), q(x)) under rejection sampling, and
 // confidence_prefix_targets = accept_rate.cumprod).
 //
-// Computation. With log-partitions A_q = max q + ln sum e^(q - max q) (and the
-// same for p), min(u_x, v_x) = exp(min(q_x - A_q, p_x - A_p)). So
-// a = sum_x exp(min(q_x - A_q, p_x - A_p)) needs one exponential per element
-// pair once the partitions are known:
-//   pass 1: online (max, sum-exp) of q and of p, per thread, merged over the
-//           workgroup;
-//   pass 2: the sum of exp(min(...)). The pair's rows (about 0.5 MB at
-//           V = 129280 bf16) were just read, so the re-read is served mostly
-//           from the caches.
-// Exponentials are exp2 of base-2 scaled values (hardware v_exp_f32). The
-// result is clamped to at most 1; rounding can exceed 1 by ~1e-7.
+// Computation. With base-2 log-partitions A_q = log2 sum_x 2^(q_x log2 e) (and
+// the same for p), min(u_x, v_x) = 2^min(q_x log2 e - A_q, p_x log2 e - A_p),
+// so a = sum_x 2^min(...) needs one exponential per element pair once the
+// partitions are known. One workgroup of 1024 threads per (draft row, target
+// row) pair:
+//   pass 1: each thread streams batches of 4 + 4 16-byte vectors of q and p
+//           and keeps a running (max, sum of 2^(x log2 e - max)) per row,
+//           rescaled once per batch; the workgroup merges the threads';
+//   pass 2: the sum of 2^min(...) over the same rows.
+// The pair's rows (about 0.5 MB at V = 129280 bf16) do not stay in the 4 MB
+// L2 of an XCD between the passes while 32 CUs stream, so pass 2 reads them
+// again from beyond L2 (measured: about twice the algorithmic bytes; limiting
+// residency to one pair per CU did not make the Infinity Cache serve the
+// re-read). Pass 1 uses ordinary loads, pass 2 nontemporal ones (last use).
+// Exponentials are the raw v_exp_f32 (exp2 without the denormal-range fix-up:
+// results below 2^-126 are negligible in a sum that is about 1). The result is
+// clamped to at most 1; rounding can exceed 1 by ~1e-7.
 #include <float.h>
 
 #include "common.h"
@@ -28,14 +34,18 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kWaves = kTvThreads / kWave;
+constexpr int kU = 4;  // vectors of q (and of p) per thread per batch
+
+__device__ inline float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <dspark_dtype DT>
 __device__ inline void widen(const u32x4& d, float* x) {
   if constexpr (DT == DSPARK_BF16) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      x[2 * w] = __uint_as_float(d[w] << 16);
-      x[2 * w + 1] = __uint_as_float(d[w] & 0xFFFF0000u);
+      const unsigned int v = d[w];
+      x[2 * w] = __uint_as_float(v << 16);
+      x[2 * w + 1] = __uint_as_float(v & 0xFFFF0000u);
     }
   } else {
 #pragma unroll
@@ -52,52 +62,45 @@ __device__ inline float elem(const unsigned char* row, int i) {
   }
 }
 
-struct MS {
-  float m, s;  // running max and sum of exp2(y - m), y in base-2 units
+// Running log-partition state in base-2 units: mL = max(x) * log2 e, clamped
+// to >= -FLT_MAX (so -inf inputs and empty states stay finite), and
+// s = sum 2^(x log2 e - mL).
+struct Stat {
+  float mL, s;
 };
 
-__device__ inline MS ms_merge(MS a, MS b) {
-  const float m = fmaxf(a.m, b.m);
-  return {m, a.s * exp2f(a.m - m) + b.s * exp2f(b.m - m)};
+__device__ inline Stat stat_merge(Stat a, Stat b) {
+  const float m = fmaxf(a.mL, b.mL);
+  return {m, a.s * exp2_raw(a.mL - m) + b.s * exp2_raw(b.mL - m)};
 }
 
+// Adds N values whose maximum is bm.
 template <int N>
-__device__ inline void ms_add(MS& st, const float* x) {
-  float y[N];
-  float mloc = st.m;
+__device__ inline void stat_add(Stat& st, const float* x, float bm) {
+  const float mL = fmaxf(st.mL, fmaxf(bm * kLog2e, -FLT_MAX));
+  float acc0 = st.s * exp2_raw(st.mL - mL), acc1 = 0.0f;
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    y[i] = x[i] * kLog2e;
-    mloc = fmaxf(mloc, y[i]);
+  for (int i = 0; i < N; i += 2) {
+    acc0 += exp2_raw(__fmaf_rn(x[i], kLog2e, -mL));
+    acc1 += exp2_raw(__fmaf_rn(x[i + 1], kLog2e, -mL));
   }
-  float acc = st.s * exp2f(st.m - mloc);
-#pragma unroll
-  for (int i = 0; i < N; ++i) acc += exp2f(y[i] - mloc);
-  st = {mloc, acc};
+  st = {mL, acc0 + acc1};
 }
 
-__device__ inline MS block_ms(MS v, float* sm, float* ss) {
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    MS o{__shfl_xor(v.m, off, kWave), __shfl_xor(v.s, off, kWave)};
-    v = ms_merge(v, o);
-  }
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  if (lane == 0) {
-    sm[wave] = v.m;
-    ss[wave] = v.s;
-  }
-  __syncthreads();
-  MS t{sm[0], ss[0]};
-  for (int w = 1; w < kWaves; ++w) t = ms_merge(t, MS{sm[w], ss[w]});
-  __syncthreads();
-  return t;
+__device__ inline Stat block_stat(Stat v, Stat* ws) {
+  const Stat ident{-FLT_MAX, 0.0f};
+  auto op = [](Stat a, Stat b) { return stat_merge(a, b); };
+  return block_reduce<Stat, kTvThreads>(v, ident, op, ws);
 }
 
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kTvThreads) void tv_kernel(TvArgs a) {
-  __shared__ float sm[kWaves], ss[kWaves];
-  __shared__ float sd[kWaves];
+  __shared__ Stat ws[kWaves];
+  __shared__ float wsf[kWaves];
   constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
+  constexpr int kN = kU * kEpv;  // values of one row per thread per batch
+  // -inf in every lane: no effect on a maximum, 2^-inf = 0 in a sum
+  constexpr unsigned int kNegInf = DT == DSPARK_BF16 ? 0xFF80FF80u : 0xFF800000u;
   const int pair = blockIdx.x;
   const int r = pair / a.gamma;
   const int k0 = pair - r * a.gamma;
@@ -106,53 +109,87 @@ __global__ __launch_bounds__(kTvThreads) void tv_kernel(TvArgs a) {
   const u32x4* qv = reinterpret_cast<const u32x4*>(qrow);
   const u32x4* pv = reinterpret_cast<const u32x4*>(prow);
   const int tid = threadIdx.x;
+  const u32x4 fill = (u32x4){kNegInf, kNegInf, kNegInf, kNegInf};
 
   // pass 1: log-partitions
-  MS sq{-FLT_MAX, 0.0f}, sp{-FLT_MAX, 0.0f};
-  for (int v = tid; v < a.nvec; v += kTvThreads) {
-    const u32x4 dq = qv[v], dp = pv[v];
-    float x[kEpv];
-    widen<DT>(dq, x);
-    ms_add<kEpv>(sq, x);
-    widen<DT>(dp, x);
-    ms_add<kEpv>(sp, x);
+  Stat sq{-FLT_MAX, 0.0f}, sp{-FLT_MAX, 0.0f};
+  for (int v0 = tid; v0 < a.nvec; v0 += kTvThreads * kU) {
+    u32x4 dq[kU], dp[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int v = v0 + u * kTvThreads;
+      dq[u] = fill;
+      dp[u] = fill;
+      if (v < a.nvec) {
+        dq[u] = qv[v];
+        dp[u] = pv[v];
+      }
+    }
+    float x[kN], y[kN];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      widen<DT>(dq[u], x + u * kEpv);
+      widen<DT>(dp[u], y + u * kEpv);
+    }
+    float bq = x[0], bp = y[0];
+#pragma unroll
+    for (int i = 1; i < kN; ++i) {
+      bq = fmaxf(bq, x[i]);
+      bp = fmaxf(bp, y[i]);
+    }
+    stat_add<kN>(sq, x, bq);
+    stat_add<kN>(sp, y, bp);
   }
   if (tid == 0) {
     for (int t = 0; t < a.tail; ++t) {
       const int i = a.nvec * kEpv + t;
-      float x = elem<DT>(qrow, i);
-      ms_add<1>(sq, &x);
-      x = elem<DT>(prow, i);
-      ms_add<1>(sp, &x);
+      float x[2] = {elem<DT>(qrow, i), -INFINITY};
+      stat_add<2>(sq, x, x[0]);
+      float y[2] = {elem<DT>(prow, i), -INFINITY};
+      stat_add<2>(sp, y, y[0]);
     }
   }
-  sq = block_ms(sq, sm, ss);
-  sp = block_ms(sp, sm, ss);
-  const float aq = sq.m + log2f(sq.s);  // base-2 log-partitions
-  const float ap = sp.m + log2f(sp.s);
+  sq = block_stat(sq, ws);
+  sp = block_stat(sp, ws);
+  const float aq = sq.mL + log2f(sq.s);  // base-2 log-partitions
+  const float ap = sp.mL + log2f(sp.s);
 
   // pass 2: sum of min(u, v)
-  float acc = 0.0f;
-  for (int v = tid; v < a.nvec; v += kTvThreads) {
-    const u32x4 dq = __builtin_nontemporal_load(qv + v);
-    const u32x4 dp = __builtin_nontemporal_load(pv + v);
-    float xq[kEpv], xp[kEpv];
-    widen<DT>(dq, xq);
-    widen<DT>(dp, xp);
-    float part = 0.0f;
+  float acc0 = 0.0f, acc1 = 0.0f;
+  for (int v0 = tid; v0 < a.nvec; v0 += kTvThreads * kU) {
+    u32x4 dq[kU], dp[kU];
 #pragma unroll
-    for (int i = 0; i < kEpv; ++i) {
-      part += exp2f(fminf(xq[i] * kLog2e - aq, xp[i] * kLog2e - ap));
+    for (int u = 0; u < kU; ++u) {
+      const int v = v0 + u * kTvThreads;
+      dq[u] = fill;
+      dp[u] = fill;
+      if (v < a.nvec) {
+        dq[u] = __builtin_nontemporal_load(qv + v);
+        dp[u] = __builtin_nontemporal_load(pv + v);
+      }
     }
-    acc += part;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float x[kEpv], y[kEpv];
+      widen<DT>(dq[u], x);
+      widen<DT>(dp[u], y);
+#pragma unroll
+      for (int i = 0; i < kEpv; i += 2) {
+        acc0 += exp2_raw(fminf(__fmaf_rn(x[i], kLog2e, -aq), __fmaf_rn(y[i], kLog2e, -ap)));
+        acc1 += exp2_raw(
+            fminf(__fmaf_rn(x[i + 1], kLog2e, -aq), __fmaf_rn(y[i + 1], kLog2e, -ap)));
+      }
+    }
   }
+  float acc = acc0 + acc1;
   if (tid == 0) {
     for (int t = 0; t < a.tail; ++t) {
       const int i = a.nvec * kEpv + t;
-      acc += exp2f(fminf(elem<DT>(qrow, i) * kLog2e - aq, elem<DT>(prow, i) * kLog2e - ap));
+      acc += exp2_raw(fminf(__fmaf_rn(elem<DT>(qrow, i), kLog2e, -aq),
+                            __fmaf_rn(elem<DT>(prow, i), kLog2e, -ap)));
     }
   }
-  const float total = block_sum<float, kTvThreads>(acc, sd);
+  const float total = block_sum<float, kTvThreads>(acc, wsf);
   if (tid == 0) a.a_out[pair] = total > 1.0f ? 1.0f : total;
 }
 
