@@ -37,9 +37,11 @@ from .plan import (
 from .pack import DATA_BAD_LENS, pack
 from .accept import accept, row_argmax
 from .tv import tv_accept
+from .strided import cap_accept, scatter_to_strided
 
 __all__ = [
     "sigmoid32", "survival", "plan", "pack", "accept", "row_argmax", "tv_accept",
+    "cap_accept", "scatter_to_strided",
     "IN_CONF_LOGITS", "IN_COND", "IN_SURVIVAL",
     "DATA_BAD_COST", "DATA_BAD_CONF", "DATA_BAD_LENS", "FX_SHIFT",
 ]
