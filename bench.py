@@ -373,10 +373,53 @@ def main():
     static_us = 1e3 * start.elapsed_time(stop) / n_static
     static_gbs = accept_bytes(static_rows, B, G, V, esize) / (static_us * 1e-6) / 1e9
 
-    acc_bytes = accept_bytes(total, B, G, V, esize)
-    achieved = acc_bytes / (acc_mean_us * 1e-6) / 1e9
+    # ---- cap-accept on the same strided rows (full block verified, commits
+    # capped by the planned lengths) and the scatter of the planned packed rows
+    # back to stride
+    co = dv.alloc_cap_accept_outputs(B, G, V, dt, dev)
+    lens_t = po.verify_lens
+
+    def cap(i):
+        dv.dspark_cap_accept(B, G, V, dt, stat_bufs[i % 2], V, lens_t, drafts_t, prefix_t, co,
+                             stream)
+
+    for i in range(5):
+        cap(i)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(n_static):
+        cap(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    cap_us = 1e3 * start.elapsed_time(stop) / n_static
+    assert int(co.accept_meta[1].item()) == 0
+    cap_gbs = accept_bytes(static_rows, B, G, V, esize) / (cap_us * 1e-6) / 1e9
     del stat_bufs
     torch.cuda.empty_cache()
+    dst = torch.empty(static_rows, V, dtype=tdt, device=dev)
+    smeta = torch.empty(2, dtype=torch.int32, device=dev)
+
+    def scat(i):
+        dv.dspark_scatter_to_strided(B, G + 1, ko.cu_seqlens, packed[i % n_rot], dst, V, smeta,
+                                     stream)
+
+    for i in range(5):
+        scat(i)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(n_static):
+        scat(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    scat_us = 1e3 * start.elapsed_time(stop) / n_static
+    assert smeta.tolist() == [total, 0]
+    scat_bytes = 2 * total * V * esize + (B + 1) * 4
+    scat_gbs = scat_bytes / (scat_us * 1e-6) / 1e9
+    del dst
+    torch.cuda.empty_cache()
+
+    acc_bytes = accept_bytes(total, B, G, V, esize)
+    achieved = acc_bytes / (acc_mean_us * 1e-6) / 1e9
 
     tv_res = None
     if not args.no_tv:
@@ -418,6 +461,10 @@ def main():
         "accept_us_median": statistics.median(acc_us),
         "accept_static": {"rows": static_rows, "us": static_us, "GB/s": static_gbs,
                           "frac": static_gbs / PEAK_HBM_GBS},
+        "cap_accept": {"rows": static_rows, "us": cap_us, "GB/s": cap_gbs,
+                       "frac": cap_gbs / PEAK_HBM_GBS},
+        "scatter_to_strided": {"rows": total, "us": scat_us, "GB/s": scat_gbs,
+                               "frac": scat_gbs / PEAK_HBM_GBS, "bytes": scat_bytes},
         "tv_pass": tv_res,
         "wall_s_timed": wall,
     }

@@ -25,8 +25,9 @@ from ._lib import (
 
 __all__ = [
     "load", "dspark_plan", "dspark_pack", "dspark_plan_pack", "dspark_accept", "dspark_tv_accept",
-    "dspark_accept_workspace_size", "alloc_plan_outputs", "alloc_pack_outputs",
-    "alloc_accept_outputs", "DsparkError", "F32", "BF16", "IN_CONF_LOGITS", "IN_COND",
+    "dspark_cap_accept", "dspark_scatter_to_strided", "dspark_accept_workspace_size",
+    "alloc_plan_outputs", "alloc_pack_outputs", "alloc_accept_outputs",
+    "alloc_cap_accept_outputs", "DsparkError", "F32", "BF16", "IN_CONF_LOGITS", "IN_COND",
     "IN_SURVIVAL", "DATA_BAD_COST", "DATA_BAD_CONF", "DATA_BAD_LENS",
 ]
 
@@ -261,6 +262,102 @@ def dspark_accept(B: int, gamma: int, V: int, dt: int, packed_logits: torch.Tens
     )
     _lib.check("dspark_accept", _lib.lib().dspark_accept(*args))
     return out
+
+
+# ------------------------------------------------------------------ cap-accept, scatter
+
+class CapAcceptOutputs(NamedTuple):
+    row_argmax: torch.Tensor  # [B * (gamma+1)] int32
+    ceiling: torch.Tensor  # [B] int32
+    num_correct: torch.Tensor  # [B] int32
+    bonus: torch.Tensor
+    commit_lens: torch.Tensor
+    out_tokens: torch.Tensor  # [B, gamma+1] int32
+    new_seq_lens: Optional[torch.Tensor]
+    prefix_mask: Optional[torch.Tensor]  # [B, gamma] uint8
+    accept_meta: torch.Tensor  # [2] int32
+    workspace: torch.Tensor  # uint8 scratch (no initialization needed)
+
+
+def alloc_cap_accept_outputs(B: int, gamma: int, V: int, dt: int, device, new_seq=True,
+                             mask=True) -> CapAcceptOutputs:
+    i32 = torch.int32
+    rows = B * (gamma + 1)
+    ws = dspark_accept_workspace_size(rows, V, dt)
+    return CapAcceptOutputs(
+        torch.empty(max(rows, 1), dtype=i32, device=device),
+        torch.empty(B, dtype=i32, device=device),
+        torch.empty(B, dtype=i32, device=device),
+        torch.empty(B, dtype=i32, device=device),
+        torch.empty(B, dtype=i32, device=device),
+        torch.empty(B, gamma + 1, dtype=i32, device=device),
+        torch.empty(B, dtype=i32, device=device) if new_seq else None,
+        torch.empty(B, gamma, dtype=torch.uint8, device=device) if mask else None,
+        torch.empty(2, dtype=i32, device=device),
+        torch.empty(max(ws, 256), dtype=torch.uint8, device=device),
+    )
+
+
+def dspark_cap_accept(B: int, gamma: int, V: int, dt: int, strided_logits: torch.Tensor, ld: int,
+                      verify_lens: torch.Tensor, draft_tokens: torch.Tensor, prefix_lens,
+                      out: CapAcceptOutputs, stream=None) -> CapAcceptOutputs:
+    i32 = torch.int32
+    rows = B * (gamma + 1)
+    args = (
+        B, gamma, V, dt,
+        _ptr(strided_logits, "strided_logits", _logit_dtype(dt), rows * ld if rows else 0), ld,
+        _ptr(verify_lens, "verify_lens", i32, B),
+        _ptr(draft_tokens, "draft_tokens", i32, B * gamma),
+        _ptr(prefix_lens, "prefix_lens", i32, B, required=False),
+        _ptr(out.row_argmax, "row_argmax", i32, rows),
+        _ptr(out.ceiling, "ceiling", i32, B),
+        _ptr(out.num_correct, "num_correct", i32, B),
+        _ptr(out.bonus, "bonus", i32, B),
+        _ptr(out.commit_lens, "commit_lens", i32, B),
+        _ptr(out.out_tokens, "out_tokens", i32, B * (gamma + 1)),
+        _ptr(out.new_seq_lens, "new_seq_lens", i32, B, required=False),
+        _ptr(out.prefix_mask, "prefix_mask", torch.uint8, B * gamma, required=False),
+        _ptr(out.accept_meta, "accept_meta", i32, 2),
+        _ptr(out.workspace, "workspace", torch.uint8, 1), out.workspace.numel(),
+        _stream(stream),
+    )
+    _lib.check("dspark_cap_accept", _lib.lib().dspark_cap_accept(*args))
+    return out
+
+
+def dspark_scatter_to_strided(B: int, stride: int, cu_seqlens: torch.Tensor, packed: torch.Tensor,
+                              strided: torch.Tensor, row_elems: int, scatter_meta: torch.Tensor,
+                              stream=None) -> torch.Tensor:
+    """Copy packed rows ``packed[cu[r] + j]`` to ``strided[r * stride + j]``.
+
+    ``packed`` is [max_rows, ld_p] and ``strided`` [B * stride, ld_s], both 2-D,
+    contiguous and of one element type; ``row_elems`` elements of each row are
+    copied."""
+    for name, t in (("packed", packed), ("strided", strided)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise ValueError(f"{name} must be a 2-D torch.Tensor")
+    if packed.dtype != strided.dtype:
+        raise TypeError("packed and strided must share an element type")
+    es = packed.element_size()
+    max_rows = packed.shape[0]
+    if strided.shape[0] < B * stride:
+        raise ValueError(f"strided holds {strided.shape[0]} rows, needs {B * stride}")
+    if row_elems > min(packed.shape[1], strided.shape[1]):
+        raise ValueError("row_elems exceeds a row")
+    args = (
+        B, stride,
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32, B + 1),
+        max_rows,
+        _ptr(packed, "packed", packed.dtype, 1 if max_rows else 0),
+        packed.shape[1] * es,
+        _ptr(strided, "strided", strided.dtype, 1 if B else 0),
+        strided.shape[1] * es,
+        row_elems * es,
+        _ptr(scatter_meta, "scatter_meta", torch.int32, 2),
+        _stream(stream),
+    )
+    _lib.check("dspark_scatter_to_strided", _lib.lib().dspark_scatter_to_strided(*args))
+    return strided
 
 
 # ------------------------------------------------------------------ TV

@@ -39,6 +39,13 @@ SIGNATURES = {
         c_int32, c_int32, c_int32, c_int, c_void_p, c_int64, c_int32, c_void_p, c_void_p,
         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
         c_void_p, c_void_p, c_size_t, c_void_p]),
+    "dspark_cap_accept": (c_int, [
+        c_int32, c_int32, c_int32, c_int, c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
+        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+        c_void_p, c_void_p, c_size_t, c_void_p]),
+    "dspark_scatter_to_strided": (c_int, [
+        c_int32, c_int32, c_void_p, c_int32, c_void_p, c_int64, c_void_p, c_int64, c_int64,
+        c_void_p, c_void_p]),
     "dspark_accept_workspace_size": (c_size_t, [c_int32, c_int32, c_int]),
     "dspark_tv_accept": (c_int, [
         c_int32, c_int32, c_int32, c_int, c_void_p, c_int64, c_void_p, c_int64, c_int32,

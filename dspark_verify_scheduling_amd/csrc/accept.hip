@@ -30,6 +30,13 @@
 //    counts the leading matches with a ballot, and writes the outputs; a
 //    grid-stride pass writes the row argmax of every packed row.
 //
+// Cap-accept ("DSpark接入SGLang：用置信度驱动可变长度验证" (yingzheng), the
+// three verify modes and the observability section; "DSpark 自适应 Verify
+// 怎样分配候选预算" §五, cap-accept) runs the same two kernels on the fixed
+// strided layout of B * (gamma + 1) rows: the leading matches are counted
+// over all gamma drafts (the ceiling), then clipped to verify_len - 1, which
+// commits what compact mode commits.
+//
 // The partials are fully rewritten by every call, so the workspace needs no
 // initialization and holds no state between calls.
 #include "common.h"
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_argmax_kernel(AcceptArgs a
   __shared__ unsigned int s_idx[kWaves];
   __shared__ unsigned long long s_best[kWaves];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int total = a.cu[a.B];
+  const int total = a.fixed_rows >= 0 ? a.fixed_rows : a.cu[a.B];
   const int total_eff = min(max(total, 0), a.max_rows);
   if (blockIdx.x == 0 && tid == 0) {
     a.meta[0] = total;
@@ -272,24 +279,54 @@ __device__ inline int merge_row(const AcceptArgs& a, int row) {
 }
 
 // One wave per request (blockIdx.x = r), plus a grid-stride pass that writes
-// the argmax of every packed row.
+// the argmax of every row. CAP = false: packed rows cu[r] .. cu[r+1]-1.
+// CAP = true: strided rows r * (gamma + 1) + j, every one of them computed.
+template <bool CAP>
 __global__ __launch_bounds__(kWave) void accept_finalize_kernel(AcceptArgs a) {
   __shared__ int am[DSPARK_MAX_GAMMA + 1];
   const int lane = threadIdx.x;
-  const int total = a.cu[a.B];
+  const int G = a.gamma;
+  const int total = CAP ? a.fixed_rows : a.cu[a.B];
   const int total_eff = min(max(total, 0), a.max_rows);
   for (int i = blockIdx.x * kWave + lane; i < total_eff; i += gridDim.x * kWave) {
     a.row_am[i] = merge_row(a, i);
   }
   const int r = blockIdx.x;
   if (r >= a.B) return;
-  const int G = a.gamma;
-  const int c0 = a.cu[r], c1 = a.cu[r + 1];
-  const int len = c1 - c0;
+  int c0, len;  // first row, verify length
+  bool ok;
+  if constexpr (CAP) {
+    c0 = r * (G + 1);
+    len = a.lens[r];
+    ok = len >= 1 && len <= G + 1;
+  } else {
+    c0 = a.cu[r];
+    const int c1 = a.cu[r + 1];
+    len = c1 - c0;
+    ok = c0 >= 0 && len >= 1 && len <= G + 1 && c1 <= total_eff;
+  }
   const int prefix = a.prefix ? a.prefix[r] : 0;
   const int32_t* dr = a.drafts + (size_t)r * G;
   int32_t* out = a.out_tokens + (size_t)r * (G + 1);
-  if (!(c0 >= 0 && len >= 1 && len <= G + 1 && c1 <= total_eff)) {
+  // rows whose predictions are compared: len - 1 of them, or the full block
+  const int n_chk = CAP ? G : len - 1;
+  if (CAP || ok) {
+    const int n_rows = CAP ? G + 1 : len;
+    for (int j = lane; j < n_rows; j += kWave) am[j] = merge_row(a, c0 + j);
+  }
+  __syncthreads();
+  int c = 0;
+  if (CAP || ok) {
+    // draft k (0-based, k < n_chk <= 64) against the prediction of row k
+    const bool mismatch = lane < n_chk && dr[lane] != am[lane];
+    const unsigned long long mm = __ballot(mismatch);
+    c = mm ? (int)__builtin_ctzll(mm) : n_chk;
+    if constexpr (CAP) {
+      if (lane == 0) a.ceiling[r] = c;
+      c = min(c, len - 1);
+    }
+  }
+  if (!ok) {
     for (int j = lane; j <= G; j += kWave) out[j] = -1;
     if (a.mask) {
       for (int k = lane; k < G; k += kWave) a.mask[(size_t)r * G + k] = 0;
@@ -303,12 +340,6 @@ __global__ __launch_bounds__(kWave) void accept_finalize_kernel(AcceptArgs a) {
     }
     return;
   }
-  for (int j = lane; j < len; j += kWave) am[j] = merge_row(a, c0 + j);
-  __syncthreads();
-  // draft k (0-based, k < len - 1 <= 64) against the prediction of row k
-  const bool mismatch = lane < len - 1 && dr[lane] != am[lane];
-  const unsigned long long mm = __ballot(mismatch);
-  const int c = mm ? (int)__builtin_ctzll(mm) : len - 1;
   const int bon = am[c];
   for (int j = lane; j <= G; j += kWave) out[j] = j == c ? bon : (j < G ? dr[j] : -1);
   if (a.mask) {
@@ -333,7 +364,11 @@ hipError_t launch_accept(const AcceptArgs& a, dspark_dtype dt, int grid, hipStre
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int fgrid = a.B > 0 ? a.B : 1;
-  hipLaunchKernelGGL(accept_finalize_kernel, dim3(fgrid), dim3(kWave), 0, s, a);
+  if (a.fixed_rows >= 0) {
+    hipLaunchKernelGGL(accept_finalize_kernel<true>, dim3(fgrid), dim3(kWave), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(accept_finalize_kernel<false>, dim3(fgrid), dim3(kWave), 0, s, a);
+  }
   return hipGetLastError();
 }
 

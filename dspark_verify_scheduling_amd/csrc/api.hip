@@ -66,7 +66,7 @@ size_t ws_bytes(int max_rows, int chunks) {
 
 extern "C" {
 
-int32_t dspark_version(void) { return (1 << 16) | 1; }
+int32_t dspark_version(void) { return (1 << 16) | 2; }
 
 const char* dspark_status_str(dspark_status s) {
   switch (s) {
@@ -240,6 +240,125 @@ dspark_status dspark_pack(int32_t B, int32_t gamma, const int32_t* verify_lens,
   return launched(dspark::launch_pack(a, (hipStream_t)stream), "dspark_pack");
 }
 
+dspark_status dspark_cap_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,
+                                const void* strided_logits, int64_t ld,
+                                const int32_t* verify_lens, const int32_t* draft_tokens,
+                                const int32_t* prefix_lens, int32_t* row_argmax, int32_t* ceiling,
+                                int32_t* num_correct, int32_t* bonus, int32_t* commit_lens,
+                                int32_t* out_tokens, int32_t* new_seq_lens, uint8_t* prefix_mask,
+                                int32_t* accept_meta, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (B < 0) return fail(DSPARK_E_INVALID, "dspark_cap_accept: B = %d < 0", B);
+  if (gamma < 1 || gamma > DSPARK_MAX_GAMMA)
+    return fail(DSPARK_E_INVALID, "dspark_cap_accept: gamma = %d outside [1, %d]", gamma,
+                DSPARK_MAX_GAMMA);
+  if (dt != DSPARK_F32 && dt != DSPARK_BF16)
+    return fail(DSPARK_E_UNSUPPORTED, "dspark_cap_accept: unsupported dtype %d", (int)dt);
+  if (V < 1 || V > DSPARK_MAX_VOCAB)
+    return fail(V < 1 ? DSPARK_E_INVALID : DSPARK_E_UNSUPPORTED,
+                "dspark_cap_accept: V = %d outside [1, %d]", V, DSPARK_MAX_VOCAB);
+  if (ld < V)
+    return fail(DSPARK_E_INVALID, "dspark_cap_accept: ld = %lld < V = %d", (long long)ld, V);
+  const size_t es = elem_size(dt);
+  if ((ld * (int64_t)es) % 16 != 0)
+    return fail(DSPARK_E_INVALID,
+                "dspark_cap_accept: row stride %lld bytes is not a multiple of 16",
+                (long long)(ld * (int64_t)es));
+  const int64_t rows64 = (int64_t)B * (gamma + 1);
+  const RowGeom g = row_geom(V, dt);
+  if (rows64 * g.chunks > 0x7fffffffLL)
+    return fail(DSPARK_E_UNSUPPORTED, "dspark_cap_accept: B * (gamma + 1) * chunks overflows int32");
+  const int rows = (int)rows64;
+  if (!accept_meta) return fail(DSPARK_E_INVALID, "dspark_cap_accept: accept_meta is NULL");
+  if (B > 0) {
+    if (!strided_logits || !aligned16(strided_logits))
+      return fail(DSPARK_E_INVALID, "dspark_cap_accept: strided_logits NULL or not 16-byte aligned");
+    if (!verify_lens || !draft_tokens || !row_argmax || !ceiling || !num_correct || !bonus ||
+        !commit_lens || !out_tokens)
+      return fail(DSPARK_E_INVALID, "dspark_cap_accept: a required pointer is NULL");
+  }
+  if (new_seq_lens && !prefix_lens)
+    return fail(DSPARK_E_INVALID, "dspark_cap_accept: new_seq_lens needs prefix_lens");
+  const size_t need = ws_bytes(rows, g.chunks);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
+    return fail(DSPARK_E_WORKSPACE,
+                "dspark_cap_accept: workspace needs %zu bytes, 256-byte aligned", need);
+
+  dspark::AcceptArgs a;
+  a.logits = static_cast<const unsigned char*>(strided_logits);
+  a.ld_bytes = ld * (int64_t)es;
+  a.V = V;
+  a.max_rows = rows;
+  a.B = B;
+  a.gamma = gamma;
+  a.fixed_rows = rows;
+  a.chunks = g.chunks;
+  a.chunk_vecs = g.chunk_vecs;
+  a.nvec = g.nvec;
+  a.tail = g.tail;
+  a.cu = nullptr;
+  a.drafts = draft_tokens;
+  a.prefix = prefix_lens;
+  a.row_am = row_argmax;
+  a.num_correct = num_correct;
+  a.bonus = bonus;
+  a.commit = commit_lens;
+  a.out_tokens = out_tokens;
+  a.new_seq = new_seq_lens;
+  a.mask = prefix_mask;
+  a.meta = accept_meta;
+  a.partials = static_cast<unsigned long long*>(workspace);
+  a.lens = verify_lens;
+  a.ceiling = ceiling;
+  const int64_t units = (int64_t)rows * g.chunks;
+  const int grid = units > 0 ? (int)units : 1;
+  return launched(dspark::launch_accept(a, dt, grid, (hipStream_t)stream), "dspark_cap_accept");
+}
+
+dspark_status dspark_scatter_to_strided(int32_t B, int32_t stride, const int32_t* cu_seqlens,
+                                        int32_t max_rows, const void* packed,
+                                        int64_t packed_ld_bytes, void* strided,
+                                        int64_t strided_ld_bytes, int64_t row_bytes,
+                                        int32_t* scatter_meta, void* stream) {
+  if (B < 0) return fail(DSPARK_E_INVALID, "dspark_scatter_to_strided: B = %d < 0", B);
+  if (stride < 1 || stride > DSPARK_MAX_GAMMA + 1)
+    return fail(DSPARK_E_INVALID, "dspark_scatter_to_strided: stride = %d outside [1, %d]", stride,
+                DSPARK_MAX_GAMMA + 1);
+  if (max_rows < 0)
+    return fail(DSPARK_E_INVALID, "dspark_scatter_to_strided: max_rows = %d < 0", max_rows);
+  if (row_bytes < 1 || row_bytes > (1LL << 30))
+    return fail(DSPARK_E_INVALID, "dspark_scatter_to_strided: row_bytes = %lld outside [1, 2^30]",
+                (long long)row_bytes);
+  if (packed_ld_bytes < row_bytes || strided_ld_bytes < row_bytes ||
+      packed_ld_bytes % 16 != 0 || strided_ld_bytes % 16 != 0)
+    return fail(DSPARK_E_INVALID,
+                "dspark_scatter_to_strided: row strides must be >= row_bytes and multiples of 16");
+  if (!cu_seqlens || !scatter_meta)
+    return fail(DSPARK_E_INVALID, "dspark_scatter_to_strided: cu_seqlens or scatter_meta is NULL");
+  if (B > 0 && (!strided || !aligned16(strided)))
+    return fail(DSPARK_E_INVALID, "dspark_scatter_to_strided: strided NULL or not 16-byte aligned");
+  if (max_rows > 0 && (!packed || !aligned16(packed)))
+    return fail(DSPARK_E_INVALID, "dspark_scatter_to_strided: packed NULL or not 16-byte aligned");
+  dspark::ScatterArgs a;
+  a.src = static_cast<const unsigned char*>(packed);
+  a.src_ld = packed_ld_bytes;
+  a.dst = static_cast<unsigned char*>(strided);
+  a.dst_ld = strided_ld_bytes;
+  a.B = B;
+  a.stride = stride;
+  a.max_rows = max_rows;
+  a.nvec = (int)(row_bytes / 16);
+  a.tail = (int)(row_bytes % 16);
+  const int max_unit = dspark::kScatterThreads * dspark::kScatterVecsPerThread;
+  a.chunks = std::max(1, (a.nvec + max_unit - 1) / max_unit);
+  a.chunk_vecs = (a.nvec + a.chunks - 1) / a.chunks;
+  a.cu = cu_seqlens;
+  a.meta = scatter_meta;
+  if ((int64_t)B * a.chunks > 0x7fffffffLL)
+    return fail(DSPARK_E_UNSUPPORTED, "dspark_scatter_to_strided: B * units overflows int32");
+  return launched(dspark::launch_scatter(a, (hipStream_t)stream), "dspark_scatter_to_strided");
+}
+
 size_t dspark_accept_workspace_size(int32_t max_rows, int32_t V, dspark_dtype dt) {
   if (max_rows < 0 || V < 1 || V > DSPARK_MAX_VOCAB) return 0;
   if (dt != DSPARK_F32 && dt != DSPARK_BF16) return 0;
@@ -310,6 +429,9 @@ dspark_status dspark_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt
   a.mask = prefix_mask;
   a.meta = accept_meta;
   a.partials = static_cast<unsigned long long*>(workspace);
+  a.fixed_rows = -1;
+  a.lens = nullptr;
+  a.ceiling = nullptr;
   // one workgroup per (row, unit) of the largest possible packed total; the
   // kernel reads the actual total on the device and idle workgroups exit
   const int64_t units_max = (int64_t)max_rows * g.chunks;

@@ -51,6 +51,9 @@ struct AcceptArgs {
   const unsigned char* logits;
   int64_t ld_bytes;
   int V, max_rows, B, gamma;
+  // -1: packed rows described by cu; >= 0: the strided layout of cap-accept,
+  // B * (gamma + 1) rows, request r at rows r * (gamma + 1) + j
+  int fixed_rows;
   int chunks;      // units per row
   int chunk_vecs;  // 16-byte vectors per unit
   int nvec;        // whole 16-byte vectors per row
@@ -67,11 +70,30 @@ struct AcceptArgs {
   uint8_t* mask;
   int32_t* meta;
   unsigned long long* partials;  // [max_rows * chunks] (key, index) per unit
+  const int32_t* lens;  // cap-accept: verify_lens [B]
+  int32_t* ceiling;     // cap-accept: uncapped leading matches [B]
 };
 constexpr int kAccThreads = 256;
 constexpr int kAccVecsPerThread = 8;
 constexpr int kAccMaxChunkVecs = kAccThreads * kAccVecsPerThread;
 hipError_t launch_accept(const AcceptArgs& a, dspark_dtype dt, int grid, hipStream_t s);
+
+struct ScatterArgs {
+  const unsigned char* src;
+  int64_t src_ld;  // bytes
+  unsigned char* dst;
+  int64_t dst_ld;  // bytes
+  int B, stride, max_rows;
+  int chunks;      // units per row
+  int chunk_vecs;  // 16-byte vectors per unit
+  int nvec;        // whole 16-byte vectors per row
+  int tail;        // bytes after the last whole vector
+  const int32_t* cu;
+  int32_t* meta;
+};
+constexpr int kScatterThreads = 256;
+constexpr int kScatterVecsPerThread = 8;
+hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s);
 
 struct TvArgs {
   const unsigned char* q;

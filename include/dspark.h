@@ -12,6 +12,11 @@
  *   dspark_plan_pack both of the above in one launch
  *   dspark_accept    packed target logits -> per-row argmax -> leading-match
  *                    count, bonus token, commit lengths, output tokens
+ *   dspark_cap_accept    greedy accept on the full strided block, committing
+ *                    at most verify_len - 1 drafts and reporting the uncapped
+ *                    ceiling (cap-accept mode)
+ *   dspark_scatter_to_strided  packed verify rows (logits or hidden states)
+ *                    back to the strided [B, stride] layout
  *   dspark_tv_accept (optional) soft accept-rate 1 - TV(softmax q, softmax p)
  *                    and its per-request cumulative product, which can feed
  *                    dspark_plan as survivals
@@ -259,6 +264,79 @@ dspark_status dspark_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt
                             int32_t* out_tokens, int32_t* new_seq_lens, uint8_t* prefix_mask,
                             int32_t* accept_meta, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * dspark_cap_accept - greedy accept in cap-accept mode.
+ *
+ * Defined by [SGLang] "三种 verify mode" and "可观测性" (cap-accept verifies
+ * the full drafted block but commits only inside the scheduler's window, so
+ * its output equals compact mode's while it also exposes how many tokens full
+ * verification would have accepted), [CSSD] "static、compact 与 cap-accept
+ * 三种模式", and [Budget] §五 (the target keeps the fixed B * (gamma + 1)
+ * rows; correct_len is clipped to verify_len - 1 at accept time).
+ *
+ * Rows are strided: request r's verify row j (j = 0..gamma, row 0 the root)
+ * is row r * (gamma + 1) + j. The argmax and the leading-match rule are those
+ * of dspark_accept; the count runs over all gamma drafts (the ceiling), then
+ *   num_correct = min(ceiling, verify_len - 1), bonus = prediction of row
+ *   num_correct, and the remaining outputs as in dspark_accept.
+ *
+ * Arguments (as dspark_accept unless stated):
+ *   strided_logits     [B * (gamma + 1), ld] rows, 16-byte aligned
+ *   verify_lens        [B] int32 (the planner's lengths)
+ *   row_argmax         out [B * (gamma + 1)] int32, every row written
+ *   ceiling            out [B] int32, uncapped leading matches (0..gamma)
+ *   accept_meta        out [2] int32: B * (gamma + 1), status bits
+ *   workspace          dspark_accept_workspace_size(B * (gamma + 1), V, dt)
+ *                      bytes, 256-byte aligned, contents irrelevant
+ * Data errors: a verify length outside [1, gamma + 1] sets
+ *   DSPARK_DATA_BAD_LENS and gives that request the outputs of a malformed
+ *   request of dspark_accept; its ceiling is still written.
+ */
+dspark_status dspark_cap_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,
+                                const void* strided_logits, int64_t ld,
+                                const int32_t* verify_lens, const int32_t* draft_tokens,
+                                const int32_t* prefix_lens, int32_t* row_argmax, int32_t* ceiling,
+                                int32_t* num_correct, int32_t* bonus, int32_t* commit_lens,
+                                int32_t* out_tokens, int32_t* new_seq_lens, uint8_t* prefix_mask,
+                                int32_t* accept_meta, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * dspark_scatter_to_strided - copy front-packed rows back to stride.
+ *
+ * Defined by [Round] §三 (ScatterCompactToStrided: after the target forward,
+ * logits and hidden states of the compact rows are restored to the uniform
+ * [bs x stride] logical layout so that accept can address fixed positions;
+ * rows that were not verified are not recomputed and verify_lens still says
+ * which results are valid).
+ *
+ *   strided[r * stride + j] = packed[cu_seqlens[r] + j]
+ *   for j < cu_seqlens[r + 1] - cu_seqlens[r]; other strided rows are not
+ *   written.
+ *
+ * Arguments:
+ *   B, stride          requests; strided rows per request (1..gamma_max + 1)
+ *   cu_seqlens         [B + 1] int32, as written by dspark_pack
+ *   max_rows           rows the packed buffer holds; rows at or beyond it are
+ *                      never read
+ *   packed             packed rows, packed_ld_bytes apart; 16-byte aligned
+ *   strided            destination rows, strided_ld_bytes apart; 16-byte
+ *                      aligned; must not overlap `packed`
+ *   row_bytes          bytes copied per row (any element type or width: e.g.
+ *                      V * element size for logits, H * element size for
+ *                      hidden states); both strides >= row_bytes and
+ *                      multiples of 16
+ *   scatter_meta       out [2] int32: cu_seqlens[B], status bits
+ * Data errors: a request whose rows are not 1..stride rows inside
+ *   [0, min(cu_seqlens[B], max_rows)) sets DSPARK_DATA_BAD_LENS and none of
+ *   its rows is written.
+ */
+dspark_status dspark_scatter_to_strided(int32_t B, int32_t stride, const int32_t* cu_seqlens,
+                                        int32_t max_rows, const void* packed,
+                                        int64_t packed_ld_bytes, void* strided,
+                                        int64_t strided_ld_bytes, int64_t row_bytes,
+                                        int32_t* scatter_meta, void* stream);
 
 /* Bytes of workspace dspark_accept needs for `max_rows` rows of V elements of
  * type dt (0 for invalid sizes). */

@@ -178,6 +178,48 @@ def test_tv_argument_errors():
     assert run(V=300000, ldq=300000, ldp=300000) == _lib.E_UNSUPPORTED
 
 
+def test_cap_accept_argument_errors():
+    call = _lib.lib().dspark_cap_accept
+    ok = dict(B=2, gamma=3, V=1024, dt=_lib.BF16, x=FAKE, ld=1024, lens=FAKE, drafts=FAKE,
+              prefix=NULL, am=FAKE, ceil=FAKE, nc=FAKE, bonus=FAKE, commit=FAKE, out=FAKE,
+              new_seq=NULL, mask=NULL, meta=FAKE, ws=ctypes.c_void_p(0x100000), wsb=1 << 20,
+              stream=NULL)
+
+    def run(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return call(*d.values())
+
+    assert run(gamma=0) == _lib.E_INVALID
+    assert run(ld=1000) == _lib.E_INVALID
+    assert run(lens=NULL) == _lib.E_INVALID
+    assert run(ceil=NULL) == _lib.E_INVALID
+    assert run(new_seq=FAKE) == _lib.E_INVALID  # needs prefix_lens
+    assert run(dt=7) == _lib.E_UNSUPPORTED
+    assert run(wsb=8 * 8 * 4 - 1) == _lib.E_WORKSPACE  # 8 rows, 1 unit each -> 256 bytes
+    assert run(ws=ctypes.c_void_p(0x100010)) == _lib.E_WORKSPACE
+
+
+def test_scatter_argument_errors():
+    call = _lib.lib().dspark_scatter_to_strided
+    ok = dict(B=2, stride=4, cu=FAKE, max_rows=8, src=FAKE, src_ld=4096, dst=FAKE, dst_ld=4096,
+              row_bytes=4000, meta=FAKE, stream=NULL)
+
+    def run(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return call(*d.values())
+
+    assert run(stride=0) == _lib.E_INVALID
+    assert run(stride=_lib.MAX_GAMMA + 2) == _lib.E_INVALID
+    assert run(row_bytes=0) == _lib.E_INVALID
+    assert run(row_bytes=4097) == _lib.E_INVALID  # above a row stride
+    assert run(src_ld=4104) == _lib.E_INVALID  # not a multiple of 16
+    assert run(dst=ctypes.c_void_p(0x1008)) == _lib.E_INVALID
+    assert run(cu=NULL) == _lib.E_INVALID
+    assert run(max_rows=-1) == _lib.E_INVALID
+
+
 # ---------------------------------------------------------------- sigmoid logic on the CPU
 
 def _host_sigmoid(x, force_slow=False):
