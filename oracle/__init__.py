@@ -25,6 +25,8 @@ soft accept-rate (no integer depends on it inside the stage) is fp64.
 
 from .sigmoid import sigmoid32
 from .plan import (
+    COST_ADDITIVE,
+    COST_SPS1D,
     DATA_BAD_CONF,
     DATA_BAD_COST,
     FX_SHIFT,
@@ -32,6 +34,7 @@ from .plan import (
     IN_CONF_LOGITS,
     IN_SURVIVAL,
     plan,
+    sps_floor,
     survival,
 )
 from .pack import DATA_BAD_LENS, pack
@@ -42,6 +45,6 @@ from .strided import cap_accept, scatter_to_strided
 __all__ = [
     "sigmoid32", "survival", "plan", "pack", "accept", "row_argmax", "tv_accept",
     "cap_accept", "scatter_to_strided",
-    "IN_CONF_LOGITS", "IN_COND", "IN_SURVIVAL",
+    "IN_CONF_LOGITS", "IN_COND", "IN_SURVIVAL", "COST_ADDITIVE", "COST_SPS1D", "sps_floor",
     "DATA_BAD_COST", "DATA_BAD_CONF", "DATA_BAD_LENS", "FX_SHIFT",
 ]

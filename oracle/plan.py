@@ -22,6 +22,17 @@ What it computes, step by step, in the pages' order:
    ScheduleVerifyLensTopk allocation, with min/max_verify_len and
    survival_eps).
 
+Two variants ([Budget] §一 and §四, §五):
+
+* 1D SPS cost mode: ``budget = argmax_b tau(b) * SPS(M)``, SPS read from a
+  table of probe points by floor lookup (the nearest probe at or below M,
+  no interpolation, so a cliff in the table is kept as it is).
+* Graph-tier alignment (paid-padding reclamation): once the budget is
+  chosen, the executed budget is extended with the next candidates in the
+  same order until the packed total reaches the graph tier that the chosen
+  budget already pays for; it never crosses into the next tier and never
+  adds rows that are not candidates.
+
 Readings where the pages leave a step open (each also listed in the design
 notes):
 
@@ -40,6 +51,16 @@ notes):
 * The budget range is ``[budget_lo, budget_hi]`` clipped to the number of
   candidates (``budget_hi < 0`` means no upper limit). Equal ratios go to the
   smaller budget.
+* 1D mode: a total M below the first probe takes the first probe's SPS.
+  The objective is the correctly rounded fp64 product ``tau * SPS``.
+  Probes that are not strictly ascending, or an SPS that is not positive and
+  finite at a considered budget, set DATA_BAD_COST.
+* Alignment: the tier is the smallest listed tier that holds the chosen
+  total ``B * L_min + b*``; the executed budget is
+  ``min(b* + tier - total, #candidates)``. It ignores ``budget_hi`` (the
+  cap bounds the argmax; the fill deliberately goes past it to use rows
+  that are paid for). ``meta[0]`` stays the argmax budget and ``meta[3]``
+  becomes the executed total.
 * Bad data is detected, not trapped. A non-positive or non-finite ``T`` at a
   considered budget sets DATA_BAD_COST. Confidence outside [0, 1], a NaN, or
   a non-positive/non-finite temperature sets DATA_BAD_CONF. So does a given
@@ -60,6 +81,9 @@ IN_SURVIVAL = 2
 
 DATA_BAD_COST = 1
 DATA_BAD_CONF = 2
+
+COST_ADDITIVE = 0
+COST_SPS1D = 1
 
 FX_SHIFT = 40  # tau resolution: 2**-40
 
@@ -105,14 +129,25 @@ def clamp_lens(gamma: int, min_len: int, max_len: int):
     return lmin, lmax
 
 
+def sps_floor(sps_m, sps, M):
+    """SPS of the nearest probe at or below M; the first probe when M is below all."""
+    i = 0
+    for j in range(len(sps_m)):
+        if int(sps_m[j]) <= M:
+            i = j
+    return np.float32(sps[i])
+
+
 def plan(B, gamma, kind, conf, temps, min_len, max_len, eps, budget_lo, budget_hi,
-         bias, alpha, theta):
+         bias, alpha, theta, cost_mode=COST_ADDITIVE, sps_m=None, sps=None, align_tiers=None):
     """Run the planner; returns a dict with the same outputs as ``dspark_plan``.
 
     Keys: ``verify_lens`` int32[B]; ``meta`` int32[4] = (b*, number of
-    candidates, status, B*L_min + b*); ``val`` float64[2] = (tau(b*),
-    ratio(b*)); ``survival`` float32[B, gamma]; ``sweep`` float64[B*gamma+1, 2]
-    = (tau(b), ratio(b)) for b = 0..#candidates, NaN beyond."""
+    candidates, status, executed total B*L_min + b_exec); ``val`` float64[2]
+    = (tau(b*), objective(b*)); ``survival`` float32[B, gamma]; ``sweep``
+    float64[B*gamma+1, 2] = (tau(b), objective(b)) for b = 0..#candidates, NaN
+    beyond. The objective is tau / T (additive) or tau * SPS (1D); b_exec is
+    b* unless ``align_tiers`` is given."""
     B, gamma = int(B), int(gamma)
     if budget_hi >= 0 and budget_lo > budget_hi:
         raise ValueError("budget_lo > budget_hi")
@@ -135,18 +170,32 @@ def plan(B, gamma, kind, conf, temps, min_len, max_len, eps, budget_lo, budget_h
         lo = min(max(int(budget_lo), 0), n_e)
         hi = n_e if budget_hi < 0 else min(int(budget_hi), n_e)
 
-        t_fixed = np.float64(bias) + np.float64(alpha[B])
+        if cost_mode == COST_SPS1D:
+            probes = [int(m) for m in sps_m]
+            if not probes or any(b <= a for a, b in zip(probes, probes[1:])):
+                status |= DATA_BAD_COST
+        else:
+            t_fixed = np.float64(bias) + np.float64(alpha[B])
         tau_fx = B * 2 ** FX_SHIFT + forced
         best_b, best_ratio = -1, None
         for b in range(n_e + 1):
+            if status:
+                break
             if b > 0:
                 tau_fx += _fx(cands[b - 1][0])
-            T = t_fixed + np.float64(theta[B * lmin + b])
             tau = tau_fx / 2 ** FX_SHIFT  # exact: below 2**53
-            ratio = float(np.float64(tau) / T)
+            M = B * lmin + b
+            if cost_mode == COST_SPS1D:
+                S = np.float64(sps_floor(sps_m, sps, M))
+                ratio = float(np.float64(tau) * S)
+                cost_ok = bool(np.isfinite(S) and S > 0)
+            else:
+                T = t_fixed + np.float64(theta[M])
+                ratio = float(np.float64(tau) / T)
+                cost_ok = bool(np.isfinite(T) and T > 0)
             sweep[b] = (tau, ratio)
             if lo <= b <= hi:
-                if not (np.isfinite(T) and T > 0):
+                if not cost_ok:
                     status |= DATA_BAD_COST
                 elif best_ratio is None or ratio > best_ratio:
                     best_b, best_ratio = b, ratio
@@ -157,10 +206,15 @@ def plan(B, gamma, kind, conf, temps, min_len, max_len, eps, budget_lo, budget_h
         val = np.array([np.nan, np.nan])
         sweep[:] = np.nan
     else:
+        b_exec = best_b
+        if align_tiers is not None:
+            total = B * lmin + best_b
+            tier = next(int(t) for t in align_tiers if int(t) >= total)
+            b_exec = min(best_b + tier - total, n_e)
         lens = np.full(B, lmin, dtype=np.int32)
-        for _, _, r in cands[:best_b]:
+        for _, _, r in cands[:b_exec]:
             lens[r] += 1
-        meta = np.array([best_b, n_e, 0, B * lmin + best_b], dtype=np.int32)
+        meta = np.array([best_b, n_e, 0, B * lmin + b_exec], dtype=np.int32)
         val = sweep[best_b].copy()
     return {"verify_lens": lens, "meta": meta, "val": val, "survival": s, "sweep": sweep,
             "lmin": lmin, "lmax": lmax}
