@@ -19,12 +19,14 @@ import torch
 
 from . import _lib
 from ._lib import (
-    BF16, DATA_BAD_CONF, DATA_BAD_COST, DATA_BAD_LENS, F32, IN_COND, IN_CONF_LOGITS,
+    BF16, COST_ADDITIVE, COST_SPS1D, DATA_BAD_CONF, DATA_BAD_COST, DATA_BAD_LENS, F32, IN_COND,
+    IN_CONF_LOGITS,
     IN_SURVIVAL, MAX_BATCH, MAX_CANDIDATES, MAX_GAMMA, MAX_TIERS, MAX_VOCAB, DsparkError,
 )
 
 __all__ = [
-    "load", "dspark_plan", "dspark_pack", "dspark_plan_pack", "dspark_accept", "dspark_tv_accept",
+    "load", "dspark_plan", "dspark_pack", "dspark_plan_pack", "dspark_plan_pack_ex",
+    "dspark_accept", "dspark_tv_accept", "COST_ADDITIVE", "COST_SPS1D",
     "dspark_cap_accept", "dspark_scatter_to_strided", "dspark_accept_workspace_size",
     "alloc_plan_outputs", "alloc_pack_outputs", "alloc_accept_outputs",
     "alloc_cap_accept_outputs", "DsparkError", "F32", "BF16", "IN_CONF_LOGITS", "IN_COND",
@@ -200,6 +202,61 @@ def dspark_plan_pack(B: int, gamma: int, kind: int, conf: torch.Tensor, sts_temp
         _stream(stream),
     )
     _lib.check("dspark_plan_pack", _lib.lib().dspark_plan_pack(*args))
+    return plan_out, pack_out
+
+
+def dspark_plan_pack_ex(B: int, gamma: int, kind: int, conf: torch.Tensor, sts_temp,
+                        min_verify_len: int, max_verify_len: int, survival_eps: float,
+                        budget_lo: int, budget_hi: int, cost_bias: float, cost_alpha,
+                        cost_theta, plan_out: PlanOutputs, anchor_ids: torch.Tensor,
+                        draft_tokens: torch.Tensor, tiers: Sequence[int], prefix_lens,
+                        pack_out: PackOutputs, cost_mode: int = COST_ADDITIVE, sps_m=None,
+                        sps=None, align_to_tier: bool = False, stream=None):
+    """dspark_plan_pack with the 1D SPS cost model (``cost_mode=COST_SPS1D``,
+    probe totals ``sps_m`` int32 and steps/s ``sps`` float32 on the device)
+    and/or graph-tier alignment of the executed budget."""
+    import ctypes
+
+    f32, i32, f64 = torch.float32, torch.int32, torch.float64
+    tiers = [int(t) for t in tiers]
+    if not tiers:
+        raise ValueError("tiers must not be empty")
+    cap = tiers[-1]
+    tiers_host = (ctypes.c_int32 * len(tiers))(*tiers)
+    sps1d = cost_mode == COST_SPS1D
+    n_probe = sps_m.numel() if sps1d else 0
+    opt = _lib.PlanOptions(
+        cost_mode,
+        _ptr(sps_m, "sps_m", i32, n_probe, required=sps1d) if sps1d else None,
+        _ptr(sps, "sps", f32, n_probe, required=sps1d) if sps1d else None,
+        n_probe, 1 if align_to_tier else 0)
+    args = (
+        B, gamma, kind,
+        _ptr(conf, "conf", f32, B * gamma),
+        _ptr(sts_temp, "sts_temp", f32, gamma, required=(kind == IN_CONF_LOGITS)),
+        min_verify_len, max_verify_len, survival_eps, budget_lo, budget_hi, cost_bias,
+        _ptr(cost_alpha, "cost_alpha", f32, 1, required=not sps1d),
+        cost_alpha.numel() if cost_alpha is not None else 0,
+        _ptr(cost_theta, "cost_theta", f32, 1, required=not sps1d),
+        cost_theta.numel() if cost_theta is not None else 0,
+        _ptr(plan_out.verify_lens, "verify_lens", i32, B),
+        _ptr(plan_out.plan_meta, "plan_meta", i32, 4),
+        _ptr(plan_out.plan_val, "plan_val", f64, 2),
+        _ptr(plan_out.survival_out, "survival_out", f32, B * gamma, required=False),
+        _ptr(plan_out.sweep_out, "sweep_out", f64, 2 * (B * gamma + 1), required=False),
+        _ptr(anchor_ids, "anchor_ids", i32, B),
+        _ptr(draft_tokens, "draft_tokens", i32, B * gamma),
+        ctypes.cast(tiers_host, ctypes.c_void_p), len(tiers),
+        _ptr(prefix_lens, "prefix_lens", i32, B, required=False),
+        _ptr(pack_out.cu_seqlens, "cu_seqlens", i32, B + 1),
+        _ptr(pack_out.packed_ids, "packed_ids", i32, cap),
+        _ptr(pack_out.packed_req, "packed_req", i32, cap, required=False),
+        _ptr(pack_out.packed_pos, "packed_pos", i32, cap, required=False),
+        _ptr(pack_out.pack_meta, "pack_meta", i32, 3),
+        ctypes.cast(ctypes.pointer(opt), ctypes.c_void_p),
+        _stream(stream),
+    )
+    _lib.check("dspark_plan_pack_ex", _lib.lib().dspark_plan_pack_ex(*args))
     return plan_out, pack_out
 
 

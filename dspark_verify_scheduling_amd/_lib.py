@@ -20,6 +20,15 @@ F32, BF16 = 0, 1
 IN_CONF_LOGITS, IN_COND, IN_SURVIVAL = 0, 1, 2
 DATA_BAD_COST, DATA_BAD_CONF, DATA_BAD_LENS = 1, 2, 4
 MAX_GAMMA, MAX_CANDIDATES, MAX_BATCH, MAX_TIERS, MAX_VOCAB = 64, 8192, 8192, 32, 262144
+MAX_SPS_PROBES = 512
+COST_ADDITIVE, COST_SPS1D = 0, 1
+
+
+class PlanOptions(ctypes.Structure):
+    """dspark_plan_options of include/dspark.h."""
+    _fields_ = [("cost_mode", c_int), ("sps_m", c_void_p), ("sps", c_void_p),
+                ("sps_len", c_int32), ("align_to_tier", c_int32)]
+
 
 # name -> (restype, argtypes), mirroring include/dspark.h
 SIGNATURES = {
@@ -32,6 +41,11 @@ SIGNATURES = {
         c_int32, c_float, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "dspark_plan_pack_ex": (c_int, [
+        c_int32, c_int32, c_int, c_void_p, c_void_p, c_int32, c_int32, c_float, c_int32,
+        c_int32, c_float, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dspark_pack": (c_int, [
         c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),

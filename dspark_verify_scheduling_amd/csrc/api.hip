@@ -90,7 +90,15 @@ static dspark_status check_plan(const char* fn, int32_t B, int32_t gamma, dspark
                                 int32_t budget_hi, float cost_bias, const float* cost_alpha,
                                 int32_t alpha_len, const float* cost_theta, int32_t theta_len,
                                 int32_t* verify_lens, int32_t* plan_meta, double* plan_val,
-                                float* survival_out, double* sweep_out, dspark::PlanArgs* a) {
+                                float* survival_out, double* sweep_out, dspark::PlanArgs* a,
+                                const dspark_plan_options* opt = nullptr) {
+  const bool sps1d = opt && opt->cost_mode == DSPARK_COST_SPS1D;
+  if (opt && opt->cost_mode != DSPARK_COST_ADDITIVE && !sps1d)
+    return fail(DSPARK_E_INVALID, "%s: unknown cost mode %d", fn, (int)opt->cost_mode);
+  if (sps1d && (!opt->sps_m || !opt->sps || opt->sps_len < 1 ||
+                opt->sps_len > DSPARK_MAX_SPS_PROBES))
+    return fail(DSPARK_E_INVALID, "%s: SPS table needs 1..%d probes and both arrays", fn,
+                DSPARK_MAX_SPS_PROBES);
   if (B < 0) return fail(DSPARK_E_INVALID, "%s: B = %d < 0", fn, B);
   if (gamma < 1 || gamma > DSPARK_MAX_GAMMA)
     return fail(DSPARK_E_INVALID, "%s: gamma = %d outside [1, %d]", fn, gamma, DSPARK_MAX_GAMMA);
@@ -102,7 +110,7 @@ static dspark_status check_plan(const char* fn, int32_t B, int32_t gamma, dspark
   if (B > 0 && !conf) return fail(DSPARK_E_INVALID, "%s: conf is NULL", fn);
   if (kind == DSPARK_IN_CONF_LOGITS && !sts_temp)
     return fail(DSPARK_E_INVALID, "%s: sts_temp is NULL for confidence logits", fn);
-  if (!cost_alpha || !cost_theta)
+  if (!sps1d && (!cost_alpha || !cost_theta))
     return fail(DSPARK_E_INVALID, "%s: cost table pointer is NULL", fn);
   if (!plan_meta || !plan_val || (B > 0 && !verify_lens))
     return fail(DSPARK_E_INVALID, "%s: an output pointer is NULL", fn);
@@ -112,9 +120,9 @@ static dspark_status check_plan(const char* fn, int32_t B, int32_t gamma, dspark
   if (survival_eps != survival_eps) return fail(DSPARK_E_INVALID, "%s: survival_eps is NaN", fn);
   const int lmin = std::min(std::max(min_verify_len, 1), gamma + 1);
   const int lmax = std::min(std::max(max_verify_len, lmin), gamma + 1);
-  if (alpha_len <= B)
+  if (!sps1d && alpha_len <= B)
     return fail(DSPARK_E_INVALID, "%s: alpha_len %d must exceed B = %d", fn, alpha_len, B);
-  if ((int64_t)theta_len <= (int64_t)B * lmax)
+  if (!sps1d && (int64_t)theta_len <= (int64_t)B * lmax)
     return fail(DSPARK_E_INVALID, "%s: theta_len %d must exceed B * L_max = %lld", fn, theta_len,
                 (long long)B * lmax);
   a->B = B;
@@ -136,6 +144,11 @@ static dspark_status check_plan(const char* fn, int32_t B, int32_t gamma, dspark
   a->val = plan_val;
   a->surv_out = survival_out;
   a->sweep = sweep_out;
+  a->cost_mode = sps1d ? DSPARK_COST_SPS1D : DSPARK_COST_ADDITIVE;
+  a->sps_m = sps1d ? opt->sps_m : nullptr;
+  a->sps = sps1d ? opt->sps : nullptr;
+  a->sps_len = sps1d ? opt->sps_len : 0;
+  a->align = (opt && opt->align_to_tier) ? 1 : 0;
   return DSPARK_OK;
 }
 
@@ -224,6 +237,34 @@ dspark_status dspark_plan_pack(int32_t B, int32_t gamma, dspark_input kind, cons
                   packed_pos, pack_meta, &p);
   if (st != DSPARK_OK) return st;
   return launched(dspark::launch_plan(a, &p, (hipStream_t)stream), "dspark_plan_pack");
+}
+
+dspark_status dspark_plan_pack_ex(int32_t B, int32_t gamma, dspark_input kind, const float* conf,
+                                  const float* sts_temp, int32_t min_verify_len,
+                                  int32_t max_verify_len, float survival_eps, int32_t budget_lo,
+                                  int32_t budget_hi, float cost_bias, const float* cost_alpha,
+                                  int32_t alpha_len, const float* cost_theta, int32_t theta_len,
+                                  int32_t* verify_lens, int32_t* plan_meta, double* plan_val,
+                                  float* survival_out, double* sweep_out,
+                                  const int32_t* anchor_ids, const int32_t* draft_tokens,
+                                  const int32_t* tiers_host, int32_t num_tiers,
+                                  const int32_t* prefix_lens, int32_t* cu_seqlens,
+                                  int32_t* packed_ids, int32_t* packed_req, int32_t* packed_pos,
+                                  int32_t* pack_meta, const dspark_plan_options* options,
+                                  void* stream) {
+  dspark::PlanArgs a;
+  dspark_status st = check_plan("dspark_plan_pack_ex", B, gamma, kind, conf, sts_temp,
+                                min_verify_len, max_verify_len, survival_eps, budget_lo,
+                                budget_hi, cost_bias, cost_alpha, alpha_len, cost_theta,
+                                theta_len, verify_lens, plan_meta, plan_val, survival_out,
+                                sweep_out, &a, options);
+  if (st != DSPARK_OK) return st;
+  dspark::PackArgs p;
+  st = check_pack("dspark_plan_pack_ex", B, gamma, verify_lens, false, anchor_ids, draft_tokens,
+                  tiers_host, num_tiers, prefix_lens, cu_seqlens, packed_ids, packed_req,
+                  packed_pos, pack_meta, &p);
+  if (st != DSPARK_OK) return st;
+  return launched(dspark::launch_plan(a, &p, (hipStream_t)stream), "dspark_plan_pack_ex");
 }
 
 dspark_status dspark_pack(int32_t B, int32_t gamma, const int32_t* verify_lens,

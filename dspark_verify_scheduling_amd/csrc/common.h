@@ -15,6 +15,11 @@ constexpr int kWave = 64;
 
 struct PlanArgs {
   int B, gamma, kind, lmin, lmax, b_lo, b_hi, theta_len;
+  int cost_mode;  // dspark_cost_mode
+  int sps_len;
+  int align;      // graph-tier alignment (fused plan + pack only)
+  const int32_t* sps_m;
+  const float* sps;
   float eps, bias;
   const float* conf;
   const float* temps;

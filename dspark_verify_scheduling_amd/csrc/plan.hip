@@ -34,6 +34,11 @@
 //      fp64 ratio for every b, and a (ratio desc, b asc) argmax reduction;
 //   4. per-request counts of the first b* keys give verify_lens;
 //   5. (fused variant) the exclusive scan, tier and front-packed rows.
+// Variants ("DSpark 自适应 Verify 怎样分配候选预算" §一, §四, §五): the
+// objective tau(b) * SPS(M) with SPS read by floor lookup from a table of
+// probe points (kept in LDS; each thread walks it along its budgets), and
+// graph-tier alignment, which extends the executed budget with the next
+// sorted candidates up to the tier the chosen budget already pays for.
 // The arithmetic uses explicit round-to-nearest intrinsics with contraction
 // disabled, so every step has one defined IEEE result.
 #include <float.h>
@@ -189,6 +194,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   __shared__ unsigned int wmin[kWaves], wmax[kWaves];
   __shared__ int wbad[kWaves];
   __shared__ int s_maxb;
+  __shared__ int s_pm[DSPARK_MAX_SPS_PROBES];    // SPS probe totals
+  __shared__ float s_ps[DSPARK_MAX_SPS_PROBES];  // SPS at each probe
 
   const int tid = threadIdx.x;
   const int B = a.B, G = a.gamma, lmin = a.lmin, lmax = a.lmax, span = lmax - lmin;
@@ -207,14 +214,25 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   }
 
   // cost entries of the budgets this thread will evaluate: b = base_i + e + 1
+  const bool sps_mode = a.cost_mode == DSPARK_COST_SPS1D;
   float th[kMaxItems];
+  float th0 = 0.0f, alpha_b = 0.0f;
+  if (sps_mode) {
+    for (int i = tid; i < a.sps_len; i += kPlanThreads) {
+      s_pm[i] = a.sps_m[i];
+      s_ps[i] = a.sps[i];
+    }
 #pragma unroll
-  for (int e = 0; e < kMaxItems; ++e) {
-    const int m = m0 + base_i + e + 1;
-    th[e] = (e < ipt && base_i + e < n_keys && m < a.theta_len) ? a.theta[m] : 0.0f;
+    for (int e = 0; e < kMaxItems; ++e) th[e] = 0.0f;
+  } else {
+#pragma unroll
+    for (int e = 0; e < kMaxItems; ++e) {
+      const int m = m0 + base_i + e + 1;
+      th[e] = (e < ipt && base_i + e < n_keys && m < a.theta_len) ? a.theta[m] : 0.0f;
+    }
+    th0 = a.theta[m0];
+    alpha_b = a.alpha[B];
   }
-  const float th0 = a.theta[m0];
-  const float alpha_b = a.alpha[B];
 
   // ---- 1a. calibrated confidence of every (request, position), in parallel
   int bad = 0;
@@ -263,6 +281,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
       }
     }
   }
+  // SPS probes must be strictly ascending (bit 1 of `bad`: a cost error,
+  // reported after any confidence error)
+  if (sps_mode) {
+    for (int i = tid + 1; i < a.sps_len; i += kPlanThreads) {
+      if (s_pm[i] <= s_pm[i - 1]) bad |= 2;
+    }
+  }
   // one block reduction for the five quantities: per-wave DPP reductions,
   // then lane w of every wave combines wave w's partials
   {
@@ -293,7 +318,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     __syncthreads();
   }
   if (bad) {
-    fallback<PACK>(a, p, DSPARK_DATA_BAD_CONF, lds, w32, &s_tier);
+    fallback<PACK>(a, p, (bad & 1) ? DSPARK_DATA_BAD_CONF : DSPARK_DATA_BAD_COST, lds, w32,
+                   &s_tier);
     return;
   }
 
@@ -392,6 +418,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   int best_b = 0x7fffffff;
   int cost_bad = 0;
   long long run_fx = base + offset;
+  // 1D mode: index of the last probe at or below the thread's first total M
+  // (0 when every probe is above it); later budgets walk forward from it
+  int pi = 0;
+  if (sps_mode) {
+    const int m_first = m0 + (tid == 0 ? 0 : base_i + 1);
+    int lo = 0, hi = a.sps_len - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pm[mid] <= m_first) lo = mid;
+      else hi = mid - 1;
+    }
+    pi = lo;
+  }
   // slot 0 of thread 0 is b = 0; slot t >= 1 is b = base_i + t
 #pragma unroll
   for (int t = 0; t <= kMaxItems; ++t) {
@@ -407,12 +446,23 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     if (b < 0) continue;
     const long long tfx = (t == 0) ? base : run_fx;
     const double tau = __ll2double_rn(tfx) * 0x1p-40;
-    const double T = __dadd_rn(t_fixed, (double)(t == 0 ? th0 : th[t - 1]));
-    const double ratio = __ddiv_rn(tau, T);
+    double ratio;
+    bool cost_ok;
+    if (sps_mode) {
+      const int M = m0 + b;
+      while (pi + 1 < a.sps_len && s_pm[pi + 1] <= M) ++pi;
+      const float S = s_ps[pi];
+      ratio = __dmul_rn(tau, (double)S);
+      cost_ok = S > 0.0f && S <= FLT_MAX;
+    } else {
+      const double T = __dadd_rn(t_fixed, (double)(t == 0 ? th0 : th[t - 1]));
+      ratio = __ddiv_rn(tau, T);
+      cost_ok = T > 0.0 && T <= DBL_MAX;
+    }
     tau_v[t] = tau;
     ratio_v[t] = ratio;
     if (b >= lo_b && b <= hi_b) {
-      if (!(T > 0.0 && T <= DBL_MAX)) cost_bad = 1;
+      if (!cost_ok) cost_bad = 1;
       else if (better(ratio, b, best_r, best_b)) {
         best_r = ratio;
         best_b = b;
@@ -457,13 +507,27 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     }
   }
 
-  // ---- 4. verify_lens = L_min + #(first b* keys of each request)
+  // graph-tier alignment: fill the tier the chosen total already pays for
+  int bexec = bstar;
+  if (PACK && a.align) {
+    const int total = m0 + bstar;
+    int tier = p.tiers[p.ntiers - 1];
+    for (int i = 0; i < p.ntiers; ++i) {
+      if (p.tiers[i] >= total) {
+        tier = p.tiers[i];
+        break;
+      }
+    }
+    bexec = min(bstar + (tier - total), n_el);
+  }
+
+  // ---- 4. verify_lens = L_min + #(first b_exec keys of each request)
   int32_t* cnt = reinterpret_cast<int32_t*>(lds);  // the keys now live in registers
   for (int r = tid; r < B; r += kPlanThreads) cnt[r] = lmin;
   __syncthreads();
 #pragma unroll
   for (int e = 0; e < kMaxItems; ++e) {
-    if (e < ipt && base_i + e < bstar) atomicAdd(&cnt[key_r(x[e])], 1);
+    if (e < ipt && base_i + e < bexec) atomicAdd(&cnt[key_r(x[e])], 1);
   }
   __syncthreads();
   for (int r = tid; r < B; r += kPlanThreads) a.lens[r] = cnt[r];
@@ -471,7 +535,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     a.meta[0] = bstar;
     a.meta[1] = n_el;
     a.meta[2] = 0;
-    a.meta[3] = m0 + bstar;
+    a.meta[3] = m0 + bexec;
   }
   if (PACK) pack_block<kPlanThreads>(p, cnt, cnt + B, w32, &s_tier, 0);
 }

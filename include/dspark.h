@@ -10,6 +10,8 @@
  *   dspark_pack      verify_lens -> cu_seqlens, front-packed verify rows,
  *                    packed total rounded up to a captured tier
  *   dspark_plan_pack both of the above in one launch
+ *   dspark_plan_pack_ex  the same with the 1D SPS cost model and/or graph-tier
+ *                    alignment of the executed budget
  *   dspark_accept    packed target logits -> per-row argmax -> leading-match
  *                    count, bonus token, commit lengths, output tokens
  *   dspark_cap_accept    greedy accept on the full strided block, committing
@@ -74,7 +76,8 @@ typedef enum dspark_input {
 
 /* Bits of the device-side status word (plan_meta[2], pack_meta[2],
  * accept_meta[1]). */
-#define DSPARK_DATA_BAD_COST 1 /* some T(B, M) <= 0 or non-finite in the sweep */
+#define DSPARK_DATA_BAD_COST 1 /* some T(B, M) (or SPS) <= 0 or non-finite in the
+                                  sweep, or SPS probes not strictly ascending */
 #define DSPARK_DATA_BAD_CONF 2 /* confidence/survival/temperature out of domain */
 #define DSPARK_DATA_BAD_LENS 4 /* verify lengths or cu_seqlens malformed */
 
@@ -84,6 +87,22 @@ typedef enum dspark_input {
 #define DSPARK_MAX_BATCH 8192      /* B for dspark_plan and dspark_pack */
 #define DSPARK_MAX_TIERS 32
 #define DSPARK_MAX_VOCAB 262144
+#define DSPARK_MAX_SPS_PROBES 512
+
+/* How the planner prices a budget (see dspark_plan_pack_ex). */
+typedef enum dspark_cost_mode {
+  DSPARK_COST_ADDITIVE = 0, /* objective tau(b) / T, T = bias + alpha[B] + theta[M] */
+  DSPARK_COST_SPS1D = 1     /* objective tau(b) * SPS(M), SPS by floor lookup */
+} dspark_cost_mode;
+
+/* Options of dspark_plan_pack_ex (host memory; the arrays are device memory). */
+typedef struct dspark_plan_options {
+  dspark_cost_mode cost_mode;
+  const int32_t* sps_m;  /* SPS1D: [sps_len] probe totals M, strictly ascending */
+  const float* sps;      /* SPS1D: [sps_len] steps per second at each probe */
+  int32_t sps_len;       /* SPS1D: 1..DSPARK_MAX_SPS_PROBES */
+  int32_t align_to_tier; /* nonzero: graph-tier alignment (paid-padding reclamation) */
+} dspark_plan_options;
 
 /*
  * dspark_plan - choose the extra verify budget and the per-request verify_lens.
@@ -211,6 +230,49 @@ dspark_status dspark_plan_pack(int32_t B, int32_t gamma, dspark_input kind, cons
                                int32_t num_tiers, const int32_t* prefix_lens, int32_t* cu_seqlens,
                                int32_t* packed_ids, int32_t* packed_req, int32_t* packed_pos,
                                int32_t* pack_meta, void* stream);
+
+/*
+ * dspark_plan_pack_ex - dspark_plan_pack with a choice of cost model and
+ * optional graph-tier alignment.
+ *
+ * Defined by [Budget] §一 (the objective tau(b) * SPS(B + b) with a
+ * one-dimensional SPS table, or tau(b) / T(B, B + b) with the additive one;
+ * budget = argmax_b), [Budget] §四 (the 1D SpsCostTable: steps per second
+ * measured at probe totals M and read by floor lookup, the nearest probe at
+ * or below M with no interpolation, so a cliff in the table is kept), and
+ * [Budget] §五 and §三 (graph-tier alignment: the executed budget is filled
+ * up to the graph tier the chosen budget already pays for, with the next
+ * candidates by survival; it never enters the next tier and never adds rows
+ * that are not candidates).
+ *
+ * options == NULL gives dspark_plan_pack exactly. Otherwise:
+ *   cost_mode DSPARK_COST_SPS1D: objective(b) = RN64(tau(b) * SPS(M)),
+ *     M = B * L_min + b; a total below the first probe takes the first
+ *     probe's value. cost_bias, cost_alpha and cost_theta are ignored (the
+ *     table pointers may be NULL). Probes that are not strictly ascending, or
+ *     an SPS that is not positive and finite at a considered b, set
+ *     DSPARK_DATA_BAD_COST (fallback as in dspark_plan).
+ *   align_to_tier: with b* the argmax and t the smallest tier >= B * L_min +
+ *     b*, the executed budget is b_exec = min(b* + t - (B * L_min + b*),
+ *     number of candidates); verify_lens and the packed rows follow the top
+ *     b_exec candidates. budget_hi bounds b* only.
+ * Outputs as dspark_plan_pack; plan_meta[0] is b*, plan_meta[3] the executed
+ * total B * L_min + b_exec, plan_val and sweep_out hold tau and the
+ * objective.
+ */
+dspark_status dspark_plan_pack_ex(int32_t B, int32_t gamma, dspark_input kind, const float* conf,
+                                  const float* sts_temp, int32_t min_verify_len,
+                                  int32_t max_verify_len, float survival_eps, int32_t budget_lo,
+                                  int32_t budget_hi, float cost_bias, const float* cost_alpha,
+                                  int32_t alpha_len, const float* cost_theta, int32_t theta_len,
+                                  int32_t* verify_lens, int32_t* plan_meta, double* plan_val,
+                                  float* survival_out, double* sweep_out,
+                                  const int32_t* anchor_ids, const int32_t* draft_tokens,
+                                  const int32_t* tiers_host, int32_t num_tiers,
+                                  const int32_t* prefix_lens, int32_t* cu_seqlens,
+                                  int32_t* packed_ids, int32_t* packed_req, int32_t* packed_pos,
+                                  int32_t* pack_meta, const dspark_plan_options* options,
+                                  void* stream);
 
 /*
  * dspark_accept - greedy accept over packed target logits.

@@ -98,6 +98,34 @@ def plan_pack(B, gamma, kind, conf, temps, min_len, max_len, eps, b_lo, b_hi, bi
              "meta": ko.pack_meta.cpu().numpy()})
 
 
+def plan_pack_ex(B, gamma, kind, conf, temps, min_len, max_len, eps, b_lo, b_hi, bias, alpha,
+                 theta, anchors, drafts, tiers, prefix=None, cost_mode=0, sps_m=None, sps=None,
+                 align=False, tag=""):
+    say(f"plan_pack_ex {tag} B={B} gamma={gamma} kind={kind} cost_mode={cost_mode} align={align}")
+    cap = int(tiers[-1])
+    po = dv.alloc_plan_outputs(B, gamma, DEV, survival=True, sweep=True)
+    ko = dv.alloc_pack_outputs(B, cap, DEV)
+    for t in (ko.packed_ids, ko.packed_req, ko.packed_pos):
+        t.fill_(-7)
+    temps_t = up(np.asarray(temps, np.float32)) if temps is not None else None
+    dv.dspark_plan_pack_ex(
+        B, gamma, kind, up(np.asarray(conf, np.float32).reshape(B, gamma)), temps_t, min_len,
+        max_len, float(eps), b_lo, b_hi, float(bias),
+        up(np.asarray(alpha, np.float32)) if alpha is not None else None,
+        up(np.asarray(theta, np.float32)) if theta is not None else None, po,
+        up(np.asarray(anchors, np.int32)), up(np.asarray(drafts, np.int32).reshape(B, gamma)),
+        tiers, up(np.asarray(prefix, np.int32)) if prefix is not None else None, ko,
+        cost_mode=cost_mode, sps_m=up(np.asarray(sps_m, np.int32)) if sps_m is not None else None,
+        sps=up(np.asarray(sps, np.float32)) if sps is not None else None, align_to_tier=align)
+    torch.cuda.synchronize()
+    return ({"verify_lens": po.verify_lens.cpu().numpy(), "meta": po.plan_meta.cpu().numpy(),
+             "val": po.plan_val.cpu().numpy(), "survival": po.survival_out.cpu().numpy(),
+             "sweep": po.sweep_out.cpu().numpy()},
+            {"cu_seqlens": ko.cu_seqlens.cpu().numpy(), "ids": ko.packed_ids.cpu().numpy(),
+             "req": ko.packed_req.cpu().numpy(), "pos": ko.packed_pos.cpu().numpy(),
+             "meta": ko.pack_meta.cpu().numpy()})
+
+
 def accept(B, gamma, V, dt, rows, ld, cu, drafts, prefix=None, max_rows=None, outs=None,
            logits_t=None, tag=""):
     """rows: host array [max_rows, ld] (float32 or bf16 bits), or pass logits_t."""

@@ -103,6 +103,37 @@ def test_plan_pack_argument_errors():
     assert "dspark_plan_pack" in _lib.last_error()
 
 
+def test_plan_pack_ex_argument_errors():
+    tiers = (ctypes.c_int32 * 2)(8, 20)
+    base = dict(B=4, gamma=4, kind=0, conf=FAKE, temp=FAKE, mn=1, mx=5, eps=1e-3, lo=0, hi=-1,
+                bias=0.5, alpha=FAKE, alen=5, theta=FAKE, tlen=21, lens=FAKE, meta=FAKE, val=FAKE,
+                surv=NULL, sweep=NULL, anchors=FAKE, drafts=FAKE,
+                tiers=ctypes.cast(tiers, ctypes.c_void_p), ntiers=2, prefix=NULL, cu=FAKE,
+                ids=FAKE, req=NULL, pos=NULL, pmeta=FAKE, opt=NULL, stream=NULL)
+
+    def run(opt=None, **kw):
+        d = dict(base)
+        d.update(kw)
+        if opt is not None:
+            d["opt"] = ctypes.cast(ctypes.pointer(opt), ctypes.c_void_p)
+        return _lib.lib().dspark_plan_pack_ex(*d.values())
+
+    sps1d = dict(cost_mode=_lib.COST_SPS1D, sps_m=FAKE.value, sps=FAKE.value, sps_len=4,
+                 align_to_tier=1)
+    assert run(gamma=0) == _lib.E_INVALID  # the plan rules still apply
+    assert run(ntiers=1) == _lib.E_INVALID  # and the pack rules
+    assert run(_lib.PlanOptions(cost_mode=7)) == _lib.E_INVALID
+    assert run(_lib.PlanOptions(**{**sps1d, "sps_len": 0})) == _lib.E_INVALID
+    assert run(_lib.PlanOptions(**{**sps1d, "sps_len": _lib.MAX_SPS_PROBES + 1})) == _lib.E_INVALID
+    assert run(_lib.PlanOptions(**{**sps1d, "sps": None})) == _lib.E_INVALID
+    # the additive tables are not needed in 1D mode, but the other rules hold
+    assert run(_lib.PlanOptions(**sps1d), alpha=NULL, theta=NULL, alen=0, tlen=0,
+               anchors=NULL) == _lib.E_INVALID
+    assert "dspark_plan_pack_ex: an input pointer" in _lib.last_error()
+    # additive mode still needs its tables
+    assert run(_lib.PlanOptions(align_to_tier=1), alpha=NULL) == _lib.E_INVALID
+
+
 def _pack(tiers, **kw):
     arr = (ctypes.c_int32 * len(tiers))(*tiers)
     a = dict(B=3, gamma=3, lens=FAKE, anchors=FAKE, drafts=FAKE,
