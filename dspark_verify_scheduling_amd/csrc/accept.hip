@@ -281,44 +281,61 @@ __device__ inline int merge_row(const AcceptArgs& a, int row) {
 // One wave per request (blockIdx.x = r), plus a grid-stride pass that writes
 // the argmax of every row. CAP = false: packed rows cu[r] .. cu[r+1]-1.
 // CAP = true: strided rows r * (gamma + 1) + j, every one of them computed.
+// The loads come in two rounds, each issued before anything waits on it:
+// first the layout words, drafts and prefix; then every partial the wave
+// needs (its row of the row pass and the request's rows). Stores follow.
 template <bool CAP>
 __global__ __launch_bounds__(kWave) void accept_finalize_kernel(AcceptArgs a) {
   __shared__ int am[DSPARK_MAX_GAMMA + 1];
   const int lane = threadIdx.x;
   const int G = a.gamma;
-  const int total = CAP ? a.fixed_rows : a.cu[a.B];
-  const int total_eff = min(max(total, 0), a.max_rows);
-  for (int i = blockIdx.x * kWave + lane; i < total_eff; i += gridDim.x * kWave) {
-    a.row_am[i] = merge_row(a, i);
-  }
   const int r = blockIdx.x;
-  if (r >= a.B) return;
-  int c0, len;  // first row, verify length
+  const bool has_req = r < a.B;
+  // round 1
+  const int total = CAP ? a.fixed_rows : a.cu[a.B];
+  int c0 = 0, len = 0;  // first row, verify length
+  if (has_req) {
+    if constexpr (CAP) {
+      c0 = r * (G + 1);
+      len = a.lens[r];
+    } else {
+      c0 = a.cu[r];
+      len = a.cu[r + 1] - c0;
+    }
+  }
+  const int dr = (has_req && lane < G) ? a.drafts[(size_t)r * G + lane] : 0;
+  const int prefix = (has_req && a.prefix) ? a.prefix[r] : 0;
+  const int total_eff = min(max(total, 0), a.max_rows);
   bool ok;
   if constexpr (CAP) {
-    c0 = r * (G + 1);
-    len = a.lens[r];
     ok = len >= 1 && len <= G + 1;
   } else {
-    c0 = a.cu[r];
-    const int c1 = a.cu[r + 1];
-    len = c1 - c0;
-    ok = c0 >= 0 && len >= 1 && len <= G + 1 && c1 <= total_eff;
+    ok = c0 >= 0 && len >= 1 && len <= G + 1 && c0 + len <= total_eff;
   }
-  const int prefix = a.prefix ? a.prefix[r] : 0;
-  const int32_t* dr = a.drafts + (size_t)r * G;
-  int32_t* out = a.out_tokens + (size_t)r * (G + 1);
-  // rows whose predictions are compared: len - 1 of them, or the full block
-  const int n_chk = CAP ? G : len - 1;
-  if (CAP || ok) {
-    const int n_rows = CAP ? G + 1 : len;
-    for (int j = lane; j < n_rows; j += kWave) am[j] = merge_row(a, c0 + j);
+  // round 2
+  const int i0 = blockIdx.x * kWave + lane;
+  const int n_rows = CAP ? G + 1 : len;  // rows whose predictions are read
+  const bool need = has_req && (CAP || ok);
+  const int g0 = i0 < total_eff ? merge_row(a, i0) : 0;
+  const int m0 = (need && lane < n_rows) ? merge_row(a, c0 + lane) : 0;
+  const int m1 = (need && lane + kWave < n_rows) ? merge_row(a, c0 + lane + kWave) : 0;
+  if (i0 < total_eff) a.row_am[i0] = g0;
+  for (int i = i0 + gridDim.x * kWave; i < total_eff; i += gridDim.x * kWave) {
+    a.row_am[i] = merge_row(a, i);
+  }
+  if (!has_req) return;
+  if (need) {
+    if (lane < n_rows) am[lane] = m0;
+    if (lane + kWave < n_rows) am[lane + kWave] = m1;
   }
   __syncthreads();
+  int32_t* out = a.out_tokens + (size_t)r * (G + 1);
+  // drafts compared: len - 1 of them, or all gamma for the ceiling
+  const int n_chk = CAP ? G : len - 1;
   int c = 0;
-  if (CAP || ok) {
+  if (need) {
     // draft k (0-based, k < n_chk <= 64) against the prediction of row k
-    const bool mismatch = lane < n_chk && dr[lane] != am[lane];
+    const bool mismatch = lane < n_chk && dr != am[lane];
     const unsigned long long mm = __ballot(mismatch);
     c = mm ? (int)__builtin_ctzll(mm) : n_chk;
     if constexpr (CAP) {
@@ -341,7 +358,8 @@ __global__ __launch_bounds__(kWave) void accept_finalize_kernel(AcceptArgs a) {
     return;
   }
   const int bon = am[c];
-  for (int j = lane; j <= G; j += kWave) out[j] = j == c ? bon : (j < G ? dr[j] : -1);
+  // column j < gamma holds draft j (lane j's register); column gamma starts at -1
+  for (int j = lane; j <= G; j += kWave) out[j] = j == c ? bon : (j < G ? dr : -1);
   if (a.mask) {
     for (int k = lane; k < G; k += kWave) a.mask[(size_t)r * G + k] = k < c ? 1 : 0;
   }

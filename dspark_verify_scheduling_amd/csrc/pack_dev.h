@@ -17,13 +17,40 @@
 
 namespace dspark {
 
+// Inputs of the packed rows that thread `threadIdx.x` writes in its first
+// NPRE passes over the B * (gamma + 1) verify slots (slot f = tid + q *
+// NTHREADS): the token id (anchor or draft) and the request's prefix length.
+// Loading them at kernel start hides their latency behind earlier work.
+template <int NTHREADS, int NPRE>
+struct PackPrefetch {
+  int id[NPRE > 0 ? NPRE : 1];
+  int prefix[NPRE > 0 ? NPRE : 1];
+  __device__ void load(const PackArgs& a) {
+    const int G = a.gamma, rows = a.B * (G + 1);
+#pragma unroll
+    for (int q = 0; q < NPRE; ++q) {
+      const int f = threadIdx.x + q * NTHREADS;
+      id[q] = 0;
+      prefix[q] = 0;
+      if (f < rows) {
+        const int r = f / (G + 1);
+        const int j = f - r * (G + 1);
+        id[q] = j ? a.drafts[(size_t)r * G + (j - 1)] : a.anchors[r];
+        prefix[q] = a.prefix ? a.prefix[r] : 0;
+      }
+    }
+  }
+};
+
 // Packs B requests whose (already clamped) lengths sit in LDS `lens`,
 // writing cu_seqlens into LDS `cu` (B + 1 entries) and to global memory.
 // Block-wide: every thread of the NTHREADS-thread workgroup must call it.
-// `status` is OR-ed into meta[2] by thread 0 at the end.
-template <int NTHREADS>
+// `status` is OR-ed into meta[2] by thread 0 at the end. `pre` holds the
+// inputs of this thread's first NPRE slots (see PackPrefetch).
+template <int NTHREADS, int NPRE = 0>
 __device__ void pack_block(const PackArgs& a, const int32_t* lens, int32_t* cu, int* wsum,
-                           int* s_tier, int status) {
+                           int* s_tier, int status,
+                           const PackPrefetch<NTHREADS, NPRE>* pre = nullptr) {
   const int tid = threadIdx.x;
   const int B = a.B, G = a.gamma;
   const int ipt = (B + NTHREADS - 1) / NTHREADS;
@@ -56,7 +83,21 @@ __device__ void pack_block(const PackArgs& a, const int32_t* lens, int32_t* cu, 
   }
   __syncthreads();
   const int rows = B * (G + 1);
-  for (int f = tid; f < rows; f += NTHREADS) {
+#pragma unroll
+  for (int q = 0; q < NPRE; ++q) {
+    const int f = tid + q * NTHREADS;
+    if (f < rows) {
+      const int r = f / (G + 1);
+      const int j = f - r * (G + 1);
+      if (j < lens[r]) {
+        const int i = cu[r] + j;
+        a.ids[i] = pre->id[q];
+        if (a.req) a.req[i] = r;
+        if (a.pos) a.pos[i] = pre->prefix[q] + j;
+      }
+    }
+  }
+  for (int f = tid + NPRE * NTHREADS; f < rows; f += NTHREADS) {
     const int r = f / (G + 1);
     const int j = f - r * (G + 1);
     if (j < lens[r]) {

@@ -158,15 +158,20 @@ __device__ void write_fallback(const PlanArgs& a, int flags) {
 
 // Static window for every request: the fallback for bad data (and, in the
 // fused variant, its packed layout).
+// Pack inputs prefetched per thread by the fused kernel (3 slots cover
+// B * (gamma + 1) <= 3072 verify slots, e.g. B = 256 at gamma = 8).
+constexpr int kPackPrefetch = 3;
+using PlanPrefetch = PackPrefetch<kPlanThreads, kPackPrefetch>;
+
 template <bool PACK>
 __device__ void fallback(const PlanArgs& a, const PackArgs& p, int flags, uint64_t* lds, int* w32,
-                         int* s_tier) {
+                         int* s_tier, const PlanPrefetch* pre) {
   write_fallback(a, flags);
   if (PACK) {
     int32_t* lens = reinterpret_cast<int32_t*>(lds);
     for (int r = threadIdx.x; r < a.B; r += kPlanThreads) lens[r] = a.lmax;
     __syncthreads();
-    pack_block<kPlanThreads>(p, lens, lens + a.B, w32, s_tier, 0);
+    pack_block<kPlanThreads, kPackPrefetch>(p, lens, lens + a.B, w32, s_tier, 0, pre);
   }
 }
 
@@ -213,6 +218,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     s_maxb = 0;
   }
 
+  PlanPrefetch pre;
+  if (PACK) pre.load(p);
   // cost entries of the budgets this thread will evaluate: b = base_i + e + 1
   const bool sps_mode = a.cost_mode == DSPARK_COST_SPS1D;
   float th[kMaxItems];
@@ -319,7 +326,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   }
   if (bad) {
     fallback<PACK>(a, p, (bad & 1) ? DSPARK_DATA_BAD_CONF : DSPARK_DATA_BAD_COST, lds, w32,
-                   &s_tier);
+                   &s_tier, &pre);
     return;
   }
 
@@ -478,7 +485,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   }
   __syncthreads();
   if (s_flags) {
-    fallback<PACK>(a, p, s_flags, lds, w32, &s_tier);
+    fallback<PACK>(a, p, s_flags, lds, w32, &s_tier, &pre);
     return;
   }
   double br = lane < kWaves ? wratio[lane] : -1.0;
@@ -537,7 +544,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     a.meta[2] = 0;
     a.meta[3] = m0 + bexec;
   }
-  if (PACK) pack_block<kPlanThreads>(p, cnt, cnt + B, w32, &s_tier, 0);
+  if (PACK) pack_block<kPlanThreads, kPackPrefetch>(p, cnt, cnt + B, w32, &s_tier, 0, &pre);
 }
 
 }  // namespace
