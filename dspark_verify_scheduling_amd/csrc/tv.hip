@@ -193,6 +193,165 @@ __global__ __launch_bounds__(kTvThreads) void tv_kernel(TvArgs a) {
   if (tid == 0) a.a_out[pair] = total > 1.0f ? 1.0f : total;
 }
 
+// Resident variant: the pair stays on the CU between the passes, so every
+// logit is read from HBM once. Vector pair v (16 bytes of q and of p) lives
+//   in registers of thread v % 1024 (slot v / 1024) for v < 11 * 1024, and
+//   in LDS for the rest (q at i, p at n_lds + i, i = v - 11 * 1024),
+// which holds rows of up to 11 * 1024 + 4992 vectors (bf16 V <= 130055):
+// 88 VGPRs and up to 156 KB of LDS, so one workgroup per CU. The LDS part and
+// register slots 8..10 are requested first, slots 0..7 as soon as the LDS
+// part is stored (which keeps the live registers under the 128 a 1024-thread
+// workgroup allows); the pass-1 statistics are accumulated as data arrives,
+// and pass 2 reads only registers and LDS. Longer rows take the two-pass
+// streaming kernel above.
+constexpr int kResRegSlots = 11;
+constexpr int kResLdsSlots = 5;
+constexpr int kResRegSpan = kResRegSlots * kTvThreads;
+constexpr int kResLdsMaxPairs = 4992;  // 2 * 4992 * 16 B = 156 KB
+constexpr int kEarly = 8;  // register slots kEarly.. are requested with the LDS part
+
+// One row's 16 bytes into its running statistics.
+template <dspark_dtype DT>
+__device__ inline void stat_add_vec(Stat& st, const u32x4& d) {
+  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
+  float x[kEpv];
+  widen<DT>(d, x);
+  float bm = x[0];
+#pragma unroll
+  for (int i = 1; i < kEpv; ++i) bm = fmaxf(bm, x[i]);
+  stat_add<kEpv>(st, x, bm);
+}
+
+template <dspark_dtype DT>
+__device__ inline void stat_add_pair(Stat& sq, Stat& sp, const u32x4& dq, const u32x4& dp) {
+  stat_add_vec<DT>(sq, dq);
+  stat_add_vec<DT>(sp, dp);
+}
+
+template <dspark_dtype DT>
+__device__ inline float min_sum_pair(const u32x4& dq, const u32x4& dp, float aq, float ap) {
+  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
+  float x[kEpv], y[kEpv];
+  widen<DT>(dq, x);
+  widen<DT>(dp, y);
+  float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kEpv; i += 2) {
+    s0 += exp2_raw(fminf(__fmaf_rn(x[i], kLog2e, -aq), __fmaf_rn(y[i], kLog2e, -ap)));
+    s1 += exp2_raw(fminf(__fmaf_rn(x[i + 1], kLog2e, -aq), __fmaf_rn(y[i + 1], kLog2e, -ap)));
+  }
+  return s0 + s1;
+}
+
+template <dspark_dtype DT>
+__global__ __launch_bounds__(kTvThreads) void tv_resident_kernel(TvArgs a) {
+  extern __shared__ u32x4 lds_pairs[];  // q vectors [n_lds], then p vectors [n_lds]
+  __shared__ Stat ws[kWaves];
+  __shared__ float wsf[kWaves];
+  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
+  constexpr unsigned int kNegInf = DT == DSPARK_BF16 ? 0xFF80FF80u : 0xFF800000u;
+  const int pair = blockIdx.x;
+  const int r = pair / a.gamma;
+  const int k0 = pair - r * a.gamma;
+  const unsigned char* qrow = a.q + (size_t)pair * a.ldq_bytes;
+  const unsigned char* prow = a.p + ((size_t)r * a.rows_per_req + k0) * a.ldp_bytes;
+  const u32x4* qv = reinterpret_cast<const u32x4*>(qrow);
+  const u32x4* pv = reinterpret_cast<const u32x4*>(prow);
+  const int tid = threadIdx.x;
+  const int nvec = a.nvec;
+  const int n_lds = nvec > kResRegSpan ? nvec - kResRegSpan : 0;
+  u32x4* lq = lds_pairs;
+  u32x4* lp = lds_pairs + n_lds;
+  const u32x4 fill = (u32x4){kNegInf, kNegInf, kNegInf, kNegInf};
+
+  // pass 1, phase A: the LDS part and register slots kEarly..10
+  u32x4 tq[kResLdsSlots], tp[kResLdsSlots];
+#pragma unroll
+  for (int c = 0; c < kResLdsSlots; ++c) {
+    const int i = c * kTvThreads + tid;
+    tq[c] = fill;
+    tp[c] = fill;
+    if (i < n_lds) {
+      tq[c] = qv[kResRegSpan + i];
+      tp[c] = pv[kResRegSpan + i];
+    }
+  }
+  u32x4 rq[kResRegSlots], rp[kResRegSlots];
+#pragma unroll
+  for (int c = kEarly; c < kResRegSlots; ++c) {
+    const int v = c * kTvThreads + tid;
+    rq[c] = fill;
+    rp[c] = fill;
+    if (v < nvec) {
+      rq[c] = qv[v];
+      rp[c] = pv[v];
+    }
+  }
+  Stat sq{-FLT_MAX, 0.0f}, sp{-FLT_MAX, 0.0f};
+#pragma unroll
+  for (int c = 0; c < kResLdsSlots; ++c) {
+    const int i = c * kTvThreads + tid;
+    if (i < n_lds) {
+      lq[i] = tq[c];
+      lp[i] = tp[c];
+      stat_add_pair<DT>(sq, sp, tq[c], tp[c]);
+    }
+  }
+  // phase B: register slots 0..kEarly-1. The scheduling barrier keeps these
+  // loads from being hoisted above phase A, whose registers they reuse.
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < kEarly; ++c) {
+    const int v = c * kTvThreads + tid;
+    rq[c] = fill;
+    rp[c] = fill;
+    if (v < nvec) {
+      rq[c] = qv[v];
+      rp[c] = pv[v];
+    }
+  }
+#pragma unroll
+  for (int c = kEarly; c < kResRegSlots; ++c) stat_add_pair<DT>(sq, sp, rq[c], rp[c]);
+#pragma unroll
+  for (int c = 0; c < kEarly; ++c) stat_add_pair<DT>(sq, sp, rq[c], rp[c]);
+  if (tid == 0) {
+    for (int t = 0; t < a.tail; ++t) {
+      const int i = nvec * kEpv + t;
+      float x[2] = {elem<DT>(qrow, i), -INFINITY};
+      stat_add<2>(sq, x, x[0]);
+      float y[2] = {elem<DT>(prow, i), -INFINITY};
+      stat_add<2>(sp, y, y[0]);
+    }
+  }
+  sq = block_stat(sq, ws);
+  sp = block_stat(sp, ws);
+  const float aq = sq.mL + log2f(sq.s);
+  const float ap = sp.mL + log2f(sp.s);
+
+  // pass 2 from registers and LDS. The empty asm makes the raw words opaque,
+  // so pass 2 widens them again instead of keeping pass 1's fp32 copies alive
+  // (which would double the registers the slots need).
+#pragma unroll
+  for (int c = 0; c < kResRegSlots; ++c) asm volatile("" : "+v"(rq[c]), "+v"(rp[c]));
+  float acc = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kResRegSlots; ++c) acc += min_sum_pair<DT>(rq[c], rp[c], aq, ap);
+#pragma unroll
+  for (int c = 0; c < kResLdsSlots; ++c) {
+    const int i = c * kTvThreads + tid;
+    if (i < n_lds) acc += min_sum_pair<DT>(lq[i], lp[i], aq, ap);
+  }
+  if (tid == 0) {
+    for (int t = 0; t < a.tail; ++t) {
+      const int i = nvec * kEpv + t;
+      acc += exp2_raw(fminf(__fmaf_rn(elem<DT>(qrow, i), kLog2e, -aq),
+                            __fmaf_rn(elem<DT>(prow, i), kLog2e, -ap)));
+    }
+  }
+  const float total = block_sum<float, kTvThreads>(acc, wsf);
+  if (tid == 0) a.a_out[pair] = total > 1.0f ? 1.0f : total;
+}
+
 __global__ void tv_cumprod_kernel(const float* a_in, float* s_out, int B, int G) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= B) return;
@@ -209,7 +368,17 @@ __global__ void tv_cumprod_kernel(const float* a_in, float* s_out, int B, int G)
 hipError_t launch_tv(const TvArgs& a, dspark_dtype dt, hipStream_t s) {
   const int pairs = a.B * a.gamma;
   if (pairs > 0) {
-    if (dt == DSPARK_BF16) {
+    const int n_lds = a.nvec > kResRegSpan ? a.nvec - kResRegSpan : 0;
+    if (n_lds <= kResLdsMaxPairs) {
+      const size_t lds = (size_t)2 * n_lds * sizeof(u32x4);
+      if (dt == DSPARK_BF16) {
+        hipLaunchKernelGGL(tv_resident_kernel<DSPARK_BF16>, dim3(pairs), dim3(kTvThreads), lds, s,
+                           a);
+      } else {
+        hipLaunchKernelGGL(tv_resident_kernel<DSPARK_F32>, dim3(pairs), dim3(kTvThreads), lds, s,
+                           a);
+      }
+    } else if (dt == DSPARK_BF16) {
       hipLaunchKernelGGL(tv_kernel<DSPARK_BF16>, dim3(pairs), dim3(kTvThreads), 0, s, a);
     } else {
       hipLaunchKernelGGL(tv_kernel<DSPARK_F32>, dim3(pairs), dim3(kTvThreads), 0, s, a);

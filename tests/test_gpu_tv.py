@@ -33,8 +33,15 @@ def _rand_logits(rng, shape, sigma, dt):
     return f32_to_bf16_bits(x) if dt == 1 else x
 
 
+# Row sizes around the kernel's layout limits: pairs of 16-byte vectors up to
+# 11 * 1024 stay in registers, up to 4992 more in LDS (16256 vectors: bf16
+# V <= 130055 is resident), longer rows take the two-pass streaming kernel.
 @pytest.mark.parametrize("V,pad,dt", [(257, 0, 1), (257, 7, 1), (1000, 0, 0), (1001, 3, 0),
-                                      (4096, 8, 1), (32000, 0, 1), (3, 1, 0)])
+                                      (4096, 8, 1), (32000, 0, 1), (3, 1, 0),
+                                      (90121, 5, 1),    # registers + 1 LDS pair, ragged tail
+                                      (130055, 0, 1),   # the largest resident bf16 row
+                                      (130056, 0, 1),   # one vector more: streaming
+                                      (70001, 3, 0)])   # fp32, streaming, ragged tail
 def test_tv_small(V, pad, dt):
     rng = np.random.default_rng(V * 7 + pad + dt)
     B, G = 3, 4
