@@ -41,10 +41,11 @@ from .pack import DATA_BAD_LENS, pack
 from .accept import accept, row_argmax
 from .tv import tv_accept
 from .strided import cap_accept, scatter_to_strided
+from .sts import sts_fit
 
 __all__ = [
     "sigmoid32", "survival", "plan", "pack", "accept", "row_argmax", "tv_accept",
-    "cap_accept", "scatter_to_strided",
+    "cap_accept", "scatter_to_strided", "sts_fit",
     "IN_CONF_LOGITS", "IN_COND", "IN_SURVIVAL", "COST_ADDITIVE", "COST_SPS1D", "sps_floor",
     "DATA_BAD_COST", "DATA_BAD_CONF", "DATA_BAD_LENS", "FX_SHIFT",
 ]
