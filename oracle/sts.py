@@ -27,6 +27,8 @@ Readings (also in the design notes):
 * Brier = mean (S - y)^2, each term at 2**-40 resolution likewise; it is
   reported for the chosen T and decides nothing.
 * The sigmoid is the correctly rounded one of the planner (oracle/sigmoid.py).
+* A NaN survival (only a NaN logit makes one) is binned and summed as 0; the
+  stored survival stays NaN.
 """
 
 from __future__ import annotations
@@ -43,9 +45,15 @@ def _fx(v64: np.ndarray) -> np.ndarray:
     return np.rint(v64 * FX).astype(np.int64)
 
 
+def _nan_as_zero(S) -> np.ndarray:
+    """float64 survivals; a NaN (only a NaN logit makes one) counts as 0."""
+    S64 = np.asarray(S, dtype=np.float32).astype(np.float64)
+    return np.where(np.isnan(S64), 0.0, S64)
+
+
 def ece_terms(S: np.ndarray, y: np.ndarray, nbins: int):
     """Per-bin (count, label sum, S sum at 2**-40) and the exact n * ECE * 2**40."""
-    S64 = np.asarray(S, dtype=np.float32).astype(np.float64)
+    S64 = _nan_as_zero(S)
     y = np.asarray(y).astype(np.int64)
     b = np.minimum(np.floor(S64 * nbins).astype(np.int64), nbins - 1)
     count = np.bincount(b, minlength=nbins).astype(np.int64)
@@ -58,7 +66,7 @@ def ece_terms(S: np.ndarray, y: np.ndarray, nbins: int):
 
 def brier_fx(S: np.ndarray, y: np.ndarray) -> int:
     """n * Brier * 2**40, each squared error at 2**-40 resolution."""
-    d = np.asarray(S, dtype=np.float32).astype(np.float64) - np.asarray(y, dtype=np.float64)
+    d = _nan_as_zero(S) - np.asarray(y, dtype=np.float64)
     return int(np.sum(_fx(d * d)))  # d * d is exact in float64
 
 

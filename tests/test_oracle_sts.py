@@ -108,3 +108,24 @@ def test_perfectly_calibrated_ties_take_the_first_candidate():
     assert out["ece_fx"].tolist() == [[0, 0, 0]]
     assert out["t_index"].tolist() == [0] and out["temps"].tolist() == [3.0]
     assert out["brier"][0] == 0.25
+
+
+def test_nan_survival_bins_like_zero():
+    # a NaN logit makes its survival NaN from that position on; it is binned
+    # and summed as 0, exactly like a -inf logit (whose survival is 0)
+    rng = np.random.default_rng(4)
+    n, g = 400, 3
+    z = rng.normal(0.5, 2.0, (n, g)).astype(np.float32)
+    y = np.cumprod(rng.random((n, g)) < 0.6, axis=1).astype(np.int64)
+    y[[7, 19, 30], :] = 0
+    grid = np.array([0.5, 1.0, 2.0, 4.0], np.float32)
+    zn, zi = z.copy(), z.copy()
+    zn[7, 0] = zn[19, 1] = zn[30, 2] = np.nan
+    zi[7, 0] = zi[19, 1] = zi[30, 2] = -np.inf
+    a, b = sts.sts_fit(zn, y, grid, 10), sts.sts_fit(zi, y, grid, 10)
+    assert np.array_equal(a["ece_fx"], b["ece_fx"])
+    assert np.array_equal(a["t_index"], b["t_index"]) and np.array_equal(a["brier"], b["brier"])
+    assert np.isnan(a["survival"][7]).all() and (b["survival"][7] == 0).all()
+    assert np.isnan(a["survival"][19, 1:]).all() and not np.isnan(a["survival"][19, 0])
+    # and a NaN that counted as anything else would move the error
+    assert sts.ece_terms(np.array([np.nan], np.float32), np.array([0]), 4)[3] == 0
