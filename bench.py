@@ -421,6 +421,26 @@ def main():
     acc_bytes = accept_bytes(total, B, G, V, esize)
     achieved = acc_bytes / (acc_mean_us * 1e-6) / 1e9
 
+    # ---- STS fitter: 65536 records of gamma = 8, 64 grid temperatures, 15 bins
+    rng = np.random.default_rng(5)
+    n_rec = 65536
+    z_rec = (rng.normal(1.2, 1.2, (n_rec, G)) - 0.3 * np.arange(1, G + 1)).astype(np.float32)
+    p_acc = 1.0 / (1.0 + np.exp(-z_rec.astype(np.float64) / 1.3))
+    y_rec = np.cumprod(rng.random((n_rec, G)) < p_acc, axis=1).astype(np.uint8)
+    z_t, y_t = t(z_rec), t(y_rec)
+    sts_grid = np.exp(np.linspace(np.log(0.25), np.log(4.0), 64)).astype(np.float32)
+    for _ in range(2):
+        fit = dv.dspark_sts_fit(z_t, y_t, sts_grid, 15, ece_grid=False, stream=stream)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(5):
+        fit = dv.dspark_sts_fit(z_t, y_t, sts_grid, 15, ece_grid=False, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    sts_us = 1e3 * start.elapsed_time(stop) / 5
+    sts_res = {"records": n_rec, "gamma": G, "grid": int(sts_grid.size), "bins": 15,
+               "us": sts_us, "temps": [round(float(x), 4) for x in fit.temps.cpu()]}
+
     tv_res = None
     if not args.no_tv:
         log("soft accept-rate pass at B=256, gamma=16, V=129280 bf16")
@@ -465,6 +485,7 @@ def main():
                        "frac": cap_gbs / PEAK_HBM_GBS},
         "scatter_to_strided": {"rows": total, "us": scat_us, "GB/s": scat_gbs,
                                "frac": scat_gbs / PEAK_HBM_GBS, "bytes": scat_bytes},
+        "sts_fit": sts_res,
         "tv_pass": tv_res,
         "wall_s_timed": wall,
     }

@@ -29,7 +29,7 @@ __all__ = [
     "dspark_accept", "dspark_tv_accept", "COST_ADDITIVE", "COST_SPS1D",
     "dspark_cap_accept", "dspark_scatter_to_strided", "dspark_accept_workspace_size",
     "alloc_plan_outputs", "alloc_pack_outputs", "alloc_accept_outputs",
-    "alloc_cap_accept_outputs", "DsparkError", "F32", "BF16", "IN_CONF_LOGITS", "IN_COND",
+    "alloc_cap_accept_outputs", "dspark_sts_fit", "dspark_sts_workspace_size", "DsparkError", "F32", "BF16", "IN_CONF_LOGITS", "IN_COND",
     "IN_SURVIVAL", "DATA_BAD_COST", "DATA_BAD_CONF", "DATA_BAD_LENS",
 ]
 
@@ -415,6 +415,62 @@ def dspark_scatter_to_strided(B: int, stride: int, cu_seqlens: torch.Tensor, pac
     )
     _lib.check("dspark_scatter_to_strided", _lib.lib().dspark_scatter_to_strided(*args))
     return strided
+
+
+# ------------------------------------------------------------------ STS fitter
+
+class StsFit(NamedTuple):
+    temps: torch.Tensor  # [gamma] float32
+    t_index: torch.Tensor  # [gamma] int32
+    ece: torch.Tensor  # [gamma] float64
+    brier: torch.Tensor  # [gamma] float64
+    ece_grid: Optional[torch.Tensor]  # [gamma, n_t] float64
+    survival: Optional[torch.Tensor]  # [N, gamma] float32
+
+
+def dspark_sts_workspace_size(N: int, gamma: int, n_t: int, n_bins: int) -> int:
+    return int(_lib.lib().dspark_sts_workspace_size(N, gamma, n_t, n_bins))
+
+
+def dspark_sts_fit(z: torch.Tensor, prefix_mask: torch.Tensor, t_grid: Sequence[float],
+                   n_bins: int, survival=True, ece_grid=True, stream=None) -> StsFit:
+    """Fit one STS temperature per position on records ``z`` [N, gamma] (float32
+    confidence logits) and ``prefix_mask`` [N, gamma] (uint8 greedy labels)."""
+    import ctypes
+
+    if z.dim() != 2:
+        raise ValueError("z must be [N, gamma]")
+    N, gamma = z.shape
+    grid = [float(t) for t in t_grid]
+    n_t = len(grid)
+    grid_host = (ctypes.c_float * max(n_t, 1))(*grid)
+    dev = z.device
+    out = StsFit(
+        torch.empty(gamma, dtype=torch.float32, device=dev),
+        torch.empty(gamma, dtype=torch.int32, device=dev),
+        torch.empty(gamma, dtype=torch.float64, device=dev),
+        torch.empty(gamma, dtype=torch.float64, device=dev),
+        torch.empty(gamma, max(n_t, 1), dtype=torch.float64, device=dev) if ece_grid else None,
+        torch.empty(N, gamma, dtype=torch.float32, device=dev) if survival else None,
+    )
+    ws_bytes = dspark_sts_workspace_size(N, gamma, n_t, n_bins)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    args = (
+        N, gamma,
+        _ptr(z, "z", torch.float32, N * gamma),
+        _ptr(prefix_mask, "prefix_mask", torch.uint8, N * gamma),
+        ctypes.cast(grid_host, ctypes.c_void_p), n_t, n_bins,
+        _ptr(out.temps, "temps", torch.float32, gamma),
+        _ptr(out.t_index, "t_index", torch.int32, gamma),
+        _ptr(out.ece, "ece", torch.float64, gamma),
+        _ptr(out.brier, "brier", torch.float64, gamma),
+        _ptr(out.ece_grid, "ece_grid", torch.float64, gamma * n_t, required=False),
+        _ptr(out.survival, "survival", torch.float32, N * gamma, required=False),
+        _ptr(ws, "workspace", torch.uint8, 1), ws.numel(),
+        _stream(stream),
+    )
+    _lib.check("dspark_sts_fit", _lib.lib().dspark_sts_fit(*args))
+    return out
 
 
 # ------------------------------------------------------------------ TV

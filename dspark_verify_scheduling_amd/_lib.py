@@ -21,6 +21,7 @@ IN_CONF_LOGITS, IN_COND, IN_SURVIVAL = 0, 1, 2
 DATA_BAD_COST, DATA_BAD_CONF, DATA_BAD_LENS = 1, 2, 4
 MAX_GAMMA, MAX_CANDIDATES, MAX_BATCH, MAX_TIERS, MAX_VOCAB = 64, 8192, 8192, 32, 262144
 MAX_SPS_PROBES = 512
+STS_MAX_GRID, STS_MAX_BINS, STS_MAX_RECORDS = 128, 64, 4194304
 COST_ADDITIVE, COST_SPS1D = 0, 1
 
 
@@ -61,6 +62,10 @@ SIGNATURES = {
         c_int32, c_int32, c_void_p, c_int32, c_void_p, c_int64, c_void_p, c_int64, c_int64,
         c_void_p, c_void_p]),
     "dspark_accept_workspace_size": (c_size_t, [c_int32, c_int32, c_int]),
+    "dspark_sts_fit": (c_int, [
+        c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "dspark_sts_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
     "dspark_tv_accept": (c_int, [
         c_int32, c_int32, c_int32, c_int, c_void_p, c_int64, c_void_p, c_int64, c_int32,
         c_void_p, c_void_p, c_void_p]),

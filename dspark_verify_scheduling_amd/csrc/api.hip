@@ -1,6 +1,7 @@
 // C ABI of libdspark: argument validation on the host, then kernel launches
 // on the caller's stream. No allocation, no synchronization, no host reads of
 // device data.
+#include <float.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -55,6 +56,27 @@ RowGeom row_geom(int V, dspark_dtype dt) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of dspark_sts_fit: survivals, chosen temperatures, histograms.
+struct StsGeom {
+  int per_block, n_blocks;
+  size_t s_off, t_off, p_off, bytes;
+};
+
+StsGeom sts_geom(int N, int gamma, int n_t, int n_bins) {
+  StsGeom g;
+  // at least kStsRecordsPerBlock records per workgroup, at most kStsMaxBlocks
+  // workgroups (which bounds the histogram slots of the workspace)
+  const int want = (N + dspark::kStsMaxBlocks - 1) / dspark::kStsMaxBlocks;
+  g.per_block = std::max(dspark::kStsRecordsPerBlock,
+                         (want + dspark::kStsThreads - 1) / dspark::kStsThreads * dspark::kStsThreads);
+  g.n_blocks = N > 0 ? (N + g.per_block - 1) / g.per_block : 1;
+  g.s_off = 0;
+  g.t_off = align256((size_t)N * sizeof(float));
+  g.p_off = g.t_off + align256((size_t)gamma * sizeof(float));
+  g.bytes = g.p_off + align256((size_t)g.n_blocks * n_t * (2 * n_bins + 1) * sizeof(long long));
+  return g;
+}
 
 // Workspace of dspark_accept: one 64-bit (key, index) partial per unit.
 size_t ws_bytes(int max_rows, int chunks) {
@@ -398,6 +420,66 @@ dspark_status dspark_scatter_to_strided(int32_t B, int32_t stride, const int32_t
   if ((int64_t)B * a.chunks > 0x7fffffffLL)
     return fail(DSPARK_E_UNSUPPORTED, "dspark_scatter_to_strided: B * units overflows int32");
   return launched(dspark::launch_scatter(a, (hipStream_t)stream), "dspark_scatter_to_strided");
+}
+
+size_t dspark_sts_workspace_size(int32_t N, int32_t gamma, int32_t n_t, int32_t n_bins) {
+  if (N < 0 || N > DSPARK_STS_MAX_RECORDS || gamma < 1 || gamma > DSPARK_MAX_GAMMA || n_t < 1 ||
+      n_t > DSPARK_STS_MAX_GRID || n_bins < 1 || n_bins > DSPARK_STS_MAX_BINS)
+    return 0;
+  return sts_geom(N, gamma, n_t, n_bins).bytes;
+}
+
+dspark_status dspark_sts_fit(int32_t N, int32_t gamma, const float* z, const uint8_t* prefix_mask,
+                             const float* t_grid_host, int32_t n_t, int32_t n_bins, float* temps,
+                             int32_t* t_index, double* ece, double* brier, double* ece_grid,
+                             float* survival_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (N < 0 || N > DSPARK_STS_MAX_RECORDS)
+    return fail(N < 0 ? DSPARK_E_INVALID : DSPARK_E_UNSUPPORTED,
+                "dspark_sts_fit: N = %d outside [0, %d]", N, DSPARK_STS_MAX_RECORDS);
+  if (gamma < 1 || gamma > DSPARK_MAX_GAMMA)
+    return fail(DSPARK_E_INVALID, "dspark_sts_fit: gamma = %d outside [1, %d]", gamma,
+                DSPARK_MAX_GAMMA);
+  if (!t_grid_host || n_t < 1 || n_t > DSPARK_STS_MAX_GRID)
+    return fail(DSPARK_E_INVALID, "dspark_sts_fit: need 1..%d grid temperatures, got %d",
+                DSPARK_STS_MAX_GRID, n_t);
+  for (int t = 0; t < n_t; ++t) {
+    if (!(t_grid_host[t] > 0.0f && t_grid_host[t] <= FLT_MAX))
+      return fail(DSPARK_E_INVALID, "dspark_sts_fit: grid temperature %d is not positive and finite",
+                  t);
+  }
+  if (n_bins < 1 || n_bins > DSPARK_STS_MAX_BINS)
+    return fail(DSPARK_E_INVALID, "dspark_sts_fit: n_bins = %d outside [1, %d]", n_bins,
+                DSPARK_STS_MAX_BINS);
+  if (N > 0 && (!z || !prefix_mask))
+    return fail(DSPARK_E_INVALID, "dspark_sts_fit: z or prefix_mask is NULL");
+  if (!temps || !t_index || !ece || !brier)
+    return fail(DSPARK_E_INVALID, "dspark_sts_fit: an output pointer is NULL");
+  const StsGeom g = sts_geom(N, gamma, n_t, n_bins);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < g.bytes)
+    return fail(DSPARK_E_WORKSPACE, "dspark_sts_fit: workspace needs %zu bytes, 256-byte aligned",
+                g.bytes);
+  dspark::StsArgs a;
+  a.N = N;
+  a.gamma = gamma;
+  a.n_t = n_t;
+  a.nbins = n_bins;
+  a.per_block = g.per_block;
+  a.n_blocks = g.n_blocks;
+  a.z = z;
+  a.labels = prefix_mask;
+  for (int t = 0; t < DSPARK_STS_MAX_GRID; ++t) a.grid[t] = t < n_t ? t_grid_host[t] : 0.0f;
+  a.temps = temps;
+  a.t_index = t_index;
+  a.ece = ece;
+  a.brier = brier;
+  a.ece_grid = ece_grid;
+  a.surv_out = survival_out;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  a.s_work = reinterpret_cast<float*>(ws + g.s_off);
+  a.chosen_t = reinterpret_cast<float*>(ws + g.t_off);
+  a.partials = reinterpret_cast<long long*>(ws + g.p_off);
+  return launched(dspark::launch_sts(a, (hipStream_t)stream), "dspark_sts_fit");
 }
 
 size_t dspark_accept_workspace_size(int32_t max_rows, int32_t V, dspark_dtype dt) {

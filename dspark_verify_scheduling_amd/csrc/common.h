@@ -113,6 +113,27 @@ struct TvArgs {
 constexpr int kTvThreads = 1024;
 hipError_t launch_tv(const TvArgs& a, dspark_dtype dt, hipStream_t s);
 
+struct StsArgs {
+  int N, gamma, n_t, nbins;
+  int per_block, n_blocks;  // records per workgroup of the bin kernel, workgroups
+  const float* z;           // [N, gamma] confidence logits
+  const uint8_t* labels;    // [N, gamma] greedy prefix labels (nonzero = survived)
+  float grid[DSPARK_STS_MAX_GRID];
+  float* temps;             // [gamma]
+  int32_t* t_index;         // [gamma]
+  double* ece;              // [gamma]
+  double* brier;            // [gamma]
+  double* ece_grid;         // [gamma, n_t] or null
+  float* surv_out;          // [N, gamma] or null
+  float* s_work;            // workspace: [N] survival of the previous position
+  float* chosen_t;          // workspace: [gamma] chosen temperatures
+  long long* partials;      // workspace: [n_blocks, n_t, 2 * nbins + 1]
+};
+constexpr int kStsThreads = 256;
+constexpr int kStsRecordsPerBlock = 256;  // at least
+constexpr int kStsMaxBlocks = 1024;
+hipError_t launch_sts(const StsArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------- helpers
 
 __device__ inline int lane_id() { return threadIdx.x & (kWave - 1); }

@@ -19,6 +19,8 @@
  *                    ceiling (cap-accept mode)
  *   dspark_scatter_to_strided  packed verify rows (logits or hidden states)
  *                    back to the strided [B, stride] layout
+ *   dspark_sts_fit   (offline) the per-position STS temperatures that feed
+ *                    dspark_plan, fitted on recorded logits and prefix_masks
  *   dspark_tv_accept (optional) soft accept-rate 1 - TV(softmax q, softmax p)
  *                    and its per-request cumulative product, which can feed
  *                    dspark_plan as survivals
@@ -88,6 +90,9 @@ typedef enum dspark_input {
 #define DSPARK_MAX_TIERS 32
 #define DSPARK_MAX_VOCAB 262144
 #define DSPARK_MAX_SPS_PROBES 512
+#define DSPARK_STS_MAX_GRID 128        /* temperature candidates of dspark_sts_fit */
+#define DSPARK_STS_MAX_BINS 64         /* calibration bins of dspark_sts_fit */
+#define DSPARK_STS_MAX_RECORDS 4194304 /* records of dspark_sts_fit */
 
 /* How the planner prices a budget (see dspark_plan_pack_ex). */
 typedef enum dspark_cost_mode {
@@ -433,6 +438,54 @@ dspark_status dspark_tv_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype
                                const void* target_logits, int64_t ld_p,
                                int32_t target_rows_per_req, float* accept_rate,
                                float* survival, void* stream);
+
+/*
+ * dspark_sts_fit - fit the per-position STS temperatures on recorded data.
+ *
+ * Defined by [Budget] §二 (runtime STS c_k = sigmoid(z_k / T_k), S_k =
+ * prod_{i<=k} c_i; the fitter searches a positive temperature per position,
+ * in order, keeping the cumulative survival already fitted for the earlier
+ * positions, and keeps the candidate with the lower expected calibration
+ * error against the greedy prefix label) and [CSSD] "为什么置信度必须校准"
+ * (ECE = sum_b |I_b| / n * |acc(I_b) - conf(I_b)| over confidence bins; a
+ * position's label is only meaningful given that the earlier ones survived).
+ *
+ * For k = 1..gamma in order and every candidate T of t_grid_host:
+ *   S_k(T) = RN32(S_{k-1} * sigmoid32(RN32(z[n, k-1] / T))), S_0 = 1,
+ *   n * ECE_k(T) = sum_b |#labels in b - sum of S_k(T) in b| with bins
+ *   b = min(floor(S * n_bins), n_bins - 1) and each S taken at 2^-40
+ *   resolution (nearest), so the comparison is exact;
+ * T_k = the candidate with the smallest ECE (the first one on ties), and
+ * S_k = S_k(T_k). sigmoid32 is the correctly rounded sigmoid of dspark_plan.
+ * The labels are the prefix_mask that dspark_accept writes: prefix_mask[n,
+ * k-1] nonzero means draft k of record n was accepted.
+ *
+ * Arguments:
+ *   N, gamma           records (0..DSPARK_STS_MAX_RECORDS), positions (1..64)
+ *   z                  [N, gamma] float32 confidence logits
+ *   prefix_mask        [N, gamma] uint8 labels
+ *   t_grid_host        HOST [n_t] float32 candidates, each > 0 and finite
+ *                      (1 <= n_t <= DSPARK_STS_MAX_GRID)
+ *   n_bins             1..DSPARK_STS_MAX_BINS
+ *   temps              out [gamma] float32 chosen temperatures
+ *   t_index            out [gamma] int32 their grid indices
+ *   ece, brier         out [gamma] float64: ECE and Brier score (mean of
+ *                      (S - label)^2, each term at 2^-40) of the chosen S_k
+ *   ece_grid           out [gamma, n_t] float64 ECE of every candidate, or NULL
+ *   survival_out       out [N, gamma] float32 fitted S_k, or NULL
+ *   workspace          dspark_sts_workspace_size() bytes, 256-byte aligned;
+ *                      contents irrelevant, no state between calls
+ * Errors: argument errors only. Infinite logits give survivals 0 or 1; a NaN
+ *   logit gives a NaN survival, which is binned and summed as 0.
+ */
+dspark_status dspark_sts_fit(int32_t N, int32_t gamma, const float* z, const uint8_t* prefix_mask,
+                             const float* t_grid_host, int32_t n_t, int32_t n_bins, float* temps,
+                             int32_t* t_index, double* ece, double* brier, double* ece_grid,
+                             float* survival_out, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Bytes of workspace dspark_sts_fit needs (0 for invalid sizes). */
+size_t dspark_sts_workspace_size(int32_t N, int32_t gamma, int32_t n_t, int32_t n_bins);
 
 /* Name of a status code (static string). */
 const char* dspark_status_str(dspark_status s);

@@ -251,6 +251,37 @@ def test_scatter_argument_errors():
     assert run(max_rows=-1) == _lib.E_INVALID
 
 
+def test_sts_fit_argument_errors():
+    call = _lib.lib().dspark_sts_fit
+    grid = (ctypes.c_float * 3)(0.5, 1.0, 2.0)
+    bad_grid = (ctypes.c_float * 3)(0.5, 0.0, 2.0)
+    ok = dict(N=100, gamma=4, z=FAKE, mask=FAKE, grid=ctypes.cast(grid, ctypes.c_void_p), nt=3,
+              nb=15, temps=FAKE, idx=FAKE, ece=FAKE, brier=FAKE, eg=NULL, surv=NULL,
+              ws=ctypes.c_void_p(0x100000), wsb=0, stream=NULL)
+
+    def run(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return call(*d.values())
+
+    assert run(N=-1) == _lib.E_INVALID
+    assert run(N=_lib.STS_MAX_RECORDS + 1) == _lib.E_UNSUPPORTED
+    assert run(gamma=0) == _lib.E_INVALID
+    assert run(nt=0) == _lib.E_INVALID
+    assert run(nt=_lib.STS_MAX_GRID + 1) == _lib.E_INVALID
+    assert run(grid=ctypes.cast(bad_grid, ctypes.c_void_p)) == _lib.E_INVALID
+    assert run(nb=0) == _lib.E_INVALID and run(nb=_lib.STS_MAX_BINS + 1) == _lib.E_INVALID
+    assert run(z=NULL) == _lib.E_INVALID
+    assert run(temps=NULL) == _lib.E_INVALID
+    assert run() == _lib.E_WORKSPACE  # 0 bytes given
+    size = _lib.lib().dspark_sts_workspace_size
+    # 100 survivals, 4 temperatures, one block of 3 x 31 histogram words
+    assert size(100, 4, 3, 15) == 512 + 256 + 3 * 31 * 8 + (256 - 3 * 31 * 8 % 256)
+    # 300 records: two workgroups of 256
+    assert size(300, 4, 3, 15) == 1280 + 256 + 2 * 3 * 31 * 8 + (256 - 2 * 3 * 31 * 8 % 256)
+    assert size(0, 4, 3, 15) > 0 and size(-1, 4, 3, 15) == 0 and size(10, 4, 129, 15) == 0
+
+
 # ---------------------------------------------------------------- sigmoid logic on the CPU
 
 def _host_sigmoid(x, force_slow=False):
