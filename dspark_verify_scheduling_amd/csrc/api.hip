@@ -57,23 +57,27 @@ RowGeom row_geom(int V, dspark_dtype dt) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace of dspark_sts_fit: survivals, chosen temperatures, histograms.
+// Workspace of dspark_sts_fit: two survival buffers, per-candidate error sums,
+// per-workgroup histograms.
 struct StsGeom {
   int per_block, n_blocks;
-  size_t s_off, t_off, p_off, bytes;
+  size_t s_off[2], e_off, b_off, p_off, bytes;
 };
 
 StsGeom sts_geom(int N, int gamma, int n_t, int n_bins) {
   StsGeom g;
-  // at least kStsRecordsPerBlock records per workgroup, at most kStsMaxBlocks
+  // whole passes of kStsPass records per workgroup, at most kStsMaxBlocks
   // workgroups (which bounds the histogram slots of the workspace)
   const int want = (N + dspark::kStsMaxBlocks - 1) / dspark::kStsMaxBlocks;
-  g.per_block = std::max(dspark::kStsRecordsPerBlock,
-                         (want + dspark::kStsThreads - 1) / dspark::kStsThreads * dspark::kStsThreads);
+  g.per_block = std::max(1, (want + dspark::kStsPass - 1) / dspark::kStsPass) * dspark::kStsPass;
   g.n_blocks = N > 0 ? (N + g.per_block - 1) / g.per_block : 1;
-  g.s_off = 0;
-  g.t_off = align256((size_t)N * sizeof(float));
-  g.p_off = g.t_off + align256((size_t)gamma * sizeof(float));
+  const size_t sv = align256((size_t)N * sizeof(float));
+  const size_t ev = align256((size_t)gamma * n_t * sizeof(long long));
+  g.s_off[0] = 0;
+  g.s_off[1] = sv;
+  g.e_off = 2 * sv;
+  g.b_off = g.e_off + ev;
+  g.p_off = g.b_off + ev;
   g.bytes = g.p_off + align256((size_t)g.n_blocks * n_t * (2 * n_bins + 1) * sizeof(long long));
   return g;
 }
@@ -476,8 +480,10 @@ dspark_status dspark_sts_fit(int32_t N, int32_t gamma, const float* z, const uin
   a.ece_grid = ece_grid;
   a.surv_out = survival_out;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  a.s_work = reinterpret_cast<float*>(ws + g.s_off);
-  a.chosen_t = reinterpret_cast<float*>(ws + g.t_off);
+  a.s_work[0] = reinterpret_cast<float*>(ws + g.s_off[0]);
+  a.s_work[1] = reinterpret_cast<float*>(ws + g.s_off[1]);
+  a.err_fx = reinterpret_cast<long long*>(ws + g.e_off);
+  a.brier_fx = reinterpret_cast<long long*>(ws + g.b_off);
   a.partials = reinterpret_cast<long long*>(ws + g.p_off);
   return launched(dspark::launch_sts(a, (hipStream_t)stream), "dspark_sts_fit");
 }

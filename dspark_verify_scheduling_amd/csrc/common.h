@@ -125,13 +125,17 @@ struct StsArgs {
   double* brier;            // [gamma]
   double* ece_grid;         // [gamma, n_t] or null
   float* surv_out;          // [N, gamma] or null
-  float* s_work;            // workspace: [N] survival of the previous position
-  float* chosen_t;          // workspace: [gamma] chosen temperatures
+  float* s_work[2];         // workspace: two [N] survival buffers, used alternately
+  long long* err_fx;        // workspace: [gamma, n_t] n * ECE * 2^40 per candidate
+  long long* brier_fx;      // workspace: [gamma, n_t] n * Brier * 2^40 per candidate
   long long* partials;      // workspace: [n_blocks, n_t, 2 * nbins + 1]
 };
-constexpr int kStsThreads = 256;
-constexpr int kStsRecordsPerBlock = 256;  // at least
-constexpr int kStsMaxBlocks = 1024;
+constexpr int kStsPass = 256;        // records a bin workgroup takes at a time
+constexpr int kStsPhases = 4;        // threads per record, each on every 4th candidate
+constexpr int kStsBinThreads = kStsPass * kStsPhases;
+constexpr int kStsReduceThreads = 1024;
+constexpr int kStsThreads = 256;     // finish kernel
+constexpr int kStsMaxBlocks = 1024;  // bin workgroups (histogram slots) at most
 hipError_t launch_sts(const StsArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- helpers

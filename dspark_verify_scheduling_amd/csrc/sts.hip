@@ -15,17 +15,22 @@
 // exact, order-independent decision. Brier terms likewise.
 //
 // Per position k:
-//   sts_bin_kernel: each workgroup takes a range of records. For k >= 1 it
-//     first advances the stored survival by the temperature chosen for k - 1
-//     (S_{k-1} = RN32(S_{k-2} * sigmoid(z / T*))) and writes it out. Then, for
+//   sts_bin_kernel: each workgroup takes a range of records, four threads per
+//     record, each on every fourth candidate. For k >= 1 it first picks the
+//     temperature of position k - 1 (the smallest summed error, the first
+//     candidate on ties; workgroup 0 records it) and advances the stored
+//     survival by it (S_{k-1} = RN32(S_{k-2} * sigmoid(z / T*))). Then, for
 //     every grid temperature T, S = RN32(S_{k-1} * sigmoid(RN32(z_k / T)))
 //     is binned into LDS histograms (label count and survival sum per bin,
 //     Brier sum per T) with LDS atomics, and the workgroup writes its
 //     histograms to its slot of the workspace (no cross-workgroup atomics).
-//   sts_select_kernel: one workgroup sums the slots per T, forms n * ECE,
-//     picks the smallest (the first T on ties) and records the result.
-// sts_finish_kernel advances the survival for the last position.
+//   sts_reduce_kernel: one workgroup per candidate sums the slots and forms
+//     n * ECE and n * Brier for it.
+// sts_finish_kernel picks the last position's temperature and advances the
+// survival by it. The survival lives in two buffers used alternately, so a
+// kernel never overwrites what another of its threads still has to read.
 #include <float.h>
+#include <limits.h>
 
 #include "common.h"
 #include "sigmoid_cr.h"
@@ -40,99 +45,133 @@ constexpr double kFx = 0x1p40;
 
 __device__ inline long long fx40(double v) { return __double2ll_rn(v * kFx); }
 
-// Survival of the previous position: 1 at k = 0, else advanced in place.
-__device__ inline float prev_survival(const StsArgs& a, int k, int n) {
+// Picks the temperature of position kk from the summed errors (one wave):
+// the smallest n * ECE, the first candidate on ties. Every lane returns it;
+// with `record` set, lane 0 also stores the position's results.
+__device__ int select_candidate(const StsArgs& a, int kk, bool record) {
+  const int lane = lane_id();
+  const long long* err = a.err_fx + (size_t)kk * a.n_t;
+  long long e = LLONG_MAX;
+  int t = INT_MAX;
+  for (int c = lane; c < a.n_t; c += kWave) {
+    const long long v = err[c];
+    if (v < e) e = v, t = c;  // c ascends, so equal errors keep the first
+  }
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const long long oe = __shfl_xor(e, off, kWave);
+    const int ot = __shfl_xor(t, off, kWave);
+    if (oe < e || (oe == e && ot < t)) e = oe, t = ot;
+  }
+  if (record && lane == 0) {
+    const double scale = (double)a.N * kFx;
+    a.temps[kk] = a.grid[t];
+    a.t_index[kk] = t;
+    a.ece[kk] = a.N ? (double)e / scale : 0.0;
+    a.brier[kk] = a.N ? (double)a.brier_fx[(size_t)kk * a.n_t + t] / scale : 0.0;
+  }
+  return t;
+}
+
+// S_{k-1} for record n: 1 at k = 0, else S_{k-2} times the calibrated
+// confidence of position k - 1 at its chosen temperature. The writer stores
+// it (buffer (k - 1) & 1, and the survival output).
+__device__ inline float advance_survival(const StsArgs& a, int k, int n, float t_prev, bool writer) {
   if (k == 0) return 1.0f;
-  const float t = a.chosen_t[k - 1];
-  const float c = sigmoid_cr(__fdiv_rn(a.z[(size_t)n * a.gamma + (k - 1)], t));
-  const float s0 = k == 1 ? 1.0f : a.s_work[n];
+  const float c = sigmoid_cr(__fdiv_rn(a.z[(size_t)n * a.gamma + (k - 1)], t_prev));
+  const float s0 = k == 1 ? 1.0f : a.s_work[k & 1][n];
   const float s = __fmul_rn(s0, c);
-  a.s_work[n] = s;
-  if (a.surv_out) a.surv_out[(size_t)n * a.gamma + (k - 1)] = s;
+  if (writer) {
+    a.s_work[(k - 1) & 1][n] = s;
+    if (a.surv_out) a.surv_out[(size_t)n * a.gamma + (k - 1)] = s;
+  }
   return s;
 }
 
-__global__ __launch_bounds__(kStsThreads) void sts_bin_kernel(StsArgs a, int k) {
+__global__ __launch_bounds__(kStsBinThreads) void sts_bin_kernel(StsArgs a, int k) {
   extern __shared__ long long hist[];  // [nT][2 * nbins + 1]: labels, survival sums, Brier
+  __shared__ int s_prev;
   const int tid = threadIdx.x;
   const int nb = a.nbins, nT = a.n_t, stride = 2 * nb + 1;
-  for (int i = tid; i < nT * stride; i += kStsThreads) hist[i] = 0;
+  for (int i = tid; i < nT * stride; i += kStsBinThreads) hist[i] = 0;
+  if (k > 0 && tid < kWave) {
+    const int t = select_candidate(a, k - 1, blockIdx.x == 0);
+    if (tid == 0) s_prev = t;
+  }
   __syncthreads();
+  const float t_prev = k > 0 ? a.grid[s_prev] : 1.0f;
+  const int slot = tid % kStsPass, phase = tid / kStsPass;  // phase is wave-uniform
+  // a lane visits candidates (lane + phase + 4 i) mod nT, so the four phases
+  // cover every candidate once and the lanes of a wave start on different rows
+  const int t0 = (lane_id() + phase) % nT;
   const int r0 = blockIdx.x * a.per_block;
   const int r1 = min(r0 + a.per_block, a.N);
-  for (int n = r0 + tid; n < r1; n += kStsThreads) {
-    const float sp = prev_survival(a, k, n);
+  for (int n = r0 + slot; n < r1; n += kStsPass) {
+    const float sp = advance_survival(a, k, n, t_prev, phase == 0);
     const float zk = a.z[(size_t)n * a.gamma + k];
-    const int y = a.labels[(size_t)n * a.gamma + k] ? 1 : 0;
-    // lanes start at different candidates so their LDS atomics hit different rows
-    for (int tt = 0, t = lane_id() % nT; tt < nT; ++tt, t = t + 1 < nT ? t + 1 : 0) {
+    const unsigned long long y = a.labels[(size_t)n * a.gamma + k] ? 1ull : 0ull;
+    for (int j = phase, t = t0; j < nT; j += kStsPhases) {
       const float s = __fmul_rn(sp, sigmoid_cr(__fdiv_rn(zk, a.grid[t])));
       const double sd = s == s ? (double)s : 0.0;  // a NaN survival counts as 0
       int b = (int)floor(sd * nb);
       b = b < nb ? b : nb - 1;
-      long long* h = hist + t * stride;
-      if (y) atomicAdd(reinterpret_cast<unsigned long long*>(h + b), 1ull);
-      atomicAdd(reinterpret_cast<unsigned long long*>(h + nb + b), (unsigned long long)fx40(sd));
+      unsigned long long* h = reinterpret_cast<unsigned long long*>(hist + t * stride);
+      if (y) atomicAdd(h + b, 1ull);
+      atomicAdd(h + nb + b, (unsigned long long)fx40(sd));
       const double d = sd - (double)y;  // exact, and so is d * d
-      atomicAdd(reinterpret_cast<unsigned long long*>(h + 2 * nb), (unsigned long long)fx40(d * d));
+      atomicAdd(h + 2 * nb, (unsigned long long)fx40(d * d));
+      t += kStsPhases;
+      if (t >= nT) t -= nT;  // once past the end only when nT > 4: then t < nT again
     }
   }
   __syncthreads();
   long long* out = a.partials + (size_t)blockIdx.x * nT * stride;
-  for (int i = tid; i < nT * stride; i += kStsThreads) out[i] = hist[i];
+  for (int i = tid; i < nT * stride; i += kStsBinThreads) out[i] = hist[i];
 }
 
-__global__ __launch_bounds__(kStsThreads) void sts_select_kernel(StsArgs a, int k) {
-  __shared__ long long s_err[DSPARK_STS_MAX_GRID];
-  __shared__ long long s_brier[DSPARK_STS_MAX_GRID];
-  const int tid = threadIdx.x;
+// Workgroup t: sums candidate t's histogram slots over the bin workgroups.
+// Thread (q, c) adds column c of slots q, q + Q, q + 2Q, ... in a register.
+__global__ __launch_bounds__(kStsReduceThreads) void sts_reduce_kernel(StsArgs a, int k) {
+  __shared__ long long col[2 * DSPARK_STS_MAX_BINS + 1];
+  __shared__ long long s_err;
+  const int tid = threadIdx.x, t = blockIdx.x;
   const int nb = a.nbins, nT = a.n_t, stride = 2 * nb + 1;
-  for (int t = tid; t < nT; t += kStsThreads) s_err[t] = 0;
+  for (int c = tid; c < stride; c += kStsReduceThreads) col[c] = 0;
+  if (tid == 0) s_err = 0;
   __syncthreads();
-  // one (T, bin) item per thread at a time; the last column of a T is its Brier sum
-  for (int p = tid; p < nT * (nb + 1); p += kStsThreads) {
-    const int t = p / (nb + 1);
-    const int b = p - t * (nb + 1);
-    if (b < nb) {
-      long long lab = 0, conf = 0;
-      for (int g = 0; g < a.n_blocks; ++g) {
-        const long long* h = a.partials + ((size_t)g * nT + t) * stride;
-        lab += h[b];
-        conf += h[nb + b];
-      }
-      const long long diff = lab * (1ll << 40) - conf;
-      atomicAdd(reinterpret_cast<unsigned long long*>(s_err + t),
-                (unsigned long long)(diff < 0 ? -diff : diff));
-    } else {
-      long long brier = 0;
-      for (int g = 0; g < a.n_blocks; ++g) brier += a.partials[((size_t)g * nT + t) * stride + 2 * nb];
-      s_brier[t] = brier;
-    }
+  const int Q = kStsReduceThreads / stride;  // >= 7: stride <= 2 * 64 + 1
+  if (tid < Q * stride) {
+    const int q = tid / stride, c = tid - q * stride;
+    const long long* p = a.partials + ((size_t)q * nT + t) * stride + c;
+    const size_t step = (size_t)Q * nT * stride;
+    long long acc = 0;
+#pragma unroll 8
+    for (int g = q; g < a.n_blocks; g += Q, p += step) acc += *p;
+    atomicAdd(reinterpret_cast<unsigned long long*>(col + c), (unsigned long long)acc);
   }
   __syncthreads();
-  const double scale = (double)a.N * kFx;
-  if (a.ece_grid) {
-    for (int t = tid; t < nT; t += kStsThreads) {
-      a.ece_grid[(size_t)k * nT + t] = a.N ? (double)s_err[t] / scale : 0.0;
-    }
+  for (int b = tid; b < nb; b += kStsReduceThreads) {
+    const long long diff = col[b] * (1ll << 40) - col[nb + b];
+    atomicAdd(reinterpret_cast<unsigned long long*>(&s_err),
+              (unsigned long long)(diff < 0 ? -diff : diff));
   }
+  __syncthreads();
   if (tid == 0) {
-    int best = 0;
-    for (int t = 1; t < nT; ++t) {
-      if (s_err[t] < s_err[best]) best = t;
-    }
-    a.chosen_t[k] = a.grid[best];
-    a.temps[k] = a.grid[best];
-    a.t_index[k] = best;
-    a.ece[k] = a.N ? (double)s_err[best] / scale : 0.0;
-    a.brier[k] = a.N ? (double)s_brier[best] / scale : 0.0;
+    a.err_fx[(size_t)k * nT + t] = s_err;
+    a.brier_fx[(size_t)k * nT + t] = col[2 * nb];
+    if (a.ece_grid) a.ece_grid[(size_t)k * nT + t] = a.N ? (double)s_err / ((double)a.N * kFx) : 0.0;
   }
 }
 
-// Advances the survival by the temperature chosen for the last position.
+// Picks the last position's temperature and advances the survival by it.
 __global__ __launch_bounds__(kStsThreads) void sts_finish_kernel(StsArgs a) {
+  __shared__ int s_prev;
+  if (threadIdx.x < kWave) {
+    const int t = select_candidate(a, a.gamma - 1, blockIdx.x == 0);
+    if (threadIdx.x == 0) s_prev = t;
+  }
+  __syncthreads();
   const int n = blockIdx.x * kStsThreads + threadIdx.x;
-  if (n < a.N) prev_survival(a, a.gamma, n);
+  if (a.surv_out && n < a.N) advance_survival(a, a.gamma, n, a.grid[s_prev], true);
 }
 
 }  // namespace
@@ -140,17 +179,15 @@ __global__ __launch_bounds__(kStsThreads) void sts_finish_kernel(StsArgs a) {
 hipError_t launch_sts(const StsArgs& a, hipStream_t s) {
   const size_t lds = (size_t)a.n_t * (2 * a.nbins + 1) * sizeof(long long);
   for (int k = 0; k < a.gamma; ++k) {
-    hipLaunchKernelGGL(sts_bin_kernel, dim3(a.n_blocks), dim3(kStsThreads), lds, s, a, k);
+    hipLaunchKernelGGL(sts_bin_kernel, dim3(a.n_blocks), dim3(kStsBinThreads), lds, s, a, k);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sts_select_kernel, dim3(1), dim3(kStsThreads), 0, s, a, k);
+    hipLaunchKernelGGL(sts_reduce_kernel, dim3(a.n_t), dim3(kStsReduceThreads), 0, s, a, k);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.N > 0) {
-    hipLaunchKernelGGL(sts_finish_kernel, dim3((a.N + kStsThreads - 1) / kStsThreads),
-                       dim3(kStsThreads), 0, s, a);
-  }
+  const int fin = a.surv_out && a.N > 0 ? (a.N + kStsThreads - 1) / kStsThreads : 1;
+  hipLaunchKernelGGL(sts_finish_kernel, dim3(fin), dim3(kStsThreads), 0, s, a);
   return hipGetLastError();
 }
 
