@@ -11,15 +11,14 @@
 // so a = sum_x 2^min(...) needs one exponential per element pair once the
 // partitions are known. One workgroup of 1024 threads per (draft row, target
 // row) pair:
-//   pass 1: each thread streams batches of 4 + 4 16-byte vectors of q and p
-//           and keeps a running (max, sum of 2^(x log2 e - max)) per row,
-//           rescaled once per batch; the workgroup merges the threads';
+//   pass 1: the running (max, sum of 2^(x log2 e - max)) of each row; the
+//           workgroup merges the threads';
 //   pass 2: the sum of 2^min(...) over the same rows.
-// The pair's rows (about 0.5 MB at V = 129280 bf16) do not stay in the 4 MB
-// L2 of an XCD between the passes while 32 CUs stream, so pass 2 reads them
-// again from beyond L2 (measured: about twice the algorithmic bytes; limiting
-// residency to one pair per CU did not make the Infinity Cache serve the
-// re-read). Pass 1 uses ordinary loads, pass 2 nontemporal ones (last use).
+// Rows that fit on one CU (bf16 V up to 130055) take tv_resident_kernel,
+// which keeps the pair in registers and LDS between the passes and so reads
+// it from HBM once. Longer rows take tv_kernel, which streams them twice
+// (pass 1 with ordinary loads, pass 2 with nontemporal ones); the pair's rows
+// are then mostly gone from the XCD's 4 MB L2 when pass 2 comes back to them.
 // Exponentials are the raw v_exp_f32 (exp2 without the denormal-range fix-up:
 // results below 2^-126 are negligible in a sum that is about 1). The result is
 // clamped to at most 1; rounding can exceed 1 by ~1e-7.
