@@ -42,10 +42,11 @@ from .accept import accept, row_argmax
 from .tv import tv_accept
 from .strided import cap_accept, scatter_to_strided
 from .sts import sts_fit
+from .sampling import DATA_BAD_LOGITS, accept_sampling
 
 __all__ = [
     "sigmoid32", "survival", "plan", "pack", "accept", "row_argmax", "tv_accept",
-    "cap_accept", "scatter_to_strided", "sts_fit",
+    "cap_accept", "scatter_to_strided", "sts_fit", "accept_sampling", "DATA_BAD_LOGITS",
     "IN_CONF_LOGITS", "IN_COND", "IN_SURVIVAL", "COST_ADDITIVE", "COST_SPS1D", "sps_floor",
     "DATA_BAD_COST", "DATA_BAD_CONF", "DATA_BAD_LENS", "FX_SHIFT",
 ]

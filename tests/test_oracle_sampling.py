@@ -1,0 +1,295 @@
+"""Pins for the chain speculative-sampling accept oracle.
+
+Fixed by:
+* the exp tables against an independent 80-bit long-double evaluation;
+* the fixed-resolution probabilities against the float64 softmax (closed
+  form), the value 2^40 at the maximum, monotonicity and the power-of-two
+  scaling invariance of x / T;
+* the theorem of speculative sampling: one chain step outputs a token
+  distributed exactly as p (to the 2^-24 resolution of the random words),
+  whatever q is, and its acceptance rate is sum min(p, q) = 1 - TV, the
+  pages' identity; both computed by exhaustive counting over all 2^24
+  values of each random word, with the oracle's own decision functions;
+* closed cases: p == q always accepts, disjoint one-hot rows always reject
+  and resample the target token, a draft outside the vocabulary is rejected;
+* the greedy path (temperature 0) equal to the greedy accept oracle;
+* compaction invariance: compact accept with length l agrees with the
+  full-width (static) accept under the same random words wherever the
+  static chain stops before l - 1 ([CSSD], compact vs static).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import sampling as S
+
+
+def test_exp_tables_against_long_double():
+    e0, e1, e2 = S.exp_tables()
+    ld = np.longdouble
+    assert np.finfo(ld).eps < 1e-18  # 80-bit extended on this host
+    for tab, den, scale, n in ((e0, 16, 40, 455), (e1, 1024, 23, 64), (e2, 65536, 23, 64)):
+        assert len(tab) == n
+        for i, v in enumerate(tab):
+            ref = ld(2) ** scale * np.exp(-ld(i) / ld(den))
+            assert abs(ld(v) - ref) <= 0.5 + ref * 1e-17, (den, i, v, ref)
+    assert e0[0] == 2**40 and e1[0] == 2**23 and e2[0] == 2**23
+    # the last E0 entry is the last one that does not round to 0
+    assert e0[-1] == 1 and ld(2) ** 40 * np.exp(-ld(455) / 16) < 0.5
+
+
+@pytest.mark.parametrize("T", [0.05, 0.6, 1.0, 1.7, 8.0])
+def test_weights_match_softmax(T):
+    rng = np.random.default_rng(int(T * 100))
+    x = rng.normal(0.0, 3.0, 5000).astype(np.float32)
+    W = S.weights(x, T)
+    assert W.max() == 2**40 and W[np.argmax(x)] == 2**40
+    p = W.astype(np.float64) / float(W.sum())
+    y = (x.astype(np.float64) - x.max()) / np.float64(np.float32(T))
+    q = np.exp(y) / np.exp(y).sum()
+    big = q > 1e-6 * q.max()
+    assert np.max(np.abs(p - q)[big] / q[big]) < 2e-5
+    assert 0.5 * np.abs(p - q).sum() < 1e-5
+    # monotone in the logit wherever one step of j (a factor 1 - 1.5e-5)
+    # exceeds the rounding of the three table stages; within 2 units of
+    # 2^-40 everywhere
+    order = np.argsort(x, kind="stable")
+    Wo = W[order].astype(np.int64)
+    assert np.all(np.diff(Wo) >= -2)
+    big = Wo[:-1] > 2**20
+    assert np.all(np.diff(Wo)[big] >= 0)
+
+
+def test_weights_scaling_invariance_and_special_values():
+    rng = np.random.default_rng(2)
+    x = rng.normal(0.0, 4.0, 3000).astype(np.float32)
+    for T in (0.3, 1.0, 2.5):
+        assert np.array_equal(S.weights(x, T), S.weights(x * 4, T * 4))
+        assert np.array_equal(S.weights(x, T), S.weights(x / 8, T / 8))
+    # -inf has weight 0; a logit 30 below the max at T = 1 is below 2^-40
+    z = np.array([0.0, -np.inf, -30.0, -1.0], np.float32)
+    W = S.weights(z, 1.0)
+    assert W[0] == 2**40 and W[1] == 0 and W[2] == 0
+    assert abs(int(W[3]) - 2**40 * np.exp(-1.0)) < 2**40 * 1e-5
+
+
+def _count_accept(Wp_d, Zp, Wq_d, Zq):
+    """#u in [0, 2^24) accepted: the test is monotone in u, so bisect."""
+    lo, hi = 0, 1 << 24  # accepts(lo - 1) true, accepts(hi) false
+    if not S.accepts(Wp_d, Zp, Wq_d, Zq, 0):
+        return 0
+    if S.accepts(Wp_d, Zp, Wq_d, Zq, ((1 << 24) - 1) << 8):
+        return 1 << 24
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if S.accepts(Wp_d, Zp, Wq_d, Zq, mid << 8):
+            lo = mid
+        else:
+            hi = mid
+    return hi
+
+
+def _draw_counts(w):
+    """#v in [0, 2^24) drawing each index: draw is monotone in v, so bisect
+    for the first v of each index."""
+    n = len(w)
+    first = []
+    for i in range(n + 1):
+        lo, hi = 0, 1 << 24
+        while lo < hi:  # first v with draw(v) >= i
+            mid = (lo + hi) // 2
+            if S.draw(w, mid << 8) >= i:
+                hi = mid
+            else:
+                lo = mid + 1
+        first.append(lo)
+    first[n] = 1 << 24
+    return np.diff(np.array(first, dtype=np.int64))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_one_chain_step_outputs_the_target_distribution(seed):
+    rng = np.random.default_rng(100 + seed)
+    V = 6
+    p_row = rng.normal(0, 2, V).astype(np.float32)
+    q_row = rng.normal(0, 2, V).astype(np.float32)
+    if seed == 5:
+        q_row[2] = -np.inf  # the draft never proposes token 2
+    T = [1.0, 0.5, 2.0, 1.0, 0.8, 1.0][seed]
+    Wp, Wq = S.weights(p_row, T), S.weights(q_row, T)
+    Zp, Zq = int(Wp.sum()), int(Wq.sum())
+    p = np.array([int(v) for v in Wp], dtype=object)
+    R = S.residual(Wp, Zp, Wq, Zq)
+    rho = _draw_counts(R if int(np.sum(R)) else Wp)
+    out = np.zeros(V)
+    acc_rate = 0.0
+    for d in range(V):
+        qd = int(Wq[d]) / Zq
+        a = _count_accept(int(Wp[d]), Zp, int(Wq[d]), Zq) / 2**24
+        acc_rate += qd * a
+        out[d] += qd * a
+        out += qd * (1 - a) * rho / 2**24
+    target = np.array([float(v) for v in p]) / Zp
+    assert np.max(np.abs(out - target)) < 2 * 2.0**-24, (out, target)
+    ptrue, qtrue = Wp.astype(np.float64) / Zp, Wq.astype(np.float64) / Zq
+    assert abs(acc_rate - np.minimum(ptrue, qtrue).sum()) < 2 * 2.0**-24
+    assert abs(acc_rate - (1 - 0.5 * np.abs(ptrue - qtrue).sum())) < 2 * 2.0**-24
+
+
+def _batch(rng, B, gamma, V, lens, dtype="f32"):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tgt = rng.normal(0, 2, (int(cu[-1]) + 3, V)).astype(np.float32)
+    drf = rng.normal(0, 2, (B * gamma, V)).astype(np.float32)
+    drafts = rng.integers(0, V, (B, gamma)).astype(np.int32)
+    ra = rng.integers(0, 2**32, (B, gamma), dtype=np.uint64).astype(np.uint32)
+    rs = rng.integers(0, 2**32, (B, gamma + 1), dtype=np.uint64).astype(np.uint32)
+    return cu, tgt, drf, drafts, ra, rs
+
+
+def test_identical_rows_always_accept_and_disjoint_rows_always_reject():
+    rng = np.random.default_rng(5)
+    B, gamma, V = 6, 4, 50
+    lens = np.array([5, 3, 1, 5, 2, 4])
+    cu, tgt, drf, drafts, ra, rs = _batch(rng, B, gamma, V, lens)
+    for r in range(B):
+        for k in range(1, lens[r]):
+            drf[r * gamma + k - 1] = tgt[cu[r] + k - 1]
+    res = S.accept_sampling(B, gamma, tgt, drf, "f32", cu, drafts, np.ones(B), ra, rs)
+    assert res["num_correct"].tolist() == (lens - 1).tolist()
+    # disjoint one-hots: q proposes token 3, p puts all mass on token 7
+    tgt[:] = -np.inf
+    tgt[:, 7] = 0.0
+    drf[:] = -np.inf
+    drf[:, 3] = 0.0
+    drafts[:] = 3
+    res = S.accept_sampling(B, gamma, tgt, drf, "f32", cu, drafts, np.ones(B), ra, rs)
+    expect_bonus = [7 if l > 1 else 7 for l in lens]
+    assert res["num_correct"].tolist() == [0] * B and res["bonus"].tolist() == expect_bonus
+    assert res["status"] == 0
+    # a draft outside the vocabulary is rejected even when p == q
+    drf[:] = tgt[0]
+    drafts[:] = V
+    res = S.accept_sampling(B, gamma, tgt, drf, "f32", cu, drafts, np.ones(B), ra, rs)
+    assert res["num_correct"].tolist() == [0] * B and res["bonus"].tolist() == [7] * B
+
+
+def test_greedy_requests_follow_the_greedy_oracle():
+    rng = np.random.default_rng(9)
+    B, gamma, V = 9, 5, 40
+    lens = rng.integers(1, gamma + 2, B)
+    cu, tgt, drf, drafts, ra, rs = _batch(rng, B, gamma, V, lens)
+    am = oracle.row_argmax(tgt)
+    for r in range(B):  # make some drafts match
+        for k in range(1, lens[r]):
+            if rng.random() < 0.7:
+                drafts[r, k - 1] = am[cu[r] + k - 1]
+    tgt[1, 4] = np.nan
+    got = S.accept_sampling(B, gamma, tgt, drf, "f32", cu, drafts, np.zeros(B), ra, rs,
+                            prefix_lens=np.arange(B))
+    ref = oracle.accept(B, gamma, tgt, "f32", cu, drafts, prefix_lens=np.arange(B))
+    for k in ("num_correct", "bonus", "commit", "new_seq", "out_tokens"):
+        assert np.array_equal(got[k], ref[k]), k
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_compact_agrees_with_static_under_the_same_random_words(seed):
+    rng = np.random.default_rng(200 + seed)
+    B, gamma, V = 12, 6, 30
+    full = np.full(B, gamma + 1)
+    cu_s, tgt_s, drf, drafts, ra, rs = _batch(rng, B, gamma, V, full)
+    # make acceptance likely: q close to p
+    for r in range(B):
+        for k in range(1, gamma + 1):
+            drf[r * gamma + k - 1] = tgt_s[cu_s[r] + k - 1] + rng.normal(0, 0.3, V).astype(np.float32)
+    temps = rng.choice([0.7, 1.0, 1.3], B).astype(np.float32)
+    static = S.accept_sampling(B, gamma, tgt_s, drf, "f32", cu_s, drafts, temps, ra, rs)
+    lens = rng.integers(1, gamma + 2, B)
+    cu_c = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tgt_c = np.concatenate([tgt_s[cu_s[r]:cu_s[r] + lens[r]] for r in range(B)])
+    comp = S.accept_sampling(B, gamma, tgt_c, drf, "f32", cu_c, drafts, temps, ra, rs)
+    assert np.array_equal(comp["num_correct"], np.minimum(static["num_correct"], lens - 1))
+    stops = static["num_correct"] < lens - 1
+    assert np.array_equal(comp["bonus"][stops], static["bonus"][stops])
+    for r in np.flatnonzero(~stops):  # capped: the bonus is drawn from p of row l - 1
+        W = S.weights(tgt_c[cu_c[r] + lens[r] - 1], temps[r])
+        assert comp["bonus"][r] == S.draw(W, rs[r, lens[r] - 1])
+    assert stops.any() and (~stops).any()
+
+
+def test_bad_data_falls_back():
+    rng = np.random.default_rng(11)
+    B, gamma, V = 5, 3, 20
+    lens = np.array([4, 2, 3, 1, 4])
+    cu, tgt, drf, drafts, ra, rs = _batch(rng, B, gamma, V, lens)
+    temps = np.array([1.0, -1.0, 1.0, np.nan, 0.0], np.float32)
+    tgt[cu[2] + 1, 3] = np.inf  # request 2's second row
+    tgt[cu[4], 5] = np.nan  # greedy request: NaN is an ordinary (largest) value
+    res = S.accept_sampling(B, gamma, tgt, drf, "f32", cu, drafts, temps, ra, rs,
+                            prefix_lens=np.full(B, 10))
+    assert res["status"] == S.DATA_BAD_LOGITS | oracle.DATA_BAD_CONF
+    for r in (1, 2, 3):
+        assert res["num_correct"][r] == 0 and res["bonus"][r] == -1 and res["commit"][r] == 0
+        assert res["new_seq"][r] == 10 and (res["out_tokens"][r] == -1).all()
+    assert res["bonus"][4] == 5 and res["commit"][0] >= 1
+    bad = cu.copy()
+    bad[2] = bad[1]  # request 1 gets no rows
+    res = S.accept_sampling(B, gamma, tgt, drf, "f32", bad, drafts, np.ones(B), ra, rs)
+    assert res["status"] & oracle.DATA_BAD_LENS and res["bonus"][1] == -1
+
+
+def test_bf16_rows_widen_exactly():
+    rng = np.random.default_rng(12)
+    B, gamma, V = 4, 3, 24
+    lens = np.array([4, 4, 2, 3])
+    cu, tgt, drf, drafts, ra, rs = _batch(rng, B, gamma, V, lens)
+    tb = (tgt.view(np.uint32) >> 16).astype(np.uint16)
+    db = (drf.view(np.uint32) >> 16).astype(np.uint16)
+    a = S.accept_sampling(B, gamma, tb, db, "bf16", cu, drafts, np.ones(B), ra, rs)
+    tw = (tb.astype(np.uint32) << 16).view(np.float32)
+    dw = (db.astype(np.uint32) << 16).view(np.float32)
+    b = S.accept_sampling(B, gamma, tw, dw, "f32", cu, drafts, np.ones(B), ra, rs)
+    for k in ("num_correct", "bonus", "out_tokens"):
+        assert np.array_equal(a[k], b[k])
+
+
+def test_zero_probability_is_never_drawn_or_accepted():
+    # counts over all 2^24 values of the word are exactly the integer shares
+    w = np.array([0, 3, 0, 5, 0], dtype=object)
+    counts = _draw_counts(w)
+    assert counts[0] == 0 and counts[2] == 0 and counts[4] == 0
+    assert counts.sum() == 2**24 and abs(counts[1] - 3 * 2**24 / 8) <= 1
+    assert S.draw(w, 0) == 1 and S.draw(w, 0xFFFFFFFF) == 3
+    # min(1, p/q) is 0 when p(d) = 0, whatever q(d) is
+    Z = 5 * 2**40
+    assert _count_accept(0, Z, 2**40, Z) == 0
+    assert _count_accept(0, Z, 0, Z) == 0
+    # and 1 when p(d) >= q(d) > 0
+    assert _count_accept(2**40, Z, 2**40, Z) == 2**24
+    assert _count_accept(2**39, Z, 2**40, Z) == 2**23
+
+
+def test_each_output_column_draws_with_its_own_word():
+    # one request, gamma = 3, length 4: draft 1 is always rejected (disjoint
+    # rows), and the residual is p = uniform over tokens 5 and 9
+    B, gamma, V = 1, 3, 12
+    tgt = np.full((4, V), -np.inf, np.float32)
+    tgt[:, [5, 9]] = 0.0
+    drf = np.full((3, V), -np.inf, np.float32)
+    drf[:, 1] = 0.0
+    drafts = np.array([[1, 1, 1]], np.int32)
+    cu = np.array([0, 4], np.int32)
+    ra = np.zeros((1, 3), np.uint32)
+    lo, hi = np.uint32(0), np.uint32(0xFFFFFFFF)
+    for col0, expect in ((lo, 5), (hi, 9)):
+        rs = np.array([[col0, hi - col0, hi - col0, hi - col0]], np.uint32)
+        res = S.accept_sampling(B, gamma, tgt, drf, "f32", cu, drafts, np.ones(1), ra, rs)
+        assert res["num_correct"][0] == 0 and res["bonus"][0] == expect
+    # all accepted (q == p, drafts in the support): column 3 draws from row 3
+    drf[:] = tgt[0]
+    drafts[:] = 9
+    for col3, expect in ((lo, 5), (hi, 9)):
+        rs = np.array([[hi - col3] * 3 + [col3]], np.uint32)
+        res = S.accept_sampling(B, gamma, tgt, drf, "f32", cu, drafts, np.ones(1), ra, rs)
+        assert res["num_correct"][0] == 3 and res["bonus"][0] == expect
+        assert res["out_tokens"][0].tolist() == [9, 9, 9, expect]
