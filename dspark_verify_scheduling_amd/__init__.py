@@ -19,7 +19,8 @@ import torch
 
 from . import _lib
 from ._lib import (
-    BF16, COST_ADDITIVE, COST_SPS1D, DATA_BAD_CONF, DATA_BAD_COST, DATA_BAD_LENS, F32, IN_COND,
+    BF16, COST_ADDITIVE, COST_SPS1D, DATA_BAD_CONF, DATA_BAD_COST, DATA_BAD_LENS,
+    DATA_BAD_LOGITS, F32, IN_COND,
     IN_CONF_LOGITS,
     IN_SURVIVAL, MAX_BATCH, MAX_CANDIDATES, MAX_GAMMA, MAX_TIERS, MAX_VOCAB, DsparkError,
 )
@@ -30,7 +31,9 @@ __all__ = [
     "dspark_cap_accept", "dspark_scatter_to_strided", "dspark_accept_workspace_size",
     "alloc_plan_outputs", "alloc_pack_outputs", "alloc_accept_outputs",
     "alloc_cap_accept_outputs", "dspark_sts_fit", "dspark_sts_workspace_size", "DsparkError", "F32", "BF16", "IN_CONF_LOGITS", "IN_COND",
-    "IN_SURVIVAL", "DATA_BAD_COST", "DATA_BAD_CONF", "DATA_BAD_LENS",
+    "IN_SURVIVAL", "DATA_BAD_COST", "DATA_BAD_CONF", "DATA_BAD_LENS", "DATA_BAD_LOGITS",
+    "dspark_accept_sampling", "dspark_accept_sampling_workspace_size",
+    "alloc_sampling_outputs",
 ]
 
 
@@ -318,6 +321,70 @@ def dspark_accept(B: int, gamma: int, V: int, dt: int, packed_logits: torch.Tens
         _stream(stream),
     )
     _lib.check("dspark_accept", _lib.lib().dspark_accept(*args))
+    return out
+
+
+# ------------------------------------------------------------------ sampling accept
+
+class SamplingOutputs(NamedTuple):
+    num_correct: torch.Tensor  # [B] int32
+    bonus: torch.Tensor  # [B] int32
+    commit_lens: torch.Tensor  # [B] int32
+    out_tokens: torch.Tensor  # [B, gamma+1] int32
+    new_seq_lens: Optional[torch.Tensor]
+    accept_meta: torch.Tensor  # [2] int32
+    workspace: torch.Tensor  # uint8 scratch (no initialization needed)
+
+
+def dspark_accept_sampling_workspace_size(B: int, gamma: int, max_rows: int) -> int:
+    return int(_lib.lib().dspark_accept_sampling_workspace_size(B, gamma, max_rows))
+
+
+def alloc_sampling_outputs(B: int, gamma: int, max_rows: int, device,
+                           new_seq=True) -> SamplingOutputs:
+    i32 = torch.int32
+    ws = dspark_accept_sampling_workspace_size(B, gamma, max_rows)
+    return SamplingOutputs(
+        torch.empty(B, dtype=i32, device=device),
+        torch.empty(B, dtype=i32, device=device),
+        torch.empty(B, dtype=i32, device=device),
+        torch.empty(B, gamma + 1, dtype=i32, device=device),
+        torch.empty(B, dtype=i32, device=device) if new_seq else None,
+        torch.empty(2, dtype=i32, device=device),
+        torch.empty(max(ws, 256), dtype=torch.uint8, device=device),
+    )
+
+
+def dspark_accept_sampling(B: int, gamma: int, V: int, dt: int, packed_logits: torch.Tensor,
+                           ld: int, max_rows: int, cu_seqlens: torch.Tensor,
+                           draft_logits: torch.Tensor, ld_q: int, draft_tokens: torch.Tensor,
+                           temperatures: torch.Tensor, rand_accept: torch.Tensor,
+                           rand_sample: torch.Tensor, prefix_lens, out: SamplingOutputs,
+                           stream=None) -> SamplingOutputs:
+    """Chain speculative-sampling accept. The random words are int32 tensors
+    holding the uint32 bit patterns ([B, gamma] and [B, gamma + 1])."""
+    i32 = torch.int32
+    ldt = _logit_dtype(dt)
+    args = (
+        B, gamma, V, dt,
+        _ptr(packed_logits, "packed_logits", ldt, max_rows * ld if max_rows else 0), ld, max_rows,
+        _ptr(cu_seqlens, "cu_seqlens", i32, B + 1),
+        _ptr(draft_logits, "draft_logits", ldt, (B * gamma - 1) * ld_q + V if B else 0), ld_q,
+        _ptr(draft_tokens, "draft_tokens", i32, B * gamma),
+        _ptr(temperatures, "temperatures", torch.float32, B),
+        _ptr(rand_accept, "rand_accept", i32, B * gamma),
+        _ptr(rand_sample, "rand_sample", i32, B * (gamma + 1)),
+        _ptr(prefix_lens, "prefix_lens", i32, B, required=False),
+        _ptr(out.num_correct, "num_correct", i32, B),
+        _ptr(out.bonus, "bonus", i32, B),
+        _ptr(out.commit_lens, "commit_lens", i32, B),
+        _ptr(out.out_tokens, "out_tokens", i32, B * (gamma + 1)),
+        _ptr(out.new_seq_lens, "new_seq_lens", i32, B, required=False),
+        _ptr(out.accept_meta, "accept_meta", i32, 2),
+        _ptr(out.workspace, "workspace", torch.uint8, 1), out.workspace.numel(),
+        _stream(stream),
+    )
+    _lib.check("dspark_accept_sampling", _lib.lib().dspark_accept_sampling(*args))
     return out
 
 

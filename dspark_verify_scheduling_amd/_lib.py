@@ -18,7 +18,7 @@ HOSTCHECK_PATH = _PKG / "libdspark_hostcheck.so"
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_LAUNCH = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 IN_CONF_LOGITS, IN_COND, IN_SURVIVAL = 0, 1, 2
-DATA_BAD_COST, DATA_BAD_CONF, DATA_BAD_LENS = 1, 2, 4
+DATA_BAD_COST, DATA_BAD_CONF, DATA_BAD_LENS, DATA_BAD_LOGITS = 1, 2, 4, 8
 MAX_GAMMA, MAX_CANDIDATES, MAX_BATCH, MAX_TIERS, MAX_VOCAB = 64, 8192, 8192, 32, 262144
 MAX_SPS_PROBES = 512
 STS_MAX_GRID, STS_MAX_BINS, STS_MAX_RECORDS = 128, 64, 4194304
@@ -62,6 +62,11 @@ SIGNATURES = {
         c_int32, c_int32, c_void_p, c_int32, c_void_p, c_int64, c_void_p, c_int64, c_int64,
         c_void_p, c_void_p]),
     "dspark_accept_workspace_size": (c_size_t, [c_int32, c_int32, c_int]),
+    "dspark_accept_sampling": (c_int, [
+        c_int32, c_int32, c_int32, c_int, c_void_p, c_int64, c_int32, c_void_p, c_void_p,
+        c_int64, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "dspark_accept_sampling_workspace_size": (c_size_t, [c_int32, c_int32, c_int32]),
     "dspark_sts_fit": (c_int, [
         c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),

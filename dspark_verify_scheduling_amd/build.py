@@ -22,7 +22,7 @@ LIB = PKG / "libdspark.so"
 HOSTCHECK = PKG / "libdspark_hostcheck.so"
 ARCH = "gfx950"
 
-LIB_SOURCES = ["api.hip", "plan.hip", "pack.hip", "accept.hip", "tv.hip", "scatter.hip", "sts.hip"]
+LIB_SOURCES = ["api.hip", "plan.hip", "pack.hip", "accept.hip", "tv.hip", "scatter.hip", "sts.hip", "sampling.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -82,6 +82,13 @@ StsGeom sts_geom(int N, int gamma, int n_t, int n_bins) {
   return g;
 }
 
+// Workspace of dspark_accept_sampling: row statistics and draw jobs.
+size_t samp_ws_bytes(int B, int gamma, int max_rows) {
+  return align256((size_t)max_rows * sizeof(dspark::SampRowStat)) +
+         align256((size_t)B * gamma * sizeof(dspark::SampRowStat)) +
+         align256((size_t)(B > 0 ? B : 1) * sizeof(dspark::SampJob));
+}
+
 // Workspace of dspark_accept: one 64-bit (key, index) partial per unit.
 size_t ws_bytes(int max_rows, int chunks) {
   const size_t b = align256((size_t)max_rows * chunks * sizeof(unsigned long long));
@@ -566,6 +573,88 @@ dspark_status dspark_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt
   const int64_t units_max = (int64_t)max_rows * g.chunks;
   const int grid = units_max > 0 ? (int)units_max : 1;
   return launched(dspark::launch_accept(a, dt, grid, (hipStream_t)stream), "dspark_accept");
+}
+
+size_t dspark_accept_sampling_workspace_size(int32_t B, int32_t gamma, int32_t max_rows) {
+  if (B < 0 || gamma < 1 || gamma > DSPARK_MAX_GAMMA || max_rows < 0 ||
+      (int64_t)max_rows + (int64_t)B * gamma > 0x7fffffffLL)
+    return 0;
+  return samp_ws_bytes(B, gamma, max_rows);
+}
+
+dspark_status dspark_accept_sampling(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,
+                                     const void* packed_logits, int64_t ld, int32_t max_rows,
+                                     const int32_t* cu_seqlens, const void* draft_logits,
+                                     int64_t ld_q, const int32_t* draft_tokens,
+                                     const float* temperatures, const uint32_t* rand_accept,
+                                     const uint32_t* rand_sample, const int32_t* prefix_lens,
+                                     int32_t* num_correct, int32_t* bonus, int32_t* commit_lens,
+                                     int32_t* out_tokens, int32_t* new_seq_lens,
+                                     int32_t* accept_meta, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  const char* fn = "dspark_accept_sampling";
+  if (B < 0) return fail(DSPARK_E_INVALID, "%s: B = %d < 0", fn, B);
+  if (gamma < 1 || gamma > DSPARK_MAX_GAMMA)
+    return fail(DSPARK_E_INVALID, "%s: gamma = %d outside [1, %d]", fn, gamma, DSPARK_MAX_GAMMA);
+  if (dt != DSPARK_F32 && dt != DSPARK_BF16)
+    return fail(DSPARK_E_UNSUPPORTED, "%s: unsupported dtype %d", fn, (int)dt);
+  if (V < 1 || V > DSPARK_MAX_VOCAB)
+    return fail(V < 1 ? DSPARK_E_INVALID : DSPARK_E_UNSUPPORTED, "%s: V = %d outside [1, %d]", fn,
+                V, DSPARK_MAX_VOCAB);
+  if (max_rows < 0) return fail(DSPARK_E_INVALID, "%s: max_rows = %d < 0", fn, max_rows);
+  if ((int64_t)max_rows + (int64_t)B * gamma > 0x7fffffffLL)
+    return fail(DSPARK_E_UNSUPPORTED, "%s: max_rows + B * gamma overflows int32", fn);
+  if (ld < V || ld_q < V)
+    return fail(DSPARK_E_INVALID, "%s: ld = %lld or ld_q = %lld below V = %d", fn, (long long)ld,
+                (long long)ld_q, V);
+  const size_t es = elem_size(dt);
+  if ((ld * (int64_t)es) % 16 != 0 || (ld_q * (int64_t)es) % 16 != 0)
+    return fail(DSPARK_E_INVALID, "%s: a row stride is not a multiple of 16 bytes", fn);
+  if (max_rows > 0 && (!packed_logits || !aligned16(packed_logits)))
+    return fail(DSPARK_E_INVALID, "%s: packed_logits NULL or not 16-byte aligned", fn);
+  if (B > 0 && (!draft_logits || !aligned16(draft_logits)))
+    return fail(DSPARK_E_INVALID, "%s: draft_logits NULL or not 16-byte aligned", fn);
+  if (!cu_seqlens || !accept_meta)
+    return fail(DSPARK_E_INVALID, "%s: cu_seqlens or accept_meta is NULL", fn);
+  if (B > 0 && (!draft_tokens || !temperatures || !rand_accept || !rand_sample || !num_correct ||
+                !bonus || !commit_lens || !out_tokens))
+    return fail(DSPARK_E_INVALID, "%s: a required per-request pointer is NULL", fn);
+  if (new_seq_lens && !prefix_lens)
+    return fail(DSPARK_E_INVALID, "%s: new_seq_lens needs prefix_lens", fn);
+  const size_t need = samp_ws_bytes(B, gamma, max_rows);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
+    return fail(DSPARK_E_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned", fn, need);
+  const RowGeom g = row_geom(V, dt);
+  dspark::SampArgs a;
+  a.tgt = static_cast<const unsigned char*>(packed_logits);
+  a.ld_t = ld * (int64_t)es;
+  a.drf = static_cast<const unsigned char*>(draft_logits);
+  a.ld_q = ld_q * (int64_t)es;
+  a.V = V;
+  a.nvec = g.nvec;
+  a.tail = g.tail;
+  a.max_rows = max_rows;
+  a.B = B;
+  a.gamma = gamma;
+  a.cu = cu_seqlens;
+  a.drafts = draft_tokens;
+  a.temps = temperatures;
+  a.ra = rand_accept;
+  a.rs = rand_sample;
+  a.prefix = prefix_lens;
+  a.num_correct = num_correct;
+  a.bonus = bonus;
+  a.commit = commit_lens;
+  a.out_tokens = out_tokens;
+  a.new_seq = new_seq_lens;
+  a.meta = accept_meta;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  a.tstat = reinterpret_cast<dspark::SampRowStat*>(ws);
+  ws += align256((size_t)max_rows * sizeof(dspark::SampRowStat));
+  a.dstat = reinterpret_cast<dspark::SampRowStat*>(ws);
+  ws += align256((size_t)B * gamma * sizeof(dspark::SampRowStat));
+  a.jobs = reinterpret_cast<dspark::SampJob*>(ws);
+  return launched(dspark::launch_sampling(a, dt, (hipStream_t)stream), fn);
 }
 
 dspark_status dspark_tv_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,

@@ -138,6 +138,47 @@ constexpr int kStsThreads = 256;     // finish kernel
 constexpr int kStsMaxBlocks = 1024;  // bin workgroups (histogram slots) at most
 hipError_t launch_sts(const StsArgs& a, hipStream_t s);
 
+// Chain speculative-sampling accept (sampling.hip).
+struct SampRowStat {
+  unsigned long long Z;  // sum of the row's integer weights (sampling rows)
+  float m;               // row maximum (finite when bad == 0)
+  int am;                // first index of the maximum, NaN highest (greedy)
+  int bad;               // NaN or +inf in the row, or no finite maximum
+  int pad;
+};
+struct SampJob {
+  int mode;  // 0 none, 1 draw from p, 2 draw from the residual of (p, q)
+  int prow, qrow;
+  unsigned int word;
+  int col;   // output column of the drawn token (= num_correct)
+  int pad;
+};
+struct SampArgs {
+  const unsigned char* tgt;  // packed target rows
+  int64_t ld_t;              // bytes
+  const unsigned char* drf;  // draft rows, row r * gamma + k - 1 for draft k
+  int64_t ld_q;              // bytes
+  int V, nvec, tail, max_rows, B, gamma;
+  const int32_t* cu;
+  const int32_t* drafts;
+  const float* temps;
+  const uint32_t* ra;  // [B, gamma]
+  const uint32_t* rs;  // [B, gamma + 1]
+  const int32_t* prefix;
+  int32_t* num_correct;
+  int32_t* bonus;
+  int32_t* commit;
+  int32_t* out_tokens;
+  int32_t* new_seq;
+  int32_t* meta;
+  SampRowStat* tstat;  // workspace: [max_rows]
+  SampRowStat* dstat;  // workspace: [B * gamma]
+  SampJob* jobs;       // workspace: [B]
+};
+constexpr int kSampThreads = 1024;
+constexpr int kSampRegSlots = 16;  // 16-byte vectors per thread kept in registers
+hipError_t launch_sampling(const SampArgs& a, dspark_dtype dt, hipStream_t s);
+
 // ---------------------------------------------------------------- helpers
 
 __device__ inline int lane_id() { return threadIdx.x & (kWave - 1); }

@@ -21,6 +21,8 @@
  *                    back to the strided [B, stride] layout
  *   dspark_sts_fit   (offline) the per-position STS temperatures that feed
  *                    dspark_plan, fitted on recorded logits and prefix_masks
+ *   dspark_accept_sampling  chain speculative-sampling accept (temperature > 0;
+ *                    temperature 0 requests take the greedy rule)
  *   dspark_tv_accept (optional) soft accept-rate 1 - TV(softmax q, softmax p)
  *                    and its per-request cumulative product, which can feed
  *                    dspark_plan as survivals
@@ -82,6 +84,8 @@ typedef enum dspark_input {
                                   sweep, or SPS probes not strictly ascending */
 #define DSPARK_DATA_BAD_CONF 2 /* confidence/survival/temperature out of domain */
 #define DSPARK_DATA_BAD_LENS 4 /* verify lengths or cu_seqlens malformed */
+#define DSPARK_DATA_BAD_LOGITS 8 /* a row a sampling request reads holds NaN or
+                                    +inf, or has no finite maximum */
 
 /* Limits. */
 #define DSPARK_MAX_GAMMA 64
@@ -408,6 +412,85 @@ dspark_status dspark_scatter_to_strided(int32_t B, int32_t stride, const int32_t
 /* Bytes of workspace dspark_accept needs for `max_rows` rows of V elements of
  * type dt (0 for invalid sizes). */
 size_t dspark_accept_workspace_size(int32_t max_rows, int32_t V, dspark_dtype dt);
+
+/*
+ * dspark_accept_sampling - chain speculative-sampling accept over packed
+ * target logits.
+ *
+ * Defined by [Round] §五 (AcceptSampling: acceptance by speculative sampling
+ * over the draft-side probabilities that actually proposed each draft and
+ * the target probabilities, giving correct_len and the bonus), [Budget] §二
+ * (a draft drawn from q is accepted with probability min(1, p/q); the mean
+ * acceptance is sum_x min(p, q) = 1 - TV) and [CSSD] "截短为什么不会改变目标分布"
+ * (accept, reject and the residual resample follow the speculative
+ * algorithm; random numbers keep their meaning under compaction).
+ *
+ * Request r owns packed rows cu[r] .. cu[r+1]-1 (l rows). With T =
+ * temperatures[r]:
+ *   T == 0   greedy: exactly dspark_accept's rule (argmax ties, NaN order).
+ *   T > 0    drafts k = 1..l-1 in order: p is target row k-1, q is draft row
+ *            r * gamma + k - 1 (the distribution that proposed draft k),
+ *            both at temperature T. The first rejected draft k ends the
+ *            chain with num_correct = k - 1 and the token of column k - 1
+ *            drawn from the residual max(0, p - q) of that pair; if all pass,
+ *            column l - 1 gets a token drawn from p of target row l - 1.
+ * Probabilities at fixed resolution, so every decision is exact: for a row x
+ * with maximum m, t = RN64(RN64(m - x) * RN64(65536 / T)), j = nearest
+ * integer, W = 0 if t or j >= 455 * 4096, else W = (((E0[j >> 12] *
+ * E1[(j >> 6) & 63] + 2^22) >> 23) * E2[j & 63] + 2^22) >> 23 with E0[h],
+ * E1[a], E2[b] the nearest integers to 2^40 e^(-h/16), 2^23 e^(-a/1024),
+ * 2^23 e^(-b/65536); p = W / sum W. Within about 8e-6 relative of the
+ * softmax of x / T.
+ *   accept draft d  iff  (rand_accept >> 8) * Wq[d] * Zp < 2^24 * Wp[d] * Zq
+ *   draw from integer weights w (total S) with word v: the smallest index
+ *   whose running sum exceeds floor((v >> 8) * S / 2^24); residual weights
+ *   max(0, Wp * Zq - Wq * Zp), and if they are all 0, w = Wp.
+ * A draft outside [0, V) is rejected.
+ *
+ * Arguments:
+ *   B, gamma, V, dt    as for dspark_accept
+ *   packed_logits      [max_rows, ld] target rows, as for dspark_accept
+ *   max_rows           rows the target buffer holds
+ *   cu_seqlens         [B + 1] int32; the total cu_seqlens[B] is read on the
+ *                      device
+ *   draft_logits       [B * gamma, ld_q] draft rows (row r * gamma + k - 1
+ *                      proposed draft k), same dtype; 16-byte aligned, ld_q *
+ *                      element size a multiple of 16, ld_q >= V
+ *   draft_tokens       [B, gamma] int32
+ *   temperatures       [B] float32: 0 for greedy, > 0 for sampling
+ *   rand_accept        [B, gamma] uint32 random words; [r, k-1] tests draft k
+ *   rand_sample        [B, gamma + 1] uint32; [r, c] draws the token of
+ *                      output column c. A word w stands for the uniform
+ *                      (w >> 8) / 2^24.
+ *   prefix_lens        [B] int32 or NULL (then new_seq_lens must be NULL)
+ *   num_correct, bonus, commit_lens   out [B] int32
+ *   out_tokens         out [B, gamma + 1] int32 (drafts, the drawn token at
+ *                      column num_correct, -1 after)
+ *   new_seq_lens       out [B] int32 or NULL
+ *   accept_meta        out [2] int32: cu_seqlens[B], status bits
+ *   workspace          dspark_accept_sampling_workspace_size() bytes,
+ *                      256-byte aligned; no state between calls; calls that
+ *                      share it must not overlap in time.
+ * Data errors: a malformed layout (as for dspark_accept) sets
+ *   DSPARK_DATA_BAD_LENS; a negative, NaN or infinite temperature sets
+ *   DSPARK_DATA_BAD_CONF; a row the sampling request reads with a NaN or
+ *   +inf, or with every element -inf, sets DSPARK_DATA_BAD_LOGITS. Such a
+ *   request gets num_correct 0, bonus -1, commit 0, out_tokens -1 and
+ *   new_seq = prefix.
+ */
+dspark_status dspark_accept_sampling(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,
+                                     const void* packed_logits, int64_t ld, int32_t max_rows,
+                                     const int32_t* cu_seqlens, const void* draft_logits,
+                                     int64_t ld_q, const int32_t* draft_tokens,
+                                     const float* temperatures, const uint32_t* rand_accept,
+                                     const uint32_t* rand_sample, const int32_t* prefix_lens,
+                                     int32_t* num_correct, int32_t* bonus, int32_t* commit_lens,
+                                     int32_t* out_tokens, int32_t* new_seq_lens,
+                                     int32_t* accept_meta, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace dspark_accept_sampling needs (0 for invalid sizes). */
+size_t dspark_accept_sampling_workspace_size(int32_t B, int32_t gamma, int32_t max_rows);
 
 /*
  * dspark_tv_accept - soft accept-rate and its cumulative product.

@@ -328,3 +328,33 @@ def test_inputs_that_reach_the_exact_path():
     assert len(hits) >= 1
     for xv, yv in hits:
         assert np.float32(yv).view(np.uint32) == nearest_f32(sigmoid_decimal(float(xv))).view(np.uint32)
+
+
+def test_accept_sampling_argument_errors():
+    call = _lib.lib().dspark_accept_sampling
+    ok = dict(B=4, gamma=3, V=1000, dt=_lib.BF16, tgt=FAKE, ld=1000, max_rows=16, cu=FAKE,
+              drf=FAKE, ld_q=1000, drafts=FAKE, temps=FAKE, ra=FAKE, rs=FAKE, prefix=NULL,
+              nc=FAKE, bonus=FAKE, commit=FAKE, out=FAKE, new_seq=NULL, meta=FAKE,
+              ws=ctypes.c_void_p(0x100000), wsb=0, stream=NULL)
+
+    def run(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return call(*d.values())
+
+    assert run(B=-1) == _lib.E_INVALID
+    assert run(gamma=0) == _lib.E_INVALID and run(gamma=65) == _lib.E_INVALID
+    assert run(dt=7) == _lib.E_UNSUPPORTED
+    assert run(V=0) == _lib.E_INVALID and run(V=_lib.MAX_VOCAB + 1) == _lib.E_UNSUPPORTED
+    assert run(ld=999) == _lib.E_INVALID and run(ld_q=999) == _lib.E_INVALID
+    assert run(ld=1001) == _lib.E_INVALID  # 2002 bytes: not a multiple of 16
+    assert run(tgt=ctypes.c_void_p(0x1002)) == _lib.E_INVALID
+    assert run(drf=NULL) == _lib.E_INVALID
+    assert run(temps=NULL) == _lib.E_INVALID and run(rs=NULL) == _lib.E_INVALID
+    assert run(new_seq=FAKE) == _lib.E_INVALID  # needs prefix_lens
+    assert run(max_rows=2**31 - 8) == _lib.E_UNSUPPORTED  # + B * gamma overflows
+    assert run() == _lib.E_WORKSPACE
+    size = _lib.lib().dspark_accept_sampling_workspace_size
+    # 24-byte row statistics for 16 target and 12 draft rows, 24-byte jobs
+    assert size(4, 3, 16) == 512 + 512 + 256
+    assert size(0, 3, 0) == 256 and size(-1, 3, 0) == 0 and size(4, 65, 0) == 0

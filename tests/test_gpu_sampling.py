@@ -1,0 +1,207 @@
+"""GPU parity of dspark_accept_sampling against the CPU oracle, through the C ABI.
+
+Bar: bit-exact. Every decision (accept tests, the drawn tokens) is an exact
+integer comparison on both sides, so num_correct, bonus, commit, new_seq,
+out_tokens and the status word must match exactly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import dspark_verify_scheduling_amd as dv
+import oracle
+from oracle import sampling as S
+from workloads import gen
+from _gpu import DEV, logits_up, say, up
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu(hip):
+    return hip
+
+
+def _bits(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.uint32)).view(np.int32)
+
+
+def run_gpu(B, gamma, V, dt, tgt, drf, cu, drafts, temps, ra, rs, prefix=None, max_rows=None,
+            tag=""):
+    """tgt [>= cu[B], V] and drf [B * gamma, V] as float32 or bf16 bits."""
+    max_rows = tgt.shape[0] if max_rows is None else max_rows
+    say(f"accept_sampling {tag} B={B} gamma={gamma} V={V} dt={dt} rows={max_rows}")
+    ld = V if (V * (2 if dt == dv.BF16 else 4)) % 16 == 0 else None
+    if ld is None:  # pad rows to a 16-byte stride
+        per = 8 if dt == dv.BF16 else 4
+        ld = (V + per - 1) // per * per
+        pad = lambda x: np.pad(x, ((0, 0), (0, ld - V)))
+        tgt, drf = pad(tgt), pad(drf)
+    out = dv.alloc_sampling_outputs(B, gamma, max_rows, DEV)
+    for t in (out.num_correct, out.bonus, out.commit_lens, out.out_tokens, out.new_seq_lens):
+        t.fill_(-9)
+    dv.dspark_accept_sampling(
+        B, gamma, V, dt, logits_up(tgt, dt), ld, max_rows, up(np.asarray(cu, np.int32)),
+        logits_up(drf if B else np.zeros((1, ld), tgt.dtype), dt), ld,
+        up(np.asarray(drafts, np.int32).reshape(B, gamma)), up(np.asarray(temps, np.float32)),
+        up(_bits(ra).reshape(B, gamma)), up(_bits(rs).reshape(B, gamma + 1)),
+        up(np.asarray(prefix if prefix is not None else np.zeros(B), np.int32)), out)
+    torch.cuda.synchronize()
+    return {"num_correct": out.num_correct.cpu().numpy(), "bonus": out.bonus.cpu().numpy(),
+            "commit": out.commit_lens.cpu().numpy(), "new_seq": out.new_seq_lens.cpu().numpy(),
+            "out_tokens": out.out_tokens.cpu().numpy(), "meta": out.accept_meta.cpu().numpy()}
+
+
+def check(got, ref, total, reqs=None):
+    sel = slice(None) if reqs is None else reqs
+    for k in ("num_correct", "bonus", "commit", "new_seq", "out_tokens"):
+        a, b = got[k][sel], ref[k]
+        assert np.array_equal(a, b), (k, np.argwhere(a != b)[:5].tolist(),
+                                      a[np.any(a != b, axis=-1) if a.ndim > 1 else a != b][:3],
+                                      b[np.any(a != b, axis=-1) if b.ndim > 1 else a != b][:3])
+    if reqs is None:
+        assert got["meta"][0] == total and got["meta"][1] == ref["status"], (got["meta"], ref["status"])
+
+
+def rand_case(seed, B, gamma, V, dt, greedy_frac=0.2, q_noise=0.5):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, gamma + 2, B)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total = int(cu[-1])
+    tgt = rng.normal(0, 2.5, (total + 2, V)).astype(np.float32)
+    drf = np.empty((B * gamma, V), np.float32)
+    drafts = np.empty((B, gamma), np.int32)
+    for r in range(B):
+        for k in range(gamma):
+            src = tgt[cu[r] + k] if k < lens[r] else rng.normal(0, 2.5, V)
+            drf[r * gamma + k] = src + rng.normal(0, q_noise, V)
+            # the draft is drawn from its own q (temperature 1)
+            q = np.exp(drf[r * gamma + k] - drf[r * gamma + k].max())
+            drafts[r, k] = rng.choice(V, p=q / q.sum())
+    temps = rng.uniform(0.5, 1.5, B).astype(np.float32)
+    temps[rng.random(B) < greedy_frac] = 0.0
+    ra = rng.integers(0, 2**32, (B, gamma), dtype=np.uint64).astype(np.uint32)
+    rs = rng.integers(0, 2**32, (B, gamma + 1), dtype=np.uint64).astype(np.uint32)
+    prefix = rng.integers(5, 500, B).astype(np.int32)
+    if dt == dv.BF16:
+        tgt, drf = gen.f32_to_bf16_bits(tgt), gen.f32_to_bf16_bits(drf)
+    return dict(B=B, gamma=gamma, V=V, dt=dt, tgt=tgt, drf=drf, cu=cu, drafts=drafts,
+                temps=temps, ra=ra, rs=rs, prefix=prefix)
+
+
+def both(c, tag, max_rows=None):
+    got = run_gpu(c["B"], c["gamma"], c["V"], c["dt"], c["tgt"], c["drf"], c["cu"], c["drafts"],
+                  c["temps"], c["ra"], c["rs"], c["prefix"], max_rows=max_rows, tag=tag)
+    ref = S.accept_sampling(c["B"], c["gamma"], c["tgt"], c["drf"],
+                            "bf16" if c["dt"] == dv.BF16 else "f32", c["cu"], c["drafts"],
+                            c["temps"], c["ra"], c["rs"], prefix_lens=c["prefix"],
+                            max_rows=max_rows)
+    check(got, ref, int(c["cu"][-1]))
+    return got, ref
+
+
+@pytest.mark.parametrize("seed,B,gamma,V,dt", [
+    (1, 12, 4, 1000, dv.F32),
+    (2, 16, 6, 4096, dv.BF16),
+    (3, 9, 8, 4099, dv.BF16),   # ragged tail of 3 elements
+    (4, 7, 3, 777, dv.F32),     # ragged tail of 1
+    (5, 20, 5, 20000, dv.BF16), # several register slots
+    (6, 5, 64, 300, dv.F32),    # gamma = 64: 65 rows and columns
+])
+def test_sampling_parity_small(seed, B, gamma, V, dt):
+    c = rand_case(seed, B, gamma, V, dt)
+    got, ref = both(c, f"seed={seed}")
+    say(f"correct {got['num_correct'].tolist()[:12]} temps {np.round(c['temps'][:12], 2).tolist()}")
+
+
+def test_sampling_parity_long_rows():
+    # rows beyond the register-resident part: bf16 V > 131072, f32 V > 65536
+    both(rand_case(7, 3, 3, 200003, dv.BF16, greedy_frac=0.0), "bf16 long rows")
+    both(rand_case(8, 3, 3, 70001, dv.F32, greedy_frac=0.0), "f32 long rows")
+
+
+def test_all_greedy_equals_dspark_accept():
+    w = gen.make(1)
+    rng = np.random.default_rng(3)
+    lens = rng.integers(1, w.gamma + 2, w.B)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tgt = np.concatenate([w.target[r, :lens[r]] for r in range(w.B)])
+    ex = gen.sampling_extras(w)
+    drf = ex.draft_logits.reshape(w.B * w.gamma, w.V)
+    got = run_gpu(w.B, w.gamma, w.V, dv.F32, tgt, drf, cu, w.drafts, np.zeros(w.B), ex.rand_accept,
+                  ex.rand_sample, w.prefix_lens, tag="all greedy")
+    ref = oracle.accept(w.B, w.gamma, tgt, "f32", cu, w.drafts, prefix_lens=w.prefix_lens)
+    for k in ("num_correct", "bonus", "commit", "new_seq", "out_tokens"):
+        assert np.array_equal(got[k], ref[k]), k
+
+
+def test_sampling_edge_cases():
+    c = rand_case(11, 8, 4, 512, dv.F32, greedy_frac=0.25)
+    t = c["tgt"]
+    t[c["cu"][1] + 1, 7] = np.nan         # request 1: NaN in a sampled row
+    t[c["cu"][2], 3] = np.inf             # request 2: +inf
+    t[c["cu"][3] + 0, :] = -np.inf        # request 3: no finite maximum
+    c["temps"][[1, 2, 3]] = 1.0
+    c["temps"][4] = -0.5                  # bad temperature
+    c["temps"][5] = np.inf
+    c["drafts"][6, 0] = c["V"] + 3        # outside the vocabulary
+    c["drafts"][7, 1] = -1
+    got, ref = both(c, "bad data")
+    assert ref["status"] == S.DATA_BAD_LOGITS | oracle.DATA_BAD_CONF
+    # identical p and q rows: every draft in the support passes
+    c = rand_case(12, 6, 5, 640, dv.BF16, greedy_frac=0.0)
+    for r in range(c["B"]):
+        for k in range(c["gamma"]):
+            if c["cu"][r] + k < c["cu"][r + 1]:
+                c["drf"][r * c["gamma"] + k] = c["tgt"][c["cu"][r] + k]
+    got, _ = both(c, "p == q")
+    assert np.array_equal(got["num_correct"], np.diff(c["cu"]) - 1)
+    # malformed layout, and a total beyond max_rows
+    c = rand_case(13, 6, 3, 256, dv.F32)
+    c["cu"][3] = c["cu"][2]
+    both(c, "empty request")
+    c = rand_case(14, 6, 3, 256, dv.F32)
+    both(c, "max_rows below the total", max_rows=int(c["cu"][-1]) - 2)
+    # no requests
+    c = rand_case(15, 1, 3, 256, dv.F32)
+    got = run_gpu(0, 3, 256, dv.F32, c["tgt"][:4], np.zeros((0, 256), np.float32),
+                  np.zeros(1, np.int32), np.zeros((0, 3)), np.zeros(0), np.zeros((0, 3)),
+                  np.zeros((0, 4)), np.zeros(0), tag="B = 0")
+    assert got["meta"].tolist() == [0, 0]
+
+
+def test_sampling_full_size_cfg3_sampled_requests():
+    """B = 256, gamma = 8, V = 129280 bf16 on the planned cfg3 layout, in the
+    launch configuration the benchmark times; the oracle checks 48 requests."""
+    w = gen.make(3)
+    p = oracle.plan(w.B, w.gamma, oracle.IN_CONF_LOGITS, w.conf, w.temps, w.min_len, w.max_len,
+                    w.eps, w.b_lo, w.b_hi, w.bias, w.alpha, w.theta)
+    lens = p["verify_lens"]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tgt = np.concatenate([w.target[r, :lens[r]] for r in range(w.B)])
+    ex = gen.sampling_extras(w, greedy_frac=0.1)
+    drf = ex.draft_logits.reshape(w.B * w.gamma, w.V)
+    max_rows = int(w.tiers[np.searchsorted(w.tiers, cu[-1])])
+    tgt_pad = np.zeros((max_rows, w.V), np.uint16)
+    tgt_pad[:cu[-1]] = tgt
+    got = run_gpu(w.B, w.gamma, w.V, dv.BF16, tgt_pad, drf, cu, w.drafts, ex.temps,
+                  ex.rand_accept, ex.rand_sample, w.prefix_lens, tag="cfg3 full")
+    assert got["meta"].tolist() == [int(cu[-1]), 0]
+    rng = np.random.default_rng(0)
+    reqs = np.sort(rng.choice(w.B, 48, replace=False))
+    sub_lens = lens[reqs]
+    sub_cu = np.concatenate([[0], np.cumsum(sub_lens)]).astype(np.int32)
+    sub_tgt = np.concatenate([tgt[cu[r]:cu[r + 1]] for r in reqs])
+    sub_drf = np.concatenate([drf[r * w.gamma:(r + 1) * w.gamma] for r in reqs])
+    ref = S.accept_sampling(len(reqs), w.gamma, sub_tgt, sub_drf, "bf16", sub_cu,
+                            w.drafts[reqs], ex.temps[reqs], ex.rand_accept[reqs],
+                            ex.rand_sample[reqs], prefix_lens=w.prefix_lens[reqs])
+    check(got, ref, None, reqs=reqs)
+    assert ref["status"] == 0
+    say(f"mean correct {got['num_correct'].mean():.3f} over {w.B} requests, {cu[-1]} rows")
+    # a second call on the same inputs is identical (no state in the workspace)
+    again = run_gpu(w.B, w.gamma, w.V, dv.BF16, tgt_pad, drf, cu, w.drafts, ex.temps,
+                    ex.rand_accept, ex.rand_sample, w.prefix_lens, tag="cfg3 repeat")
+    for k in ("num_correct", "bonus", "out_tokens"):
+        assert np.array_equal(got[k], again[k])

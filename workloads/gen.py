@@ -201,9 +201,10 @@ def _draft_logits(spec, ss, target, d_ids, sig_r):
     """Config 4 draft logits q[r, k] = clip(p[r, k-1] + N(0, sigma_r)), peak at d."""
     B, g, V = spec.B, spec.gamma, spec.V
     n_rows = B * g
+    bf16 = spec.dtype == "bf16"
     cap = np.float32(5.0 * spec.sigma + 3.0)
     peak = np.float32(5.0 * spec.sigma + 5.0)
-    out = np.empty((n_rows, V), dtype=np.uint16)
+    out = np.empty((n_rows, V), dtype=np.uint16 if bf16 else np.float32)
     children = ss.spawn((n_rows + _ROW_BLOCK - 1) // _ROW_BLOCK)
     d_f = d_ids.reshape(-1)
 
@@ -212,13 +213,13 @@ def _draft_logits(spec, ss, target, d_ids, sig_r):
         rng = np.random.Generator(np.random.PCG64(children[i]))
         qi = np.arange(q0, q1)
         r, k0 = qi // g, qi % g  # k0 = k - 1: paired target row
-        p = bf16_bits_to_f32(target[r, k0])
+        p = bf16_bits_to_f32(target[r, k0]) if bf16 else target[r, k0]
         noise = rng.standard_normal((q1 - q0, V), dtype=np.float32)
         noise *= sig_r[r].astype(np.float32)[:, None]
         x = p + noise
         np.clip(x, -cap, cap, out=x)
         x[np.arange(q1 - q0), d_f[q0:q1]] = peak
-        out[q0:q1] = f32_to_bf16_bits(x)
+        out[q0:q1] = f32_to_bf16_bits(x) if bf16 else x
 
     _fill_blocks(n_rows, work)
     return out.reshape(B, g, V)
@@ -293,3 +294,34 @@ def make(cfg: int, seed: Optional[int] = None, *, logits: bool = True) -> Worklo
         anchors=anchors, drafts=drafts, prefix_lens=prefix_lens,
         planted_top=top, target=target, draft_logits=draft_l,
     )
+
+
+@dataclass
+class SamplingExtras:
+    draft_logits: np.ndarray  # [B, gamma, V]: uint16 bf16 bits or float32
+    temps: np.ndarray  # [B] f32 per-request sampling temperature (0 = greedy)
+    rand_accept: np.ndarray  # [B, gamma] uint32 random words
+    rand_sample: np.ndarray  # [B, gamma + 1] uint32 random words
+
+
+def sampling_extras(w: Workload, seed: Optional[int] = None, greedy_frac: float = 0.0,
+                    t_range=(0.6, 1.4)) -> SamplingExtras:
+    """Inputs of the sampling accept for workload ``w``: draft logits (config
+    4's own, or drawn with config 4's recipe, q[r, k] = clip(p[r, k-1] +
+    N(0, sigma_r)) with the draft's maximum planted at d[r, k]), a
+    temperature per request (a ``greedy_frac`` share of them 0) and the
+    random words."""
+    seed = 7919 * (w.cfg + 1) if seed is None else int(seed)
+    ss_meta, ss_draft = np.random.SeedSequence(seed).spawn(2)
+    rng = np.random.Generator(np.random.PCG64(ss_meta))
+    B, g = w.B, w.gamma
+    if w.draft_logits is not None:
+        dl = w.draft_logits
+    else:
+        sig_r = rng.uniform(0.2, 2.0, size=B)
+        dl = _draft_logits(w.spec, ss_draft, w.target, w.drafts, sig_r)
+    temps = rng.uniform(t_range[0], t_range[1], size=B).astype(np.float32)
+    temps[rng.random(B) < greedy_frac] = 0.0
+    ra = rng.integers(0, 2**32, size=(B, g), dtype=np.uint64).astype(np.uint32)
+    rs = rng.integers(0, 2**32, size=(B, g + 1), dtype=np.uint64).astype(np.uint32)
+    return SamplingExtras(dl, temps, ra, rs)
