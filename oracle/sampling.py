@@ -31,16 +31,17 @@ exact integer comparison, identical on any device and in any summation
 order:
 
 * Probabilities at fixed resolution. For a row x (float32; bfloat16 widens
-  exactly) at temperature T > 0, with m = max x:
-      t_i = RN64(RN64(m - x_i) * RN64(65536 / T)),   j_i = nearest integer
-      (ties to even), and W_i = 0 when t_i or j_i >= 455 * 4096; otherwise
-      P = (E0[j >> 12] * E1[(j >> 6) & 63] + 2^22) >> 23
-      W = (P * E2[j & 63] + 2^22) >> 23
-  with E0[h] = round(2^40 e^(-h/16)) (h < 455), E1[a] = round(2^23
-  e^(-a/1024)) and E2[b] = round(2^23 e^(-b/65536)) (a, b < 64), each the
-  nearest integer to the real value. So W_i ~ 2^40 exp((x_i - m) / T) within
-  about 8e-6 relative, W = 2^40 at the maximum, and p_i = W_i / Z with
-  Z = sum W (an integer below 2^58).
+  exactly) at temperature T > 0, with m = max x, every step one IEEE float32
+  operation (nearest, ties to even):
+      c = K / T with K = 94548.4609375, the float32 nearest to 2^16 log2(e)
+      u_i = (-(x_i - m)) * c         (u ~ 2^16 * (m - x_i) * log2(e) / T)
+      W_i = 0 unless u_i < 2^21; else j = nearest integer to u_i (ties to
+      even), h = j >> 8, r = j & 255 and
+      W_i = A[h] - (((A[h] - A[h+1]) * r + 128) >> 8)
+  with A[h] = the nearest integer to 2^31 * 2^(-h/256) (h = 0..8193; A is 0
+  from h = 8192 on). So W_i ~ 2^31 exp((x_i - m) / T) within about 6e-6
+  relative (the 2^-16 step of j and the linear interpolation), W = 2^31 at
+  the maximum, and p_i = W_i / Z with Z = sum W (an integer below 2^49).
 * Random words. The caller passes 32-bit words; a word w stands for the
   uniform U = (w >> 8) / 2^24. ``rand_accept[r, k-1]`` tests draft k;
   ``rand_sample[r, c]`` draws the token of output column c. Keying them by
@@ -64,8 +65,6 @@ order:
 
 from __future__ import annotations
 
-from fractions import Fraction
-
 import numpy as np
 
 from .accept import as_f32_rows, row_argmax
@@ -73,43 +72,40 @@ from .pack import DATA_BAD_LENS
 from .plan import DATA_BAD_CONF
 
 DATA_BAD_LOGITS = 8
-E0_LEN = 455
-J_MAX = E0_LEN * 4096
+K_LOG2E_16 = np.float32(94548.4609375)  # float32 nearest to 2^16 * log2(e)
+U_MAX = np.float32(2.0**21)
+A_LEN = 8194
 
-_TABLES = None
+_TABLE = None
 
 
-def _nearest_int_exp(num: int, den: int, scale_log2: int) -> int:
-    """Nearest integer to 2**scale_log2 * exp(-num/den), from the exact
-    rational Taylor series of exp(num/den) with a bound on its remainder."""
-    x = Fraction(num, den)
-    if num == 0:
-        return 1 << scale_log2
-    term, total, n = Fraction(1), Fraction(1), 0
-    while True:
+def _nearest_int_pow2(e_num: int, e_den: int) -> int:
+    """Nearest integer (ties to even) to 2**(e_num / e_den), exactly.
+
+    An integer exponent gives a power of two: 2**-1 = 1/2 is the only tie
+    (it goes to 0). Otherwise the value is irrational, so N is the nearest
+    integer iff (2N - 1)**e_den < 2**(e_den + e_num) < (2N + 1)**e_den, all
+    integers; below 1/2 (e_den + e_num < 0) it is 0."""
+    if e_num % e_den == 0:
+        k = e_num // e_den
+        return 1 << k if k >= 0 else 0
+    if e_den + e_num < 0:
+        return 0
+    target = 1 << (e_den + e_num)
+    n = max(0, int(round(2.0 ** (e_num / e_den))))
+    while (2 * n + 1) ** e_den <= target:
         n += 1
-        term = term * x / n
-        total += term
-        # once the terms decrease, the remainder is below term * x / (n + 1 - x)
-        if n + 1 > 2 * x:
-            rem = term * x / (n + 1 - x)
-            lo = Fraction(1 << scale_log2) / (total + rem)
-            hi = Fraction(1 << scale_log2) / total
-            a, b = lo - Fraction(1, 2), hi - Fraction(1, 2)
-            # nearest integer of every value in [lo, hi] is the same
-            if a.__ceil__() == b.__ceil__() and a != a.__ceil__() and b != b.__ceil__():
-                return int(a.__ceil__())
+    while n > 0 and (2 * n - 1) ** e_den >= target:
+        n -= 1
+    return n
 
 
-def exp_tables():
-    """(E0, E1, E2) as lists of Python ints, computed once."""
-    global _TABLES
-    if _TABLES is None:
-        e0 = [_nearest_int_exp(h, 16, 40) for h in range(E0_LEN)]
-        e1 = [_nearest_int_exp(a, 1024, 23) for a in range(64)]
-        e2 = [_nearest_int_exp(b, 65536, 23) for b in range(64)]
-        _TABLES = (e0, e1, e2)
-    return _TABLES
+def exp_table():
+    """A[h] = nearest integer to 2^31 * 2^(-h/256), h = 0..8193 (Python ints)."""
+    global _TABLE
+    if _TABLE is None:
+        _TABLE = [_nearest_int_pow2(31 * 256 - h, 256) for h in range(A_LEN)]
+    return _TABLE
 
 
 def row_is_bad(x: np.ndarray) -> bool:
@@ -121,22 +117,18 @@ def row_is_bad(x: np.ndarray) -> bool:
 
 
 def weights(x: np.ndarray, T: float) -> np.ndarray:
-    """Integer weights W (uint64) of one float32 row at temperature T > 0."""
-    e0, e1, e2 = (np.array(t, dtype=np.uint64) for t in exp_tables())
-    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    """Integer weights W (int64) of one float32 row at temperature T > 0."""
+    A = np.array(exp_table(), dtype=np.int64)
+    x = np.asarray(x, dtype=np.float32)
     m = np.max(x)
-    s = np.float64(65536.0) / np.float64(np.float32(T))
+    c = K_LOG2E_16 / np.float32(T)  # float32 division
     with np.errstate(invalid="ignore", over="ignore"):
-        t = (m - x) * s  # two float64 roundings, as in the definition
-    W = np.zeros(x.shape, dtype=np.uint64)
-    ok = t < J_MAX
-    j = np.rint(t[ok]).astype(np.int64)
-    keep = j < J_MAX
-    j = j[keep]
-    P = (e0[j >> 12] * e1[(j >> 6) & 63] + np.uint64(1 << 22)) >> np.uint64(23)
-    w = (P * e2[j & 63] + np.uint64(1 << 22)) >> np.uint64(23)
-    idx = np.flatnonzero(ok)[keep]
-    W[idx] = w
+        u = (-(x - m)) * c  # float32 subtraction, negation, product
+    W = np.zeros(x.shape, dtype=np.int64)
+    ok = u < U_MAX
+    j = np.rint(u[ok]).astype(np.int64)
+    h, r = j >> 8, j & 255
+    W[ok] = A[h] - (((A[h] - A[h + 1]) * r + 128) >> 8)
     return W
 
 

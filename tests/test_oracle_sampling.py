@@ -1,10 +1,11 @@
 """Pins for the chain speculative-sampling accept oracle.
 
 Fixed by:
-* the exp tables against an independent 80-bit long-double evaluation;
+* the exp2 table against an independent 80-bit long-double evaluation, and
+  K against a 50-digit decimal 2^16 / ln 2;
 * the fixed-resolution probabilities against the float64 softmax (closed
-  form), the value 2^40 at the maximum, monotonicity and the power-of-two
-  scaling invariance of x / T;
+  form), the value 2^31 at the maximum, table entries hit exactly,
+  monotonicity and the power-of-two scaling invariance of x / T;
 * the theorem of speculative sampling: one chain step outputs a token
   distributed exactly as p (to the 2^-24 resolution of the random words),
   whatever q is, and its acceptance rate is sum min(p, q) = 1 - TV, the
@@ -25,18 +26,23 @@ import oracle
 from oracle import sampling as S
 
 
-def test_exp_tables_against_long_double():
-    e0, e1, e2 = S.exp_tables()
+def test_exp_table_against_long_double():
+    A = S.exp_table()
     ld = np.longdouble
     assert np.finfo(ld).eps < 1e-18  # 80-bit extended on this host
-    for tab, den, scale, n in ((e0, 16, 40, 455), (e1, 1024, 23, 64), (e2, 65536, 23, 64)):
-        assert len(tab) == n
-        for i, v in enumerate(tab):
-            ref = ld(2) ** scale * np.exp(-ld(i) / ld(den))
-            assert abs(ld(v) - ref) <= 0.5 + ref * 1e-17, (den, i, v, ref)
-    assert e0[0] == 2**40 and e1[0] == 2**23 and e2[0] == 2**23
-    # the last E0 entry is the last one that does not round to 0
-    assert e0[-1] == 1 and ld(2) ** 40 * np.exp(-ld(455) / 16) < 0.5
+    assert len(A) == S.A_LEN == 8194
+    for h, v in enumerate(A):
+        ref = ld(2) ** (31 - ld(h) / 256)
+        assert abs(ld(v) - ref) <= 0.5 + ref * 1e-17, (h, v, ref)
+    assert A[0] == 2**31 and A[256] == 2**30 and A[8191] == 1 and A[8192] == A[8193] == 0
+    # K is the float32 nearest to 2^16 log2(e)
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    k = Decimal(65536) / Decimal(2).ln()
+    below = np.nextafter(S.K_LOG2E_16, np.float32(0))
+    above = np.nextafter(S.K_LOG2E_16, np.float32(1e9))
+    d0 = abs(Decimal(float(S.K_LOG2E_16)) - k)
+    assert d0 < abs(Decimal(float(below)) - k) and d0 < abs(Decimal(float(above)) - k)
 
 
 @pytest.mark.parametrize("T", [0.05, 0.6, 1.0, 1.7, 8.0])
@@ -44,21 +50,18 @@ def test_weights_match_softmax(T):
     rng = np.random.default_rng(int(T * 100))
     x = rng.normal(0.0, 3.0, 5000).astype(np.float32)
     W = S.weights(x, T)
-    assert W.max() == 2**40 and W[np.argmax(x)] == 2**40
+    assert W.max() == 2**31 and W[np.argmax(x)] == 2**31
     p = W.astype(np.float64) / float(W.sum())
     y = (x.astype(np.float64) - x.max()) / np.float64(np.float32(T))
     q = np.exp(y) / np.exp(y).sum()
-    big = q > 1e-6 * q.max()
-    assert np.max(np.abs(p - q)[big] / q[big]) < 2e-5
+    big = q > 1e-3 * q.max()  # W above 2^21: the 2^-31 grid is below 5e-7 relative
+    assert np.max(np.abs(p - q)[big] / q[big]) < 1.5e-5
     assert 0.5 * np.abs(p - q).sum() < 1e-5
-    # monotone in the logit wherever one step of j (a factor 1 - 1.5e-5)
-    # exceeds the rounding of the three table stages; within 2 units of
-    # 2^-40 everywhere
+    # monotone in the logit (up to one unit of the interpolation's rounding)
     order = np.argsort(x, kind="stable")
-    Wo = W[order].astype(np.int64)
-    assert np.all(np.diff(Wo) >= -2)
-    big = Wo[:-1] > 2**20
-    assert np.all(np.diff(Wo)[big] >= 0)
+    Wo = W[order]
+    assert np.all(np.diff(Wo) >= -1)
+    assert np.all(np.diff(Wo)[Wo[:-1] > 2**16] >= 0)
 
 
 def test_weights_scaling_invariance_and_special_values():
@@ -67,11 +70,19 @@ def test_weights_scaling_invariance_and_special_values():
     for T in (0.3, 1.0, 2.5):
         assert np.array_equal(S.weights(x, T), S.weights(x * 4, T * 4))
         assert np.array_equal(S.weights(x, T), S.weights(x / 8, T / 8))
-    # -inf has weight 0; a logit 30 below the max at T = 1 is below 2^-40
-    z = np.array([0.0, -np.inf, -30.0, -1.0], np.float32)
+    # -inf has weight 0; a logit 30 below the max at T = 1 is below 2^-32
+    z = np.array([0.0, -np.inf, -30.0, -1.0, -22.0], np.float32)
     W = S.weights(z, 1.0)
-    assert W[0] == 2**40 and W[1] == 0 and W[2] == 0
-    assert abs(int(W[3]) - 2**40 * np.exp(-1.0)) < 2**40 * 1e-5
+    assert W[0] == 2**31 and W[1] == 0 and W[2] == 0
+    assert abs(int(W[3]) - 2**31 * np.exp(-1.0)) < 2**31 * 1e-5
+    assert abs(int(W[4]) - 2**31 * np.exp(-22.0)) <= 1
+    # j = 256 i lands on table entries: W = A[i]
+    A = S.exp_table()
+    for i in (1, 7, 100, 4000):
+        x = np.array([0.0, -np.float32(i * 256) / np.float32(S.K_LOG2E_16)], np.float32)
+        u = (-(x[1] - x[0])) * S.K_LOG2E_16
+        if np.rint(u) == i * 256:
+            assert S.weights(x, 1.0)[1] == A[i]
 
 
 def _count_accept(Wp_d, Zp, Wq_d, Zq):
@@ -261,12 +272,12 @@ def test_zero_probability_is_never_drawn_or_accepted():
     assert counts.sum() == 2**24 and abs(counts[1] - 3 * 2**24 / 8) <= 1
     assert S.draw(w, 0) == 1 and S.draw(w, 0xFFFFFFFF) == 3
     # min(1, p/q) is 0 when p(d) = 0, whatever q(d) is
-    Z = 5 * 2**40
-    assert _count_accept(0, Z, 2**40, Z) == 0
+    Z = 5 * 2**31
+    assert _count_accept(0, Z, 2**31, Z) == 0
     assert _count_accept(0, Z, 0, Z) == 0
     # and 1 when p(d) >= q(d) > 0
-    assert _count_accept(2**40, Z, 2**40, Z) == 2**24
-    assert _count_accept(2**39, Z, 2**40, Z) == 2**23
+    assert _count_accept(2**31, Z, 2**31, Z) == 2**24
+    assert _count_accept(2**30, Z, 2**31, Z) == 2**23
 
 
 def test_each_output_column_draws_with_its_own_word():
@@ -293,3 +304,25 @@ def test_each_output_column_draws_with_its_own_word():
         res = S.accept_sampling(B, gamma, tgt, drf, "f32", cu, drafts, np.ones(1), ra, rs)
         assert res["num_correct"][0] == 3 and res["bonus"][0] == expect
         assert res["out_tokens"][0].tolist() == [9, 9, 9, expect]
+
+
+@pytest.mark.parametrize("T", [0.7, 1.0, 2.0])
+def test_weights_are_unbiased(T):
+    # nearest rounding of j leaves no systematic error: the mean signed
+    # relative error of W against 2^31 exp((x - m) / T) is about 0, while a
+    # floor (or any one-sided rounding) biases it by about 2^-17 ln 2 = 5e-6
+    rng = np.random.default_rng(31)
+    x = (rng.uniform(-22.0, 0.0, 200000) * T).astype(np.float32)
+    x[0] = 0.0
+    W = S.weights(x, T)
+    ref = 2.0**31 * np.exp(x.astype(np.float64) / np.float64(np.float32(T)))
+    big = W > 2**20
+    rel = W[big] / ref[big] - 1.0
+    assert abs(rel.mean()) < 1e-6, rel.mean()
+    assert np.max(np.abs(rel)) < 1.2e-5
+    # small weights: the interpolation rounds to nearest too (mean error in
+    # units of 2^-31 about 0, not the +1/2 of a truncating interpolation)
+    small = (W > 2**8) & (W < 2**14)
+    assert small.sum() > 5000
+    err = W[small] - ref[small]
+    assert abs(err.mean()) < 0.1, err.mean()
