@@ -34,14 +34,16 @@ order:
   exactly) at temperature T > 0, with m = max x, every step one IEEE float32
   operation (nearest, ties to even):
       c = K / T with K = 94548.4609375, the float32 nearest to 2^16 log2(e)
-      u_i = (-(x_i - m)) * c         (u ~ 2^16 * (m - x_i) * log2(e) / T)
-      W_i = 0 unless u_i < 2^21; else j = nearest integer to u_i (ties to
-      even), h = j >> 8, r = j & 255 and
-      W_i = A[h] - (((A[h] - A[h+1]) * r + 128) >> 8)
-  with A[h] = the nearest integer to 2^31 * 2^(-h/256) (h = 0..8193; A is 0
-  from h = 8192 on). So W_i ~ 2^31 exp((x_i - m) / T) within about 6e-6
-  relative (the 2^-16 step of j and the linear interpolation), W = 2^31 at
-  the maximum, and p_i = W_i / Z with Z = sum W (an integer below 2^49).
+      u_i = (m - x_i) * c            (u ~ 2^16 * (m - x_i) * log2(e) / T)
+  then, in integers, W_i = 0 unless j = (nearest integer to u_i, ties to
+  even) is below 2^21; else with n = j >> 16, h = (j >> 8) & 255, r = j & 255,
+      Y = B[h] - (((B[h] - B[h+1]) * r + 128) >> 8)
+      W_i = (Y + (2^n >> 1)) >> n
+  where B[i] is the nearest integer to 2^31 * 2^(-i/256) (i = 0..256). So
+  W_i ~ 2^31 * 2^(-j/65536) ~ 2^31 exp((x_i - m) / T): the octave n is a
+  rounding shift and the fraction a linear interpolation, within about 6e-6
+  relative (the 2^-16 step of j and the interpolation) plus half a unit.
+  W = 2^31 at the maximum, and p_i = W_i / Z with Z = sum W (below 2^49).
 * Random words. The caller passes 32-bit words; a word w stands for the
   uniform U = (w >> 8) / 2^24. ``rand_accept[r, k-1]`` tests draft k;
   ``rand_sample[r, c]`` draws the token of output column c. Keying them by
@@ -73,8 +75,8 @@ from .plan import DATA_BAD_CONF
 
 DATA_BAD_LOGITS = 8
 K_LOG2E_16 = np.float32(94548.4609375)  # float32 nearest to 2^16 * log2(e)
-U_MAX = np.float32(2.0**21)
-A_LEN = 8194
+J_MAX = 1 << 21
+B_LEN = 257
 
 _TABLE = None
 
@@ -101,10 +103,10 @@ def _nearest_int_pow2(e_num: int, e_den: int) -> int:
 
 
 def exp_table():
-    """A[h] = nearest integer to 2^31 * 2^(-h/256), h = 0..8193 (Python ints)."""
+    """B[i] = nearest integer to 2^31 * 2^(-i/256), i = 0..256 (Python ints)."""
     global _TABLE
     if _TABLE is None:
-        _TABLE = [_nearest_int_pow2(31 * 256 - h, 256) for h in range(A_LEN)]
+        _TABLE = [_nearest_int_pow2(31 * 256 - i, 256) for i in range(B_LEN)]
     return _TABLE
 
 
@@ -118,17 +120,20 @@ def row_is_bad(x: np.ndarray) -> bool:
 
 def weights(x: np.ndarray, T: float) -> np.ndarray:
     """Integer weights W (int64) of one float32 row at temperature T > 0."""
-    A = np.array(exp_table(), dtype=np.int64)
+    Bt = np.array(exp_table(), dtype=np.int64)
     x = np.asarray(x, dtype=np.float32)
     m = np.max(x)
     c = K_LOG2E_16 / np.float32(T)  # float32 division
     with np.errstate(invalid="ignore", over="ignore"):
-        u = (-(x - m)) * c  # float32 subtraction, negation, product
+        u = (m - x) * c  # float32 subtraction and product
     W = np.zeros(x.shape, dtype=np.int64)
-    ok = u < U_MAX
+    ok = u < np.float32(J_MAX)
     j = np.rint(u[ok]).astype(np.int64)
-    h, r = j >> 8, j & 255
-    W[ok] = A[h] - (((A[h] - A[h + 1]) * r + 128) >> 8)
+    keep = j < J_MAX
+    j = j[keep]
+    n, h, r = j >> 16, (j >> 8) & 255, j & 255
+    Y = Bt[h] - (((Bt[h] - Bt[h + 1]) * r + 128) >> 8)
+    W[np.flatnonzero(ok)[keep]] = (Y + ((1 << n) >> 1)) >> n
     return W
 
 

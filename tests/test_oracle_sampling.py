@@ -27,14 +27,14 @@ from oracle import sampling as S
 
 
 def test_exp_table_against_long_double():
-    A = S.exp_table()
+    Bt = S.exp_table()
     ld = np.longdouble
     assert np.finfo(ld).eps < 1e-18  # 80-bit extended on this host
-    assert len(A) == S.A_LEN == 8194
-    for h, v in enumerate(A):
-        ref = ld(2) ** (31 - ld(h) / 256)
-        assert abs(ld(v) - ref) <= 0.5 + ref * 1e-17, (h, v, ref)
-    assert A[0] == 2**31 and A[256] == 2**30 and A[8191] == 1 and A[8192] == A[8193] == 0
+    assert len(Bt) == S.B_LEN == 257
+    for i, v in enumerate(Bt):
+        ref = ld(2) ** (31 - ld(i) / 256)
+        assert abs(ld(v) - ref) <= 0.5 + ref * 1e-17, (i, v, ref)
+    assert Bt[0] == 2**31 and Bt[256] == 2**30
     # K is the float32 nearest to 2^16 log2(e)
     from decimal import Decimal, getcontext
     getcontext().prec = 50
@@ -76,13 +76,14 @@ def test_weights_scaling_invariance_and_special_values():
     assert W[0] == 2**31 and W[1] == 0 and W[2] == 0
     assert abs(int(W[3]) - 2**31 * np.exp(-1.0)) < 2**31 * 1e-5
     assert abs(int(W[4]) - 2**31 * np.exp(-22.0)) <= 1
-    # j = 256 i lands on table entries: W = A[i]
-    A = S.exp_table()
+    # j = 256 i lands on table entries, shifted by the octave: W = round(B[i % 256] / 2^n)
+    Bt = S.exp_table()
     for i in (1, 7, 100, 4000):
         x = np.array([0.0, -np.float32(i * 256) / np.float32(S.K_LOG2E_16)], np.float32)
-        u = (-(x[1] - x[0])) * S.K_LOG2E_16
+        u = (x[0] - x[1]) * S.K_LOG2E_16
         if np.rint(u) == i * 256:
-            assert S.weights(x, 1.0)[1] == A[i]
+            n = i >> 8
+            assert S.weights(x, 1.0)[1] == (Bt[i & 255] + ((1 << n) >> 1)) >> n
 
 
 def _count_accept(Wp_d, Zp, Wq_d, Zq):
