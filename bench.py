@@ -218,6 +218,7 @@ def main():
 
     import dspark_verify_scheduling_amd as dv
     from workloads import make
+    from workloads.gen import sampling_extras
 
     dev = "cuda"
     dv.load()
@@ -418,6 +419,48 @@ def main():
     del dst
     torch.cuda.empty_cache()
 
+    # ---- chain speculative-sampling accept on the same planned layout: every
+    # request samples (temperatures 0.6..1.4); draft rows drawn with the
+    # draft-logit recipe of the generator, two copies rotating
+    log("sampling accept on the planned layout")
+    ex = sampling_extras(w)
+    n_drot = 2
+    dl_host = ex.draft_logits.reshape(B * G, V)
+    drf_bufs = []
+    for _ in range(n_drot):
+        tb = torch.from_numpy(dl_host.view(np.int16) if dt == dv.BF16 else dl_host).to(dev)
+        drf_bufs.append(tb.view(torch.bfloat16) if dt == dv.BF16 else tb)
+    del dl_host
+    stemps_t = t(ex.temps)
+    ra_t = t(ex.rand_accept.view(np.int32))
+    rs_t = t(ex.rand_sample.view(np.int32))
+    so = dv.alloc_sampling_outputs(B, G, V, dt, dev)
+
+    def samp(i):
+        dv.dspark_accept_sampling(B, G, V, dt, packed[i % n_rot], V, tier, ko.cu_seqlens,
+                                  drf_bufs[i % n_drot], V, drafts_t, stemps_t, ra_t, rs_t,
+                                  prefix_t, so, stream)
+
+    for i in range(5):
+        samp(i)
+    torch.cuda.synchronize()
+    n_samp = 50
+    start.record(stream)
+    for i in range(n_samp):
+        samp(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    samp_us = 1e3 * start.elapsed_time(stop) / n_samp
+    assert so.accept_meta.tolist() == [total, 0]
+    live_drafts = int(np.sum(lens - 1))  # every request samples
+    samp_bytes = (total + live_drafts) * V * esize
+    samp_gbs = samp_bytes / (samp_us * 1e-6) / 1e9
+    samp_res = {"rows_target": total, "rows_draft": live_drafts, "us": samp_us, "GB/s": samp_gbs,
+                "frac": samp_gbs / PEAK_HBM_GBS, "bytes": samp_bytes,
+                "mean_correct": float(so.num_correct.float().mean().item())}
+    del drf_bufs
+    torch.cuda.empty_cache()
+
     acc_bytes = accept_bytes(total, B, G, V, esize)
     achieved = acc_bytes / (acc_mean_us * 1e-6) / 1e9
 
@@ -485,6 +528,7 @@ def main():
                        "frac": cap_gbs / PEAK_HBM_GBS},
         "scatter_to_strided": {"rows": total, "us": scat_us, "GB/s": scat_gbs,
                                "frac": scat_gbs / PEAK_HBM_GBS, "bytes": scat_bytes},
+        "sampling_accept": samp_res,
         "sts_fit": sts_res,
         "tv_pass": tv_res,
         "wall_s_timed": wall,

@@ -336,14 +336,14 @@ class SamplingOutputs(NamedTuple):
     workspace: torch.Tensor  # uint8 scratch (no initialization needed)
 
 
-def dspark_accept_sampling_workspace_size(B: int, gamma: int, max_rows: int) -> int:
-    return int(_lib.lib().dspark_accept_sampling_workspace_size(B, gamma, max_rows))
+def dspark_accept_sampling_workspace_size(B: int, gamma: int, V: int, dt: int) -> int:
+    return int(_lib.lib().dspark_accept_sampling_workspace_size(B, gamma, V, dt))
 
 
-def alloc_sampling_outputs(B: int, gamma: int, max_rows: int, device,
+def alloc_sampling_outputs(B: int, gamma: int, V: int, dt: int, device,
                            new_seq=True) -> SamplingOutputs:
     i32 = torch.int32
-    ws = dspark_accept_sampling_workspace_size(B, gamma, max_rows)
+    ws = dspark_accept_sampling_workspace_size(B, gamma, V, dt)
     return SamplingOutputs(
         torch.empty(B, dtype=i32, device=device),
         torch.empty(B, dtype=i32, device=device),

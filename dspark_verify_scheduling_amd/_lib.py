@@ -66,7 +66,7 @@ SIGNATURES = {
         c_int32, c_int32, c_int32, c_int, c_void_p, c_int64, c_int32, c_void_p, c_void_p,
         c_int64, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
-    "dspark_accept_sampling_workspace_size": (c_size_t, [c_int32, c_int32, c_int32]),
+    "dspark_accept_sampling_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int]),
     "dspark_sts_fit": (c_int, [
         c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),

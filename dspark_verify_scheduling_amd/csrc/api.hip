@@ -82,11 +82,22 @@ StsGeom sts_geom(int N, int gamma, int n_t, int n_bins) {
   return g;
 }
 
-// Workspace of dspark_accept_sampling: row statistics and draw jobs.
-size_t samp_ws_bytes(int B, int gamma, int max_rows) {
-  return align256((size_t)max_rows * sizeof(dspark::SampRowStat)) +
-         align256((size_t)B * gamma * sizeof(dspark::SampRowStat)) +
-         align256((size_t)(B > 0 ? B : 1) * sizeof(dspark::SampJob));
+// Workspace of dspark_accept_sampling: a maximum key and a weight sum per
+// (slot, chunk), slots B * (2 * gamma + 1), and one draw job per request.
+struct SampGeom {
+  int chunks, chunk_vecs;
+  size_t part_bytes, bytes;
+};
+
+SampGeom samp_geom(int B, int gamma, int V, dspark_dtype dt) {
+  const RowGeom rg = row_geom(V, dt);
+  SampGeom g;
+  g.chunks = (rg.nvec + dspark::kSampChunkVecs - 1) / dspark::kSampChunkVecs;
+  if (g.chunks < 1) g.chunks = 1;
+  g.chunk_vecs = (rg.nvec + g.chunks - 1) / g.chunks;
+  g.part_bytes = align256((size_t)B * (2 * gamma + 1) * g.chunks * sizeof(unsigned long long));
+  g.bytes = 2 * g.part_bytes + align256((size_t)(B > 0 ? B : 1) * sizeof(dspark::SampJob));
+  return g;
 }
 
 // Workspace of dspark_accept: one 64-bit (key, index) partial per unit.
@@ -575,11 +586,13 @@ dspark_status dspark_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt
   return launched(dspark::launch_accept(a, dt, grid, (hipStream_t)stream), "dspark_accept");
 }
 
-size_t dspark_accept_sampling_workspace_size(int32_t B, int32_t gamma, int32_t max_rows) {
-  if (B < 0 || gamma < 1 || gamma > DSPARK_MAX_GAMMA || max_rows < 0 ||
-      (int64_t)max_rows + (int64_t)B * gamma > 0x7fffffffLL)
+size_t dspark_accept_sampling_workspace_size(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt) {
+  if (B < 0 || gamma < 1 || gamma > DSPARK_MAX_GAMMA || V < 1 || V > DSPARK_MAX_VOCAB ||
+      (dt != DSPARK_F32 && dt != DSPARK_BF16))
     return 0;
-  return samp_ws_bytes(B, gamma, max_rows);
+  const SampGeom g = samp_geom(B, gamma, V, dt);
+  if ((int64_t)B * (2 * gamma + 1) * g.chunks > 0x7fffffffLL) return 0;
+  return g.bytes;
 }
 
 dspark_status dspark_accept_sampling(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,
@@ -602,8 +615,10 @@ dspark_status dspark_accept_sampling(int32_t B, int32_t gamma, int32_t V, dspark
     return fail(V < 1 ? DSPARK_E_INVALID : DSPARK_E_UNSUPPORTED, "%s: V = %d outside [1, %d]", fn,
                 V, DSPARK_MAX_VOCAB);
   if (max_rows < 0) return fail(DSPARK_E_INVALID, "%s: max_rows = %d < 0", fn, max_rows);
-  if ((int64_t)max_rows + (int64_t)B * gamma > 0x7fffffffLL)
-    return fail(DSPARK_E_UNSUPPORTED, "%s: max_rows + B * gamma overflows int32", fn);
+  const SampGeom sg = samp_geom(B, gamma, V, dt);
+  if ((int64_t)B * (2 * gamma + 1) * sg.chunks > 0x7fffffffLL ||
+      (int64_t)max_rows + (int64_t)B * gamma > 0x7fffffffLL)
+    return fail(DSPARK_E_UNSUPPORTED, "%s: B, gamma and V give too many work units", fn);
   if (ld < V || ld_q < V)
     return fail(DSPARK_E_INVALID, "%s: ld = %lld or ld_q = %lld below V = %d", fn, (long long)ld,
                 (long long)ld_q, V);
@@ -621,9 +636,10 @@ dspark_status dspark_accept_sampling(int32_t B, int32_t gamma, int32_t V, dspark
     return fail(DSPARK_E_INVALID, "%s: a required per-request pointer is NULL", fn);
   if (new_seq_lens && !prefix_lens)
     return fail(DSPARK_E_INVALID, "%s: new_seq_lens needs prefix_lens", fn);
-  const size_t need = samp_ws_bytes(B, gamma, max_rows);
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
-    return fail(DSPARK_E_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned", fn, need);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+      workspace_bytes < sg.bytes)
+    return fail(DSPARK_E_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned", fn,
+                sg.bytes);
   const RowGeom g = row_geom(V, dt);
   dspark::SampArgs a;
   a.tgt = static_cast<const unsigned char*>(packed_logits);
@@ -633,6 +649,8 @@ dspark_status dspark_accept_sampling(int32_t B, int32_t gamma, int32_t V, dspark
   a.V = V;
   a.nvec = g.nvec;
   a.tail = g.tail;
+  a.chunks = sg.chunks;
+  a.chunk_vecs = sg.chunk_vecs;
   a.max_rows = max_rows;
   a.B = B;
   a.gamma = gamma;
@@ -649,11 +667,9 @@ dspark_status dspark_accept_sampling(int32_t B, int32_t gamma, int32_t V, dspark
   a.new_seq = new_seq_lens;
   a.meta = accept_meta;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  a.tstat = reinterpret_cast<dspark::SampRowStat*>(ws);
-  ws += align256((size_t)max_rows * sizeof(dspark::SampRowStat));
-  a.dstat = reinterpret_cast<dspark::SampRowStat*>(ws);
-  ws += align256((size_t)B * gamma * sizeof(dspark::SampRowStat));
-  a.jobs = reinterpret_cast<dspark::SampJob*>(ws);
+  a.kpart = reinterpret_cast<unsigned long long*>(ws);
+  a.zpart = reinterpret_cast<unsigned long long*>(ws + sg.part_bytes);
+  a.jobs = reinterpret_cast<dspark::SampJob*>(ws + 2 * sg.part_bytes);
   return launched(dspark::launch_sampling(a, dt, (hipStream_t)stream), fn);
 }
 

@@ -139,26 +139,21 @@ constexpr int kStsMaxBlocks = 1024;  // bin workgroups (histogram slots) at most
 hipError_t launch_sts(const StsArgs& a, hipStream_t s);
 
 // Chain speculative-sampling accept (sampling.hip).
-struct SampRowStat {
-  unsigned long long Z;  // sum of the row's integer weights (sampling rows)
-  float m;               // row maximum (finite when bad == 0)
-  int am;                // first index of the maximum, NaN highest (greedy)
-  int bad;               // NaN or +inf in the row, or no finite maximum
-  int pad;
-};
 struct SampJob {
   int mode;  // 0 none, 1 draw from p, 2 draw from the residual of (p, q)
   int prow, qrow;
   unsigned int word;
-  int col;   // output column of the drawn token (= num_correct)
+  int col;  // output column of the drawn token (= num_correct)
+  float mp, mq;  // row maxima
   int pad;
+  unsigned long long zp, zq;  // weight sums
 };
 struct SampArgs {
   const unsigned char* tgt;  // packed target rows
   int64_t ld_t;              // bytes
   const unsigned char* drf;  // draft rows, row r * gamma + k - 1 for draft k
   int64_t ld_q;              // bytes
-  int V, nvec, tail, max_rows, B, gamma;
+  int V, nvec, tail, chunks, chunk_vecs, max_rows, B, gamma;
   const int32_t* cu;
   const int32_t* drafts;
   const float* temps;
@@ -171,12 +166,17 @@ struct SampArgs {
   int32_t* out_tokens;
   int32_t* new_seq;
   int32_t* meta;
-  SampRowStat* tstat;  // workspace: [max_rows]
-  SampRowStat* dstat;  // workspace: [B * gamma]
-  SampJob* jobs;       // workspace: [B]
+  // workspace, per slot and chunk: target slots r * (gamma + 1) + j (packed
+  // row cu[r] + j), then draft slots B * (gamma + 1) + r * gamma + k (draft
+  // row r * gamma + k)
+  unsigned long long* kpart;  // maximum key with its index
+  unsigned long long* zpart;  // weight sum
+  SampJob* jobs;              // [B]
 };
-constexpr int kSampThreads = 1024;
-constexpr int kSampRegSlots = 16;  // 16-byte vectors per thread kept in registers
+constexpr int kSampThreads = 256;       // max and weight-sum kernels
+constexpr int kSampVecsPerThread = 8;
+constexpr int kSampChunkVecs = kSampThreads * kSampVecsPerThread;
+constexpr int kSampDrawThreads = 1024;  // draw kernel
 hipError_t launch_sampling(const SampArgs& a, dspark_dtype dt, hipStream_t s);
 
 // ---------------------------------------------------------------- helpers

@@ -435,12 +435,13 @@ size_t dspark_accept_workspace_size(int32_t max_rows, int32_t V, dspark_dtype dt
  *            drawn from the residual max(0, p - q) of that pair; if all pass,
  *            column l - 1 gets a token drawn from p of target row l - 1.
  * Probabilities at fixed resolution, so every decision is exact: for a row x
- * with maximum m, t = RN64(RN64(m - x) * RN64(65536 / T)), j = nearest
- * integer, W = 0 if t or j >= 455 * 4096, else W = (((E0[j >> 12] *
- * E1[(j >> 6) & 63] + 2^22) >> 23) * E2[j & 63] + 2^22) >> 23 with E0[h],
- * E1[a], E2[b] the nearest integers to 2^40 e^(-h/16), 2^23 e^(-a/1024),
- * 2^23 e^(-b/65536); p = W / sum W. Within about 8e-6 relative of the
- * softmax of x / T.
+ * with maximum m, every float step one IEEE float32 operation, u = (m - x) *
+ * (K / T) with K = 94548.4609375 (the float32 nearest to 2^16 log2 e); j = u
+ * rounded to the nearest integer; W = 0 unless j < 2^21, else with
+ * n = j >> 16, h = (j >> 8) & 255, r = j & 255:
+ * Y = B[h] - (((B[h] - B[h+1]) * r + 128) >> 8) and W = (Y + (2^n >> 1)) >> n,
+ * where B[i] is the nearest integer to 2^31 * 2^(-i/256). p = W / sum W,
+ * within about 6e-6 relative of the softmax of x / T.
  *   accept draft d  iff  (rand_accept >> 8) * Wq[d] * Zp < 2^24 * Wp[d] * Zq
  *   draw from integer weights w (total S) with word v: the smallest index
  *   whose running sum exceeds floor((v >> 8) * S / 2^24); residual weights
@@ -468,7 +469,7 @@ size_t dspark_accept_workspace_size(int32_t max_rows, int32_t V, dspark_dtype dt
  *                      column num_correct, -1 after)
  *   new_seq_lens       out [B] int32 or NULL
  *   accept_meta        out [2] int32: cu_seqlens[B], status bits
- *   workspace          dspark_accept_sampling_workspace_size() bytes,
+ *   workspace          dspark_accept_sampling_workspace_size(B, gamma, V, dt) bytes,
  *                      256-byte aligned; no state between calls; calls that
  *                      share it must not overlap in time.
  * Data errors: a malformed layout (as for dspark_accept) sets
@@ -490,7 +491,8 @@ dspark_status dspark_accept_sampling(int32_t B, int32_t gamma, int32_t V, dspark
                                      size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace dspark_accept_sampling needs (0 for invalid sizes). */
-size_t dspark_accept_sampling_workspace_size(int32_t B, int32_t gamma, int32_t max_rows);
+size_t dspark_accept_sampling_workspace_size(int32_t B, int32_t gamma, int32_t V,
+                                             dspark_dtype dt);
 
 /*
  * dspark_tv_accept - soft accept-rate and its cumulative product.

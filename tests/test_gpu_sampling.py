@@ -38,7 +38,7 @@ def run_gpu(B, gamma, V, dt, tgt, drf, cu, drafts, temps, ra, rs, prefix=None, m
         ld = (V + per - 1) // per * per
         pad = lambda x: np.pad(x, ((0, 0), (0, ld - V)))
         tgt, drf = pad(tgt), pad(drf)
-    out = dv.alloc_sampling_outputs(B, gamma, max_rows, DEV)
+    out = dv.alloc_sampling_outputs(B, gamma, V, dt, DEV)
     for t in (out.num_correct, out.bonus, out.commit_lens, out.out_tokens, out.new_seq_lens):
         t.fill_(-9)
     dv.dspark_accept_sampling(
