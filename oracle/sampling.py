@@ -59,7 +59,8 @@ order:
   drawn from p.
 * A row with a NaN or +inf logit, or with no finite maximum, in a sampling
   request sets DATA_BAD_LOGITS; a temperature that is negative, NaN or
-  infinite sets DATA_BAD_CONF. Either way the request gets the malformed-
+  infinite, or so small that K / T overflows float32 (T below about
+  2.8e-34), sets DATA_BAD_CONF. Either way the request gets the malformed-
   layout outputs of ``oracle.accept`` (correct 0, bonus -1, commit 0,
   out_tokens -1, new_seq = prefix). Greedy requests follow ``oracle.accept``
   in full, NaN ordering included.
@@ -118,12 +119,18 @@ def row_is_bad(x: np.ndarray) -> bool:
     return not np.isfinite(np.max(x))
 
 
+def temp_scale(T) -> np.float32:
+    """c = K / T, one float32 division."""
+    with np.errstate(over="ignore", divide="ignore"):
+        return K_LOG2E_16 / np.float32(T)
+
+
 def weights(x: np.ndarray, T: float) -> np.ndarray:
     """Integer weights W (int64) of one float32 row at temperature T > 0."""
     Bt = np.array(exp_table(), dtype=np.int64)
     x = np.asarray(x, dtype=np.float32)
     m = np.max(x)
-    c = K_LOG2E_16 / np.float32(T)  # float32 division
+    c = temp_scale(T)
     with np.errstate(invalid="ignore", over="ignore"):
         u = (m - x) * c  # float32 subtraction and product
     W = np.zeros(x.shape, dtype=np.int64)
@@ -209,7 +216,7 @@ def accept_sampling(B, gamma, target_rows, draft_rows, dtype, cu_seqlens, drafts
             while c < l - 1 and drafts[r, c] == am[c]:
                 c += 1
             tok = int(am[c])
-        elif not (T > 0.0 and np.isfinite(T)):
+        elif not (T > 0.0 and np.isfinite(T) and np.isfinite(temp_scale(T))):
             status |= DATA_BAD_CONF
             continue
         else:

@@ -235,11 +235,20 @@ def test_bad_data_falls_back():
     lens = np.array([4, 2, 3, 1, 4])
     cu, tgt, drf, drafts, ra, rs = _batch(rng, B, gamma, V, lens)
     temps = np.array([1.0, -1.0, 1.0, np.nan, 0.0], np.float32)
+    # a scale K / T that overflows float32 is out of domain too; just above
+    # it, the row's maximum keeps the full weight
+    tiny = np.float32(1e-34)
+    assert not np.isfinite(S.temp_scale(tiny)) and np.isfinite(S.temp_scale(np.float32(3e-34)))
+    assert S.weights(np.array([0.0, -1e-30], np.float32), np.float32(3e-34))[0] == 2**31
     tgt[cu[2] + 1, 3] = np.inf  # request 2's second row
     tgt[cu[4], 5] = np.nan  # greedy request: NaN is an ordinary (largest) value
     res = S.accept_sampling(B, gamma, tgt, drf, "f32", cu, drafts, temps, ra, rs,
                             prefix_lens=np.full(B, 10))
     assert res["status"] == S.DATA_BAD_LOGITS | oracle.DATA_BAD_CONF
+    t2 = temps.copy()
+    t2[1] = tiny
+    res2 = S.accept_sampling(B, gamma, tgt, drf, "f32", cu, drafts, t2, ra, rs)
+    assert res2["status"] == res["status"] and res2["bonus"][1] == -1
     for r in (1, 2, 3):
         assert res["num_correct"][r] == 0 and res["bonus"][r] == -1 and res["commit"][r] == 0
         assert res["new_seq"][r] == 10 and (res["out_tokens"][r] == -1).all()
