@@ -39,130 +39,19 @@
 //
 // The partials are fully rewritten by every call, so the workspace needs no
 // initialization and holds no state between calls.
+#include "argmax_unit.h"
 #include "common.h"
 
 namespace dspark {
 
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kWaves = kAccThreads / kWave;
-
-// Reinterpret a dword as two 16-bit lanes. The dword is taken by value: with
-// this toolchain, __builtin_bit_cast applied directly to an ext_vector element
-// (d[j][w]) reads element 0 of the vector whatever the subscript.
-__device__ inline i16x2 as_i16x2(unsigned int x) { return __builtin_bit_cast(i16x2, x); }
-__device__ inline u16x2 as_u16x2(unsigned int x) { return __builtin_bit_cast(u16x2, x); }
-
-// 16-bit order key of two bf16 values packed in one dword (each half
-// independently): larger value -> larger key; -0 == +0; NaN above +inf.
-//   m = sign mask (0xFFFF for negatives); (h ^ (m | 0x8000)) - m maps the
-//   sign-magnitude bits to an order-preserving integer (-0 and +0 both to
-//   0x8000, -inf to 0x0080). Subtracting 0x80 moves -inf to 0 and every NaN to
-//   0xFF01..0xFFFF (wrapping); the final min folds all NaNs onto 0xFF01.
-//   A positive non-NaN h maps to h + 0x7F80.
-__device__ inline unsigned int bf16x2_keys(unsigned int w) {
-  const i16x2 v = __builtin_bit_cast(i16x2, w);
-  const i16x2 m = v >> (i16x2){15, 15};
-  const unsigned int mu = __builtin_bit_cast(unsigned int, m);
-  const unsigned int x = w ^ (mu | 0x80008000u);
-  const u16x2 c = __builtin_bit_cast(u16x2, mu) + (u16x2){0x80, 0x80};
-  u16x2 k = __builtin_bit_cast(u16x2, x) - c;
-  k = __builtin_elementwise_min(k, (u16x2){0xFF01, 0xFF01});
-  return __builtin_bit_cast(unsigned int, k);
-}
-
-// 32-bit order key of a float32 with the same conventions.
-__device__ inline unsigned int f32_key(unsigned int b) {
-  const unsigned int m = (unsigned int)((int)b >> 31);
-  const unsigned int x = b ^ (m | 0x80000000u);
-  const unsigned int k = x - (m + 0x00800000u);
-  return k < 0xFF000001u ? k : 0xFF000001u;
-}
-
-// Partial of a unit: key in the high word, 0xFFFFFFFF - index in the low word,
-// so the maximum is the largest value at the lowest index. 0 = no element.
-__device__ inline unsigned long long pack_best(unsigned int key, unsigned int gidx) {
-  return ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - gidx);
-}
-
-template <typename T>
-__device__ inline T wave_max(T v) {
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const T o = __shfl_xor(v, off, kWave);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
-template <typename T>
-__device__ inline T wave_min(T v) {
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const T o = __shfl_xor(v, off, kWave);
-    v = o < v ? o : v;
-  }
-  return v;
-}
-
-// Exact per-thread (key, lowest index) over this thread's elements of a unit.
-template <dspark_dtype DT>
-__device__ inline unsigned long long exact_thread_best(const u32x4* d, int v0, int v1) {
-  const int tid = threadIdx.x;
-  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
-  unsigned long long best = 0;
-  if constexpr (DT == DSPARK_BF16) {
-    // key << 16 | (0xFFFF - p) with p = j * 8 + element: the in-thread order
-    unsigned int b32 = 0;
-#pragma unroll
-    for (int j = 0; j < kAccVecsPerThread; ++j) {
-      if (v0 + j * kAccThreads + tid < v1) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const unsigned int k = bf16x2_keys(d[j][w]);
-          const unsigned int p = (unsigned int)(j * 8 + w * 2);
-          const unsigned int lo = (k << 16) | (0xFFFFu - p);
-          const unsigned int hi = (k & 0xFFFF0000u) | (0xFFFFu - (p + 1));
-          b32 = max(b32, max(lo, hi));
-        }
-      }
-    }
-    if (b32) {
-      const unsigned int p = 0xFFFFu - (b32 & 0xFFFFu);
-      const unsigned int v = (unsigned int)(v0 + (int)(p >> 3) * kAccThreads + tid);
-      best = pack_best(b32 >> 16, v * kEpv + (p & 7u));
-    }
-  } else {
-    unsigned long long b64 = 0;
-#pragma unroll
-    for (int j = 0; j < kAccVecsPerThread; ++j) {
-      if (v0 + j * kAccThreads + tid < v1) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const unsigned int p = (unsigned int)(j * 4 + w);
-          const unsigned long long c =
-              ((unsigned long long)f32_key(d[j][w]) << 32) | (0xFFFFFFFFu - p);
-          b64 = c > b64 ? c : b64;
-        }
-      }
-    }
-    if (b64) {
-      const unsigned int p = 0xFFFFFFFFu - (unsigned int)(b64 & 0xFFFFFFFFu);
-      const unsigned int v = (unsigned int)(v0 + (int)(p >> 2) * kAccThreads + tid);
-      best = pack_best((unsigned int)(b64 >> 32), v * kEpv + (p & 3u));
-    }
-  }
-  return best;
-}
+using namespace argmax;
 
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kAccThreads) void accept_argmax_kernel(AcceptArgs a) {
-  __shared__ int s_max[kWaves];
-  __shared__ unsigned int s_idx[kWaves];
-  __shared__ unsigned long long s_best[kWaves];
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  __shared__ UnitSmem sm;
+  const int tid = threadIdx.x;
   const int total = a.fixed_rows >= 0 ? a.fixed_rows : a.cu[a.B];
   const int total_eff = min(max(total, 0), a.max_rows);
   if (blockIdx.x == 0 && tid == 0) {
@@ -176,7 +65,6 @@ __global__ __launch_bounds__(kAccThreads) void accept_argmax_kernel(AcceptArgs a
   const u32x4* rp = reinterpret_cast<const u32x4*>(a.logits + (size_t)row * a.ld_bytes);
   const int v0 = chunk * a.chunk_vecs;
   const int v1 = min(v0 + a.chunk_vecs, a.nvec);
-  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
 
   u32x4 d[kAccVecsPerThread];
 #pragma unroll
@@ -187,86 +75,10 @@ __global__ __launch_bounds__(kAccThreads) void accept_argmax_kernel(AcceptArgs a
     if (v < v1) d[j] = __builtin_nontemporal_load(rp + v);
   }
 
-  unsigned long long best = 0;
-  bool exact = true;
-  if constexpr (DT == DSPARK_BF16) {
-    // fast path: raw signed-16 max and NaN detection
-    i16x2 mi = (i16x2){(short)0x8000, (short)0x8000};
-    u16x2 mu = (u16x2){0, 0};
-#pragma unroll
-    for (int j = 0; j < kAccVecsPerThread; ++j) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const unsigned int x = d[j][w];
-        mi = __builtin_elementwise_max(mi, as_i16x2(x));
-        mu = __builtin_elementwise_max(mu, as_u16x2(x));
-      }
-    }
-    const int lm = max((int)mi[0], (int)mi[1]);
-    const int lu = max((int)mu[0], (int)mu[1]);
-    // positive NaN: raw value above +inf (0x7F80); negative NaN: above 0xFF80 unsigned
-    int v = (lm > 0x7F80 || lu > 0xFF80) ? 0x7FFFFFFF : lm;
-    v = wave_max(v);
-    if (lane == 0) s_max[wave] = v;
-    __syncthreads();
-    int M = s_max[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = max(M, s_max[w]);
-    if (M > 0 && M <= 0x7F80) {  // uniform over the workgroup
-      exact = false;
-      unsigned int cand = 0xFFFFFFFFu;
-      if (lm == M) {
-        // this lane holds the maximum: its first position (lowest j, w, half)
-#pragma unroll
-        for (int j = kAccVecsPerThread - 1; j >= 0; --j) {
-#pragma unroll
-          for (int w = 3; w >= 0; --w) {
-            const unsigned int x = d[j][w];
-            const unsigned int base = (unsigned int)(v0 + j * kAccThreads + tid) * 8u + 2u * w;
-            if ((int)(short)(x >> 16) == M) cand = base + 1u;
-            if ((int)(short)(x & 0xFFFFu) == M) cand = base;
-          }
-        }
-      }
-      cand = wave_min(cand);
-      if (lane == 0) s_idx[wave] = cand;
-      __syncthreads();
-      if (tid == 0) {
-        unsigned int c = s_idx[0];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) c = min(c, s_idx[w]);
-        best = pack_best((unsigned int)M + 0x7F80u, c);
-      }
-    }
-  }
-  if (exact) {  // uniform over the workgroup
-    unsigned long long b = exact_thread_best<DT>(d, v0, v1);
-    b = wave_max(b);
-    if (lane == 0) s_best[wave] = b;
-    __syncthreads();
-    if (tid == 0) {
-      best = s_best[0];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) best = s_best[w] > best ? s_best[w] : best;
-    }
-  }
+  const unsigned long long best =
+      unit_best<DT>(d, v0, v1, a.logits + (size_t)row * a.ld_bytes, a.nvec, a.tail,
+                    chunk == a.chunks - 1, sm);
   if (tid == 0) {
-    // elements after the last whole vector (V * size not a multiple of 16)
-    if (a.tail && chunk == a.chunks - 1) {
-      const unsigned char* row_p = a.logits + (size_t)row * a.ld_bytes;
-      for (int t = 0; t < a.tail; ++t) {
-        const unsigned int gi = (unsigned int)(a.nvec * kEpv + t);
-        unsigned int key;
-        if constexpr (DT == DSPARK_BF16) {
-          key = bf16x2_keys((unsigned int)reinterpret_cast<const unsigned short*>(row_p)[gi]) &
-                0xFFFFu;
-        } else {
-          key = f32_key(reinterpret_cast<const unsigned int*>(row_p)[gi]);
-        }
-        const unsigned long long c = pack_best(key, gi);
-        best = c > best ? c : best;
-      }
-    }
     a.partials[u] = best;
   }
 }

@@ -83,10 +83,11 @@ StsGeom sts_geom(int N, int gamma, int n_t, int n_bins) {
 }
 
 // Workspace of dspark_accept_sampling: a maximum key and a weight sum per
-// (slot, chunk), slots B * (2 * gamma + 1), and one draw job per request.
+// (slot, chunk), slots B * (2 * gamma + 1); two residual sums per (request,
+// chunk); one draw job per request.
 struct SampGeom {
   int chunks, chunk_vecs;
-  size_t part_bytes, bytes;
+  size_t part_bytes, rpart_bytes, bytes;
 };
 
 SampGeom samp_geom(int B, int gamma, int V, dspark_dtype dt) {
@@ -95,8 +96,13 @@ SampGeom samp_geom(int B, int gamma, int V, dspark_dtype dt) {
   g.chunks = (rg.nvec + dspark::kSampChunkVecs - 1) / dspark::kSampChunkVecs;
   if (g.chunks < 1) g.chunks = 1;
   g.chunk_vecs = (rg.nvec + g.chunks - 1) / g.chunks;
+  static_assert((DSPARK_MAX_VOCAB * 4 / 16 + dspark::kSampChunkVecs - 1) / dspark::kSampChunkVecs <=
+                    dspark::kSampMaxChunks,
+                "the draw kernel holds the chunk sums of the longest row in LDS");
   g.part_bytes = align256((size_t)B * (2 * gamma + 1) * g.chunks * sizeof(unsigned long long));
-  g.bytes = 2 * g.part_bytes + align256((size_t)(B > 0 ? B : 1) * sizeof(dspark::SampJob));
+  g.rpart_bytes = align256((size_t)B * g.chunks * 2 * sizeof(unsigned long long));
+  g.bytes = 2 * g.part_bytes + g.rpart_bytes +
+            align256((size_t)(B > 0 ? B : 1) * sizeof(dspark::SampJob));
   return g;
 }
 
@@ -669,7 +675,8 @@ dspark_status dspark_accept_sampling(int32_t B, int32_t gamma, int32_t V, dspark
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   a.kpart = reinterpret_cast<unsigned long long*>(ws);
   a.zpart = reinterpret_cast<unsigned long long*>(ws + sg.part_bytes);
-  a.jobs = reinterpret_cast<dspark::SampJob*>(ws + 2 * sg.part_bytes);
+  a.rpart = reinterpret_cast<unsigned long long*>(ws + 2 * sg.part_bytes);
+  a.jobs = reinterpret_cast<dspark::SampJob*>(ws + 2 * sg.part_bytes + sg.rpart_bytes);
   return launched(dspark::launch_sampling(a, dt, (hipStream_t)stream), fn);
 }
 

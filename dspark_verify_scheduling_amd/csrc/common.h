@@ -171,12 +171,14 @@ struct SampArgs {
   // row r * gamma + k)
   unsigned long long* kpart;  // maximum key with its index
   unsigned long long* zpart;  // weight sum
+  unsigned long long* rpart;  // [B, chunks, 2]: residual member sums of Wp, Wq
   SampJob* jobs;              // [B]
 };
 constexpr int kSampThreads = 256;       // max and weight-sum kernels
 constexpr int kSampVecsPerThread = 8;
 constexpr int kSampChunkVecs = kSampThreads * kSampVecsPerThread;
 constexpr int kSampDrawThreads = 1024;  // draw kernel
+constexpr int kSampMaxChunks = 32;      // chunks of a DSPARK_MAX_VOCAB float32 row
 hipError_t launch_sampling(const SampArgs& a, dspark_dtype dt, hipStream_t s);
 
 // ---------------------------------------------------------------- helpers

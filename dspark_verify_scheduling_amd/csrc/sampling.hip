@@ -38,12 +38,15 @@
 //   samp_decide_kernel: one wave per request: the chain tests, lane k on
 //     draft k + 1, the first rejection by ballot, every output except the
 //     drawn token; a draw job for sampling requests.
-//   samp_draw_kernel: one workgroup per draw job: each wave sums the weights
-//     of a contiguous sixteenth of the row; the sixteenth holding the
-//     crossing point is split over all 1024 threads (a few elements each) and
-//     scanned; the thread holding it walks its elements in order.
+//   samp_rsum_kernel: per (request, chunk) of a residual draw, the sums of
+//     Wp and Wq over the tokens where the residual is positive.
+//   samp_draw_kernel: one workgroup per draw job: the crossing chunk from the
+//     chunk sums (the weight sums for a plain draw), then that chunk split
+//     over all 1024 threads (a few elements each) and scanned; the thread
+//     holding the crossing point walks its elements in order.
 #include <float.h>
 
+#include "argmax_unit.h"
 #include "common.h"
 #include "exp_tables.h"
 
@@ -59,47 +62,35 @@ typedef unsigned __int128 u128;
 constexpr float kLog2e16 = 94548.4609375f;  // float32 nearest to 2^16 log2(e)
 constexpr unsigned int kJmax = 1u << 21;     // from here on the weight is 0
 constexpr int kRedWaves = kSampThreads / kWave;
+static_assert(kSampThreads == kAccThreads && kSampVecsPerThread == kAccVecsPerThread,
+              "the max kernel runs the greedy accept's unit argmax");
 
 __device__ inline float temp_coef(float T) { return __fdiv_rn(kLog2e16, T); }
 
-// The integer weight of x in a row with maximum m (x <= m); Bt is the table
-// in LDS. Branch-free: out-of-range values read entry 0 and are masked.
-__device__ inline unsigned int weight(float x, float m, float c, const unsigned int* Bt) {
+// The integer weight of x in a row with maximum m (x <= m); Bt holds the
+// pairs (B[h], B[h] - B[h+1]) in LDS. Branch-free: a value past the cutoff
+// reads pair 0 and is masked.
+__device__ inline unsigned int weight(float x, float m, float c, const uint2* Bt) {
   const float u = __fmul_rn(__fsub_rn(m, x), c);  // >= 0, or +inf
-  const bool in = u < (float)kJmax;
+  // j = RNE(u) < 2^21 exactly when u < 2^21 - 1/2 (a tie at it rounds up, to even)
+  const bool ok = u < 2097151.5f;
   // adding 1.5 * 2^23 rounds u in [0, 2^22) to the nearest integer (ties to
-  // even) and leaves it in the low mantissa bits
-  const unsigned int j = __float_as_uint(__fadd_rn(in ? u : 0.0f, 12582912.0f)) & 0x3FFFFFu;
-  const bool ok = in && j < kJmax;
-  const unsigned int n = (j >> 16) & 31u, h = (j >> 8) & 255u, r = j & 255u;
-  const unsigned int b0 = Bt[h], b1 = Bt[h + 1];
-  const unsigned int d = (b0 - b1) & 0xFFFFFFu;  // < 2^23; the mask admits the 24-bit multiplier
-  const unsigned int y = b0 - ((d * r + 128u) >> 8);
+  // even) and leaves it in the low 22 mantissa bits: j = bits & 0x3FFFFF
+  const unsigned int bits = __float_as_uint(__fadd_rn(ok ? u : 0.0f, 12582912.0f));
+  const unsigned int n = __builtin_amdgcn_ubfe(bits, 16, 6);  // j >> 16 (0x4B40 >> 0 & 63 = 0)
+  const unsigned int h = __builtin_amdgcn_ubfe(bits, 8, 8);
+  const unsigned int r = bits & 255u;
+  const uint2 bd = Bt[h];
+  const unsigned int y = bd.x - (((unsigned int)__umul24(bd.y, r) + 128u) >> 8);
   const unsigned int w = (y + ((1u << n) >> 1)) >> n;
   return ok ? w : 0u;
 }
 
-__device__ inline void load_table(unsigned int* Bt) {
-  for (int i = threadIdx.x; i < kExp2Len; i += blockDim.x) Bt[i] = kExp2B[i];
+__device__ inline void load_table(uint2* Bt) {
+  for (int i = threadIdx.x; i < kExp2Len - 1; i += blockDim.x) {
+    Bt[i] = make_uint2(kExp2B[i], kExp2B[i] - kExp2B[i + 1]);
+  }
 }
-
-// 32-bit order key: larger value -> larger key, -0 == +0, +inf -> 0xFF000000,
-// every NaN -> 0xFF000001, -inf -> 0.
-__device__ inline unsigned int f32_key(unsigned int b) {
-  const unsigned int m = (unsigned int)((int)b >> 31);
-  const unsigned int x = b ^ (m | 0x80000000u);
-  const unsigned int k = x - (m + 0x00800000u);
-  return k < 0xFF000001u ? k : 0xFF000001u;
-}
-
-// The float of a non-NaN key (both zeros decode to +0).
-__device__ inline float key_value(unsigned int k) {
-  return __uint_as_float(k >= 0x7F800000u ? k - 0x7F800000u : ~(k + 0x007FFFFFu));
-}
-
-// A row is unusable for sampling when its maximum is NaN or +inf (a NaN
-// anywhere ranks highest) or -inf (no finite element).
-__device__ inline bool key_bad(unsigned int k) { return k >= 0xFF000000u || k == 0u; }
 
 template <dspark_dtype DT>
 __device__ inline float elem(const unsigned char* row, int i) {
@@ -125,28 +116,15 @@ __device__ inline void widen(const u32x4& d, float* x) {
   }
 }
 
-__device__ inline unsigned long long pack_best(unsigned int key, unsigned int idx) {
-  return ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - idx);
-}
-
-__device__ inline int best_index(unsigned long long b) {
-  return (int)(0xFFFFFFFFu - (unsigned int)b);
-}
-
-__device__ inline unsigned long long wave_max_u64(unsigned long long v) {
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const unsigned long long o = __shfl_xor(v, off, kWave);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
 __device__ inline unsigned long long wave_sum_u64(unsigned long long v) {
   for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
   return v;
 }
 
-__device__ inline bool is_sampling_temp(float T) { return T > 0.0f && T <= FLT_MAX; }
+// A sampling temperature: positive, finite, and with a finite scale K / T.
+__device__ inline bool is_sampling_temp(float T) {
+  return T > 0.0f && T <= FLT_MAX && temp_coef(T) <= FLT_MAX;
+}
 
 // What a slot is: its row, whether a request reads it, whether it needs the
 // weight sum, and the temperature of the request.
@@ -181,9 +159,8 @@ __device__ inline Slot resolve_slot(const SampArgs& a, int slot) {
 
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kSampThreads) void samp_max_kernel(SampArgs a) {
-  __shared__ unsigned long long s_red[kRedWaves];
-  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  __shared__ argmax::UnitSmem sm;
+  const int tid = threadIdx.x;
   if (blockIdx.x == 0 && tid == 0) {
     a.meta[0] = a.cu[a.B];
     a.meta[1] = 0;
@@ -198,39 +175,18 @@ __global__ __launch_bounds__(kSampThreads) void samp_max_kernel(SampArgs a) {
 #pragma unroll
   for (int i = 0; i < kSampVecsPerThread; ++i) {
     const int v = v0 + i * kSampThreads + tid;
-    d[i] = v < v1 ? __builtin_nontemporal_load(rv + v) : (u32x4){0, 0, 0, 0};
+    // -0.0 fill: below any positive value, never a NaN
+    d[i] = (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    if (v < v1) d[i] = __builtin_nontemporal_load(rv + v);
   }
-  unsigned long long best = 0;
-  if (ch == a.chunks - 1 && tid < a.tail) {
-    const int i = a.nvec * kEpv + tid;
-    best = pack_best(f32_key(__float_as_uint(elem<DT>(s.row, i))), i);
-  }
-#pragma unroll
-  for (int i = 0; i < kSampVecsPerThread; ++i) {
-    const int v = v0 + i * kSampThreads + tid;
-    if (v < v1) {
-      float x[kEpv];
-      widen<DT>(d[i], x);
-#pragma unroll
-      for (int e = 0; e < kEpv; ++e) {
-        const unsigned long long b = pack_best(f32_key(__float_as_uint(x[e])), v * kEpv + e);
-        best = b > best ? b : best;
-      }
-    }
-  }
-  best = wave_max_u64(best);
-  if (lane == 0) s_red[wave] = best;
-  __syncthreads();
-  if (tid == 0) {
-    unsigned long long b = 0;
-    for (int w = 0; w < kRedWaves; ++w) b = s_red[w] > b ? s_red[w] : b;
-    a.kpart[(size_t)slot * a.chunks + ch] = b;
-  }
+  const unsigned long long best =
+      argmax::unit_best<DT>(d, v0, v1, s.row, a.nvec, a.tail, ch == a.chunks - 1, sm);
+  if (tid == 0) a.kpart[(size_t)slot * a.chunks + ch] = best;
 }
 
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kSampThreads) void samp_z_kernel(SampArgs a) {
-  __shared__ unsigned int s_B[kExp2Len];
+  __shared__ uint2 s_B[kExp2Len - 1];
   __shared__ unsigned long long s_red[kRedWaves];
   constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -249,14 +205,14 @@ __global__ __launch_bounds__(kSampThreads) void samp_z_kernel(SampArgs a) {
   load_table(s_B);
   unsigned long long best = 0;
   const unsigned long long* kp = a.kpart + (size_t)slot * a.chunks;
+#pragma unroll 8
   for (int c = 0; c < a.chunks; ++c) best = kp[c] > best ? kp[c] : best;
-  const unsigned int key = (unsigned int)(best >> 32);
   __syncthreads();  // the table
-  if (key_bad(key)) {
+  if (argmax::best_bad<DT>(best)) {
     if (tid == 0) a.zpart[(size_t)slot * a.chunks + ch] = 0;
     return;
   }
-  const float m = key_value(key), c = temp_coef(s.T);
+  const float m = argmax::best_value<DT>(best), c = temp_coef(s.T);
   unsigned long long z = 0;
   if (ch == a.chunks - 1 && tid < a.tail) z = weight(elem<DT>(s.row, a.nvec * kEpv + tid), m, c, s_B);
 #pragma unroll
@@ -282,6 +238,9 @@ __global__ __launch_bounds__(kSampThreads) void samp_z_kernel(SampArgs a) {
 // One wave per request.
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kWave) void samp_decide_kernel(SampArgs a) {
+  __shared__ uint2 s_B[kExp2Len - 1];
+  load_table(s_B);
+  __syncthreads();
   const int r = blockIdx.x, lane = threadIdx.x, G = a.gamma;
   const int total = a.cu[a.B];
   const int total_eff = min(max(total, 0), a.max_rows);
@@ -296,12 +255,14 @@ __global__ __launch_bounds__(kWave) void samp_decide_kernel(SampArgs a) {
   auto key_of = [&](size_t slot) {
     const unsigned long long* p = a.kpart + slot * C;
     unsigned long long b = 0;
+#pragma unroll 8
     for (int c = 0; c < C; ++c) b = p[c] > b ? p[c] : b;
     return b;
   };
   auto z_of = [&](size_t slot) {
     const unsigned long long* p = a.zpart + slot * C;
     unsigned long long z = 0;
+#pragma unroll 8
     for (int c = 0; c < C; ++c) z += p[c];
     return z;
   };
@@ -309,16 +270,20 @@ __global__ __launch_bounds__(kWave) void samp_decide_kernel(SampArgs a) {
   const bool ok = c0 >= 0 && len >= 1 && len <= G + 1 && c0 + len <= total_eff;
   const bool greedy = T == 0.0f;
   const bool samp = is_sampling_temp(T);
+  // this lane's target slot and draft slot, merged once
+  const bool mine_t = ok && (greedy || samp) && lane < len;
+  const bool mine_d = ok && samp && lane < len - 1;
+  const unsigned long long kt = mine_t ? key_of(tslot + lane) : 0;
+  const unsigned long long kd = mine_d ? key_of(dslot + lane) : 0;
+  const unsigned long long zt = mine_t && samp ? z_of(tslot + lane) : 0;
+  const unsigned long long zd = mine_d ? z_of(dslot + lane) : 0;
   if (!ok) {
     status = DSPARK_DATA_BAD_LENS;
   } else if (!greedy && !samp) {
     status = DSPARK_DATA_BAD_CONF;
   } else if (samp) {
-    bool b = false;
-    for (int j = lane; j < len; j += kWave) {  // len can be 65
-      b |= key_bad((unsigned int)(key_of(tslot + j) >> 32));
-      if (j < len - 1) b |= key_bad((unsigned int)(key_of(dslot + j) >> 32));
-    }
+    bool b = (mine_t && argmax::best_bad<DT>(kt)) || (mine_d && argmax::best_bad<DT>(kd));
+    if (len > kWave) b |= argmax::best_bad<DT>(key_of(tslot + kWave));  // the 65th row
     if (__ballot(b)) status = DSPARK_DATA_BAD_LOGITS;
   }
   int32_t* out = a.out_tokens + (size_t)r * (G + 1);
@@ -338,25 +303,30 @@ __global__ __launch_bounds__(kWave) void samp_decide_kernel(SampArgs a) {
   bool pass = false;
   if (lane < len - 1) {
     if (greedy) {
-      pass = dr == best_index(key_of(tslot + lane));
+      pass = dr == argmax::best_index(kt);
     } else if (dr >= 0 && dr < a.V) {
       const float cT = temp_coef(T);
-      const float mp = key_value((unsigned int)(key_of(tslot + lane) >> 32));
-      const float mq = key_value((unsigned int)(key_of(dslot + lane) >> 32));
+      const float mp = argmax::best_value<DT>(kt);
+      const float mq = argmax::best_value<DT>(kd);
       const float xp = elem<DT>(a.tgt + (size_t)(c0 + lane) * a.ld_t, dr);
       const float xq = elem<DT>(a.drf + ((size_t)r * G + lane) * a.ld_q, dr);
-      const unsigned long long wp = weight(xp, mp, cT, kExp2B);
-      const unsigned long long wq = weight(xq, mq, cT, kExp2B);
+      const unsigned long long wp = weight(xp, mp, cT, s_B);
+      const unsigned long long wq = weight(xq, mq, cT, s_B);
       const unsigned int u = a.ra[(size_t)r * G + lane] >> 8;
       // u * wq < 2^55 and wp * Zq < 2^80: both sides below 2^104
-      const u128 lhs = (u128)((unsigned long long)u * wq) * z_of(tslot + lane);
-      const u128 rhs = ((u128)wp * z_of(dslot + lane)) << 24;
+      const u128 lhs = (u128)((unsigned long long)u * wq) * zt;
+      const u128 rhs = ((u128)wp * zd) << 24;
       pass = lhs < rhs;
     }
   }
   const unsigned long long fails = __ballot(lane < len - 1 && !pass);
   const int c = fails ? __builtin_ctzll(fails) : len - 1;
-  const int am_c = greedy ? best_index(key_of(tslot + c)) : 0;
+  // the slot values of lane c (c <= len - 1 <= 64; slot 64 is merged directly)
+  const unsigned long long kt_c = c < kWave ? __shfl(kt, c, kWave) : key_of(tslot + c);
+  const unsigned long long kd_c = __shfl(kd, c < kWave ? c : 0, kWave);
+  const unsigned long long zt_c = c < kWave ? __shfl(zt, c, kWave) : z_of(tslot + c);
+  const unsigned long long zd_c = __shfl(zd, c < kWave ? c : 0, kWave);
+  const int am_c = greedy ? argmax::best_index(kt_c) : 0;
   for (int j = lane; j <= G; j += kWave) {  // G + 1 can be 65 columns
     if (j != c || greedy) out[j] = j == c ? am_c : (j < G ? dr : -1);
   }
@@ -371,10 +341,10 @@ __global__ __launch_bounds__(kWave) void samp_decide_kernel(SampArgs a) {
     jb.word = greedy ? 0u : a.rs[(size_t)r * (G + 1) + c];
     jb.col = c;
     jb.pad = 0;
-    jb.mp = greedy ? 0.0f : key_value((unsigned int)(key_of(tslot + c) >> 32));
-    jb.zp = greedy ? 0ull : z_of(tslot + c);
-    jb.mq = jb.mode == 2 ? key_value((unsigned int)(key_of(dslot + c) >> 32)) : 0.0f;
-    jb.zq = jb.mode == 2 ? z_of(dslot + c) : 0ull;
+    jb.mp = greedy ? 0.0f : argmax::best_value<DT>(kt_c);
+    jb.zp = greedy ? 0ull : zt_c;
+    jb.mq = jb.mode == 2 ? argmax::best_value<DT>(kd_c) : 0.0f;
+    jb.zq = jb.mode == 2 ? zd_c : 0ull;
     a.jobs[r] = jb;
     if (greedy) a.bonus[r] = am_c;
   }
@@ -413,7 +383,7 @@ __device__ inline u128 run_value(const DrawCtx& c, Pair s) {
 }
 
 template <dspark_dtype DT>
-__device__ inline void add_elem(const DrawCtx& c, int i, const unsigned int* Bt, Pair& s) {
+__device__ inline void add_elem(const DrawCtx& c, int i, const uint2* Bt, Pair& s) {
   const unsigned int wp = weight(elem<DT>(c.p, i), c.mp, c.cT, Bt);
   const unsigned int wq = c.resid ? weight(elem<DT>(c.q, i), c.mq, c.cT, Bt) : 0u;
   if (member(c, wp, wq)) {
@@ -422,122 +392,212 @@ __device__ inline void add_elem(const DrawCtx& c, int i, const unsigned int* Bt,
   }
 }
 
-// One workgroup per request with a draw job.
-template <dspark_dtype DT>
-__global__ __launch_bounds__(kSampDrawThreads) void samp_draw_kernel(SampArgs a) {
-  constexpr int kWaves = kSampDrawThreads / kWave;
-  __shared__ unsigned int s_B[kExp2Len];
-  __shared__ Pair s_wsum[kWaves];
-  __shared__ unsigned long long s_scan[kWaves];
-  __shared__ int s_ctl[2];  // residual flag; crossing wave
-  __shared__ u128 s_t;      // threshold left at the start of the crossing wave
-  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int r = blockIdx.x;
-  const SampJob job = a.jobs[r];
-  if (job.mode == 0) return;
-  load_table(s_B);
-  if (tid == 0) s_ctl[0] = job.mode == 2;
-  __syncthreads();
+__device__ inline void set_mode(DrawCtx& c, const SampJob& job, bool resid) {
+  c.resid = resid;
+  c.zp = resid ? job.zp : 0ull;
+  c.zq = resid ? job.zq : 1ull;
+  c.zpd = (double)c.zp;
+  c.zqd = (double)c.zq;
+}
+
+__device__ inline DrawCtx draw_ctx(const SampArgs& a, const SampJob& job, int r) {
   DrawCtx c;
   c.p = a.tgt + (size_t)job.prow * a.ld_t;
   c.mp = job.mp;
   c.cT = temp_coef(a.temps[r]);
   c.q = job.mode == 2 ? a.drf + (size_t)job.qrow * a.ld_q : nullptr;
   c.mq = job.mq;
-  // wave w covers whole vectors [w * per, (w + 1) * per); the last wave also
-  // takes the tail elements
-  const int nvec = a.nvec, V = a.V;
-  const int per = (nvec + kWaves - 1) / kWaves;
-  const int v0 = min(wave * per, nvec), v1 = min(v0 + per, nvec);
+  set_mode(c, job, job.mode == 2);
+  return c;
+}
+
+// Per (request, chunk) of a residual draw: the member sums of Wp and Wq.
+template <dspark_dtype DT>
+__global__ __launch_bounds__(kSampThreads) void samp_rsum_kernel(SampArgs a) {
+  __shared__ uint2 s_B[kExp2Len - 1];
+  __shared__ Pair s_red[kRedWaves];
+  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int r = blockIdx.x / a.chunks, ch = blockIdx.x - r * a.chunks;
+  const SampJob job = a.jobs[r];
+  if (job.mode != 2) return;
+  const DrawCtx c = draw_ctx(a, job, r);
   const u32x4* pv = reinterpret_cast<const u32x4*>(c.p);
   const u32x4* qv = reinterpret_cast<const u32x4*>(c.q);
-  for (;;) {
-    c.resid = s_ctl[0] != 0;
-    c.zp = c.resid ? job.zp : 0ull;
-    c.zq = c.resid ? job.zq : 1ull;
-    c.zpd = (double)c.zp;
-    c.zqd = (double)c.zq;
-    Pair s{0, 0};
-    for (int v = v0 + lane; v < v1; v += kWave) {
-      float x[kEpv], y[kEpv];
-      widen<DT>(__builtin_nontemporal_load(pv + v), x);
-      if (c.resid) {
-        widen<DT>(__builtin_nontemporal_load(qv + v), y);
-      } else {
+  const int v0 = ch * a.chunk_vecs, v1 = min(v0 + a.chunk_vecs, a.nvec);
+  u32x4 dp[kSampVecsPerThread], dq[kSampVecsPerThread];
 #pragma unroll
-        for (int e = 0; e < kEpv; ++e) y[e] = 0.0f;
-      }
+  for (int i = 0; i < kSampVecsPerThread; ++i) {
+    const int v = v0 + i * kSampThreads + tid;
+    dp[i] = v < v1 ? __builtin_nontemporal_load(pv + v) : (u32x4){0, 0, 0, 0};
+    dq[i] = v < v1 ? __builtin_nontemporal_load(qv + v) : (u32x4){0, 0, 0, 0};
+  }
+  load_table(s_B);
+  __syncthreads();
+  Pair s{0, 0};
+  if (ch == a.chunks - 1 && tid < a.tail) add_elem<DT>(c, a.nvec * kEpv + tid, s_B, s);
+#pragma unroll
+  for (int i = 0; i < kSampVecsPerThread; ++i) {
+    if (v0 + i * kSampThreads + tid < v1) {
+      float x[kEpv], y[kEpv];
+      widen<DT>(dp[i], x);
+      widen<DT>(dq[i], y);
 #pragma unroll
       for (int e = 0; e < kEpv; ++e) {
         const unsigned int wp = weight(x[e], c.mp, c.cT, s_B);
-        const unsigned int wq = c.resid ? weight(y[e], c.mq, c.cT, s_B) : 0u;
+        const unsigned int wq = weight(y[e], c.mq, c.cT, s_B);
         if (member(c, wp, wq)) {
           s.a += wp;
           s.b += wq;
         }
       }
     }
-    if (wave == kWaves - 1 && lane < a.tail) add_elem<DT>(c, nvec * kEpv + lane, s_B, s);
-    s.a = wave_sum_u64(s.a);
-    s.b = wave_sum_u64(s.b);
-    if (lane == 0) s_wsum[wave] = s;
-    __syncthreads();
-    if (tid == 0) {
-      Pair tot{0, 0};
-      for (int w = 0; w < kWaves; ++w) {
-        tot.a += s_wsum[w].a;
-        tot.b += s_wsum[w].b;
-      }
-      const u128 S = run_value(c, tot);
-      if (S == 0 && c.resid) {
-        s_ctl[0] = 0;  // p == q at this resolution: draw from p
-        s_ctl[1] = -1;
-      } else {
-        const u128 t = ((u128)(job.word >> 8) * S) >> 24;  // S < 2^98
-        Pair run{0, 0};
-        int w = 0;
-        for (; w < kWaves - 1; ++w) {
-          const Pair nx{run.a + s_wsum[w].a, run.b + s_wsum[w].b};
-          if (run_value(c, nx) > t) break;
-          run = nx;
+  }
+  s.a = wave_sum_u64(s.a);
+  s.b = wave_sum_u64(s.b);
+  if (lane == 0) s_red[wave] = s;
+  __syncthreads();
+  if (tid == 0) {
+    Pair t{0, 0};
+    for (int w = 0; w < kRedWaves; ++w) {
+      t.a += s_red[w].a;
+      t.b += s_red[w].b;
+    }
+    a.rpart[((size_t)r * a.chunks + ch) * 2] = t.a;
+    a.rpart[((size_t)r * a.chunks + ch) * 2 + 1] = t.b;
+  }
+}
+
+// One workgroup per request with a draw job: the crossing chunk from the
+// per-chunk sums (residual: samp_rsum_kernel; plain: the weight sums of the
+// target slot), then the chunk's elements split over the threads, scanned,
+// and walked by the thread holding the crossing point.
+template <dspark_dtype DT>
+__global__ __launch_bounds__(kSampDrawThreads) void samp_draw_kernel(SampArgs a) {
+  constexpr int kWaves = kSampDrawThreads / kWave;
+  __shared__ uint2 s_B[kExp2Len - 1];
+  __shared__ unsigned long long s_scan[kWaves];
+  __shared__ int s_ctl[2];  // residual flag; crossing chunk
+  __shared__ u128 s_t;      // threshold left at the start of the crossing chunk
+  __shared__ Pair s_rs[kSampMaxChunks];            // residual chunk sums
+  __shared__ unsigned long long s_zs[kSampMaxChunks];  // plain chunk sums
+  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x, C = a.chunks;
+  const SampJob job = a.jobs[r];
+  if (job.mode == 0) return;
+  load_table(s_B);
+  DrawCtx c = draw_ctx(a, job, r);
+  if (tid < C) {  // one load per thread, not a chain of them in one thread
+    s_zs[tid] = a.zpart[((size_t)r * (a.gamma + 1) + job.col) * C + tid];
+    if (job.mode == 2) {
+      s_rs[tid].a = a.rpart[((size_t)r * C + tid) * 2];
+      s_rs[tid].b = a.rpart[((size_t)r * C + tid) * 2 + 1];
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    bool resid = job.mode == 2;
+    // the chunk sums of the draw's weights
+    auto chunk_pair = [&](int ch, bool res) { return res ? s_rs[ch] : Pair{s_zs[ch], 0ull}; };
+    Pair tot{0, 0};
+    for (int ch = 0; ch < C; ++ch) {
+      const Pair q = chunk_pair(ch, resid);
+      tot.a += q.a;
+      tot.b += q.b;
+    }
+    if (resid && run_value(c, tot) == 0) {  // p == q at this resolution: draw from p
+      resid = false;
+      set_mode(c, job, false);
+      tot = Pair{0, 0};
+      for (int ch = 0; ch < C; ++ch) tot.a += s_zs[ch];
+    }
+    const u128 t = ((u128)(job.word >> 8) * run_value(c, tot)) >> 24;  // the total < 2^98
+    Pair run{0, 0};
+    int ch = 0;
+    for (; ch < C - 1; ++ch) {
+      const Pair q = chunk_pair(ch, resid);
+      const Pair nx{run.a + q.a, run.b + q.b};
+      if (run_value(c, nx) > t) break;
+      run = nx;
+    }
+    s_ctl[0] = resid;
+    s_ctl[1] = ch;
+    s_t = t - run_value(c, run);
+  }
+  __syncthreads();
+  set_mode(c, job, s_ctl[0] != 0);
+  const int ch = s_ctl[1];
+  // read before the scans' barriers: the crossing thread rewrites s_ctl and s_t
+  const u128 t = s_t;
+  // level 2: the crossing chunk, whole vectors in contiguous runs of `vpt`
+  // per thread; the last thread also takes the tail elements
+  const int vv0 = ch * a.chunk_vecs, vv1 = min(vv0 + a.chunk_vecs, a.nvec);
+  const int vpt = (vv1 - vv0 + kSampDrawThreads - 1) / kSampDrawThreads;  // <= 2
+  const int my0 = min(vv0 + tid * vpt, vv1), my1 = min(my0 + vpt, vv1);
+  const u32x4* pv = reinterpret_cast<const u32x4*>(c.p);
+  const u32x4* qv = reinterpret_cast<const u32x4*>(c.q);
+  u32x4 dp[2], dq[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int v = my0 + k;
+    dp[k] = v < my1 ? pv[v] : (u32x4){0, 0, 0, 0};
+    dq[k] = v < my1 && c.resid ? qv[v] : (u32x4){0, 0, 0, 0};
+  }
+  const bool last = tid == kSampDrawThreads - 1;
+  const int t0 = a.nvec * kEpv;  // first tail element
+  const bool has_tail = last && ch == C - 1 && a.tail > 0;
+  Pair mine{0, 0};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    if (my0 + k < my1) {
+      float x[kEpv], y[kEpv];
+      widen<DT>(dp[k], x);
+      widen<DT>(dq[k], y);
+#pragma unroll
+      for (int e = 0; e < kEpv; ++e) {
+        const unsigned int wp = weight(x[e], c.mp, c.cT, s_B);
+        const unsigned int wq = c.resid ? weight(y[e], c.mq, c.cT, s_B) : 0u;
+        if (member(c, wp, wq)) {
+          mine.a += wp;
+          mine.b += wq;
         }
-        s_ctl[1] = w;
-        s_t = t - run_value(c, run);
       }
     }
-    __syncthreads();
-    if (s_ctl[1] >= 0) break;
   }
-  // the crossing wave's elements [e0, e1), a contiguous run of `each` per thread
-  const int ws = s_ctl[1];
-  const int e0 = min(ws * per, nvec) * kEpv;
-  const int e1 = ws == kWaves - 1 ? V : min(ws * per + per, nvec) * kEpv;
-  const int each = (e1 - e0 + kSampDrawThreads - 1) / kSampDrawThreads;
-  const int l0 = min(e0 + tid * each, e1), l1 = min(l0 + each, e1);
-  Pair mine{0, 0};
-  for (int i = l0; i < l1; ++i) add_elem<DT>(c, i, s_B, mine);
+  if (has_tail) {
+    for (int i = t0; i < a.V; ++i) add_elem<DT>(c, i, s_B, mine);
+  }
   unsigned long long tot_a, tot_b;
   const unsigned long long ea =
       block_excl_scan<unsigned long long, kSampDrawThreads>(mine.a, s_scan, &tot_a);
   const unsigned long long eb =
       block_excl_scan<unsigned long long, kSampDrawThreads>(mine.b, s_scan, &tot_b);
-  const u128 t = s_t;
   const u128 before = run_value(c, Pair{ea, eb});
   const u128 after = run_value(c, Pair{ea + mine.a, eb + mine.b});
-  // exactly one thread has before <= t < after
-  if (!(before <= t && t < after)) return;
-  Pair run{ea, eb};
-  int tok = l1 - 1;
-  for (int i = l0; i < l1; ++i) {
-    add_elem<DT>(c, i, s_B, run);
-    if (run_value(c, run) > t) {
-      tok = i;
-      break;
-    }
+  // exactly one thread has before <= t < after: it hands its element range
+  // and what is left of t to wave 0
+  if (before <= t && t < after) {
+    s_ctl[0] = my0 * kEpv;
+    s_ctl[1] = has_tail ? a.V : my1 * kEpv;
+    s_t = t - before;
   }
-  a.bonus[r] = tok;
-  a.out_tokens[(size_t)r * (a.gamma + 1) + job.col] = tok;
+  __syncthreads();
+  if (tid >= kWave) return;
+  // level 3: one element per lane (at most 2 vectors plus the tail: < 64)
+  const int i = s_ctl[0] + tid;
+  const bool in = i < s_ctl[1];
+  const unsigned int wp = in ? weight(elem<DT>(c.p, i), c.mp, c.cT, s_B) : 0u;
+  const unsigned int wq = in && c.resid ? weight(elem<DT>(c.q, i), c.mq, c.cT, s_B) : 0u;
+  const bool mem = in && member(c, wp, wq);
+  const unsigned long long ia = wave_incl_scan_op(mem ? (unsigned long long)wp : 0ull, 0ull, OpAdd{});
+  const unsigned long long ib = wave_incl_scan_op(mem ? (unsigned long long)wq : 0ull, 0ull, OpAdd{});
+  const unsigned long long cross = __ballot(in && run_value(c, Pair{ia, ib}) > s_t);
+  if (tid == 0) {
+    const int tok = s_ctl[0] + (cross ? __builtin_ctzll(cross) : 0);
+    a.bonus[r] = tok;
+    a.out_tokens[(size_t)r * (a.gamma + 1) + job.col] = tok;
+  }
 }
 
 template <dspark_dtype DT>
@@ -551,6 +611,10 @@ hipError_t launch_dt(const SampArgs& a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(samp_decide_kernel<DT>, dim3(a.B), dim3(kWave), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(samp_rsum_kernel<DT>, dim3((unsigned)(a.B * a.chunks)), dim3(kSampThreads), 0,
+                     s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(samp_draw_kernel<DT>, dim3(a.B), dim3(kSampDrawThreads), 0, s, a);
