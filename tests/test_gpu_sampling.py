@@ -163,6 +163,25 @@ def test_sampling_edge_cases():
     both(c, "empty request")
     c = rand_case(14, 6, 3, 256, dv.F32)
     both(c, "max_rows below the total", max_rows=int(c["cu"][-1]) - 2)
+    # overlapping packed ranges (cu not increasing): requests 0 and 2 are each
+    # well formed but share rows 3 and 4 at different temperatures; request 1
+    # is malformed. Each valid request is decided at its own temperature.
+    c = rand_case(16, 3, 5, 333, dv.BF16, greedy_frac=0.0)
+    c["cu"] = np.array([0, 5, 3, 8], np.int32)
+    if c["tgt"].shape[0] < 8:
+        c["tgt"] = np.concatenate([c["tgt"]] * 4)[:10]
+    c["temps"] = np.array([0.6, 1.0, 1.7], np.float32)
+    got, ref = both(c, "overlapping ranges")
+    assert ref["status"] == oracle.DATA_BAD_LENS and got["bonus"][0] >= 0 and got["bonus"][2] >= 0
+    # a draw whose crossing point lies among the tail elements: all the mass
+    # of the last target row on its final element (V = 4099 bf16: 3 tail elements)
+    c = rand_case(17, 4, 3, 4099, dv.BF16, greedy_frac=0.0)
+    for r in range(4):
+        last = c["cu"][r + 1] - 1
+        row = np.full(4099, -60.0, np.float32)
+        row[4098] = 5.0
+        c["tgt"][last] = gen.f32_to_bf16_bits(row)
+    got, _ = both(c, "tail draw")
     # no requests
     c = rand_case(15, 1, 3, 256, dv.F32)
     got = run_gpu(0, 3, 256, dv.F32, c["tgt"][:4], np.zeros((0, 256), np.float32),
