@@ -36,7 +36,9 @@ sys.path.insert(0, str(ROOT))
 PEAK_HBM_GBS = 8000.0
 METRIC = "plan+accept steps/s and logit-pass HBM GB/s (% peak) at B=256,γ=8,V=129280"
 TRAFFIC_FILE = ROOT / "profiles" / "accept_b256_g8_v129280_bf16_traffic.json"
-ACCEPT_SRC = ROOT / "dspark_verify_scheduling_amd" / "csrc" / "accept.hip"
+# the greedy accept kernels: accept.hip and the unit argmax it includes
+ACCEPT_SRCS = [ROOT / "dspark_verify_scheduling_amd" / "csrc" / n
+               for n in ("accept.hip", "argmax_unit.h")]
 
 
 def parse():
@@ -72,8 +74,8 @@ def traffic_for(total_rows):
     if not TRAFFIC_FILE.exists():
         return None
     rec = json.loads(TRAFFIC_FILE.read_text())
-    src_hash = hashlib.sha256(ACCEPT_SRC.read_bytes()).hexdigest()
-    if rec.get("accept_hip_sha256") != src_hash or rec.get("rows") != total_rows:
+    src_hash = hashlib.sha256(b"".join(p.read_bytes() for p in ACCEPT_SRCS)).hexdigest()
+    if rec.get("accept_src_sha256") != src_hash or rec.get("rows") != total_rows:
         return None
     return rec.get("bytes_per_launch")
 
