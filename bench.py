@@ -516,7 +516,10 @@ def main():
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_for(total),
                      "kernel": "dspark_accept: accept_argmax_kernel<bf16> then accept_finalize_kernel",
                      "bytes_per_launch": acc_bytes,
-                     "mean_us": acc_mean_us},
+                     "mean_us": acc_mean_us,
+                     "p10_us": float(np.percentile(acc_us, 10)),
+                     "p50_us": float(np.percentile(acc_us, 50)),
+                     "p90_us": float(np.percentile(acc_us, 90))},
         "cpu_baseline": cpu,
         "steps_per_s_graph": 1e3 / ms_step_graph,
         "ms_per_step_graph": ms_step_graph,
