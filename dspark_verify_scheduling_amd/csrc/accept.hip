@@ -25,7 +25,8 @@
 //    first position. Otherwise the unit is redone exactly from the same
 //    registers with a total-order key (NaN highest, -0 == +0, lowest index
 //    wins). Each unit writes one 64-bit (key, index) partial. The kernel has
-//    no atomics and no cross-workgroup waits.
+//    no atomics and no cross-workgroup waits. The per-unit argmax lives in
+//    argmax_unit.h, which the sampling accept's maximum pass shares.
 // 2. accept_finalize_kernel: one wave per request merges its rows' partials,
 //    counts the leading matches with a ballot, and writes the outputs; a
 //    grid-stride pass writes the row argmax of every packed row.
