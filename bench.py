@@ -68,13 +68,26 @@ def accept_bytes(total, B, gamma, V, esize):
     return logits + inputs + outputs
 
 
+def code_hash(paths):
+    """sha256 of C++ sources with // comments and blank lines removed, so that
+    a comment edit does not invalidate counters taken on the same code."""
+    import re
+    h = hashlib.sha256()
+    for p in paths:
+        for line in p.read_text().splitlines():
+            line = re.sub(r"//.*$", "", line).rstrip()
+            if line:
+                h.update(line.encode() + b"\n")
+    return h.hexdigest()
+
+
 def traffic_for(total_rows):
     """HBM bytes per accept launch from committed rocprofv3 counter runs, if
     they were taken on the current kernel source."""
     if not TRAFFIC_FILE.exists():
         return None
     rec = json.loads(TRAFFIC_FILE.read_text())
-    src_hash = hashlib.sha256(b"".join(p.read_bytes() for p in ACCEPT_SRCS)).hexdigest()
+    src_hash = code_hash(ACCEPT_SRCS)
     if rec.get("accept_src_sha256") != src_hash or rec.get("rows") != total_rows:
         return None
     return rec.get("bytes_per_launch")
