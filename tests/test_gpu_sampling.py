@@ -283,3 +283,35 @@ def test_sampling_graph_replay_matches_eager():
         torch.cuda.synchronize()
     # and the words mattered: the four expected results are not all equal
     assert any(not torch.equal(expect[0][1], e[1]) for e in expect[1:])
+
+
+@pytest.mark.parametrize("cfg,n_check", [(4, 24), (1, 8)])
+def test_sampling_full_size_other_workloads(cfg, n_check):
+    """cfg4 (gamma = 16, V = 129280 bf16, its own draft logits, random verify
+    lengths) and cfg1 (f32, V = 32000, planned lengths) at full size; the
+    oracle checks n_check requests."""
+    w = gen.make(cfg)
+    if cfg == 4:
+        rng = np.random.default_rng(4)
+        lens = rng.integers(1, w.gamma + 2, w.B)  # a spread of verify lengths
+    else:
+        p = oracle.plan(w.B, w.gamma, oracle.IN_CONF_LOGITS, w.conf, w.temps, w.min_len,
+                        w.max_len, w.eps, w.b_lo, w.b_hi, w.bias, w.alpha, w.theta)
+        lens = p["verify_lens"]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tgt = np.concatenate([w.target[r, :lens[r]] for r in range(w.B)])
+    ex = gen.sampling_extras(w, greedy_frac=0.1)
+    drf = ex.draft_logits.reshape(w.B * w.gamma, w.V)
+    dt = dv.BF16 if w.dtype == "bf16" else dv.F32
+    got = run_gpu(w.B, w.gamma, w.V, dt, tgt, drf, cu, w.drafts, ex.temps, ex.rand_accept,
+                  ex.rand_sample, w.prefix_lens, tag=f"cfg{cfg} full")
+    assert got["meta"].tolist() == [int(cu[-1]), 0]
+    reqs = np.sort(np.random.default_rng(cfg).choice(w.B, n_check, replace=False))
+    sub_cu = np.concatenate([[0], np.cumsum(lens[reqs])]).astype(np.int32)
+    sub_tgt = np.concatenate([tgt[cu[r]:cu[r + 1]] for r in reqs])
+    sub_drf = np.concatenate([drf[r * w.gamma:(r + 1) * w.gamma] for r in reqs])
+    ref = S.accept_sampling(len(reqs), w.gamma, sub_tgt, sub_drf, w.dtype, sub_cu, w.drafts[reqs],
+                            ex.temps[reqs], ex.rand_accept[reqs], ex.rand_sample[reqs],
+                            prefix_lens=w.prefix_lens[reqs])
+    check(got, ref, None, reqs=reqs)
+    say(f"cfg{cfg}: mean correct {got['num_correct'].mean():.3f}, {cu[-1]} rows")
