@@ -192,23 +192,6 @@ __global__ __launch_bounds__(kTvThreads) void tv_kernel(TvArgs a) {
   if (tid == 0) a.a_out[pair] = total > 1.0f ? 1.0f : total;
 }
 
-// Resident variant: the pair stays on the CU between the passes, so every
-// logit is read from HBM once. Vector pair v (16 bytes of q and of p) lives
-//   in registers of thread v % 1024 (slot v / 1024) for v < 11 * 1024, and
-//   in LDS for the rest (q at i, p at n_lds + i, i = v - 11 * 1024),
-// which holds rows of up to 11 * 1024 + 4992 vectors (bf16 V <= 130055):
-// 88 VGPRs and up to 156 KB of LDS, so one workgroup per CU. The LDS part and
-// register slots 8..10 are requested first, slots 0..7 as soon as the LDS
-// part is stored (which keeps the live registers under the 128 a 1024-thread
-// workgroup allows); the pass-1 statistics are accumulated as data arrives,
-// and pass 2 reads only registers and LDS. Longer rows take the two-pass
-// streaming kernel above.
-constexpr int kResRegSlots = 11;
-constexpr int kResLdsSlots = 5;
-constexpr int kResRegSpan = kResRegSlots * kTvThreads;
-constexpr int kResLdsMaxPairs = 4992;  // 2 * 4992 * 16 B = 156 KB
-constexpr int kEarly = 8;  // register slots kEarly.. are requested with the LDS part
-
 // One row's 16 bytes into its running statistics.
 template <dspark_dtype DT>
 __device__ inline void stat_add_vec(Stat& st, const u32x4& d) {
@@ -242,113 +225,242 @@ __device__ inline float min_sum_pair(const u32x4& dq, const u32x4& dp, float aq,
   return s0 + s1;
 }
 
-template <dspark_dtype DT>
+// Direct global-to-LDS copy of one wave's 64 x 16 bytes: lane l's vector
+// src[l] lands at dst[l], without passing through registers. src and dst are
+// wave-uniform (SGPR base address, the lane's byte offset in a VGPR); M0 holds
+// dst's LDS byte address (one wait state before the load reads it; nothing
+// else in these kernels uses M0, so it is not saved). Written
+// as inline assembly so that the compiler's wait-count bookkeeping does not
+// see it: its waits for the register loads stay exact positions in the load
+// queue (the copies only make them more conservative), and the callers wait
+// for the copies themselves (vmcnt(0) and a barrier) before reading the LDS.
+__device__ inline void lds_dma16(const u32x4* src, u32x4* dst, unsigned int lane_bytes) {
+  const unsigned int lds_addr = (unsigned int)(size_t)(__attribute__((address_space(3))) void*)dst;
+  const unsigned long long g = (unsigned long long)src;
+  const unsigned long long g_uniform =
+      ((unsigned long long)(unsigned int)__builtin_amdgcn_readfirstlane((int)(g >> 32)) << 32) |
+      (unsigned int)__builtin_amdgcn_readfirstlane((int)(unsigned int)g);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(lane_bytes), "s"(g_uniform), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+
+__device__ inline void pair_rows(const TvArgs& a, int pair, const u32x4*& qv, const u32x4*& pv) {
+  const int r = pair / a.gamma;
+  const int k0 = pair - r * a.gamma;
+  qv = reinterpret_cast<const u32x4*>(a.q + (size_t)pair * a.ldq_bytes);
+  pv = reinterpret_cast<const u32x4*>(a.p + ((size_t)r * a.rows_per_req + k0) * a.ldp_bytes);
+}
+
+struct OpMaxF {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+// Wave-wide merge of a Stat on DPP lane exchanges (no LDS, no address
+// registers); the result is uniform over the wave.
+__device__ inline Stat wave_stat(Stat st) {
+  const float m = read_lane(wave_incl_scan_op(st.mL, -FLT_MAX, OpMaxF{}), kWave - 1);
+  const float s = read_lane(wave_incl_scan_op(st.s * exp2_raw(st.mL - m), 0.0f, OpAdd{}), kWave - 1);
+  return {m, s};
+}
+
+__device__ inline float wave_total(float v) {
+  return read_lane(wave_incl_scan_op(v, 0.0f, OpAdd{}), kWave - 1);
+}
+
+// Both rows' statistics merged over the workgroup in one round: each wave
+// merges its lanes', lane w of every wave then reads wave w's and merges
+// those. Every thread returns with the workgroup's statistics.
+__device__ inline void block_stat2(Stat& sq, Stat& sp, float4* ws) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  sq = wave_stat(sq);
+  sp = wave_stat(sp);
+  if (lane == 0) ws[wave] = make_float4(sq.mL, sq.s, sp.mL, sp.s);
+  __syncthreads();
+  const float4 w = lane < kWaves ? ws[lane] : make_float4(-FLT_MAX, 0.0f, -FLT_MAX, 0.0f);
+  sq = wave_stat({w.x, w.y});
+  sp = wave_stat({w.z, w.w});
+}
+
+// Resident, persistent variant: one workgroup per CU walks the pairs
+// blockIdx.x, blockIdx.x + gridDim.x, ..., keeping each pair on the CU between
+// the passes so that every logit is read from HBM once. Vector pair v (16
+// bytes of q and of p) lives
+//   in registers of thread v % 1024 (slot v / 1024) for v < 11 * 1024, and
+//   in LDS for the rest (q at i, p at n_lds + i, i = v - 11 * 1024),
+// which holds rows of up to 11 * 1024 + 4992 vectors (bf16 V <= 130055):
+// 88 VGPRs and up to 156 KB of LDS. The next pair's loads are issued while
+// pass 2 of the current one runs: each register slot is reloaded as soon as
+// pass 2 has consumed it, and the LDS part is copied straight from HBM into
+// LDS (no registers) once every wave has read the current one. Pass 1 of the
+// next pair then consumes the slots in the order they arrive.
+//
+// FULL (rows of at least 11 * 1024 vectors) issues every register-slot load
+// unconditionally, so the compiler can wait for each slot by its position in
+// the load queue instead of for the whole queue; after the last pair the
+// reloads read the current row's first 1 KB again (cached), and are unused.
+// Shorter rows fill the slots past the row end with -inf instead. Longer rows
+// take the two-pass streaming kernel above.
+constexpr int kResRegSlots = 11;
+constexpr int kResLdsSlots = 5;
+constexpr int kResRegSpan = kResRegSlots * kTvThreads;
+constexpr int kResLdsMaxPairs = 4992;  // 2 * 4992 * 16 B = 156 KB
+
+template <dspark_dtype DT, bool FULL>
 __global__ __launch_bounds__(kTvThreads) void tv_resident_kernel(TvArgs a) {
   extern __shared__ u32x4 lds_pairs[];  // q vectors [n_lds], then p vectors [n_lds]
-  __shared__ Stat ws[kWaves];
+  __shared__ float4 ws[kWaves];
   __shared__ float wsf[kWaves];
   constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
   constexpr unsigned int kNegInf = DT == DSPARK_BF16 ? 0xFF80FF80u : 0xFF800000u;
-  const int pair = blockIdx.x;
-  const int r = pair / a.gamma;
-  const int k0 = pair - r * a.gamma;
-  const unsigned char* qrow = a.q + (size_t)pair * a.ldq_bytes;
-  const unsigned char* prow = a.p + ((size_t)r * a.rows_per_req + k0) * a.ldp_bytes;
-  const u32x4* qv = reinterpret_cast<const u32x4*>(qrow);
-  const u32x4* pv = reinterpret_cast<const u32x4*>(prow);
+  const int pairs = a.B * a.gamma;
   const int tid = threadIdx.x;
+  const int wave_off = __builtin_amdgcn_readfirstlane(tid & ~(kWave - 1));
+  const unsigned int lane_bytes = (unsigned int)(tid & (kWave - 1)) * sizeof(u32x4);
   const int nvec = a.nvec;
-  const int n_lds = nvec > kResRegSpan ? nvec - kResRegSpan : 0;
+  const int n_lds = FULL ? nvec - kResRegSpan : 0;
   u32x4* lq = lds_pairs;
   u32x4* lp = lds_pairs + n_lds;
   const u32x4 fill = (u32x4){kNegInf, kNegInf, kNegInf, kNegInf};
 
-  // pass 1, phase A: the LDS part and register slots kEarly..10
-  u32x4 tq[kResLdsSlots], tp[kResLdsSlots];
-#pragma unroll
-  for (int c = 0; c < kResLdsSlots; ++c) {
-    const int i = c * kTvThreads + tid;
-    tq[c] = fill;
-    tp[c] = fill;
-    if (i < n_lds) {
-      tq[c] = qv[kResRegSpan + i];
-      tp[c] = pv[kResRegSpan + i];
-    }
-  }
+  int pair = blockIdx.x;
+  const u32x4 *qv, *pv;
+  pair_rows(a, pair, qv, pv);
   u32x4 rq[kResRegSlots], rp[kResRegSlots];
 #pragma unroll
-  for (int c = kEarly; c < kResRegSlots; ++c) {
+  for (int c = 0; c < kResRegSlots; ++c) {
     const int v = c * kTvThreads + tid;
-    rq[c] = fill;
-    rp[c] = fill;
-    if (v < nvec) {
+    if (FULL) {
+      // issued in slot order, the order pass 1 consumes them in
       rq[c] = qv[v];
       rp[c] = pv[v];
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      rq[c] = fill;
+      rp[c] = fill;
+      if (v < nvec) {
+        rq[c] = qv[v];
+        rp[c] = pv[v];
+      }
     }
   }
-  Stat sq{-FLT_MAX, 0.0f}, sp{-FLT_MAX, 0.0f};
+  if (FULL) {
 #pragma unroll
-  for (int c = 0; c < kResLdsSlots; ++c) {
-    const int i = c * kTvThreads + tid;
-    if (i < n_lds) {
-      lq[i] = tq[c];
-      lp[i] = tp[c];
-      stat_add_pair<DT>(sq, sp, tq[c], tp[c]);
+    for (int c = 0; c < kResLdsSlots; ++c) {
+      const int i = c * kTvThreads + tid;
+      if (i < n_lds) {
+        const int w0 = c * kTvThreads + wave_off;
+        lds_dma16(qv + kResRegSpan + w0, lq + w0, lane_bytes);
+        lds_dma16(pv + kResRegSpan + w0, lp + w0, lane_bytes);
+      }
     }
   }
-  // phase B: register slots 0..kEarly-1. The scheduling barrier keeps these
-  // loads from being hoisted above phase A, whose registers they reuse.
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int c = 0; c < kEarly; ++c) {
-    const int v = c * kTvThreads + tid;
-    rq[c] = fill;
-    rp[c] = fill;
-    if (v < nvec) {
-      rq[c] = qv[v];
-      rp[c] = pv[v];
-    }
-  }
-#pragma unroll
-  for (int c = kEarly; c < kResRegSlots; ++c) stat_add_pair<DT>(sq, sp, rq[c], rp[c]);
-#pragma unroll
-  for (int c = 0; c < kEarly; ++c) stat_add_pair<DT>(sq, sp, rq[c], rp[c]);
-  if (tid == 0) {
-    for (int t = 0; t < a.tail; ++t) {
-      const int i = nvec * kEpv + t;
-      float x[2] = {elem<DT>(qrow, i), -INFINITY};
-      stat_add<2>(sq, x, x[0]);
-      float y[2] = {elem<DT>(prow, i), -INFINITY};
-      stat_add<2>(sp, y, y[0]);
-    }
-  }
-  sq = block_stat(sq, ws);
-  sp = block_stat(sp, ws);
-  const float aq = sq.mL + log2f(sq.s);
-  const float ap = sp.mL + log2f(sp.s);
 
-  // pass 2 from registers and LDS. The empty asm makes the raw words opaque,
-  // so pass 2 widens them again instead of keeping pass 1's fp32 copies alive
-  // (which would double the registers the slots need).
+  for (;;) {
+    const unsigned char* qrow = reinterpret_cast<const unsigned char*>(qv);
+    const unsigned char* prow = reinterpret_cast<const unsigned char*>(pv);
+    // pass 1: register slots in arrival order, then (every wave's copies
+    // complete) the LDS part
+    Stat sq{-FLT_MAX, 0.0f}, sp{-FLT_MAX, 0.0f};
 #pragma unroll
-  for (int c = 0; c < kResRegSlots; ++c) asm volatile("" : "+v"(rq[c]), "+v"(rp[c]));
-  float acc = 0.0f;
-#pragma unroll
-  for (int c = 0; c < kResRegSlots; ++c) acc += min_sum_pair<DT>(rq[c], rp[c], aq, ap);
-#pragma unroll
-  for (int c = 0; c < kResLdsSlots; ++c) {
-    const int i = c * kTvThreads + tid;
-    if (i < n_lds) acc += min_sum_pair<DT>(lq[i], lp[i], aq, ap);
-  }
-  if (tid == 0) {
-    for (int t = 0; t < a.tail; ++t) {
-      const int i = nvec * kEpv + t;
-      acc += exp2_raw(fminf(__fmaf_rn(elem<DT>(qrow, i), kLog2e, -aq),
-                            __fmaf_rn(elem<DT>(prow, i), kLog2e, -ap)));
+    for (int c = 0; c < kResRegSlots; ++c) stat_add_pair<DT>(sq, sp, rq[c], rp[c]);
+    if (tid == 0) {
+      for (int t = 0; t < a.tail; ++t) {
+        const int i = nvec * kEpv + t;
+        float x[2] = {elem<DT>(qrow, i), -INFINITY};
+        stat_add<2>(sq, x, x[0]);
+        float y[2] = {elem<DT>(prow, i), -INFINITY};
+        stat_add<2>(sp, y, y[0]);
+      }
     }
+    if (FULL) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < kResLdsSlots; ++c) {
+        const int i = c * kTvThreads + tid;
+        if (i < n_lds) stat_add_pair<DT>(sq, sp, lq[i], lp[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    block_stat2(sq, sp, ws);
+    const float aq = sq.mL + log2f(sq.s);  // base-2 log-partitions
+    const float ap = sp.mL + log2f(sp.s);
+
+    // pass 2: the tail first (its loads are then not queued behind the
+    // reloads), then the register slots, each reloaded with the next pair once
+    // consumed, then the LDS part. The empty asm makes the raw words opaque, so
+    // pass 2 widens them again instead of keeping pass 1's fp32 copies alive.
+    float acc = 0.0f;
+    if (tid == 0) {
+      for (int t = 0; t < a.tail; ++t) {
+        const int i = nvec * kEpv + t;
+        acc += exp2_raw(fminf(__fmaf_rn(elem<DT>(qrow, i), kLog2e, -aq),
+                              __fmaf_rn(elem<DT>(prow, i), kLog2e, -ap)));
+      }
+    }
+    const int next = pair + gridDim.x;
+    const bool more = next < pairs;
+    const u32x4 *nqv = qv, *npv = pv;
+    if (more) pair_rows(a, next, nqv, npv);
+#pragma unroll
+    for (int c = 0; c < kResRegSlots; ++c) asm volatile("" : "+v"(rq[c]), "+v"(rp[c]));
+#pragma unroll
+    for (int c = 0; c < kResRegSlots; ++c) {
+      acc += min_sum_pair<DT>(rq[c], rp[c], aq, ap);
+      // The reload's address depends on this opaque copy of the thread index,
+      // tied to acc, so the slot's old words are consumed before it is issued.
+      int lt = tid;
+      asm volatile("" : "+v"(lt), "+v"(acc));
+      const int v = c * kTvThreads + lt;
+      if (FULL) {
+        const int vl = more ? v : (lt & (kWave - 1));
+        rq[c] = nqv[vl];
+        rp[c] = npv[vl];
+      } else {
+        rq[c] = fill;
+        rp[c] = fill;
+        if (more && v < nvec) {
+          rq[c] = nqv[v];
+          rp[c] = npv[v];
+        }
+      }
+    }
+    if (FULL) {
+#pragma unroll
+      for (int c = 0; c < kResLdsSlots; ++c) {
+        const int i = c * kTvThreads + tid;
+        if (i < n_lds) acc += min_sum_pair<DT>(lq[i], lp[i], aq, ap);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    acc = wave_total(acc);
+    if (lane_id() == 0) wsf[tid / kWave] = acc;
+    // after this barrier no wave reads the LDS part any more
+    __syncthreads();
+    if (FULL && more) {
+#pragma unroll
+      for (int c = 0; c < kResLdsSlots; ++c) {
+        const int i = c * kTvThreads + tid;
+        if (i < n_lds) {
+          const int w0 = c * kTvThreads + wave_off;
+          lds_dma16(nqv + kResRegSpan + w0, lq + w0, lane_bytes);
+          lds_dma16(npv + kResRegSpan + w0, lp + w0, lane_bytes);
+        }
+      }
+    }
+    if (tid == 0) {
+      float total = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) total += wsf[w];
+      a.a_out[pair] = total > 1.0f ? 1.0f : total;
+    }
+    if (!more) break;
+    pair = next;
+    qv = nqv;
+    pv = npv;
   }
-  const float total = block_sum<float, kTvThreads>(acc, wsf);
-  if (tid == 0) a.a_out[pair] = total > 1.0f ? 1.0f : total;
 }
 
 __global__ void tv_cumprod_kernel(const float* a_in, float* s_out, int B, int G) {
@@ -369,14 +481,21 @@ hipError_t launch_tv(const TvArgs& a, dspark_dtype dt, hipStream_t s) {
   if (pairs > 0) {
     const int n_lds = a.nvec > kResRegSpan ? a.nvec - kResRegSpan : 0;
     if (n_lds <= kResLdsMaxPairs) {
+      // one persistent workgroup per CU (the registers hold one per CU)
+      int dev = 0, cus = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess) return e;
+      const int grid = pairs < cus ? pairs : (cus > 0 ? cus : 1);
       const size_t lds = (size_t)2 * n_lds * sizeof(u32x4);
+      const bool full = n_lds > 0 || a.nvec == kResRegSpan;
+      void (*kern)(TvArgs);
       if (dt == DSPARK_BF16) {
-        hipLaunchKernelGGL(tv_resident_kernel<DSPARK_BF16>, dim3(pairs), dim3(kTvThreads), lds, s,
-                           a);
+        kern = full ? tv_resident_kernel<DSPARK_BF16, true> : tv_resident_kernel<DSPARK_BF16, false>;
       } else {
-        hipLaunchKernelGGL(tv_resident_kernel<DSPARK_F32>, dim3(pairs), dim3(kTvThreads), lds, s,
-                           a);
+        kern = full ? tv_resident_kernel<DSPARK_F32, true> : tv_resident_kernel<DSPARK_F32, false>;
       }
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(kTvThreads), lds, s, a);
     } else if (dt == DSPARK_BF16) {
       hipLaunchKernelGGL(tv_kernel<DSPARK_BF16>, dim3(pairs), dim3(kTvThreads), 0, s, a);
     } else {

@@ -71,6 +71,41 @@ def test_tv_small(V, pad, dt):
             assert S[r, kk] == acc
 
 
+# More pairs than the chip has CUs: each persistent workgroup then walks
+# several pairs, reloading registers and LDS while it finishes the last one.
+# Rows with all register slots full (FULL) and shorter ones, ragged tails, an
+# LDS part of one pair, and pair counts that do not divide by the CU count.
+@pytest.mark.parametrize("V,pad,dt,B,G", [(90121, 5, 1, 37, 9),   # 333 pairs, 1 LDS pair
+                                          (130055, 0, 1, 33, 8),  # 264 pairs, full LDS
+                                          (98304, 0, 1, 20, 26),  # 520 pairs, 3 per CU at most
+                                          (32000, 0, 0, 40, 8),   # fp32, registers only
+                                          (45056, 0, 0, 35, 8),   # fp32, exactly 11 * 1024 vectors
+                                          (3, 1, 0, 30, 10)])     # tail only
+def test_tv_many_pairs(V, pad, dt, B, G):
+    rng = np.random.default_rng(V * 13 + B)
+    epv = 8 if dt == 1 else 4
+    ld = V + pad
+    ld += (-ld) % epv
+    sig = rng.uniform(0.3, 3.0, (B, 1, 1)).astype(np.float32)
+    p32 = rng.normal(0, 2.0, (B, G + 1, V)).astype(np.float32)
+    q32 = p32[:, :G] + sig * rng.normal(0, 1.0, (B, G, V)).astype(np.float32)
+    q = f32_to_bf16_bits(q32) if dt == 1 else q32
+    p = f32_to_bf16_bits(p32) if dt == 1 else p32
+    nan = np.uint16(0x7FC1) if dt == 1 else np.float32(np.nan)
+    qs = np.full((B * G, ld), nan, dtype=q.dtype)
+    ps = np.full((B * (G + 1), ld), nan, dtype=p.dtype)
+    qs[:, :V] = q.reshape(B * G, V)
+    ps[:, :V] = p.reshape(B * (G + 1), V)
+    a, S = tv(B, G, V, dt, logits_up(qs, dt), ld, logits_up(ps, dt), ld, G + 1,
+              tag=f"many pairs V={V} pairs={B * G}")
+    ref_a, ref_S = oracle.tv_accept(B, G, q, p, "bf16" if dt == 1 else "f32")
+    err = np.abs(a - ref_a)
+    say(f"max |a - oracle| = {err.max():.3e}")
+    assert err.max() <= A_TOL
+    k = np.arange(1, G + 1)
+    assert np.all(np.abs(S - ref_S) <= A_TOL * k)
+
+
 def test_tv_closed_forms():
     # uniform q against one spike in p: a = 1/V + (V-1)/(e^L + V - 1)
     V, L = 4096, 6.0
