@@ -210,6 +210,40 @@ __device__ inline void stat_add_pair(Stat& sq, Stat& sp, const u32x4& dq, const 
   stat_add_vec<DT>(sp, dp);
 }
 
+// Sum of 2^(x log2 e - off) over one row's 16 bytes.
+template <dspark_dtype DT>
+__device__ inline float exp_sum_vec(const u32x4& d, float off) {
+  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
+  float x[kEpv];
+  widen<DT>(d, x);
+  float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kEpv; i += 2) {
+    s0 += exp2_raw(__fmaf_rn(x[i], kLog2e, -off));
+    s1 += exp2_raw(__fmaf_rn(x[i + 1], kLog2e, -off));
+  }
+  return s0 + s1;
+}
+
+// Maximum of one row's 16 bytes (NaN ignored).
+template <dspark_dtype DT>
+__device__ inline float vec_max(const u32x4& d) {
+  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
+  float x[kEpv];
+  widen<DT>(d, x);
+  float bm = x[0];
+#pragma unroll
+  for (int i = 1; i < kEpv; ++i) bm = fmaxf(bm, x[i]);
+  return bm;
+}
+
+// The offset of a thread's fixed-offset sums: the maximum of its first
+// vector (base-2 units), finite.
+template <dspark_dtype DT>
+__device__ inline float first_offset(const u32x4& d) {
+  return fmaxf(vec_max<DT>(d) * kLog2e, -FLT_MAX);
+}
+
 template <dspark_dtype DT>
 __device__ inline float min_sum_pair(const u32x4& dq, const u32x4& dp, float aq, float ap) {
   constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
@@ -361,29 +395,80 @@ __global__ __launch_bounds__(kTvThreads) void tv_resident_kernel(TvArgs a) {
     const unsigned char* qrow = reinterpret_cast<const unsigned char*>(qv);
     const unsigned char* prow = reinterpret_cast<const unsigned char*>(pv);
     // pass 1: register slots in arrival order, then (every wave's copies
-    // complete) the LDS part
-    Stat sq{-FLT_MAX, 0.0f}, sp{-FLT_MAX, 0.0f};
+    // complete) the LDS part. Each thread sums 2^(x log2 e - off) with one
+    // offset per row, the maximum of its first vector: no running maximum and
+    // no rescaling. A lane whose sums overflow (an element about 2^7 or more
+    // above that maximum in base-2 units, or non-finite data) sums again with
+    // its exact maximum as the offset.
+    auto row_sums = [&](float oq, float op, float& fq, float& fp) {
+      fq = 0.0f;
+      fp = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kResRegSlots; ++c) stat_add_pair<DT>(sq, sp, rq[c], rp[c]);
-    if (tid == 0) {
-      for (int t = 0; t < a.tail; ++t) {
-        const int i = nvec * kEpv + t;
-        float x[2] = {elem<DT>(qrow, i), -INFINITY};
-        stat_add<2>(sq, x, x[0]);
-        float y[2] = {elem<DT>(prow, i), -INFINITY};
-        stat_add<2>(sp, y, y[0]);
+      for (int c = 0; c < kResRegSlots; ++c) {
+        fq += exp_sum_vec<DT>(rq[c], oq);
+        fp += exp_sum_vec<DT>(rp[c], op);
       }
-    }
-    if (FULL) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      if (tid == 0) {
+        for (int t = 0; t < a.tail; ++t) {
+          const int i = nvec * kEpv + t;
+          fq += exp2_raw(__fmaf_rn(elem<DT>(qrow, i), kLog2e, -oq));
+          fp += exp2_raw(__fmaf_rn(elem<DT>(prow, i), kLog2e, -op));
+        }
+      }
+    };
+    auto lds_sums = [&](float oq, float op, float& fq, float& fp) {
 #pragma unroll
       for (int c = 0; c < kResLdsSlots; ++c) {
         const int i = c * kTvThreads + tid;
-        if (i < n_lds) stat_add_pair<DT>(sq, sp, lq[i], lp[i]);
+        if (i < n_lds) {
+          fq += exp_sum_vec<DT>(lq[i], oq);
+          fp += exp_sum_vec<DT>(lp[i], op);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    float oq = first_offset<DT>(rq[0]);
+    float op = first_offset<DT>(rp[0]);
+    float fq, fp;
+    row_sums(oq, op, fq, fp);
+    if (FULL) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      lds_sums(oq, op, fq, fp);
     }
+    if (!(fq <= FLT_MAX && fp <= FLT_MAX)) {
+      // rare: two sweeps over this thread's vectors, read again from memory
+      float mq = -FLT_MAX, mp = -FLT_MAX;
+#pragma unroll 1
+      for (int v = tid; v < nvec; v += kTvThreads) {
+        mq = fmaxf(mq, vec_max<DT>(qv[v]));
+        mp = fmaxf(mp, vec_max<DT>(pv[v]));
+      }
+      if (tid == 0) {
+        for (int t = 0; t < a.tail; ++t) {
+          const int i = nvec * kEpv + t;
+          mq = fmaxf(mq, elem<DT>(qrow, i));
+          mp = fmaxf(mp, elem<DT>(prow, i));
+        }
+      }
+      oq = fmaxf(mq * kLog2e, -FLT_MAX);
+      op = fmaxf(mp * kLog2e, -FLT_MAX);
+      fq = 0.0f;
+      fp = 0.0f;
+#pragma unroll 1
+      for (int v = tid; v < nvec; v += kTvThreads) {
+        fq += exp_sum_vec<DT>(qv[v], oq);
+        fp += exp_sum_vec<DT>(pv[v], op);
+      }
+      if (tid == 0) {
+        for (int t = 0; t < a.tail; ++t) {
+          const int i = nvec * kEpv + t;
+          fq += exp2_raw(__fmaf_rn(elem<DT>(qrow, i), kLog2e, -oq));
+          fp += exp2_raw(__fmaf_rn(elem<DT>(prow, i), kLog2e, -op));
+        }
+      }
+    }
+    Stat sq{oq, fq}, sp{op, fp};
     block_stat2(sq, sp, ws);
     const float aq = sq.mL + log2f(sq.s);  // base-2 log-partitions
     const float ap = sp.mL + log2f(sp.s);

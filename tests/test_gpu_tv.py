@@ -106,6 +106,37 @@ def test_tv_many_pairs(V, pad, dt, B, G):
     assert np.all(np.abs(S - ref_S) <= A_TOL * k)
 
 
+# Pass 1 sums each thread's exponentials against the maximum of its first
+# vector; a thread whose sums overflow (an element about 2^7 base-2 units
+# above that, or a first vector of -inf only) sums again against its exact
+# maximum. Spikes far above the rest and -inf blocks take that path.
+@pytest.mark.parametrize("V,dt", [(129280, 1), (98304, 1), (32000, 0), (45056, 0)])
+def test_tv_overflow_fallback(V, dt):
+    rng = np.random.default_rng(V + 5)
+    B, G = 6, 4
+    epv = 8 if dt == 1 else 4
+    p32 = rng.normal(0, 1.0, (B, G + 1, V)).astype(np.float32)
+    q32 = p32[:, :G] + rng.normal(0, 0.5, (B, G, V)).astype(np.float32)
+    p32[0, 0, V // 2 + 3] = 150.0      # spike in a later vector: overflow
+    q32[0, 0, V // 3 + 1] = 149.0
+    q32[1, 1, : epv * 1024] = -np.inf   # every thread's first q vector is -inf
+    p32[1, 1, : epv * 1024] = -np.inf
+    p32[2, 2, :] = -60.0               # flat row, its maximum in thread 0's first
+    p32[2, 2, 7] = 200.0               # vector: offsets 375 units apart, no fallback
+    q32[3, 0, -1] = 300.0              # the last element (tail or last vector)
+    q = f32_to_bf16_bits(q32) if dt == 1 else q32
+    p = f32_to_bf16_bits(p32) if dt == 1 else p32
+    a, S = tv(B, G, V, dt, logits_up(q.reshape(B * G, V), dt), V,
+              logits_up(p.reshape(B * (G + 1), V), dt), V, G + 1, tag=f"overflow V={V}")
+    ref_a, ref_S = oracle.tv_accept(B, G, q, p, "bf16" if dt == 1 else "f32")
+    err = np.abs(a - ref_a)
+    say(f"max |a - oracle| = {err.max():.3e}")
+    assert np.all(np.isfinite(a))
+    assert err.max() <= A_TOL
+    k = np.arange(1, G + 1)
+    assert np.all(np.abs(S - ref_S) <= A_TOL * k)
+
+
 def test_tv_closed_forms():
     # uniform q against one spike in p: a = 1/V + (V-1)/(e^L + V - 1)
     V, L = 4096, 6.0
