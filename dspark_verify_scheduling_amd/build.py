@@ -34,6 +34,10 @@ COMMON_FLAGS = [
     "-Wno-unused-function",
     # no packed fp32 instructions: plain scalar fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no contraction of a product and a sum into one rounding anywhere, also
+    # inside inlined header functions such as __fmul_rn (a plain x * y): the
+    # exact paths round each operation on its own; FMAs are written as such
+    "-ffp-contract=off",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

@@ -12,6 +12,7 @@ import torch
 import dspark_verify_scheduling_amd as dv
 import oracle
 from oracle import sampling as S
+from oracle.accept import as_f32_rows
 from workloads import gen
 from _gpu import DEV, logits_up, say, up
 
@@ -315,3 +316,51 @@ def test_sampling_full_size_other_workloads(cfg, n_check):
                             prefix_lens=w.prefix_lens[reqs])
     check(got, ref, None, reqs=reqs)
     say(f"cfg{cfg}: mean correct {got['num_correct'].mean():.3f}, {cu[-1]} rows")
+
+
+# White-box pin of the weights themselves: the per-chunk weight sums the
+# kernels leave in the workspace, added up per slot, must equal the oracle's
+# Z = sum W exactly. (Decisions agree even when a few weights are off by one
+# step, so the outputs alone would not show it.) The layout read here is the
+# library's internal one: per (slot, chunk) 64-bit maxima, then 64-bit weight
+# sums, slots = B (gamma + 1) target slots then B gamma draft slots, chunks of
+# 2048 16-byte vectors, each part padded to 256 bytes.
+@pytest.mark.parametrize("seed,B,gamma,V,dt,t_lo,t_hi", [
+    (21, 6, 4, 129280, dv.BF16, 0.3, 2.0),
+    (22, 5, 3, 32000, dv.F32, 0.05, 1.5),   # small T: u near the 2^21 cutoff
+    (23, 4, 5, 4099, dv.BF16, 0.5, 4.0),
+])
+def test_sampling_weight_sums_exact(seed, B, gamma, V, dt, t_lo, t_hi):
+    c = rand_case(seed, B, gamma, V, dt, greedy_frac=0.0)
+    rng = np.random.default_rng(seed + 100)
+    c["temps"] = rng.uniform(t_lo, t_hi, B).astype(np.float32)
+    esize = 2 if dt == dv.BF16 else 4
+    nvec = V * esize // 16
+    chunks = max(1, -(-nvec // 2048))
+    slots = B * (2 * gamma + 1)
+    part_bytes = -(-(slots * chunks * 8) // 256) * 256
+    ld = V if (V * esize) % 16 == 0 else (V + 16 // esize - 1) // (16 // esize) * (16 // esize)
+    pad = (lambda x: np.pad(x, ((0, 0), (0, ld - V)))) if ld != V else (lambda x: x)
+    out = dv.alloc_sampling_outputs(B, gamma, V, dt, DEV)
+    say(f"weight sums seed={seed} V={V} dt={dt} chunks={chunks}")
+    dv.dspark_accept_sampling(
+        B, gamma, V, dt, logits_up(pad(c["tgt"]), dt), ld, c["tgt"].shape[0],
+        up(np.asarray(c["cu"], np.int32)), logits_up(pad(c["drf"]), dt), ld,
+        up(c["drafts"].reshape(B, gamma)), up(c["temps"]), up(_bits(c["ra"]).reshape(B, gamma)),
+        up(_bits(c["rs"]).reshape(B, gamma + 1)), up(c["prefix"]), out)
+    torch.cuda.synchronize()
+    ws = out.workspace.cpu().numpy()
+    z = ws[part_bytes:part_bytes + slots * chunks * 8].view(np.uint64).reshape(slots, chunks)
+    tgt = as_f32_rows(c["tgt"], "bf16" if dt == dv.BF16 else "f32")
+    drf = as_f32_rows(c["drf"], "bf16" if dt == dv.BF16 else "f32")
+    cu, checked = c["cu"], 0
+    for r in range(B):
+        l, T = int(cu[r + 1] - cu[r]), float(c["temps"][r])
+        rows = [(r * (gamma + 1) + j, tgt[cu[r] + j]) for j in range(l)]
+        rows += [(B * (gamma + 1) + r * gamma + k, drf[r * gamma + k]) for k in range(l - 1)]
+        for slot, x in rows:
+            want = int(S.weights(x, T).sum())
+            got = int(z[slot].astype(object).sum())
+            assert got == want, (r, slot, T, got, want)
+            checked += 1
+    say(f"{checked} slot weight sums exact")
