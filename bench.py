@@ -117,7 +117,9 @@ def tv_section(dv, torch, dev, stream, reps):
     def tv():
         dv.dspark_tv_accept(B, G, V, dv.BF16, q, V, p, V, G + 1, a, S, stream)
 
-    for _ in range(3):
+    # about 10 ms of warm-up: with only a few calls the first timed ones still
+    # ran up to 20% slower
+    for _ in range(25):
         tv()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -163,7 +165,7 @@ def tv_section(dv, torch, dev, stream, reps):
         dv.dspark_accept(B, G, V, dv.BF16, packed, V, tier, ko.cu_seqlens, drafts_t, prefix_t,
                          ao, stream)
 
-    for _ in range(3):
+    for _ in range(10):
         chain()
     torch.cuda.synchronize()
     ev0.record(stream)
