@@ -95,7 +95,9 @@ SampGeom samp_geom(int B, int gamma, int V, dspark_dtype dt) {
   SampGeom g;
   g.chunks = (rg.nvec + dspark::kSampChunkVecs - 1) / dspark::kSampChunkVecs;
   if (g.chunks < 1) g.chunks = 1;
-  g.chunk_vecs = (rg.nvec + g.chunks - 1) / g.chunks;
+  // whole chunks of kSampChunkVecs vectors (the last one partial): the
+  // row-statistics kernel holds chunk c in its register slots 2c and 2c + 1
+  g.chunk_vecs = dspark::kSampChunkVecs;
   static_assert((DSPARK_MAX_VOCAB * 4 / 16 + dspark::kSampChunkVecs - 1) / dspark::kSampChunkVecs <=
                     dspark::kSampMaxChunks,
                 "the draw kernel holds the chunk sums of the longest row in LDS");

@@ -169,6 +169,7 @@ struct SampArgs {
   // workspace, per slot and chunk: target slots r * (gamma + 1) + j (packed
   // row cu[r] + j), then draft slots B * (gamma + 1) + r * gamma + k (draft
   // row r * gamma + k)
+  int rowstat;                // the row statistics come from samp_rowstat_kernel
   unsigned long long* kpart;  // maximum key with its index
   unsigned long long* zpart;  // weight sum
   unsigned long long* rpart;  // [B, chunks, 2]: residual member sums of Wp, Wq
@@ -179,6 +180,9 @@ constexpr int kSampVecsPerThread = 8;
 constexpr int kSampChunkVecs = kSampThreads * kSampVecsPerThread;
 constexpr int kSampDrawThreads = 1024;  // draw kernel
 constexpr int kSampMaxChunks = 32;      // chunks of a DSPARK_MAX_VOCAB float32 row
+constexpr int kRsThreads = 1024;        // row-statistics kernel
+constexpr int kRsMaxSlots = 16;         // 16-byte register slots per thread, at most
+constexpr int kRsMaxList = 64;          // rows per row-statistics workgroup, at most
 hipError_t launch_sampling(const SampArgs& a, dspark_dtype dt, hipStream_t s);
 
 // ---------------------------------------------------------------- helpers

@@ -46,6 +46,8 @@
 //     holding the crossing point walks its elements in order.
 #include <float.h>
 
+#include <algorithm>
+
 #include "argmax_unit.h"
 #include "common.h"
 #include "exp_tables.h"
@@ -232,6 +234,256 @@ __global__ __launch_bounds__(kSampThreads) void samp_z_kernel(SampArgs a) {
     unsigned long long t = 0;
     for (int w = 0; w < kRedWaves; ++w) t += s_red[w];
     a.zpart[(size_t)slot * a.chunks + ch] = t;
+  }
+}
+
+// Row statistics of the sampling slots with one read of each row: the
+// maximum key, then the weight sums per chunk. One persistent 1024-thread
+// workgroup per CU takes the live slots of rank blockIdx.x, blockIdx.x +
+// gridDim.x, ... (ranks in slot order). A row stays in registers
+// between the two passes: vector v in register slot v / 1024 of thread
+// v % 1024, so slots 2c and 2c + 1 hold chunk c (chunks are 2048 vectors).
+// While the weight pass consumes a register slot it reloads it with the
+// workgroup's next row, so the next row streams in under this row's
+// arithmetic; the maximum pass then takes the slots in the order they arrive.
+// A greedy row gets the lowest index of its maximum instead of weight sums.
+// Rows of 1024 to SLOTS * 1024 vectors; it also initializes accept_meta.
+template <dspark_dtype DT, int SLOTS>
+__global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
+  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
+  constexpr int kWaves = kRsThreads / kWave;
+  constexpr int kChunks = (SLOTS + 1) / 2;
+  __shared__ uint2 s_B[kExp2Len - 1];
+  __shared__ int s_list[kRsMaxList];
+  __shared__ int s_scan[kWaves];
+  __shared__ unsigned int s_key[kWaves];
+  __shared__ int s_flag[kWaves];
+  __shared__ unsigned long long s_z[kWaves][kChunks];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int nvec = a.nvec;
+  load_table(s_B);
+
+  if (blockIdx.x == 0 && tid == 0) {
+    a.meta[0] = a.cu[a.B];
+    a.meta[1] = 0;
+  }
+  // ---- this workgroup's rows: thread t looks at slots [t k, t k + k)
+  const int nslots = a.B * (2 * a.gamma + 1);
+  const int per = (nslots + kRsThreads - 1) / kRsThreads;
+  const int s0 = tid * per;
+  int cnt = 0;
+  for (int j = 0; j < per; ++j) {
+    const int slot = s0 + j;
+    if (slot < nslots && resolve_slot(a, slot).live) ++cnt;
+  }
+  int total = 0;
+  int rank = block_excl_scan<int, kRsThreads>(cnt, s_scan, &total);
+  if (cnt) {
+    for (int j = 0; j < per; ++j) {
+      const int slot = s0 + j;
+      if (slot < nslots && resolve_slot(a, slot).live) {
+        if (rank % (int)gridDim.x == (int)blockIdx.x) {
+          const int i = rank / (int)gridDim.x;
+          if (i < kRsMaxList) s_list[i] = slot;
+        }
+        ++rank;
+      }
+    }
+  }
+  __syncthreads();
+  const int mine = total > (int)blockIdx.x ? (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+  const int n_rows = mine < kRsMaxList ? mine : kRsMaxList;  // the host sizes the grid for this
+  if (n_rows == 0) return;
+
+  // ---- prologue: the first row's register slots, unconditionally and in
+  // order (an index past the row end reads its last vector, never used)
+  Slot cur = resolve_slot(a, s_list[0]);
+  const u32x4* rv = reinterpret_cast<const u32x4*>(cur.row);
+  // a row's tail elements (after its last whole vector), one per lane <
+  // tail, are loaded before its register slots, so that waiting for them
+  // never waits for the slots; every lane loads (an index past the row end
+  // reads its last element) and lanes >= tail use -inf instead
+  const int ti = min(nvec * kEpv + tid, a.V - 1);
+  float xr = elem<DT>(cur.row, ti);
+  u32x4 r[SLOTS];
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) {
+    const int v = i * kRsThreads + tid;
+    r[i] = rv[v < nvec ? v : nvec - 1];
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const u32x4 fill = DT == DSPARK_BF16 ? (u32x4){0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u}
+                                       : (u32x4){0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u};
+  const int last_chunk = (nvec - 1) / kSampChunkVecs;
+
+  for (int k = 0; k < n_rows; ++k) {
+    const int slot = s_list[k];
+    const float xt = tid < a.tail ? xr : -INFINITY;
+
+    // ---- pass 1: the maximum key, slots in arrival order
+    auto slot_vec = [&](int i) -> u32x4 {
+      // lanes past the row end see -inf (no maximum, zero weight)
+      return i * kRsThreads + tid < nvec ? r[i] : fill;
+    };
+    unsigned int key;
+    if constexpr (DT == DSPARK_BF16) {
+      // fast path: raw signed-16 maximum (exact for a positive maximum) and
+      // NaN detection; the raw order is reversed for negatives
+      argmax::i16x2 mi = (argmax::i16x2){(short)0xFF80, (short)0xFF80};
+      argmax::u16x2 mu = (argmax::u16x2){0, 0};
+#pragma unroll
+      for (int i = 0; i < SLOTS; ++i) {
+        if (i * kRsThreads < nvec) {
+          const u32x4 d = slot_vec(i);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            mi = __builtin_elementwise_max(mi, argmax::as_i16x2(d[w]));
+            mu = __builtin_elementwise_max(mu, argmax::as_u16x2(d[w]));
+          }
+        }
+      }
+      const unsigned int xt_w = (__float_as_uint(xt) >> 16) | 0xFF800000u;  // tail in the low half
+      mi = __builtin_elementwise_max(mi, argmax::as_i16x2(xt_w));
+      mu = __builtin_elementwise_max(mu, argmax::as_u16x2(xt_w));
+      const int lm = max((int)mi[0], (int)mi[1]);
+      const int lu = max((int)mu[0], (int)mu[1]);
+      int v = (lm > 0x7F80 || lu > 0xFF80) ? 0x7FFFFFFF : lm;
+      v = argmax::wave_max(v);
+      if (lane == 0) s_flag[wave] = v;
+      __syncthreads();
+      int M = s_flag[0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) M = max(M, s_flag[w]);
+      if (M > 0 && M <= 0x7F80) {
+        key = (unsigned int)M + 0x7F80u;
+      } else {  // a non-positive maximum or a NaN: exact 16-bit keys
+        unsigned int kk = 0;
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+          if (i * kRsThreads < nvec) {
+            const u32x4 d = slot_vec(i);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const unsigned int kw = argmax::bf16x2_keys(d[w]);
+              kk = max(kk, max(kw & 0xFFFFu, kw >> 16));
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (tid < a.tail) kk = max(kk, argmax::bf16x2_keys(__float_as_uint(xt) >> 16) & 0xFFFFu);
+        kk = argmax::wave_max(kk);
+        if (lane == 0) s_key[wave] = kk;
+        __syncthreads();
+        key = s_key[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) key = max(key, s_key[w]);
+      }
+    } else {
+      unsigned int kk = 0;
+#pragma unroll
+      for (int i = 0; i < SLOTS; ++i) {
+        if (i * kRsThreads < nvec) {
+          const u32x4 d = slot_vec(i);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) kk = max(kk, argmax::f32_key(d[w]));
+        }
+      }
+      if (tid < a.tail) kk = max(kk, argmax::f32_key(__float_as_uint(xt)));
+      kk = argmax::wave_max(kk);
+      if (lane == 0) s_key[wave] = kk;
+      __syncthreads();
+      key = s_key[0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) key = max(key, s_key[w]);
+    }
+    // a greedy row also needs the lowest index holding the maximum key (a
+    // sampling row only the value: its index field is left 0)
+    unsigned int idx = 0;
+    if (!cur.samp) {
+      unsigned int cand = 0xFFFFFFFFu;
+      // element e of dword w of slot i: index (i * 1024 + tid) * kEpv + e;
+      // walked from the end so that the last match kept is the first one
+      if (tid < a.tail) {
+        const unsigned int kt = DT == DSPARK_BF16
+                                    ? (argmax::bf16x2_keys(__float_as_uint(xt) >> 16) & 0xFFFFu)
+                                    : argmax::f32_key(__float_as_uint(xt));
+        if (kt == key) cand = (unsigned int)(nvec * kEpv + tid);
+      }
+#pragma unroll
+      for (int i = SLOTS - 1; i >= 0; --i) {
+        if (i * kRsThreads < nvec) {
+          const u32x4 d = slot_vec(i);
+          const unsigned int base = (unsigned int)(i * kRsThreads + tid) * kEpv;
+#pragma unroll
+          for (int w = 3; w >= 0; --w) {
+            if constexpr (DT == DSPARK_BF16) {
+              const unsigned int kw = argmax::bf16x2_keys(d[w]);
+              if ((kw >> 16) == key) cand = base + 2u * w + 1u;
+              if ((kw & 0xFFFFu) == key) cand = base + 2u * w;
+            } else {
+              if (argmax::f32_key(d[w]) == key) cand = base + w;
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      cand = argmax::wave_min(cand);
+      if (lane == 0) s_key[wave] = cand;
+      __syncthreads();
+      idx = s_key[0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) idx = min(idx, s_key[w]);
+    }
+    const unsigned long long best = argmax::pack_best(key, idx);
+    const bool bad = argmax::best_bad<DT>(best);
+    const float m = argmax::best_value<DT>(best), c = temp_coef(cur.T);
+
+    // ---- pass 2: weight sums per chunk, each register slot reloaded with
+    // the next row once consumed (after the last row: the current row again,
+    // cached and unused)
+    const bool more = k + 1 < n_rows;
+    Slot nxt = cur;
+    if (more) nxt = resolve_slot(a, s_list[k + 1]);
+    const u32x4* nv = reinterpret_cast<const u32x4*>(nxt.row);
+    const float xr_next = elem<DT>(nxt.row, ti);
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) asm volatile("" : "+v"(r[i]));
+    unsigned long long zc = 0;
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      if (cur.samp && !bad && i * kRsThreads < nvec) {
+        const u32x4 d = slot_vec(i);
+        float x[kEpv];
+        widen<DT>(d, x);
+#pragma unroll
+        for (int e = 0; e < kEpv; ++e) zc += weight(x[e], m, c, s_B);
+      }
+      // the reload's address depends on an opaque copy of the thread index
+      // tied to the sum, so the slot's words are consumed before it is issued
+      int lt = tid;
+      asm volatile("" : "+v"(lt), "+v"(zc));
+      const int v = i * kRsThreads + lt;
+      r[i] = nv[v < nvec ? v : nvec - 1];
+      if ((i & 1) || i == SLOTS - 1) {
+        const int ch = i >> 1;
+        if (ch == last_chunk && cur.samp && !bad && tid < a.tail) zc += weight(xt, m, c, s_B);
+        zc = wave_sum_u64(zc);
+        if (lane == 0) s_z[wave][ch] = zc;
+        zc = 0;
+      }
+    }
+    __syncthreads();
+    if (tid < a.chunks) {
+      unsigned long long t = 0;
+      if (tid < kChunks) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) t += s_z[w][tid];
+      }
+      a.zpart[(size_t)slot * a.chunks + tid] = bad || !cur.samp ? 0ull : t;
+      a.kpart[(size_t)slot * a.chunks + tid] = tid == 0 ? best : 0ull;
+    }
+    cur = nxt;
+    xr = xr_next;
   }
 }
 
@@ -601,14 +853,47 @@ __global__ __launch_bounds__(kSampDrawThreads) void samp_draw_kernel(SampArgs a)
 }
 
 template <dspark_dtype DT>
-hipError_t launch_dt(const SampArgs& a, hipStream_t s) {
+hipError_t launch_rowstat(const SampArgs& a, int grid, hipStream_t s) {
+  const int slots = (a.nvec + kRsThreads - 1) / kRsThreads;
+  if (slots <= 2) {
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(samp_rowstat_kernel<DT, 2>), dim3(grid), dim3(kRsThreads), 0, s, a);
+  } else if (slots <= 4) {
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(samp_rowstat_kernel<DT, 4>), dim3(grid), dim3(kRsThreads), 0, s, a);
+  } else if (slots <= 8) {
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(samp_rowstat_kernel<DT, 8>), dim3(grid), dim3(kRsThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(samp_rowstat_kernel<DT, 16>), dim3(grid), dim3(kRsThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <dspark_dtype DT>
+hipError_t launch_dt(SampArgs a, hipStream_t s) {
   const long long units = (long long)a.B * (2 * a.gamma + 1) * a.chunks;
-  hipLaunchKernelGGL(samp_max_kernel<DT>, dim3(units > 0 ? (unsigned)units : 1u),
-                     dim3(kSampThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.B == 0) return e;
-  hipLaunchKernelGGL(samp_z_kernel<DT>, dim3((unsigned)units), dim3(kSampThreads), 0, s, a);
-  e = hipGetLastError();
+  // rows of 1024 to 16384 vectors take the one-read row-statistics kernel:
+  // one persistent workgroup per CU, at most kRsMaxList rows each
+  int grid = 0;
+  if (a.B > 0 && a.nvec >= kRsThreads && a.nvec <= kRsMaxSlots * kRsThreads) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const long long slots = (long long)a.B * (2 * a.gamma + 1);
+    const long long need = (slots + kRsMaxList - 1) / kRsMaxList;
+    grid = (int)std::max<long long>(std::min<long long>(cus > 0 ? cus : 1, slots), need);
+  }
+  a.rowstat = grid > 0;
+  hipError_t e;
+  if (a.rowstat) {
+    e = launch_rowstat<DT>(a, grid, s);
+  } else {
+    hipLaunchKernelGGL(samp_max_kernel<DT>, dim3(units > 0 ? (unsigned)units : 1u),
+                       dim3(kSampThreads), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess || a.B == 0) return e;
+    hipLaunchKernelGGL(samp_z_kernel<DT>, dim3((unsigned)units), dim3(kSampThreads), 0, s, a);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(samp_decide_kernel<DT>, dim3(a.B), dim3(kWave), 0, s, a);
   e = hipGetLastError();

@@ -191,6 +191,44 @@ def test_sampling_edge_cases():
     assert got["meta"].tolist() == [0, 0]
 
 
+# Rows of 1024 to 16384 16-byte vectors take the one-read row-statistics
+# kernel (persistent workgroups, rows held in 2, 4, 8 or 16 register slots per
+# thread; more sampling rows than workgroups): its slot-count boundaries,
+# ragged tails, greedy rows mixed in (which keep the per-unit maximum kernel),
+# and rows whose maximum is not positive (exact keys) or is not finite.
+@pytest.mark.parametrize("seed,B,gamma,V,dt,greedy", [
+    (31, 40, 6, 10007, dv.BF16, 0.0),   # 1250 vectors: 2 slots, tail of 7, ~280 rows
+    (32, 12, 4, 50000, dv.BF16, 0.3),   # 6250 vectors: 8 slots, greedy mixed in
+    (33, 6, 3, 131072, dv.BF16, 0.0),   # 16384 vectors: 16 full slots
+    (34, 9, 5, 8192, dv.BF16, 0.2),     # 1024 vectors: the smallest row it takes
+    (35, 10, 4, 32001, dv.F32, 0.0),    # 8000 vectors and a tail of 1, float32
+])
+def test_sampling_rowstat_path(seed, B, gamma, V, dt, greedy):
+    c = rand_case(seed, B, gamma, V, dt, greedy_frac=greedy)
+    both(c, f"rowstat V={V}")
+
+
+def test_sampling_rowstat_special_rows():
+    c = rand_case(36, 10, 4, 10007, dv.BF16, greedy_frac=0.0)
+    cu, V = c["cu"], c["V"]
+    t32 = lambda row: gen.f32_to_bf16_bits(np.asarray(row, np.float32))
+    rng = np.random.default_rng(36)
+    c["tgt"][cu[0]] = t32(rng.normal(-20.0, 1.0, V))          # maximum below 0: exact keys
+    row = np.full(V, -3.0, np.float32)
+    row[V - 1] = 0.0                                            # maximum +0, in the tail
+    c["tgt"][cu[1]] = t32(row)
+    row = rng.normal(0, 2.0, V).astype(np.float32)
+    row[V - 3] = 40.0                                           # maximum in the tail
+    c["tgt"][cu[2]] = t32(row)
+    c["drf"][3 * c["gamma"]] = t32(np.full(V, -1.5, np.float32))  # flat negative draft row
+    c["tgt"][cu[4], 5] = 0x7FC0                                  # NaN
+    c["tgt"][cu[5] + (1 if cu[6] - cu[5] > 1 else 0), V - 2] = 0x7F80  # +inf in the tail
+    c["tgt"][cu[6]] = 0xFF80                                     # -inf row
+    c["tgt"][cu[7], 100] = 0xFFC1                                # negative NaN
+    got, ref = both(c, "rowstat special rows")
+    assert ref["status"] & S.DATA_BAD_LOGITS
+
+
 def test_sampling_full_size_cfg3_sampled_requests():
     """B = 256, gamma = 8, V = 129280 bf16 on the planned cfg3 layout, in the
     launch configuration the benchmark times; the oracle checks 48 requests."""
