@@ -30,9 +30,13 @@
 // Work is indexed by slot, not by packed row: target slot (r, j) is row
 // cu[r] + j of request r and draft slot (r, k) is draft row r * gamma + k, so
 // every statistic is taken at the temperature of the request that reads it.
-// Kernels:
-//   samp_max_kernel: per (slot, chunk of up to 2048 16-byte vectors), the
-//     maximum with its first index (NaN highest), for every slot read.
+// Kernels (chunks are 2048 16-byte vectors, the last one partial):
+//   samp_rowstat_kernel (rows of 1024 to 16384 vectors): the statistics of
+//     every slot read with one read of its row: the maximum key (with its
+//     first index for a greedy row), then the per-chunk sums of W.
+//   Other rows take two kernels instead:
+//   samp_max_kernel: per (slot, chunk), the maximum with its first index
+//     (NaN highest), for every slot read.
 //   samp_z_kernel: per (slot, chunk) of a sampling request, the row maximum
 //     from the chunk maxima, then the chunk's sum of W (a second read).
 //   samp_decide_kernel: one wave per request: the chain tests, lane k on
@@ -70,27 +74,31 @@ static_assert(kSampThreads == kAccThreads && kSampVecsPerThread == kAccVecsPerTh
 __device__ inline float temp_coef(float T) { return __fdiv_rn(kLog2e16, T); }
 
 // The integer weight of x in a row with maximum m (x <= m); Bt holds the
-// pairs (B[h], B[h] - B[h+1]) in LDS. Branch-free: a value past the cutoff
-// reads pair 0 and is masked.
+// pairs (B[h], B[h] - B[h+1]) for h < 256 and a zero pair at 256, in LDS.
+// Branch-free:
+// - adding 1.5 * 2^23 rounds u in [0, 2^22) to the nearest integer (ties to
+//   even) and leaves it in the low 22 mantissa bits: j = bits & 0x3FFFFF, so
+//   n = j >> 16 (five bits suffice below the cutoff), h = (j >> 8) & 255 and
+//   r = j & 255;
+// - j = RNE(u) < 2^21 exactly when u < 2^21 - 1/2 (a tie there rounds up, to
+//   even); past that (or for u = +inf) h is the zero pair, so y = 0 and the
+//   rounding shift gives 0 whatever n the bits hold.
 __device__ inline unsigned int weight(float x, float m, float c, const uint2* Bt) {
   const float u = __fmul_rn(__fsub_rn(m, x), c);  // >= 0, or +inf
-  // j = RNE(u) < 2^21 exactly when u < 2^21 - 1/2 (a tie at it rounds up, to even)
-  const bool ok = u < 2097151.5f;
-  // adding 1.5 * 2^23 rounds u in [0, 2^22) to the nearest integer (ties to
-  // even) and leaves it in the low 22 mantissa bits: j = bits & 0x3FFFFF
-  const unsigned int bits = __float_as_uint(__fadd_rn(ok ? u : 0.0f, 12582912.0f));
-  const unsigned int n = __builtin_amdgcn_ubfe(bits, 16, 6);  // j >> 16 (0x4B40 >> 0 & 63 = 0)
-  const unsigned int h = __builtin_amdgcn_ubfe(bits, 8, 8);
+  const unsigned int bits = __float_as_uint(__fadd_rn(u, 12582912.0f));
+  const unsigned int n = __builtin_amdgcn_ubfe(bits, 16, 5);
+  const unsigned int h = u < 2097151.5f ? __builtin_amdgcn_ubfe(bits, 8, 8) : 256u;
   const unsigned int r = bits & 255u;
   const uint2 bd = Bt[h];
   const unsigned int y = bd.x - (((unsigned int)__umul24(bd.y, r) + 128u) >> 8);
-  const unsigned int w = (y + ((1u << n) >> 1)) >> n;
-  return ok ? w : 0u;
+  return (y + ((1u << n) >> 1)) >> n;
 }
 
+// The weight table in LDS: kExp2Len - 1 interpolation pairs, then the zero
+// pair.
 __device__ inline void load_table(uint2* Bt) {
-  for (int i = threadIdx.x; i < kExp2Len - 1; i += blockDim.x) {
-    Bt[i] = make_uint2(kExp2B[i], kExp2B[i] - kExp2B[i + 1]);
+  for (int i = threadIdx.x; i < kExp2Len; i += blockDim.x) {
+    Bt[i] = i < kExp2Len - 1 ? make_uint2(kExp2B[i], kExp2B[i] - kExp2B[i + 1]) : make_uint2(0u, 0u);
   }
 }
 
@@ -188,7 +196,7 @@ __global__ __launch_bounds__(kSampThreads) void samp_max_kernel(SampArgs a) {
 
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kSampThreads) void samp_z_kernel(SampArgs a) {
-  __shared__ uint2 s_B[kExp2Len - 1];
+  __shared__ uint2 s_B[kExp2Len];
   __shared__ unsigned long long s_red[kRedWaves];
   constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -253,7 +261,7 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
   constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
   constexpr int kWaves = kRsThreads / kWave;
   constexpr int kChunks = (SLOTS + 1) / 2;
-  __shared__ uint2 s_B[kExp2Len - 1];
+  __shared__ uint2 s_B[kExp2Len];
   __shared__ int s_list[kRsMaxList];
   __shared__ int s_scan[kWaves];
   __shared__ unsigned int s_key[kWaves];
@@ -458,12 +466,17 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
 #pragma unroll
         for (int e = 0; e < kEpv; ++e) zc += weight(x[e], m, c, s_B);
       }
-      // the reload's address depends on an opaque copy of the thread index
-      // tied to the sum, so the slot's words are consumed before it is issued
-      int lt = tid;
-      asm volatile("" : "+v"(lt), "+v"(zc));
-      const int v = i * kRsThreads + lt;
-      r[i] = nv[v < nvec ? v : nvec - 1];
+      // both slots of a chunk are summed before either is reloaded (the
+      // reload's address depends on an opaque copy of the thread index tied
+      // to the sum, so the slots' words are consumed before it is issued)
+      if (!(i & 1) && i != SLOTS - 1) continue;
+#pragma unroll
+      for (int i2 = (i & ~1); i2 <= i; ++i2) {
+        int lt = tid;
+        asm volatile("" : "+v"(lt), "+v"(zc));
+        const int v = i2 * kRsThreads + lt;
+        r[i2] = nv[v < nvec ? v : nvec - 1];
+      }
       if ((i & 1) || i == SLOTS - 1) {
         const int ch = i >> 1;
         if (ch == last_chunk && cur.samp && !bad && tid < a.tail) zc += weight(xt, m, c, s_B);
@@ -490,7 +503,7 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
 // One wave per request.
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kWave) void samp_decide_kernel(SampArgs a) {
-  __shared__ uint2 s_B[kExp2Len - 1];
+  __shared__ uint2 s_B[kExp2Len];
   load_table(s_B);
   __syncthreads();
   const int r = blockIdx.x, lane = threadIdx.x, G = a.gamma;
@@ -666,7 +679,7 @@ __device__ inline DrawCtx draw_ctx(const SampArgs& a, const SampJob& job, int r)
 // Per (request, chunk) of a residual draw: the member sums of Wp and Wq.
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kSampThreads) void samp_rsum_kernel(SampArgs a) {
-  __shared__ uint2 s_B[kExp2Len - 1];
+  __shared__ uint2 s_B[kExp2Len];
   __shared__ Pair s_red[kRedWaves];
   constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -727,7 +740,7 @@ __global__ __launch_bounds__(kSampThreads) void samp_rsum_kernel(SampArgs a) {
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kSampDrawThreads) void samp_draw_kernel(SampArgs a) {
   constexpr int kWaves = kSampDrawThreads / kWave;
-  __shared__ uint2 s_B[kExp2Len - 1];
+  __shared__ uint2 s_B[kExp2Len];
   __shared__ unsigned long long s_scan[kWaves];
   __shared__ int s_ctl[2];  // residual flag; crossing chunk
   __shared__ u128 s_t;      // threshold left at the start of the crossing chunk
