@@ -624,7 +624,7 @@ struct DrawCtx {
   const unsigned char* q;
   float mp, mq, cT;
   unsigned long long zp, zq;  // 0 and 1 for a plain draw
-  double zpd, zqd;
+  float zpf, zqf;             // the same, rounded to float32
   bool resid;
 };
 
@@ -635,11 +635,13 @@ struct Pair {
 __device__ inline bool member(const DrawCtx& c, unsigned int wp, unsigned int wq) {
   if (wp == 0) return false;
   if (!c.resid) return true;
-  // products below 2^81, rounded once in float64 (Zp, Zq < 2^49 are exact):
-  // a margin of 2^-50 decides every case but near-equality exactly
-  const double x = (double)wp * c.zqd, y = (double)wq * c.zpd;
-  if (x > y * (1.0 + 0x1p-50)) return true;
-  if (x < y * (1.0 - 0x1p-50)) return false;
+  // Wp Zq against Wq Zp (below 2^80) screened in float32: each side is within
+  // 3 * 2^-24 relative of its exact value (three roundings), the margin
+  // product within 2^-24, so a margin of 2^-20 decides every case it passes
+  // correctly; near-equality is decided exactly
+  const float x = (float)wp * c.zqf, y = (float)wq * c.zpf;
+  if (x > y * (1.0f + 0x1p-20f)) return true;
+  if (x < y * (1.0f - 0x1p-20f)) return false;
   return (u128)wp * c.zq > (u128)wq * c.zp;
 }
 
@@ -661,8 +663,8 @@ __device__ inline void set_mode(DrawCtx& c, const SampJob& job, bool resid) {
   c.resid = resid;
   c.zp = resid ? job.zp : 0ull;
   c.zq = resid ? job.zq : 1ull;
-  c.zpd = (double)c.zp;
-  c.zqd = (double)c.zq;
+  c.zpf = (float)c.zp;
+  c.zqf = (float)c.zq;
 }
 
 __device__ inline DrawCtx draw_ctx(const SampArgs& a, const SampJob& job, int r) {
