@@ -447,8 +447,8 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
     const float m = argmax::best_value<DT>(best), c = temp_coef(cur.T);
 
     // ---- pass 2: weight sums per chunk, each register slot reloaded with
-    // the next row once consumed (after the last row: the current row again,
-    // cached and unused)
+    // the next row once consumed (after the last row: the first 64 vectors of
+    // the current row, the same 1 KB for every slot, unused)
     const bool more = k + 1 < n_rows;
     Slot nxt = cur;
     if (more) nxt = resolve_slot(a, s_list[k + 1]);
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
       for (int i2 = (i & ~1); i2 <= i; ++i2) {
         int lt = tid;
         asm volatile("" : "+v"(lt), "+v"(zc));
-        const int v = i2 * kRsThreads + lt;
+        const int v = more ? i2 * kRsThreads + lt : (lt & (kWave - 1));
         r[i2] = nv[v < nvec ? v : nvec - 1];
       }
       if ((i & 1) || i == SLOTS - 1) {
