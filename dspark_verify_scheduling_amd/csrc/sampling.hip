@@ -265,6 +265,7 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
   __shared__ int s_list[kRsMaxList];
   __shared__ int s_scan[kWaves];
   __shared__ unsigned int s_key[kWaves];
+  __shared__ unsigned int s_idx[kWaves];  // apart from s_key: waves may still read the key
   __shared__ int s_flag[kWaves];
   __shared__ unsigned long long s_z[kWaves][kChunks];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -328,10 +329,12 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
     const int slot = s_list[k];
     const float xt = tid < a.tail ? xr : -INFINITY;
 
-    // ---- pass 1: the maximum key, slots in arrival order
+    // ---- pass 1: the maximum key, slots in arrival order. The first use of
+    // a slot stores it back with -inf in the lanes past the row end (no
+    // maximum, zero weight); later uses read r[i] as it is.
     auto slot_vec = [&](int i) -> u32x4 {
-      // lanes past the row end see -inf (no maximum, zero weight)
-      return i * kRsThreads + tid < nvec ? r[i] : fill;
+      r[i] = i * kRsThreads + tid < nvec ? r[i] : fill;
+      return r[i];
     };
     unsigned int key;
     if constexpr (DT == DSPARK_BF16) {
@@ -369,7 +372,7 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
           if (i * kRsThreads < nvec) {
-            const u32x4 d = slot_vec(i);
+            const u32x4 d = r[i];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
               const unsigned int kw = argmax::bf16x2_keys(d[w]);
@@ -420,7 +423,7 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
 #pragma unroll
       for (int i = SLOTS - 1; i >= 0; --i) {
         if (i * kRsThreads < nvec) {
-          const u32x4 d = slot_vec(i);
+          const u32x4 d = r[i];
           const unsigned int base = (unsigned int)(i * kRsThreads + tid) * kEpv;
 #pragma unroll
           for (int w = 3; w >= 0; --w) {
@@ -436,11 +439,11 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       cand = argmax::wave_min(cand);
-      if (lane == 0) s_key[wave] = cand;
+      if (lane == 0) s_idx[wave] = cand;
       __syncthreads();
-      idx = s_key[0];
+      idx = s_idx[0];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) idx = min(idx, s_key[w]);
+      for (int w = 1; w < kWaves; ++w) idx = min(idx, s_idx[w]);
     }
     const unsigned long long best = argmax::pack_best(key, idx);
     const bool bad = argmax::best_bad<DT>(best);
@@ -460,7 +463,7 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) {
       if (cur.samp && !bad && i * kRsThreads < nvec) {
-        const u32x4 d = slot_vec(i);
+        const u32x4 d = r[i];
         float x[kEpv];
         widen<DT>(d, x);
 #pragma unroll

@@ -202,6 +202,7 @@ def test_sampling_edge_cases():
     (33, 6, 3, 131072, dv.BF16, 0.0),   # 16384 vectors: 16 full slots
     (34, 9, 5, 8192, dv.BF16, 0.2),     # 1024 vectors: the smallest row it takes
     (35, 10, 4, 32001, dv.F32, 0.0),    # 8000 vectors and a tail of 1, float32
+    (37, 16, 4, 32001, dv.F32, 0.5),    # float32 greedy rows: key, then index, merged
 ])
 def test_sampling_rowstat_path(seed, B, gamma, V, dt, greedy):
     c = rand_case(seed, B, gamma, V, dt, greedy_frac=greedy)
@@ -227,6 +228,29 @@ def test_sampling_rowstat_special_rows():
     c["tgt"][cu[7], 100] = 0xFFC1                                # negative NaN
     got, ref = both(c, "rowstat special rows")
     assert ref["status"] & S.DATA_BAD_LOGITS
+
+
+def test_sampling_rowstat_greedy_special_rows():
+    """Greedy rows in the row-statistics kernel: the first index of the
+    maximum when the maximum is negative (exact keys, then the index from the
+    same workgroup), tied, NaN (highest, first one wins) or in the tail."""
+    c = rand_case(38, 8, 4, 10007, dv.BF16, greedy_frac=1.0)
+    cu, V = c["cu"], c["V"]
+    t32 = lambda row: gen.f32_to_bf16_bits(np.asarray(row, np.float32))
+    rng = np.random.default_rng(38)
+    c["tgt"][cu[0]] = t32(rng.normal(-20.0, 1.0, V))          # negative maximum
+    row = np.full(V, -7.0, np.float32)
+    row[[500, 9000, 9100]] = -2.0                               # negative, tied three times
+    c["tgt"][cu[1]] = t32(row)
+    row = rng.normal(0, 2.0, V).astype(np.float32)
+    row[[77, 4000]] = 30.0                                      # positive tie
+    c["tgt"][cu[2]] = t32(row)
+    c["tgt"][cu[3], [900, 20]] = 0x7FC0                         # two NaNs: the first, 20
+    row = rng.normal(0, 2.0, V).astype(np.float32)
+    row[V - 2] = 50.0                                           # maximum in the tail
+    c["tgt"][cu[4]] = t32(row)
+    c["tgt"][cu[5], 33] = 0xFFC1                                # a negative NaN
+    both(c, "rowstat greedy special rows")
 
 
 def test_sampling_full_size_cfg3_sampled_requests():
