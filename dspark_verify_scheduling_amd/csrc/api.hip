@@ -116,6 +116,30 @@ size_t ws_bytes(int max_rows, int chunks) {
 
 }  // namespace
 
+namespace dspark {
+
+hipError_t current_cu_count(int* cus) {
+  // per device; a racing first query stores the same value
+  constexpr int kMaxDevices = 64;
+  static int cache[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && cache[dev] > 0) {
+    *cus = cache[dev];
+    return hipSuccess;
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (n < 1) n = 1;
+  if (dev >= 0 && dev < kMaxDevices) cache[dev] = n;
+  *cus = n;
+  return hipSuccess;
+}
+
+}  // namespace dspark
+
 extern "C" {
 
 int32_t dspark_version(void) { return (1 << 16) | 2; }

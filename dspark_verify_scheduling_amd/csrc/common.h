@@ -185,6 +185,10 @@ constexpr int kRsMaxSlots = 16;         // 16-byte register slots per thread, at
 constexpr int kRsMaxList = 64;          // rows per row-statistics workgroup, at most
 hipError_t launch_sampling(const SampArgs& a, dspark_dtype dt, hipStream_t s);
 
+// Compute units of the current device, queried once per device (the
+// persistent kernels launch one workgroup per CU).
+hipError_t current_cu_count(int* cus);
+
 // ---------------------------------------------------------------- helpers
 
 __device__ inline int lane_id() { return threadIdx.x & (kWave - 1); }

@@ -892,13 +892,12 @@ hipError_t launch_dt(SampArgs a, hipStream_t s) {
   // one persistent workgroup per CU, at most kRsMaxList rows each
   int grid = 0;
   if (a.B > 0 && a.nvec >= kRsThreads && a.nvec <= kRsMaxSlots * kRsThreads) {
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = 1;
+    hipError_t e = current_cu_count(&cus);
     if (e != hipSuccess) return e;
     const long long slots = (long long)a.B * (2 * a.gamma + 1);
     const long long need = (slots + kRsMaxList - 1) / kRsMaxList;
-    grid = (int)std::max<long long>(std::min<long long>(cus > 0 ? cus : 1, slots), need);
+    grid = (int)std::max<long long>(std::min<long long>(cus, slots), need);
   }
   a.rowstat = grid > 0;
   hipError_t e;

@@ -567,11 +567,10 @@ hipError_t launch_tv(const TvArgs& a, dspark_dtype dt, hipStream_t s) {
     const int n_lds = a.nvec > kResRegSpan ? a.nvec - kResRegSpan : 0;
     if (n_lds <= kResLdsMaxPairs) {
       // one persistent workgroup per CU (the registers hold one per CU)
-      int dev = 0, cus = 0;
-      hipError_t e = hipGetDevice(&dev);
-      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      int cus = 1;
+      hipError_t e = current_cu_count(&cus);
       if (e != hipSuccess) return e;
-      const int grid = pairs < cus ? pairs : (cus > 0 ? cus : 1);
+      const int grid = pairs < cus ? pairs : cus;
       const size_t lds = (size_t)2 * n_lds * sizeof(u32x4);
       const bool full = n_lds > 0 || a.nvec == kResRegSpan;
       void (*kern)(TvArgs);
