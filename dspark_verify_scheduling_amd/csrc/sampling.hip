@@ -889,15 +889,17 @@ template <dspark_dtype DT>
 hipError_t launch_dt(SampArgs a, hipStream_t s) {
   const long long units = (long long)a.B * (2 * a.gamma + 1) * a.chunks;
   // rows of 1024 to 16384 vectors take the one-read row-statistics kernel:
-  // one persistent workgroup per CU, at most kRsMaxList rows each
+  // one persistent workgroup per CU, at most kRsMaxList rows each. Every
+  // workgroup scans all the slots to find its rows, so larger batches (more
+  // than kRsMaxList slots per CU) keep the two-read kernels.
   int grid = 0;
   if (a.B > 0 && a.nvec >= kRsThreads && a.nvec <= kRsMaxSlots * kRsThreads) {
     int cus = 1;
     hipError_t e = current_cu_count(&cus);
     if (e != hipSuccess) return e;
     const long long slots = (long long)a.B * (2 * a.gamma + 1);
-    const long long need = (slots + kRsMaxList - 1) / kRsMaxList;
-    grid = (int)std::max<long long>(std::min<long long>(cus, slots), need);
+    const int g = (int)std::min<long long>(cus, slots);
+    if (slots <= (long long)kRsMaxList * g) grid = g;
   }
   a.rowstat = grid > 0;
   hipError_t e;

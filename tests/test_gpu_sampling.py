@@ -253,6 +253,34 @@ def test_sampling_rowstat_greedy_special_rows():
     both(c, "rowstat greedy special rows")
 
 
+def test_sampling_many_slots_two_read_path():
+    """More than 64 slots per CU (B = 1000, gamma = 8: 17,000 slots) with rows
+    the row-statistics kernel could hold (V = 8192 bf16): the batch keeps the
+    two-read kernels. 40 requests are checked against the oracle."""
+    B, G, V = 1000, 8, 8192
+    rng = np.random.default_rng(41)
+    lens = rng.integers(1, G + 2, B)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total = int(cu[-1])
+    tgt = gen.f32_to_bf16_bits(rng.normal(0, 2.5, (total, V)).astype(np.float32))
+    drf = gen.f32_to_bf16_bits(rng.normal(0, 2.5, (B * G, V)).astype(np.float32))
+    drafts = rng.integers(0, V, (B, G)).astype(np.int32)
+    temps = rng.uniform(0.5, 1.5, B).astype(np.float32)
+    temps[rng.random(B) < 0.2] = 0.0
+    ra = rng.integers(0, 2**32, (B, G), dtype=np.uint64).astype(np.uint32)
+    rs = rng.integers(0, 2**32, (B, G + 1), dtype=np.uint64).astype(np.uint32)
+    prefix = rng.integers(5, 500, B).astype(np.int32)
+    got = run_gpu(B, G, V, dv.BF16, tgt, drf, cu, drafts, temps, ra, rs, prefix, tag="17000 slots")
+    assert got["meta"].tolist() == [total, 0]
+    reqs = np.sort(rng.choice(B, 40, replace=False))
+    sub_cu = np.concatenate([[0], np.cumsum(lens[reqs])]).astype(np.int32)
+    sub_tgt = np.concatenate([tgt[cu[r]:cu[r + 1]] for r in reqs])
+    sub_drf = np.concatenate([drf[r * G:(r + 1) * G] for r in reqs])
+    ref = S.accept_sampling(len(reqs), G, sub_tgt, sub_drf, "bf16", sub_cu, drafts[reqs],
+                            temps[reqs], ra[reqs], rs[reqs], prefix_lens=prefix[reqs])
+    check(got, ref, None, reqs=reqs)
+
+
 def test_sampling_full_size_cfg3_sampled_requests():
     """B = 256, gamma = 8, V = 129280 bf16 on the planned cfg3 layout, in the
     launch configuration the benchmark times; the oracle checks 48 requests."""
