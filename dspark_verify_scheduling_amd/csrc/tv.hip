@@ -9,16 +9,17 @@
 // Computation. With base-2 log-partitions A_q = log2 sum_x 2^(q_x log2 e) (and
 // the same for p), min(u_x, v_x) = 2^min(q_x log2 e - A_q, p_x log2 e - A_p),
 // so a = sum_x 2^min(...) needs one exponential per element pair once the
-// partitions are known. One workgroup of 1024 threads per (draft row, target
-// row) pair:
-//   pass 1: the running (max, sum of 2^(x log2 e - max)) of each row; the
-//           workgroup merges the threads';
+// partitions are known. Two passes over each (draft row, target row) pair:
+//   pass 1: each thread's (offset, sum of 2^(x log2 e - offset)) of each row;
+//           the workgroup merges the threads' into A_q and A_p;
 //   pass 2: the sum of 2^min(...) over the same rows.
-// Rows that fit on one CU (bf16 V up to 130055) take tv_resident_kernel,
-// which keeps the pair in registers and LDS between the passes and so reads
-// it from HBM once. Longer rows take tv_kernel, which streams them twice
-// (pass 1 with ordinary loads, pass 2 with nontemporal ones); the pair's rows
-// are then mostly gone from the XCD's 4 MB L2 when pass 2 comes back to them.
+// Rows that fit on one CU (bf16 V up to 130055) take tv_resident_kernel: one
+// persistent workgroup per CU keeps each pair in registers and LDS between
+// the passes, so every logit is read from HBM once, and loads the next pair
+// while it finishes the current one. Longer rows take tv_kernel, one
+// workgroup per pair, which streams them twice (pass 1 with ordinary loads,
+// pass 2 with nontemporal ones); the pair's rows are then mostly gone from the
+// XCD's 4 MB L2 when pass 2 comes back to them.
 // Exponentials are the raw v_exp_f32 (exp2 without the denormal-range fix-up:
 // results below 2^-126 are negligible in a sum that is about 1). The result is
 // clamped to at most 1; rounding can exceed 1 by ~1e-7.
@@ -61,9 +62,10 @@ __device__ inline float elem(const unsigned char* row, int i) {
   }
 }
 
-// Running log-partition state in base-2 units: mL = max(x) * log2 e, clamped
-// to >= -FLT_MAX (so -inf inputs and empty states stay finite), and
-// s = sum 2^(x log2 e - mL).
+// Partial log-partition state in base-2 units: s = sum 2^(x log2 e - mL)
+// over the elements seen, mL >= -FLT_MAX finite (so -inf inputs and empty
+// states stay finite). The streaming kernel keeps mL at the running maximum;
+// the resident kernel uses a fixed offset per thread.
 struct Stat {
   float mL, s;
 };
@@ -190,24 +192,6 @@ __global__ __launch_bounds__(kTvThreads) void tv_kernel(TvArgs a) {
   }
   const float total = block_sum<float, kTvThreads>(acc, wsf);
   if (tid == 0) a.a_out[pair] = total > 1.0f ? 1.0f : total;
-}
-
-// One row's 16 bytes into its running statistics.
-template <dspark_dtype DT>
-__device__ inline void stat_add_vec(Stat& st, const u32x4& d) {
-  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
-  float x[kEpv];
-  widen<DT>(d, x);
-  float bm = x[0];
-#pragma unroll
-  for (int i = 1; i < kEpv; ++i) bm = fmaxf(bm, x[i]);
-  stat_add<kEpv>(st, x, bm);
-}
-
-template <dspark_dtype DT>
-__device__ inline void stat_add_pair(Stat& sq, Stat& sp, const u32x4& dq, const u32x4& dp) {
-  stat_add_vec<DT>(sq, dq);
-  stat_add_vec<DT>(sp, dp);
 }
 
 // Sum of 2^(x log2 e - off) over one row's 16 bytes.
