@@ -49,6 +49,8 @@ namespace {
 
 using namespace argmax;
 
+constexpr int kMergeRound = 8;  // partial loads per row in flight at once
+
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kAccThreads) void accept_argmax_kernel(AcceptArgs a) {
   __shared__ UnitSmem sm;
@@ -84,11 +86,43 @@ __global__ __launch_bounds__(kAccThreads) void accept_argmax_kernel(AcceptArgs a
   }
 }
 
+// A partial's low word holds 0xFFFFFFFF - index, so the largest partial is
+// the first position of the row's maximum.
+__device__ inline int partial_index(unsigned long long m) {
+  return (int)(0xFFFFFFFFu - (unsigned int)(m & 0xFFFFFFFFu));
+}
+
 __device__ inline int merge_row(const AcceptArgs& a, int row) {
   const unsigned long long* p = a.partials + (size_t)row * a.chunks;
   unsigned long long m = 0;
   for (int c = 0; c < a.chunks; ++c) m = p[c] > m ? p[c] : m;
-  return (int)(0xFFFFFFFFu - (unsigned int)(m & 0xFFFFFFFFu));
+  return partial_index(m);
+}
+
+// Maxima of two rows' partials (rows ra and rb, both below the number of rows
+// the argmax pass wrote). Each round issues all sixteen loads before the
+// first compare; chunk indices past the last repeat it, which leaves the
+// maximum unchanged.
+__device__ inline void merge_two_rows(const AcceptArgs& a, int ra, int rb, int& ia, int& ib) {
+  const unsigned long long* pa = a.partials + (size_t)ra * a.chunks;
+  const unsigned long long* pb = a.partials + (size_t)rb * a.chunks;
+  const int last = a.chunks - 1;
+  unsigned long long ma = 0, mb = 0;
+  for (int c0 = 0; c0 <= last; c0 += kMergeRound) {
+    unsigned long long va[kMergeRound], vb[kMergeRound];
+#pragma unroll
+    for (int k = 0; k < kMergeRound; ++k) {
+      va[k] = pa[min(c0 + k, last)];
+      vb[k] = pb[min(c0 + k, last)];
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeRound; ++k) {
+      ma = va[k] > ma ? va[k] : ma;
+      mb = vb[k] > mb ? vb[k] : mb;
+    }
+  }
+  ia = partial_index(ma);
+  ib = partial_index(mb);
 }
 
 // One wave per request (blockIdx.x = r), plus a grid-stride pass that writes
@@ -125,12 +159,18 @@ __global__ __launch_bounds__(kWave) void accept_finalize_kernel(AcceptArgs a) {
   } else {
     ok = c0 >= 0 && len >= 1 && len <= G + 1 && c0 + len <= total_eff;
   }
-  // round 2
+  // round 2: the lane's row of the row pass and its row of the request, read
+  // together at indices clamped into the rows written (results outside the
+  // real ranges are discarded)
   const int i0 = blockIdx.x * kWave + lane;
   const int n_rows = CAP ? G + 1 : len;  // rows whose predictions are read
   const bool need = has_req && (CAP || ok);
-  const int g0 = i0 < total_eff ? merge_row(a, i0) : 0;
-  const int m0 = (need && lane < n_rows) ? merge_row(a, c0 + lane) : 0;
+  int g0 = 0, m0 = 0;
+  if (total_eff > 0) {
+    const int last = total_eff - 1;
+    const int rr = min(min(max(c0, 0), last) + lane, last);
+    merge_two_rows(a, min(i0, last), rr, g0, m0);
+  }
   const int m1 = (need && lane + kWave < n_rows) ? merge_row(a, c0 + lane + kWave) : 0;
   if (i0 < total_eff) a.row_am[i0] = g0;
   for (int i = i0 + gridDim.x * kWave; i < total_eff; i += gridDim.x * kWave) {
