@@ -352,6 +352,26 @@ def main():
     plan_us = 1e3 * ev[0].elapsed_time(ev[1]) / reps
     pack_us = 1e3 * ev[1].elapsed_time(ev[2]) / reps
 
+    # launch floor of the latency-bound planner: one event pair around a single
+    # launch, the queue drained before each, for plan+pack and for the smallest
+    # kernel torch launches (a one-element fill); medians of 50
+    floor_t = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def single_launch_us(launch):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        out = []
+        for _ in range(50):
+            torch.cuda.synchronize()
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(1e3 * e0.elapsed_time(e1))
+        return statistics.median(out)
+
+    plan_pack_single_us = single_launch_us(lambda: plan_pack(stream))
+    launch_floor_us = single_launch_us(floor_t.zero_)
+
     graphs = []
     gs = torch.cuda.Stream()
     gs.wait_stream(stream)
@@ -549,6 +569,8 @@ def main():
         "plan_pack_us": plan_pack_us,
         "plan_us": plan_us,
         "pack_us": pack_us,
+        "plan_pack_single_launch_us": plan_pack_single_us,
+        "launch_floor_us": launch_floor_us,
         "accept_us_median": statistics.median(acc_us),
         "accept_static": {"rows": static_rows, "us": static_us, "GB/s": static_gbs,
                           "frac": static_gbs / PEAK_HBM_GBS},
