@@ -415,6 +415,32 @@ def test_accept_edge_rows(V, ld, dt):
     _check_accept(got, ref, int(cu[-1]))
 
 
+@pytest.mark.parametrize("dt", [0, 1])
+def test_accept_gamma_64(dt):
+    """gamma = 64, the largest: a request of gamma + 1 = 65 rows reads one row
+    more than a wave has lanes, and the match count runs over 64 drafts."""
+    rng = np.random.default_rng(64 + dt)
+    B, G, V = 5, 64, 2048
+    lens = np.array([65, 65, 1, 30, 64], np.int32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    x = rng.normal(0, 2, (int(cu[-1]) + 3, V)).astype(np.float32)
+    rows = x if dt == 0 else (x.view(np.uint32) >> 16).astype(np.uint16)
+    am = oracle.row_argmax(as_f32_rows(rows, "bf16" if dt else "f32"))
+    # draft k matches the prediction of row k - 1 up to a chosen first miss
+    first_miss = [G, G - 1, 0, 10, 63]  # G: every draft matches
+    drafts = np.empty((B, G), np.int32)
+    for r in range(B):
+        for k in range(G):
+            row = min(int(cu[r]) + k, x.shape[0] - 1)
+            drafts[r, k] = am[row] if k < first_miss[r] else (am[row] + 1) % V
+    prefix = rng.integers(0, 1000, B).astype(np.int32)
+    got = accept(B, G, V, dt, rows, V, cu, drafts, prefix, tag=f"gamma=64 dt={dt}")
+    ref = oracle.accept(B, G, rows, "bf16" if dt else "f32", cu, drafts, prefix,
+                        max_rows=rows.shape[0])
+    assert ref["num_correct"].tolist() == [64, 63, 0, 10, 63]
+    _check_accept(got, ref, int(cu[-1]))
+
+
 def test_accept_malformed_layouts_and_reuse():
     rng = np.random.default_rng(5)
     B, G, V = 4, 3, 4096

@@ -130,6 +130,24 @@ def test_cap_accept_bad_lengths_and_shapes(V, ld, dt):
     _check_cap(got, ref)
 
 
+def test_cap_accept_gamma_64():
+    """gamma = 64: 65 strided rows per request, a ceiling of up to 64."""
+    rng = np.random.default_rng(640)
+    B, gamma, V = 4, 64, 1500
+    x = rng.normal(0, 2, (B * (gamma + 1), V)).astype(np.float32)
+    am = oracle.row_argmax(x).reshape(B, gamma + 1)
+    drafts = am[:, :gamma].copy()
+    drafts[1, 40] = (drafts[1, 40] + 1) % V  # request 1 misses at draft 41
+    drafts[3, 0] = (drafts[3, 0] + 1) % V  # request 3 misses at once
+    lens = np.array([65, 65, 12, 65], np.int32)
+    prefix = rng.integers(0, 1000, B).astype(np.int32)
+    got = cap_accept(B, gamma, V, dv.F32, x, V, lens, drafts, prefix, tag="gamma=64")
+    ref = oracle.cap_accept(B, gamma, x, "f32", lens, drafts, prefix)
+    assert ref["ceiling"].tolist() == [64, 40, 64, 0]
+    assert ref["num_correct"].tolist() == [64, 40, 11, 0]
+    _check_cap(got, ref)
+
+
 def test_cap_accept_empty_batch():
     got = cap_accept(0, 3, 64, dv.F32, None, 64, np.zeros(0, np.int32),
                      np.zeros((0, 3), np.int32), tag="B=0")
