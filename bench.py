@@ -228,9 +228,9 @@ def cpu_baseline(w, lens_ref, packed_host, total, budget_s):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the per-step verify path "
-                                   "shards by request across GPUs (see the design notes), but "
-                                   "no multi-GPU run is provided", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "bench.py measures one GPU only; the per-step verify path "
+                                   "would shard by request across GPUs, but no multi-GPU run "
+                                   "is provided", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch

@@ -128,7 +128,7 @@ __device__ inline void merge_two_rows(const AcceptArgs& a, int ra, int rb, int& 
 // One wave per request (blockIdx.x = r), plus a grid-stride pass that writes
 // the argmax of every row. CAP = false: packed rows cu[r] .. cu[r+1]-1.
 // CAP = true: strided rows r * (gamma + 1) + j, every one of them computed.
-// The loads come in two rounds, each issued before anything waits on it:
+// The loads come in two batches, each issued before anything waits on it:
 // first the layout words, drafts and prefix; then every partial the wave
 // needs (its row of the row pass and the request's rows). Stores follow.
 template <bool CAP>
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kWave) void accept_finalize_kernel(AcceptArgs a) {
   const int G = a.gamma;
   const int r = blockIdx.x;
   const bool has_req = r < a.B;
-  // round 1
+  // first batch of loads: layout words, drafts, prefix
   const int total = CAP ? a.fixed_rows : a.cu[a.B];
   int c0 = 0, len = 0;  // first row, verify length
   if (has_req) {
@@ -159,8 +159,8 @@ __global__ __launch_bounds__(kWave) void accept_finalize_kernel(AcceptArgs a) {
   } else {
     ok = c0 >= 0 && len >= 1 && len <= G + 1 && c0 + len <= total_eff;
   }
-  // round 2: the lane's row of the row pass and its row of the request, read
-  // together at indices clamped into the rows written (results outside the
+  // second batch: the lane's row of the row pass and its row of the request,
+  // read together at indices clamped into the rows written (results outside the
   // real ranges are discarded)
   const int i0 = blockIdx.x * kWave + lane;
   const int n_rows = CAP ? G + 1 : len;  // rows whose predictions are read
