@@ -272,7 +272,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
       s = cr[k - 1];
       if (k > 1 && s > cr[k - 2]) bad = 1;
     } else {
-      for (int i = 1; i < k; ++i) s = __fmul_rn(s, cr[i]);
+      // factors 1 .. k-1 in batches of 8, each batch's LDS reads issued before
+      // its first multiply; a read past the request's last position is never
+      // multiplied, so the product keeps its left-to-right order
+      for (int i0 = 1; i0 < k; i0 += 8) {
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = cr[min(i0 + j, G - 1)];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s = i0 + j < k ? __fmul_rn(s, f[j]) : s;
+      }
     }
     if (a.surv_out) a.surv_out[idx] = s;
     if (k < lmin) {
