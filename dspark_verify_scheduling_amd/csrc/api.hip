@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 
@@ -119,21 +120,26 @@ size_t ws_bytes(int max_rows, int chunks) {
 namespace dspark {
 
 hipError_t current_cu_count(int* cus) {
-  // per device; a racing first query stores the same value
+  // per device, 0 until queried; threads that race on the first query store
+  // the same value, through atomics so that the race is well defined
   constexpr int kMaxDevices = 64;
-  static int cache[kMaxDevices] = {};
+  static std::atomic<int> cache[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < kMaxDevices && cache[dev] > 0) {
-    *cus = cache[dev];
-    return hipSuccess;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached) {
+    const int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) {
+      *cus = n;
+      return hipSuccess;
+    }
   }
   int n = 0;
   e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   if (n < 1) n = 1;
-  if (dev >= 0 && dev < kMaxDevices) cache[dev] = n;
+  if (cached) cache[dev].store(n, std::memory_order_relaxed);
   *cus = n;
   return hipSuccess;
 }
