@@ -67,6 +67,7 @@ typedef unsigned __int128 u128;
 
 constexpr float kLog2e16 = 94548.4609375f;  // float32 nearest to 2^16 log2(e)
 constexpr unsigned int kJmax = 1u << 21;     // from here on the weight is 0
+constexpr float kUcut = kJmax - 0.5f;         // j = RNE(u) < kJmax iff u < kUcut
 constexpr int kRedWaves = kSampThreads / kWave;
 static_assert(kSampThreads == kAccThreads && kSampVecsPerThread == kAccVecsPerThread,
               "the max kernel runs the greedy accept's unit argmax");
@@ -83,13 +84,17 @@ __device__ inline float temp_coef(float T) { return __fdiv_rn(kLog2e16, T); }
 // - j = RNE(u) < 2^21 exactly when u < 2^21 - 1/2 (a tie there rounds up, to
 //   even); past that (or for u = +inf) h is the zero pair, so y = 0 and the
 //   rounding shift gives 0 whatever n the bits hold.
+// W of the file header for x in a row with maximum m, c = K / T.
 __device__ inline unsigned int weight(float x, float m, float c, const uint2* Bt) {
   const float u = __fmul_rn(__fsub_rn(m, x), c);  // >= 0, or +inf
+  // adding 1.5 * 2^23 rounds u in [0, 2^22) to the nearest integer j (ties to
+  // even) and leaves j in the low 22 mantissa bits
   const unsigned int bits = __float_as_uint(__fadd_rn(u, 12582912.0f));
-  const unsigned int n = __builtin_amdgcn_ubfe(bits, 16, 5);
-  const unsigned int h = u < 2097151.5f ? __builtin_amdgcn_ubfe(bits, 8, 8) : 256u;
+  const unsigned int n = __builtin_amdgcn_ubfe(bits, 16, 5);  // j >> 16 while j < 2^21
+  // past the cut-off the zero pair at index 256 gives W = 0, whatever n is
+  const unsigned int h = u < kUcut ? __builtin_amdgcn_ubfe(bits, 8, 8) : 256u;
   const unsigned int r = bits & 255u;
-  const uint2 bd = Bt[h];
+  const uint2 bd = Bt[h];  // (B[h], B[h] - B[h + 1])
   const unsigned int y = bd.x - (((unsigned int)__umul24(bd.y, r) + 128u) >> 8);
   return (y + ((1u << n) >> 1)) >> n;
 }
