@@ -87,12 +87,25 @@ __device__ inline float advance_survival(const StsArgs& a, int k, int n, float t
   return s;
 }
 
+// RN32(z / T) as RN32(RN64(z * RN64(1 / T))), for any float32 z and T: the
+// double value is within 2^-52 (relative) of z / T, while z / T is never a
+// float32 rounding midpoint and is always more than 2^-49 (relative) away
+// from one. (A midpoint has at most 25 significant bits and is odd in its
+// last one; times T it has more bits than z, so z - M * T is a nonzero
+// multiple of 2^e with 2^e > |z| * 2^-49.) Zeros, infinities and NaNs give
+// the quotient's own special value.
+__device__ inline float div_by_rcp(double z, double rcp_t) {
+  return __double2float_rn(__dmul_rn(z, rcp_t));
+}
+
 __global__ __launch_bounds__(kStsBinThreads) void sts_bin_kernel(StsArgs a, int k) {
   extern __shared__ long long hist[];  // [nT][2 * nbins + 1]: labels, survival sums, Brier
+  __shared__ double s_rcp[DSPARK_STS_MAX_GRID];  // RN64(1 / T) per candidate
   __shared__ int s_prev;
   const int tid = threadIdx.x;
   const int nb = a.nbins, nT = a.n_t, stride = 2 * nb + 1;
   for (int i = tid; i < nT * stride; i += kStsBinThreads) hist[i] = 0;
+  for (int i = tid; i < nT; i += kStsBinThreads) s_rcp[i] = __drcp_rn((double)a.grid[i]);
   if (k > 0 && tid < kWave) {
     const int t = select_candidate(a, k - 1, blockIdx.x == 0);
     if (tid == 0) s_prev = t;
@@ -107,10 +120,10 @@ __global__ __launch_bounds__(kStsBinThreads) void sts_bin_kernel(StsArgs a, int 
   const int r1 = min(r0 + a.per_block, a.N);
   for (int n = r0 + slot; n < r1; n += kStsPass) {
     const float sp = advance_survival(a, k, n, t_prev, phase == 0);
-    const float zk = a.z[(size_t)n * a.gamma + k];
+    const double zk = (double)a.z[(size_t)n * a.gamma + k];
     const unsigned long long y = a.labels[(size_t)n * a.gamma + k] ? 1ull : 0ull;
     for (int j = phase, t = t0; j < nT; j += kStsPhases) {
-      const float s = __fmul_rn(sp, sigmoid_cr(__fdiv_rn(zk, a.grid[t])));
+      const float s = __fmul_rn(sp, sigmoid_cr(div_by_rcp(zk, s_rcp[t])));
       const double sd = s == s ? (double)s : 0.0;  // a NaN survival counts as 0
       int b = (int)floor(sd * nb);
       b = b < nb ? b : nb - 1;
