@@ -460,6 +460,17 @@ def main():
     assert smeta.tolist() == [total, 0]
     scat_bytes = 2 * total * V * esize + (B + 1) * 4
     scat_gbs = scat_bytes / (scat_us * 1e-6) / 1e9
+    # its practical ceiling: torch's device copy of the same rows, contiguous
+    for i in range(5):
+        dst[:total].copy_(packed[i % n_rot][:total])
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(n_static):
+        dst[:total].copy_(packed[i % n_rot][:total])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    copy_us = 1e3 * start.elapsed_time(stop) / n_static
+    copy_gbs = 2 * total * V * esize / (copy_us * 1e-6) / 1e9
     del dst
     torch.cuda.empty_cache()
 
@@ -577,7 +588,9 @@ def main():
         "cap_accept": {"rows": static_rows, "us": cap_us, "GB/s": cap_gbs,
                        "frac": cap_gbs / PEAK_HBM_GBS},
         "scatter_to_strided": {"rows": total, "us": scat_us, "GB/s": scat_gbs,
-                               "frac": scat_gbs / PEAK_HBM_GBS, "bytes": scat_bytes},
+                               "frac": scat_gbs / PEAK_HBM_GBS, "bytes": scat_bytes,
+                               "torch_copy_same_rows_us": copy_us,
+                               "torch_copy_GB/s": copy_gbs},
         "sampling_accept": samp_res,
         "sts_fit": sts_res,
         "tv_pass": tv_res,

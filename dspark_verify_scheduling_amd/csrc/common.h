@@ -97,7 +97,8 @@ struct ScatterArgs {
   int32_t* meta;
 };
 constexpr int kScatterThreads = 256;
-constexpr int kScatterVecsPerThread = 8;
+constexpr int kScatterVecsPerThread = 2;
+constexpr int kScatterRows = 8;  // rows of a request copied per batch
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s);
 
 struct TvArgs {

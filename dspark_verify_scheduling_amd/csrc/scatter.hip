@@ -9,11 +9,13 @@
 //
 // A pure copy, bound by HBM bandwidth: every valid packed row is read once
 // (nontemporal, its last use) and written once to row r * stride + j. One
-// 256-thread workgroup per (request, unit of up to 2048 16-byte vectors)
-// copies that unit of each of the request's rows in turn, two rows in flight
-// at a time; a malformed request's workgroups exit at once. Workgroup 0 also
-// validates every request and writes the status, so no other workgroup
-// touches the meta words.
+// 256-thread workgroup per (request, unit of up to 512 16-byte vectors)
+// copies that unit of the request's rows, up to kScatterRows rows at a
+// time with every load of the batch issued before its first store, so a
+// request of many rows costs about one memory round trip per batch and there
+// are no idle workgroups. A malformed request's workgroups exit at once.
+// Workgroup 0 also validates every request and writes the status, so no
+// other workgroup touches the meta words.
 #include "common.h"
 
 namespace dspark {
@@ -53,26 +55,27 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a)
   if (!request_ok(a, r, total_eff, &c0, &len)) return;
   const int v0 = chunk * a.chunk_vecs;
   const int v1 = min(v0 + a.chunk_vecs, a.nvec);
-  constexpr int kV = kScatterVecsPerThread;
-  for (int j0 = 0; j0 < len; j0 += 2) {
-    const bool two = j0 + 1 < len;
-    const int j1 = two ? j0 + 1 : j0;  // the second row, if there is one
-    const u32x4* s0 = reinterpret_cast<const u32x4*>(a.src + (size_t)(c0 + j0) * a.src_ld);
-    const u32x4* s1 = reinterpret_cast<const u32x4*>(a.src + (size_t)(c0 + j1) * a.src_ld);
-    u32x4* d0 = reinterpret_cast<u32x4*>(a.dst + ((size_t)r * a.stride + j0) * a.dst_ld);
-    u32x4* d1 = reinterpret_cast<u32x4*>(a.dst + ((size_t)r * a.stride + j1) * a.dst_ld);
-    u32x4 x[kV], y[kV];
+  constexpr int kV = kScatterVecsPerThread, kR = kScatterRows;
+  for (int j0 = 0; j0 < len; j0 += kR) {
+    u32x4 x[kR][kV];
 #pragma unroll
-    for (int k = 0; k < kV; ++k) {
-      const int v = v0 + k * kScatterThreads + tid;
-      if (v < v1) x[k] = __builtin_nontemporal_load(s0 + v);
-      if (two && v < v1) y[k] = __builtin_nontemporal_load(s1 + v);
+    for (int i = 0; i < kR; ++i) {
+      const u32x4* s0 = reinterpret_cast<const u32x4*>(a.src + (size_t)(c0 + j0 + i) * a.src_ld);
+#pragma unroll
+      for (int k = 0; k < kV; ++k) {
+        const int v = v0 + k * kScatterThreads + tid;
+        x[i][k] = (u32x4){0u, 0u, 0u, 0u};  // a defined value: no wait before the load
+        if (j0 + i < len && v < v1) x[i][k] = __builtin_nontemporal_load(s0 + v);
+      }
     }
 #pragma unroll
-    for (int k = 0; k < kV; ++k) {
-      const int v = v0 + k * kScatterThreads + tid;
-      if (v < v1) d0[v] = x[k];
-      if (two && v < v1) d1[v] = y[k];
+    for (int i = 0; i < kR; ++i) {
+      u32x4* d0 = reinterpret_cast<u32x4*>(a.dst + ((size_t)r * a.stride + j0 + i) * a.dst_ld);
+#pragma unroll
+      for (int k = 0; k < kV; ++k) {
+        const int v = v0 + k * kScatterThreads + tid;
+        if (j0 + i < len && v < v1) d0[v] = x[i][k];
+      }
     }
   }
   // bytes after the last whole vector
