@@ -195,6 +195,21 @@ def test_scatter_parity(width, ld_src, ld_dst, dtype):
     assert np.all(got[:, width:] == -3), "bytes past row_bytes were written"
 
 
+def test_scatter_long_requests():
+    """stride 65 (gamma = 64): requests of 1..65 rows, lengths on both sides of
+    the eight-row batches, and a row width with a byte tail."""
+    rng = np.random.default_rng(65)
+    B, stride, width = 9, 65, 1025
+    lens = np.array([65, 64, 17, 16, 9, 8, 7, 1, 33], np.int64)
+    cu, packed, init = _scatter_case(rng, B, stride, width, 1032, 1040, np.int16, lens=lens)
+    got, meta = scatter(B, stride, cu, packed, width, init, tag="stride=65")
+    ref, ref_meta = oracle.scatter_to_strided(B, stride, cu, packed[:, :width], init[:, :width],
+                                              max_rows=packed.shape[0])
+    assert meta.tolist() == ref_meta.tolist() == [int(cu[-1]), 0]
+    _eq(got[:, :width], ref, "strided rows")
+    _eq(got[:, width:], init[:, width:], "destination padding")
+
+
 def test_scatter_planned_layout_round_trip():
     """The planned cfg3 layout: scatter the packed target rows back and find
     the original strided rows at every verified slot."""
