@@ -62,24 +62,21 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // per-workgroup histograms.
 struct StsGeom {
   int per_block, n_blocks;
-  size_t s_off[2], e_off, b_off, p_off, bytes;
+  size_t s_off[2], h_off, bytes;
 };
 
-StsGeom sts_geom(int N, int gamma, int n_t, int n_bins) {
+StsGeom sts_geom(int N, int n_t, int n_bins) {
   StsGeom g;
   // whole passes of kStsPass records per workgroup, at most kStsMaxBlocks
-  // workgroups (which bounds the histogram slots of the workspace)
+  // workgroups
   const int want = (N + dspark::kStsMaxBlocks - 1) / dspark::kStsMaxBlocks;
   g.per_block = std::max(1, (want + dspark::kStsPass - 1) / dspark::kStsPass) * dspark::kStsPass;
   g.n_blocks = N > 0 ? (N + g.per_block - 1) / g.per_block : 1;
   const size_t sv = align256((size_t)N * sizeof(float));
-  const size_t ev = align256((size_t)gamma * n_t * sizeof(long long));
   g.s_off[0] = 0;
   g.s_off[1] = sv;
-  g.e_off = 2 * sv;
-  g.b_off = g.e_off + ev;
-  g.p_off = g.b_off + ev;
-  g.bytes = g.p_off + align256((size_t)g.n_blocks * n_t * (2 * n_bins + 1) * sizeof(long long));
+  g.h_off = 2 * sv;  // three summed-histogram buffers
+  g.bytes = g.h_off + align256((size_t)3 * n_t * (2 * n_bins + 1) * sizeof(long long));
   return g;
 }
 
@@ -486,7 +483,7 @@ size_t dspark_sts_workspace_size(int32_t N, int32_t gamma, int32_t n_t, int32_t 
   if (N < 0 || N > DSPARK_STS_MAX_RECORDS || gamma < 1 || gamma > DSPARK_MAX_GAMMA || n_t < 1 ||
       n_t > DSPARK_STS_MAX_GRID || n_bins < 1 || n_bins > DSPARK_STS_MAX_BINS)
     return 0;
-  return sts_geom(N, gamma, n_t, n_bins).bytes;
+  return sts_geom(N, n_t, n_bins).bytes;
 }
 
 dspark_status dspark_sts_fit(int32_t N, int32_t gamma, const float* z, const uint8_t* prefix_mask,
@@ -515,7 +512,7 @@ dspark_status dspark_sts_fit(int32_t N, int32_t gamma, const float* z, const uin
     return fail(DSPARK_E_INVALID, "dspark_sts_fit: z or prefix_mask is NULL");
   if (!temps || !t_index || !ece || !brier)
     return fail(DSPARK_E_INVALID, "dspark_sts_fit: an output pointer is NULL");
-  const StsGeom g = sts_geom(N, gamma, n_t, n_bins);
+  const StsGeom g = sts_geom(N, n_t, n_bins);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < g.bytes)
     return fail(DSPARK_E_WORKSPACE, "dspark_sts_fit: workspace needs %zu bytes, 256-byte aligned",
                 g.bytes);
@@ -538,9 +535,7 @@ dspark_status dspark_sts_fit(int32_t N, int32_t gamma, const float* z, const uin
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   a.s_work[0] = reinterpret_cast<float*>(ws + g.s_off[0]);
   a.s_work[1] = reinterpret_cast<float*>(ws + g.s_off[1]);
-  a.err_fx = reinterpret_cast<long long*>(ws + g.e_off);
-  a.brier_fx = reinterpret_cast<long long*>(ws + g.b_off);
-  a.partials = reinterpret_cast<long long*>(ws + g.p_off);
+  a.hists = reinterpret_cast<long long*>(ws + g.h_off);
   return launched(dspark::launch_sts(a, (hipStream_t)stream), "dspark_sts_fit");
 }
 

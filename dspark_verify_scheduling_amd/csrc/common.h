@@ -127,16 +127,14 @@ struct StsArgs {
   double* ece_grid;         // [gamma, n_t] or null
   float* surv_out;          // [N, gamma] or null
   float* s_work[2];         // workspace: two [N] survival buffers, used alternately
-  long long* err_fx;        // workspace: [gamma, n_t] n * ECE * 2^40 per candidate
-  long long* brier_fx;      // workspace: [gamma, n_t] n * Brier * 2^40 per candidate
-  long long* partials;      // workspace: [n_blocks, n_t, 2 * nbins + 1]
+  long long* hists;         // workspace: [3][n_t][2 * nbins + 1] summed histograms,
+                            // position k in buffer k % 3
 };
 constexpr int kStsPass = 256;        // records a bin workgroup takes at a time
 constexpr int kStsPhases = 4;        // threads per record, each on every 4th candidate
 constexpr int kStsBinThreads = kStsPass * kStsPhases;
-constexpr int kStsReduceThreads = 1024;
-constexpr int kStsThreads = 256;     // finish kernel
-constexpr int kStsMaxBlocks = 1024;  // bin workgroups (histogram slots) at most
+constexpr int kStsThreads = 256;     // finish and clear kernels
+constexpr int kStsMaxBlocks = 1024;  // bin workgroups at most
 hipError_t launch_sts(const StsArgs& a, hipStream_t s);
 
 // Chain speculative-sampling accept (sampling.hip).

@@ -14,21 +14,24 @@
 // (nearest), so every sum is an int64 and the argmin over the grid is an
 // exact, order-independent decision. Brier terms likewise.
 //
-// Per position k:
-//   sts_bin_kernel: each workgroup takes a range of records, four threads per
-//     record, each on every fourth candidate. For k >= 1 it first picks the
-//     temperature of position k - 1 (the smallest summed error, the first
-//     candidate on ties; workgroup 0 records it) and advances the stored
-//     survival by it (S_{k-1} = RN32(S_{k-2} * sigmoid(z / T*))). Then, for
-//     every grid temperature T, S = RN32(S_{k-1} * sigmoid(RN32(z_k / T)))
-//     is binned into LDS histograms (label count and survival sum per bin,
-//     Brier sum per T) with LDS atomics, and the workgroup writes its
-//     histograms to its slot of the workspace (no cross-workgroup atomics).
-//   sts_reduce_kernel: one workgroup per candidate sums the slots and forms
-//     n * ECE and n * Brier for it.
-// sts_finish_kernel picks the last position's temperature and advances the
-// survival by it. The survival lives in two buffers used alternately, so a
-// kernel never overwrites what another of its threads still has to read.
+// Per position k, sts_bin_kernel: each workgroup takes a range of records,
+// four threads per record, each on every fourth candidate. For k >= 1 it
+// first picks the temperature of position k - 1 from that position's summed
+// histograms (the smallest n * ECE, the first candidate on ties; workgroup 0
+// records it) and advances the stored survival by it (S_{k-1} =
+// RN32(S_{k-2} * sigmoid(z / T*))). Then, for every grid temperature T,
+// S = RN32(S_{k-1} * sigmoid(RN32(z_k / T))) is binned into LDS histograms
+// (label count and survival sum per bin, Brier sum per T) with LDS atomics,
+// and the workgroup adds them into the position's summed histograms with
+// 64-bit integer atomics (exact in any order).
+// The summed histograms rotate over three buffers: position k adds into
+// buffer k % 3, its successor reads it, and workgroup 0 of position k clears
+// buffer (k + 1) % 3, which no kernel touches from then until position k + 1
+// adds into it. sts_clear_kernel clears buffer 0 first, so the workspace
+// needs no initialization. sts_finish_kernel picks the last position's
+// temperature and advances the survival by it. The survival lives in two
+// buffers used alternately, so a kernel never overwrites what another of its
+// threads still has to read.
 #include <float.h>
 #include <limits.h>
 
@@ -45,31 +48,68 @@ constexpr double kFx = 0x1p40;
 
 __device__ inline long long fx40(double v) { return __double2ll_rn(v * kFx); }
 
-// Picks the temperature of position kk from the summed errors (one wave):
-// the smallest n * ECE, the first candidate on ties. Every lane returns it;
-// with `record` set, lane 0 also stores the position's results.
-__device__ int select_candidate(const StsArgs& a, int kk, bool record) {
-  const int lane = lane_id();
-  const long long* err = a.err_fx + (size_t)kk * a.n_t;
-  long long e = LLONG_MAX;
-  int t = INT_MAX;
-  for (int c = lane; c < a.n_t; c += kWave) {
-    const long long v = err[c];
-    if (v < e) e = v, t = c;  // c ascends, so equal errors keep the first
+// Shared memory of the candidate choice.
+struct SelectSmem {
+  long long err[DSPARK_STS_MAX_GRID];    // n * ECE * 2^40 per candidate
+  long long brier[DSPARK_STS_MAX_GRID];  // n * Brier * 2^40 per candidate
+  int t;
+};
+
+// Picks the temperature of position kk from its summed histograms h
+// ([n_t][2 * nbins + 1]): n * ECE = sum over bins of |labels * 2^40 - survival
+// sum|; the smallest wins, the first candidate on ties. Block-wide, one
+// (candidate, bin) pair per thread and round (a single round for up to
+// blockDim.x pairs); every thread returns the choice. With `record`, the
+// position's results are stored.
+__device__ int select_candidate(const StsArgs& a, const long long* h, int kk, bool record,
+                                SelectSmem& sm) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int nT = a.n_t, nb = a.nbins, stride = 2 * nb + 1;
+  for (int c = tid; c < nT; c += nthr) {
+    sm.err[c] = 0;
+    sm.brier[c] = h[(size_t)c * stride + 2 * nb];
   }
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const long long oe = __shfl_xor(e, off, kWave);
-    const int ot = __shfl_xor(t, off, kWave);
-    if (oe < e || (oe == e && ot < t)) e = oe, t = ot;
+  __syncthreads();
+  for (int i = tid; i < nT * nb; i += nthr) {
+    const int c = i / nb, b = i - c * nb;
+    const long long d = h[(size_t)c * stride + b] * (1ll << 40) - h[(size_t)c * stride + nb + b];
+    if (d != 0) {
+      atomicAdd(reinterpret_cast<unsigned long long*>(&sm.err[c]),
+                (unsigned long long)(d < 0 ? -d : d));
+    }
   }
-  if (record && lane == 0) {
-    const double scale = (double)a.N * kFx;
-    a.temps[kk] = a.grid[t];
-    a.t_index[kk] = t;
-    a.ece[kk] = a.N ? (double)e / scale : 0.0;
-    a.brier[kk] = a.N ? (double)a.brier_fx[(size_t)kk * a.n_t + t] / scale : 0.0;
+  __syncthreads();
+  if (tid < kWave) {
+    const int lane = tid;
+    long long e = LLONG_MAX;
+    int t = INT_MAX;
+    for (int c = lane; c < nT; c += kWave) {
+      const long long v = sm.err[c];
+      if (v < e) e = v, t = c;  // c ascends, so equal errors keep the first
+    }
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      const long long oe = __shfl_xor(e, off, kWave);
+      const int ot = __shfl_xor(t, off, kWave);
+      if (oe < e || (oe == e && ot < t)) e = oe, t = ot;
+    }
+    if (lane == 0) {
+      sm.t = t;
+      if (record) {
+        const double scale = (double)a.N * kFx;
+        a.temps[kk] = a.grid[t];
+        a.t_index[kk] = t;
+        a.ece[kk] = a.N ? (double)e / scale : 0.0;
+        a.brier[kk] = a.N ? (double)sm.brier[t] / scale : 0.0;
+      }
+    }
   }
-  return t;
+  if (record && a.ece_grid) {
+    for (int c = tid; c < nT; c += nthr) {
+      a.ece_grid[(size_t)kk * nT + c] = a.N ? (double)sm.err[c] / ((double)a.N * kFx) : 0.0;
+    }
+  }
+  __syncthreads();
+  return sm.t;
 }
 
 // S_{k-1} for record n: 1 at k = 0, else S_{k-2} times the calibrated
@@ -101,17 +141,23 @@ __device__ inline float div_by_rcp(double z, double rcp_t) {
 __global__ __launch_bounds__(kStsBinThreads) void sts_bin_kernel(StsArgs a, int k) {
   extern __shared__ long long hist[];  // [nT][2 * nbins + 1]: labels, survival sums, Brier
   __shared__ double s_rcp[DSPARK_STS_MAX_GRID];  // RN64(1 / T) per candidate
-  __shared__ int s_prev;
+  __shared__ SelectSmem s_sel;
   const int tid = threadIdx.x;
   const int nb = a.nbins, nT = a.n_t, stride = 2 * nb + 1;
+  const size_t hsize = (size_t)nT * stride;
   for (int i = tid; i < nT * stride; i += kStsBinThreads) hist[i] = 0;
   for (int i = tid; i < nT; i += kStsBinThreads) s_rcp[i] = __drcp_rn((double)a.grid[i]);
-  if (k > 0 && tid < kWave) {
-    const int t = select_candidate(a, k - 1, blockIdx.x == 0);
-    if (tid == 0) s_prev = t;
+  if (blockIdx.x == 0) {  // the buffer position k + 1 adds into
+    long long* next = a.hists + (size_t)((k + 1) % 3) * hsize;
+    for (size_t i = tid; i < hsize; i += kStsBinThreads) next[i] = 0;
   }
-  __syncthreads();
-  const float t_prev = k > 0 ? a.grid[s_prev] : 1.0f;
+  float t_prev = 1.0f;
+  if (k > 0) {
+    const long long* prev = a.hists + (size_t)((k - 1) % 3) * hsize;
+    t_prev = a.grid[select_candidate(a, prev, k - 1, blockIdx.x == 0, s_sel)];
+  } else {
+    __syncthreads();
+  }
   const int slot = tid % kStsPass, phase = tid / kStsPass;  // phase is wave-uniform
   // a lane visits candidates (lane + phase + 4 i) mod nT, so the four phases
   // cover every candidate once and the lanes of a wave start on different rows
@@ -137,65 +183,41 @@ __global__ __launch_bounds__(kStsBinThreads) void sts_bin_kernel(StsArgs a, int 
     }
   }
   __syncthreads();
-  long long* out = a.partials + (size_t)blockIdx.x * nT * stride;
-  for (int i = tid; i < nT * stride; i += kStsBinThreads) out[i] = hist[i];
+  unsigned long long* sum = reinterpret_cast<unsigned long long*>(a.hists + (size_t)(k % 3) * hsize);
+  for (int i = tid; i < nT * stride; i += kStsBinThreads) {
+    const long long v = hist[i];
+    if (v != 0) atomicAdd(sum + i, (unsigned long long)v);
+  }
 }
 
-// Workgroup t: sums candidate t's histogram slots over the bin workgroups.
-// Thread (q, c) adds column c of slots q, q + Q, q + 2Q, ... in a register.
-__global__ __launch_bounds__(kStsReduceThreads) void sts_reduce_kernel(StsArgs a, int k) {
-  __shared__ long long col[2 * DSPARK_STS_MAX_BINS + 1];
-  __shared__ long long s_err;
-  const int tid = threadIdx.x, t = blockIdx.x;
-  const int nb = a.nbins, nT = a.n_t, stride = 2 * nb + 1;
-  for (int c = tid; c < stride; c += kStsReduceThreads) col[c] = 0;
-  if (tid == 0) s_err = 0;
-  __syncthreads();
-  const int Q = kStsReduceThreads / stride;  // >= 7: stride <= 2 * 64 + 1
-  if (tid < Q * stride) {
-    const int q = tid / stride, c = tid - q * stride;
-    const long long* p = a.partials + ((size_t)q * nT + t) * stride + c;
-    const size_t step = (size_t)Q * nT * stride;
-    long long acc = 0;
-#pragma unroll 8
-    for (int g = q; g < a.n_blocks; g += Q, p += step) acc += *p;
-    atomicAdd(reinterpret_cast<unsigned long long*>(col + c), (unsigned long long)acc);
-  }
-  __syncthreads();
-  for (int b = tid; b < nb; b += kStsReduceThreads) {
-    const long long diff = col[b] * (1ll << 40) - col[nb + b];
-    atomicAdd(reinterpret_cast<unsigned long long*>(&s_err),
-              (unsigned long long)(diff < 0 ? -diff : diff));
-  }
-  __syncthreads();
-  if (tid == 0) {
-    a.err_fx[(size_t)k * nT + t] = s_err;
-    a.brier_fx[(size_t)k * nT + t] = col[2 * nb];
-    if (a.ece_grid) a.ece_grid[(size_t)k * nT + t] = a.N ? (double)s_err / ((double)a.N * kFx) : 0.0;
-  }
+// Clears summed-histogram buffer 0, which position 0 adds into.
+__global__ __launch_bounds__(kStsThreads) void sts_clear_kernel(StsArgs a) {
+  const size_t hsize = (size_t)a.n_t * (2 * a.nbins + 1);
+  const size_t i = (size_t)blockIdx.x * kStsThreads + threadIdx.x;
+  if (i < hsize) a.hists[i] = 0;
 }
 
 // Picks the last position's temperature and advances the survival by it.
 __global__ __launch_bounds__(kStsThreads) void sts_finish_kernel(StsArgs a) {
-  __shared__ int s_prev;
-  if (threadIdx.x < kWave) {
-    const int t = select_candidate(a, a.gamma - 1, blockIdx.x == 0);
-    if (threadIdx.x == 0) s_prev = t;
-  }
-  __syncthreads();
+  __shared__ SelectSmem s_sel;
+  const size_t hsize = (size_t)a.n_t * (2 * a.nbins + 1);
+  const int t = select_candidate(a, a.hists + (size_t)((a.gamma - 1) % 3) * hsize, a.gamma - 1,
+                                 blockIdx.x == 0, s_sel);
   const int n = blockIdx.x * kStsThreads + threadIdx.x;
-  if (a.surv_out && n < a.N) advance_survival(a, a.gamma, n, a.grid[s_prev], true);
+  if (a.surv_out && n < a.N) advance_survival(a, a.gamma, n, a.grid[t], true);
 }
 
 }  // namespace
 
 hipError_t launch_sts(const StsArgs& a, hipStream_t s) {
   const size_t lds = (size_t)a.n_t * (2 * a.nbins + 1) * sizeof(long long);
+  const size_t hsize = (size_t)a.n_t * (2 * a.nbins + 1);  // <= 128 * 129
+  hipLaunchKernelGGL(sts_clear_kernel, dim3((unsigned)((hsize + kStsThreads - 1) / kStsThreads)),
+                     dim3(kStsThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   for (int k = 0; k < a.gamma; ++k) {
     hipLaunchKernelGGL(sts_bin_kernel, dim3(a.n_blocks), dim3(kStsBinThreads), lds, s, a, k);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sts_reduce_kernel, dim3(a.n_t), dim3(kStsReduceThreads), 0, s, a, k);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -275,13 +275,13 @@ def test_sts_fit_argument_errors():
     assert run(temps=NULL) == _lib.E_INVALID
     assert run() == _lib.E_WORKSPACE  # 0 bytes given
     size = _lib.lib().dspark_sts_workspace_size
-    # two survival buffers of 100 floats, two [4, 3] int64 error tables, one
-    # workgroup's 3 x 31 histogram words, each region 256-byte aligned
-    assert size(100, 4, 3, 15) == 2 * 512 + 2 * 256 + 768
-    # 300 records: two workgroups of 256
-    assert size(300, 4, 3, 15) == 2 * 1280 + 2 * 256 + 1536
-    # 4194304 records: 1024 workgroups of 4096
-    assert size(4194304, 1, 1, 1) == 2 * 4 * 4194304 + 2 * 256 + 1024 * 3 * 8
+    # two survival buffers of 100 floats, then three summed-histogram buffers
+    # of 3 x 31 int64 words (one region), each region 256-byte aligned
+    assert size(100, 4, 3, 15) == 2 * 512 + 2304
+    # 300 records: only the survival buffers grow
+    assert size(300, 4, 3, 15) == 2 * 1280 + 2304
+    # 4194304 records, one candidate, one bin: three buffers of 3 words
+    assert size(4194304, 1, 1, 1) == 2 * 4 * 4194304 + 256
     assert size(0, 4, 3, 15) > 0 and size(-1, 4, 3, 15) == 0 and size(10, 4, 129, 15) == 0
 
 
