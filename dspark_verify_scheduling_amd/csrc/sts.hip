@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kStsBinThreads) void sts_bin_kernel(StsArgs a, int 
       unsigned long long* h = reinterpret_cast<unsigned long long*>(hist + t * stride);
       if (y) atomicAdd(h + b, 1ull);
       atomicAdd(h + nb + b, (unsigned long long)fx40(sd));
-      const double d = sd - (double)y;  // exact, and so is d * d
+      const double d = sd - (double)y;  // d and d * d each rounded to float64
       atomicAdd(h + 2 * nb, (unsigned long long)fx40(d * d));
       t += kStsPhases;
       if (t >= nT) t -= nT;  // once past the end only when nT > 4: then t < nT again

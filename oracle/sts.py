@@ -67,7 +67,7 @@ def ece_terms(S: np.ndarray, y: np.ndarray, nbins: int):
 def brier_fx(S: np.ndarray, y: np.ndarray) -> int:
     """n * Brier * 2**40, each squared error at 2**-40 resolution."""
     d = _nan_as_zero(S) - np.asarray(y, dtype=np.float64)
-    return int(np.sum(_fx(d * d)))  # d * d is exact in float64
+    return int(np.sum(_fx(d * d)))  # d and d * d each rounded to float64 (IEEE)
 
 
 def sts_fit(z, prefix_mask, t_grid, nbins):
