@@ -559,7 +559,8 @@ dspark_status dspark_tv_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype
  *   ece_grid           out [gamma, n_t] float64 ECE of every candidate, or NULL
  *   survival_out       out [N, gamma] float32 fitted S_k, or NULL
  *   workspace          dspark_sts_workspace_size() bytes, 256-byte aligned;
- *                      contents irrelevant, no state between calls
+ *                      contents irrelevant, no state between calls; calls
+ *                      that share it must not overlap in time
  * Errors: argument errors only. Infinite logits give survivals 0 or 1; a NaN
  *   logit gives a NaN survival, which is binned and summed as 0.
  */
