@@ -500,9 +500,12 @@ def dspark_sts_workspace_size(N: int, gamma: int, n_t: int, n_bins: int) -> int:
 
 
 def dspark_sts_fit(z: torch.Tensor, prefix_mask: torch.Tensor, t_grid: Sequence[float],
-                   n_bins: int, survival=True, ece_grid=True, stream=None) -> StsFit:
+                   n_bins: int, survival=True, ece_grid=True, stream=None,
+                   workspace: Optional[torch.Tensor] = None) -> StsFit:
     """Fit one STS temperature per position on records ``z`` [N, gamma] (float32
-    confidence logits) and ``prefix_mask`` [N, gamma] (uint8 greedy labels)."""
+    confidence logits) and ``prefix_mask`` [N, gamma] (uint8 greedy labels).
+    ``workspace`` (uint8, at least dspark_sts_workspace_size bytes) is
+    allocated per call when not given."""
     import ctypes
 
     if z.dim() != 2:
@@ -521,7 +524,8 @@ def dspark_sts_fit(z: torch.Tensor, prefix_mask: torch.Tensor, t_grid: Sequence[
         torch.empty(N, gamma, dtype=torch.float32, device=dev) if survival else None,
     )
     ws_bytes = dspark_sts_workspace_size(N, gamma, n_t, n_bins)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 256),
+                                                             dtype=torch.uint8, device=dev)
     args = (
         N, gamma,
         _ptr(z, "z", torch.float32, N * gamma),

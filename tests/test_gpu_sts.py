@@ -30,9 +30,9 @@ def _records(rng, N, gamma, t_true):
     return z, np.cumprod(acc, axis=1).astype(np.uint8)
 
 
-def _fit_both(z, y, grid, nbins, tag):
+def _fit_both(z, y, grid, nbins, tag, workspace=None):
     say(f"sts_fit {tag} N={z.shape[0]} gamma={z.shape[1]} n_t={len(grid)} bins={nbins}")
-    got = dv.dspark_sts_fit(up(z), up(y), grid, nbins)
+    got = dv.dspark_sts_fit(up(z), up(y), grid, nbins, workspace=workspace)
     torch.cuda.synchronize()
     ref = oracle.sts_fit(z, y, np.asarray(grid, np.float32), nbins)
     g = {k: getattr(got, k).cpu().numpy() for k in ("temps", "t_index", "ece", "brier",
@@ -79,3 +79,17 @@ def test_sts_fit_edge_cases():
     grid128 = np.exp(np.linspace(np.log(0.2), np.log(5.0), 128)).astype(np.float32)
     _fit_both(z, y, grid128, 64, "largest grid and bins")
     _fit_both(np.zeros((0, 3), np.float32), np.zeros((0, 3), np.uint8), GRID, 15, "no records")
+
+
+def test_sts_fit_reuses_a_dirty_workspace():
+    """The workspace's contents on entry do not matter: a garbage-filled
+    workspace, then a second, smaller fit on the same one (its histogram
+    buffers hold the first fit's sums), both equal the oracle."""
+    rng = np.random.default_rng(21)
+    z1, y1 = _records(rng, 3000, 6, np.linspace(0.8, 1.6, 6))
+    z2, y2 = _records(rng, 700, 5, np.linspace(1.2, 0.9, 5))
+    size = max(dv.dspark_sts_workspace_size(3000, 6, len(GRID), 15),
+               dv.dspark_sts_workspace_size(700, 5, len(GRID), 15))
+    ws = torch.full((size,), 0x5A, dtype=torch.uint8, device=DEV)
+    _fit_both(z1, y1, GRID, 15, "garbage workspace", workspace=ws)
+    _fit_both(z2, y2, GRID, 15, "reused workspace", workspace=ws)
