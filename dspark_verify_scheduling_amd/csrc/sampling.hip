@@ -532,10 +532,9 @@ __global__ __launch_bounds__(kWave) void samp_decide_kernel(SampArgs a) {
     for (int c = 0; c < C; ++c) b = p[c] > b ? p[c] : b;
     return b;
   };
-  auto z_of = [&](size_t slot) {
+  auto z_of = [&](size_t slot) {  // the 65th row only
     const unsigned long long* p = a.zpart + slot * C;
     unsigned long long z = 0;
-#pragma unroll 8
     for (int c = 0; c < C; ++c) z += p[c];
     return z;
   };
@@ -543,13 +542,39 @@ __global__ __launch_bounds__(kWave) void samp_decide_kernel(SampArgs a) {
   const bool ok = c0 >= 0 && len >= 1 && len <= G + 1 && c0 + len <= total_eff;
   const bool greedy = T == 0.0f;
   const bool samp = is_sampling_temp(T);
-  // this lane's target slot and draft slot, merged once
+  // this lane's target slot and draft slot, merged once: the four partial
+  // runs are read together, eight chunks a round, at slot indices clamped to
+  // the request's own slots and chunk indices clamped to the last (a repeated
+  // key leaves the maximum; a repeated sum term is not added); what a lane
+  // does not own is dropped afterwards
   const bool mine_t = ok && (greedy || samp) && lane < len;
   const bool mine_d = ok && samp && lane < len - 1;
-  const unsigned long long kt = mine_t ? key_of(tslot + lane) : 0;
-  const unsigned long long kd = mine_d ? key_of(dslot + lane) : 0;
-  const unsigned long long zt = mine_t && samp ? z_of(tslot + lane) : 0;
-  const unsigned long long zd = mine_d ? z_of(dslot + lane) : 0;
+  unsigned long long kt = 0, kd = 0, zt = 0, zd = 0;
+  {
+    const size_t ts = (tslot + min(lane, G)) * C, ds = (dslot + min(lane, G - 1)) * C;
+    for (int c0 = 0; c0 < C; c0 += 8) {
+      unsigned long long v[4][8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = min(c0 + e, C - 1);
+        v[0][e] = a.kpart[ts + c];
+        v[1][e] = a.kpart[ds + c];
+        v[2][e] = a.zpart[ts + c];
+        v[3][e] = a.zpart[ds + c];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kt = v[0][e] > kt ? v[0][e] : kt;
+        kd = v[1][e] > kd ? v[1][e] : kd;
+        zt += c0 + e < C ? v[2][e] : 0ull;
+        zd += c0 + e < C ? v[3][e] : 0ull;
+      }
+    }
+  }
+  kt = mine_t ? kt : 0;
+  kd = mine_d ? kd : 0;
+  zt = mine_t && samp ? zt : 0;
+  zd = mine_d ? zd : 0;
   if (!ok) {
     status = DSPARK_DATA_BAD_LENS;
   } else if (!greedy && !samp) {
