@@ -288,10 +288,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
       forced += fx40(s);
     } else if (k < lmax) {
       const bool el = s >= a.eps;
-      keys[r * span + (k - lmin)] = el ? make_key(s, k, r) : 0ull;
+      // -0 ranks with +0 (the order is by value): the key takes +0's bits
+      const float sk = s == 0.0f ? 0.0f : s;
+      keys[r * span + (k - lmin)] = el ? make_key(sk, k, r) : 0ull;
       if (el) {
         ++n_el;
-        const unsigned int sb = __float_as_uint(s);
+        const unsigned int sb = __float_as_uint(sk);
         smin = min(smin, sb);
         smax = max(smax, sb);
       }

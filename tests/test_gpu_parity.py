@@ -117,6 +117,12 @@ def test_plan_edge_cases():
                   rng.uniform(0.5, 2, 64).astype(np.float32), 1, 65, 1e-4, 0, -1))
     cases.append((128, 64, oracle.IN_CONF_LOGITS, rng.normal(2, 2, (128, 64)).astype(np.float32),
                   rng.uniform(0.5, 2, 64).astype(np.float32), 1, 65, 1e-3, 0, -1))
+    # -0 confidences and survivals rank with +0 (by value, then position, then request)
+    cz = np.array([[0.5, -0.0], [0.9, 0.8]], np.float32)
+    cases.append((2, 2, oracle.IN_COND, cz, None, 1, 3, 0.0, 0, -1))
+    sz = np.array([[0.7, 0.0, 0.0], [0.6, -0.0, -0.0], [-0.0, -0.0, -0.0]], np.float32)
+    cases.append((3, 3, oracle.IN_SURVIVAL, sz, None, 1, 4, 0.0, 0, -1))
+    cases.append((3, 3, oracle.IN_SURVIVAL, sz, None, 1, 4, -1.0, 4, 7))
     for i, (B, G, kind, conf, temps, mn, mx, eps, lo, hi) in enumerate(cases):
         alpha = (np.arange(B + 1) * 0.01).astype(np.float32)
         theta = (0.3 + 0.01 * np.arange(B * (G + 1) + 1)).astype(np.float32)

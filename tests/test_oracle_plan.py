@@ -281,3 +281,21 @@ def test_eps_cutoff_keeps_values_equal_to_eps():
     assert out["meta"][1] == 2
     out = oracle.plan(1, 2, oracle.IN_COND, c, None, 1, 3, 0.2500001, 0, -1, bias, alpha, theta)
     assert out["meta"][1] == 1
+
+
+def test_negative_zero_survival_ranks_with_zero():
+    # survivals (0.5, -0), (0.9, 0.72): the order is by value, so -0 comes last
+    # and a budget of 2 takes request 1's two positions
+    c = np.array([[0.5, -0.0], [0.9, 0.8]], dtype=np.float32)
+    bias, alpha, theta = _flat_cost(2, 2)
+    out = oracle.plan(2, 2, oracle.IN_COND, c, None, 1, 3, 0.0, 2, 2, bias, alpha, theta)
+    assert out["verify_lens"].tolist() == [1, 3]
+    assert out["meta"][1] == 4  # -0 >= eps = 0: a candidate
+    # -0 and +0 give the same plan (only the survival's sign bit differs)
+    cp = np.abs(c)
+    for lo, hi in ((0, -1), (3, 4), (4, 4)):
+        a = oracle.plan(2, 2, oracle.IN_COND, c, None, 1, 3, 0.0, lo, hi, bias, alpha, theta)
+        b = oracle.plan(2, 2, oracle.IN_COND, cp, None, 1, 3, 0.0, lo, hi, bias, alpha, theta)
+        assert a["verify_lens"].tolist() == b["verify_lens"].tolist()
+        assert np.array_equal(a["meta"], b["meta"])
+        assert np.array_equal(a["sweep"], b["sweep"], equal_nan=True)
