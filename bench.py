@@ -11,11 +11,15 @@ copies of the packed logits rotate (about 0.56 GB of live rows), so the
 256 MB Infinity Cache cannot serve repeated reads.
 
 Prints one JSON line. ``value`` is steps/s (eager launches). ``roofline`` is
-the accept kernel's achieved HBM bandwidth: algorithmic bytes per launch over
-its mean duration, timed with HIP events on the stream it runs on (every
-fourth timed step carries the events).
+the accept call's achieved HBM bandwidth: algorithmic bytes per launch over
+its mean duration, timed with a HIP event pair around each of 100 dedicated
+accept launches on the stream they run on (each after the step's plan+pack,
+as in a step), whatever ``--steps`` is.
 ``cpu_baseline`` is the untouched CPU oracle on a bounded sample of the same
-step.
+step, pinned to one host core. ``schedule`` reports the planner's decision
+against what the accept committed: b*, the predicted tau(b*) = B + the
+selected survivals, the committed tokens, and the tier's padding, for the
+timed step and over 16 seeded steps bucketed by tier.
 """
 
 from __future__ import annotations
@@ -37,6 +41,8 @@ sys.path.insert(0, str(ROOT))
 PEAK_HBM_GBS = 8000.0
 METRIC = "plan+accept steps/s and logit-pass HBM GB/s (% peak) at B=256,γ=8,V=129280"
 ACC_EVERY = 4  # timed steps whose accept call is bracketed by HIP events
+N_ACC = 100  # dedicated accept launches behind the roofline figure
+N_SCHED = 16  # seeded steps behind the scheduling statistics
 TRAFFIC_FILE = ROOT / "profiles" / "accept_b256_g8_v129280_bf16_traffic.json"
 # the greedy accept kernels: accept.hip and the unit argmax it includes
 ACCEPT_SRCS = [ROOT / "dspark_verify_scheduling_amd" / "csrc" / n
@@ -186,12 +192,117 @@ def tv_section(dv, torch, dev, stream, reps):
     }
 
 
+def host_facts():
+    """Logical CPUs this process may use and the host CPU's model name."""
+    model = None
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count(),
+            "cpu_model": model}
+
+
+def schedule_record(po, ao, total, tier):
+    """The planner's decision against what the accept committed, for one step:
+    b*, the predicted tau(b*) = B + the selected survivals (the expected
+    committed tokens under the calibrated survivals), the tokens committed
+    (sum of commit_lens, bonus included), and the tier's padding."""
+    meta = po.plan_meta.cpu().numpy()
+    tau = float(po.plan_val[0].item())
+    committed = int(ao.commit_lens.sum().item())
+    return {"b_star": int(meta[0]), "n_eligible": int(meta[1]), "rows": total, "tier": tier,
+            "padding_ratio": (tier - total) / tier, "predicted_tau": tau,
+            "committed": committed, "committed_minus_tau": committed - tau}
+
+
+def schedule_stats(dv, torch, dev, stream, n):
+    """The step on n seeded B=256, gamma=8, V=129280 workloads (metadata seeds
+    50000..50000+n-1): each plans and packs on the GPU, its packed rows are
+    filled on the GPU with N(0, 3) clipped to +-15 (a seeded torch generator)
+    and the planted maximum 16 at each row's planted id (no planted ties),
+    then the accept runs. Records are bucketed by the tier the step used."""
+    from workloads import make
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260611)
+    recs = []
+    for i in range(n):
+        w = make(3, seed=50000 + i, logits=False)
+        B, G, V = w.B, w.gamma, w.V
+        tiers = [int(x) for x in w.tiers]
+
+        def t(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        po = dv.alloc_plan_outputs(B, G, dev, survival=False, sweep=False)
+        ko = dv.alloc_pack_outputs(B, tiers[-1], dev)
+        drafts_t, prefix_t = t(w.drafts), t(w.prefix_lens)
+        dv.dspark_plan_pack(B, G, dv.IN_CONF_LOGITS, t(w.conf), t(w.temps), w.min_len,
+                            w.max_len, w.eps, w.b_lo, w.b_hi, float(w.bias), t(w.alpha),
+                            t(w.theta), po, t(w.anchors), drafts_t, tiers, prefix_t, ko, stream)
+        torch.cuda.synchronize()
+        lens = po.verify_lens.cpu().numpy()
+        cu = ko.cu_seqlens.cpu().numpy()
+        total, tier = int(ko.pack_meta[0].item()), int(ko.pack_meta[1].item())
+        req = np.repeat(np.arange(B), lens)
+        jrow = np.arange(total) - np.repeat(cu[:-1], lens)
+        top = torch.from_numpy(w.planted_top[req, jrow].astype(np.int64)).to(dev)
+        rows = torch.empty(tier, V, dtype=torch.float32, device=dev)
+        rows.normal_(0.0, 3.0, generator=gen).clamp_(-15.0, 15.0)
+        rows[torch.arange(total, device=dev), top] = 16.0
+        packed = rows.to(torch.bfloat16)
+        del rows
+        ao = dv.alloc_accept_outputs(B, G, tier, V, dv.BF16, dev)
+        dv.dspark_accept(B, G, V, dv.BF16, packed, V, tier, ko.cu_seqlens, drafts_t, prefix_t,
+                         ao, stream)
+        torch.cuda.synchronize()
+        assert int(ao.accept_meta[1].item()) == 0
+        recs.append(schedule_record(po, ao, total, tier))
+        del packed
+    buckets = {}
+    for r in recs:
+        buckets.setdefault(r["tier"], []).append(r)
+    out = {}
+    for tier, rs in sorted(buckets.items()):
+        out[str(tier)] = {
+            "steps": len(rs),
+            "mean_b_star": statistics.mean(r["b_star"] for r in rs),
+            "mean_rows": statistics.mean(r["rows"] for r in rs),
+            "mean_padding_ratio": statistics.mean(r["padding_ratio"] for r in rs),
+            "mean_predicted_tau": statistics.mean(r["predicted_tau"] for r in rs),
+            "mean_committed": statistics.mean(r["committed"] for r in rs),
+            "mean_committed_minus_tau": statistics.mean(r["committed_minus_tau"] for r in rs),
+        }
+    torch.cuda.empty_cache()
+    return {"steps": n, "by_tier": out}
+
+
 def cpu_baseline(w, lens_ref, packed_host, total, budget_s):
-    """The oracle as it stands, on one host core: full plan and pack, accept
-    on a 32-row sample of the packed logits, scaled to the step's rows."""
+    """The oracle as it stands, pinned to one host core: full plan and pack,
+    accept on a 32-row sample of the packed logits, scaled to the step's
+    rows."""
     import oracle
     from oracle.accept import as_f32_rows
 
+    facts = host_facts()
+    allowed = sorted(os.sched_getaffinity(0))
+    core = allowed[0]
+    os.sched_setaffinity(0, {core})
+    try:
+        res = _cpu_baseline_pinned(oracle, as_f32_rows, w, lens_ref, packed_host, total,
+                                   budget_s)
+    finally:
+        os.sched_setaffinity(0, set(allowed))
+    res.update(facts)
+    res["pinned_core"] = core
+    return res
+
+
+def _cpu_baseline_pinned(oracle, as_f32_rows, w, lens_ref, packed_host, total, budget_s):
     sample_rows = 32
     t_plan, t_pack, t_row = [], [], []
     t_end = time.perf_counter() + budget_s
@@ -218,7 +329,7 @@ def cpu_baseline(w, lens_ref, packed_host, total, budget_s):
         "kind": "oracle",
         "sample": (f"{len(t_plan)} repetitions of the full plan + pack and of the row argmax on "
                    f"{sample_rows} of the {total} packed bf16 rows; the per-row time is scaled to "
-                   f"{total} rows (median of repetitions)"),
+                   f"{total} rows (median of repetitions); the process pinned to one core"),
         "ms_plan": 1e3 * statistics.median(t_plan),
         "ms_pack": 1e3 * statistics.median(t_pack),
         "ms_accept_per_row": 1e3 * statistics.median(t_row),
@@ -331,6 +442,30 @@ def main():
 
     # results of the timed steps must be the planned ones
     assert np.array_equal(po.verify_lens.cpu().numpy(), lens)
+    assert int(ao.accept_meta[1].item()) == 0
+    sched_step = schedule_record(po, ao, total, tier)
+
+    # ---- the accept roofline: N_ACC dedicated launches, each after the step's
+    # plan+pack (as in a step) and bracketed by its own event pair on the
+    # accept's stream; then the same launches back to back under one pair
+    ea0 = [torch.cuda.Event(enable_timing=True) for _ in range(N_ACC)]
+    ea1 = [torch.cuda.Event(enable_timing=True) for _ in range(N_ACC)]
+    torch.cuda.synchronize()
+    for i in range(N_ACC):
+        plan_pack(stream)
+        ea0[i].record(stream)
+        dv.dspark_accept(B, G, V, dt, packed[i % n_rot], V, tier, ko.cu_seqlens, drafts_t,
+                         prefix_t, ao, stream)
+        ea1[i].record(stream)
+    torch.cuda.synchronize()
+    acc_ded_us = [1e3 * ea0[i].elapsed_time(ea1[i]) for i in range(N_ACC)]
+    start.record(stream)
+    for i in range(N_ACC):
+        dv.dspark_accept(B, G, V, dt, packed[i % n_rot], V, tier, ko.cu_seqlens, drafts_t,
+                         prefix_t, ao, stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    acc_b2b_us = 1e3 * start.elapsed_time(stop) / N_ACC
     assert int(ao.accept_meta[1].item()) == 0
 
     # ---- plan+pack, plan and pack alone (events), and one step as a HIP graph replay
@@ -517,7 +652,11 @@ def main():
     torch.cuda.empty_cache()
 
     acc_bytes = accept_bytes(total, B, G, V, esize)
-    achieved = acc_bytes / (acc_mean_us * 1e-6) / 1e9
+    acc_ded_mean_us = statistics.mean(acc_ded_us)
+    achieved = acc_bytes / (acc_ded_mean_us * 1e-6) / 1e9
+
+    log(f"scheduling statistics over {N_SCHED} seeded steps")
+    sched_seeded = schedule_stats(dv, torch, dev, stream, N_SCHED)
 
     # ---- STS fitter: 65536 records of gamma = 8, 64 grid temperatures, 15 bins
     rng = np.random.default_rng(5)
@@ -569,12 +708,17 @@ def main():
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_for(total),
                      "kernel": "dspark_accept: accept_argmax_kernel<bf16> then accept_finalize_kernel",
                      "bytes_per_launch": acc_bytes,
-                     "mean_us": acc_mean_us,
-                     "timed_launches": len(acc_us),
-                     "p10_us": float(np.percentile(acc_us, 10)),
-                     "p50_us": float(np.percentile(acc_us, 50)),
-                     "p90_us": float(np.percentile(acc_us, 90))},
+                     "mean_us": acc_ded_mean_us,
+                     "timed_launches": len(acc_ded_us),
+                     "p10_us": float(np.percentile(acc_ded_us, 10)),
+                     "p50_us": float(np.percentile(acc_ded_us, 50)),
+                     "p90_us": float(np.percentile(acc_ded_us, 90)),
+                     "mean_us_back_to_back": acc_b2b_us,
+                     "frac_back_to_back": acc_bytes / (acc_b2b_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                     "in_step_mean_us": acc_mean_us,
+                     "in_step_timed_launches": len(acc_us)},
         "cpu_baseline": cpu,
+        "schedule": {"step": sched_step, "seeded_steps": sched_seeded},
         "steps_per_s_graph": 1e3 / ms_step_graph,
         "ms_per_step_graph": ms_step_graph,
         "plan_pack_us": plan_pack_us,

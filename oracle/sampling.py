@@ -1,4 +1,5 @@
-"""Chain speculative-sampling accept oracle. TEST INFRASTRUCTURE ONLY.
+"""Chain speculative-sampling accept oracle, the float64 definition. TEST
+INFRASTRUCTURE ONLY.
 
 What the pages fix:
 
@@ -16,57 +17,49 @@ What the pages fix:
   under batch compaction. "常见失败模式": compact and static must agree
   under the same random conditions.
 
-The rest is the standard chain rule of speculative sampling, stated here in
-the pages' terms. For request r with verify length l (rows 0..l-1 of its
-packed block), drafts k = 1..l-1 are tested in order: draft k against target
-row k-1 (p) and draft row k-1 (q, the distribution that proposed it). The
-first rejected draft k ends the chain with correct = k - 1, and the token at
-output column k - 1 is drawn from the residual max(0, p - q) of that pair. If
-all l - 1 drafts pass, the token at column l - 1 is drawn from p of target
-row l - 1. A temperature of 0 marks a greedy request: the greedy rule of
-``oracle.accept`` applies to it.
+The rest is the standard chain rule of speculative sampling, written here
+in float64 in the pages' terms. For request r with verify length l (rows
+0..l-1 of its packed block) at temperature T > 0:
 
-Readings (also in the design notes), chosen so that every decision is an
-exact integer comparison, identical on any device and in any summation
-order:
+* p_j = softmax(x / T) of target row j, q_k = softmax(x / T) of the draft
+  row that proposed draft k (row r * gamma + k - 1); float32 logits
+  (bfloat16 widens exactly), the softmax in float64 with the row maximum
+  subtracted.
+* Drafts k = 1..l-1 in order: draft d is accepted iff U < p_{k-1}(d) /
+  q_k(d), written U * q_k(d) < p_{k-1}(d) (so a draft with q(d) = 0 passes
+  iff p(d) > 0, and one with p(d) = 0 never passes). A draft outside [0, V)
+  is rejected.
+* The first rejected draft k ends the chain with correct = k - 1; the token
+  of output column k - 1 is drawn from the residual max(0, p_{k-1} - q_k),
+  normalised (from p_{k-1} if the residual is 0 everywhere). If every draft
+  passes, the token of column l - 1 is drawn from p_{l-1}.
+* Readings where the pages give no rule (also in the design notes): the
+  caller passes 32-bit random words keyed by (request, position), a word w
+  standing for U = (w >> 8) / 2^24: ``rand_accept[r, k-1]`` tests draft k,
+  ``rand_sample[r, c]`` draws the token of column c. A draw from weights w
+  takes the smallest index i with cumsum(w)_i > U * sum(w) (inverse CDF).
+* Temperature 0 marks a greedy request: the greedy rule of
+  ``oracle.accept`` applies. A temperature that is negative, NaN or
+  infinite, or below the domain the fixed-resolution kernels accept (the
+  float32 quotient 94548.4609375 / T overflows, T below about 2.8e-34),
+  sets DATA_BAD_CONF; a NaN or +inf logit, or no finite element, in a row
+  a sampling request reads sets DATA_BAD_LOGITS. Either way the request
+  gets the malformed-layout outputs of ``oracle.accept`` (correct 0, bonus
+  -1, commit 0, out_tokens -1, new_seq = prefix).
 
-* Probabilities at fixed resolution. For a row x (float32; bfloat16 widens
-  exactly) at temperature T > 0, with m = max x, every step one IEEE float32
-  operation (nearest, ties to even):
-      c = K / T with K = 94548.4609375, the float32 nearest to 2^16 log2(e)
-      u_i = (m - x_i) * c            (u ~ 2^16 * (m - x_i) * log2(e) / T)
-  then, in integers, W_i = 0 unless j = (nearest integer to u_i, ties to
-  even) is below 2^21; else with n = j >> 16, h = (j >> 8) & 255, r = j & 255,
-      Y = B[h] - (((B[h] - B[h+1]) * r + 128) >> 8)
-      W_i = (Y + (2^n >> 1)) >> n
-  where B[i] is the nearest integer to 2^31 * 2^(-i/256) (i = 0..256). So
-  W_i ~ 2^31 * 2^(-j/65536) ~ 2^31 exp((x_i - m) / T): the octave n is a
-  rounding shift and the fraction a linear interpolation, within about 6e-6
-  relative (the 2^-16 step of j and the interpolation) plus half a unit.
-  W = 2^31 at the maximum, and p_i = W_i / Z with Z = sum W (below 2^49).
-* Random words. The caller passes 32-bit words; a word w stands for the
-  uniform U = (w >> 8) / 2^24. ``rand_accept[r, k-1]`` tests draft k;
-  ``rand_sample[r, c]`` draws the token of output column c. Keying them by
-  (request, position) keeps their meaning under compaction.
-* Accept draft d iff u * Wq[d] * Zp < 2^24 * Wp[d] * Zq (u = w >> 8), which
-  is U < p(d) / q(d), i.e. the min(1, p/q) rule. A draft outside [0, V) has
-  Wp = Wq = 0 and is rejected.
-* Drawing from integer weights w (total S) with word v: the smallest i whose
-  running sum exceeds floor((v >> 8) * S / 2^24).
-* The residual weights are R_i = max(0, Wp_i * Zq - Wq_i * Zp) (that is
-  max(0, p - q) scaled by Zp * Zq). If they are all 0 (p == q at this
-  resolution and the draft had zero weight on both sides), the token is
-  drawn from p.
-* A row with a NaN or +inf logit, or with no finite maximum, in a sampling
-  request sets DATA_BAD_LOGITS; a temperature that is negative, NaN or
-  infinite, or so small that K / T overflows float32 (T below about
-  2.8e-34), sets DATA_BAD_CONF. Either way the request gets the malformed-
-  layout outputs of ``oracle.accept`` (correct 0, bonus -1, commit 0,
-  out_tokens -1, new_seq = prefix). Greedy requests follow ``oracle.accept``
-  in full, NaN ordering included.
+An implementation that takes p and q at a finite resolution decides
+differently from this definition only where U lies within that
+resolution's error of a threshold. ``validate`` checks such an
+implementation's outputs: every decision must equal this definition's
+unless U lies inside the band the stated per-token error allows, and the
+chain then continues along the implementation's decision. The band follows
+from a per-token bound |p'(i) - p(i)| <= eps_p * p(i) + eta_p (see
+``prob_error_bound``).
 """
 
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -75,40 +68,17 @@ from .pack import DATA_BAD_LENS
 from .plan import DATA_BAD_CONF
 
 DATA_BAD_LOGITS = 8
-K_LOG2E_16 = np.float32(94548.4609375)  # float32 nearest to 2^16 * log2(e)
-J_MAX = 1 << 21
-B_LEN = 257
-
-_TABLE = None
-
-
-def _nearest_int_pow2(e_num: int, e_den: int) -> int:
-    """Nearest integer (ties to even) to 2**(e_num / e_den), exactly.
-
-    An integer exponent gives a power of two: 2**-1 = 1/2 is the only tie
-    (it goes to 0). Otherwise the value is irrational, so N is the nearest
-    integer iff (2N - 1)**e_den < 2**(e_den + e_num) < (2N + 1)**e_den, all
-    integers; below 1/2 (e_den + e_num < 0) it is 0."""
-    if e_num % e_den == 0:
-        k = e_num // e_den
-        return 1 << k if k >= 0 else 0
-    if e_den + e_num < 0:
-        return 0
-    target = 1 << (e_den + e_num)
-    n = max(0, int(round(2.0 ** (e_num / e_den))))
-    while (2 * n + 1) ** e_den <= target:
-        n += 1
-    while n > 0 and (2 * n - 1) ** e_den >= target:
-        n -= 1
-    return n
+WORD_SHIFT = 8  # a word w stands for U = (w >> 8) / 2^24
+U_SCALE = float(1 << 24)
+# the largest relative error of one unnormalised weight in the kernels' fixed
+# resolution (j = RNE(u) at 2^-16 of a base-2 unit, float32 rounding of u,
+# the 8-bit interpolation of 2^-x): 1.06e-5 + 9.3e-7, rounded up
+EPS_W = 1.2e-5
 
 
-def exp_table():
-    """B[i] = nearest integer to 2^31 * 2^(-i/256), i = 0..256 (Python ints)."""
-    global _TABLE
-    if _TABLE is None:
-        _TABLE = [_nearest_int_pow2(31 * 256 - i, 256) for i in range(B_LEN)]
-    return _TABLE
+def uniform(word) -> float:
+    """U = (word >> 8) / 2^24, in [0, 1 - 2^-24]."""
+    return float(int(word) >> WORD_SHIFT) / U_SCALE
 
 
 def row_is_bad(x: np.ndarray) -> bool:
@@ -119,69 +89,43 @@ def row_is_bad(x: np.ndarray) -> bool:
     return not np.isfinite(np.max(x))
 
 
-def temp_scale(T) -> np.float32:
-    """c = K / T, one float32 division."""
-    with np.errstate(over="ignore", divide="ignore"):
-        return K_LOG2E_16 / np.float32(T)
+def temp_ok(T) -> bool:
+    """A sampling temperature inside the domain: positive, finite, and not so
+    small that the float32 quotient 94548.4609375 / T overflows."""
+    T32 = np.float32(T)
+    if not (T32 > 0 and np.isfinite(T32)):
+        return False
+    with np.errstate(over="ignore"):
+        return bool(np.isfinite(np.float32(94548.4609375) / T32))
 
 
-def weights(x: np.ndarray, T: float) -> np.ndarray:
-    """Integer weights W (int64) of one float32 row at temperature T > 0."""
-    Bt = np.array(exp_table(), dtype=np.int64)
-    x = np.asarray(x, dtype=np.float32)
-    m = np.max(x)
-    c = temp_scale(T)
-    with np.errstate(invalid="ignore", over="ignore"):
-        u = (m - x) * c  # float32 subtraction and product
-    W = np.zeros(x.shape, dtype=np.int64)
-    ok = u < np.float32(J_MAX)
-    j = np.rint(u[ok]).astype(np.int64)
-    keep = j < J_MAX
-    j = j[keep]
-    n, h, r = j >> 16, (j >> 8) & 255, j & 255
-    Y = Bt[h] - (((Bt[h] - Bt[h + 1]) * r + 128) >> 8)
-    W[np.flatnonzero(ok)[keep]] = (Y + ((1 << n) >> 1)) >> n
-    return W
+def softmax64(x, T) -> np.ndarray:
+    """softmax(x / T) in float64 of one float32 row, the maximum subtracted."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    y = (x - np.max(x)) / np.float64(np.float32(T))
+    e = np.exp(y)
+    return e / np.sum(e)
 
 
-def draw(w, word: int) -> int:
-    """Smallest i whose running sum of the integer weights w exceeds
-    floor((word >> 8) * sum(w) / 2**24)."""
-    w = np.asarray(w, dtype=object)
-    S = int(np.sum(w))
-    t = ((int(word) >> 8) * S) >> 24
-    cum = np.cumsum(w)
-    return int(np.argmax(cum > t))
+def accepts(p_d: float, q_d: float, U: float) -> bool:
+    """U < p(d) / q(d), written without a division."""
+    return U * q_d < p_d
 
 
-def accepts(Wp_d: int, Zp: int, Wq_d: int, Zq: int, word: int) -> bool:
-    """U < p(d) / q(d) with U = (word >> 8) / 2**24, in integers."""
-    return (int(word) >> 8) * int(Wq_d) * int(Zp) < (1 << 24) * int(Wp_d) * int(Zq)
+def residual(p: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """max(0, p - q), unnormalised."""
+    return np.maximum(p - q, 0.0)
 
 
-def residual(Wp: np.ndarray, Zp: int, Wq: np.ndarray, Zq: int) -> np.ndarray:
-    """max(0, Wp * Zq - Wq * Zp) as Python ints."""
-    d = Wp.astype(object) * int(Zq) - Wq.astype(object) * int(Zp)
-    return np.where(d > 0, d, 0)
-
-
-def sample_pair(p_row, q_row, T, d, u_word, v_word, V=None):
-    """One chain step on float32 rows: (accepted, token drawn if rejected)."""
-    Wp, Wq = weights(p_row, T), weights(q_row, T)
-    Zp, Zq = int(Wp.sum()), int(Wq.sum())
-    V = Wp.size if V is None else V
-    in_range = 0 <= d < V
-    if in_range and accepts(int(Wp[d]), Zp, int(Wq[d]), Zq, u_word):
-        return True, None
-    R = residual(Wp, Zp, Wq, Zq)
-    if int(np.sum(R)) == 0:
-        return False, draw(Wp, v_word)
-    return False, draw(R, v_word)
+def draw(w: np.ndarray, U: float) -> int:
+    """Inverse CDF: the smallest i with cumsum(w)_i > U * sum(w)."""
+    c = np.cumsum(np.asarray(w, dtype=np.float64))
+    return int(np.searchsorted(c, U * c[-1], side="right"))
 
 
 def accept_sampling(B, gamma, target_rows, draft_rows, dtype, cu_seqlens, drafts, temps,
                     rand_accept, rand_sample, prefix_lens=None, max_rows=None):
-    """Chain speculative-sampling accept over packed target rows.
+    """Chain speculative-sampling accept over packed target rows, float64.
 
     target_rows [>= cu[B], V] and draft_rows [B * gamma, V] (row r * gamma +
     k - 1 proposed draft k) as float32, or bfloat16 bit patterns with
@@ -216,7 +160,7 @@ def accept_sampling(B, gamma, target_rows, draft_rows, dtype, cu_seqlens, drafts
             while c < l - 1 and drafts[r, c] == am[c]:
                 c += 1
             tok = int(am[c])
-        elif not (T > 0.0 and np.isfinite(T) and np.isfinite(temp_scale(T))):
+        elif not temp_ok(T):
             status |= DATA_BAD_CONF
             continue
         else:
@@ -226,14 +170,16 @@ def accept_sampling(B, gamma, target_rows, draft_rows, dtype, cu_seqlens, drafts
                 continue
             c, tok = l - 1, None
             for k in range(1, l):
-                ok, t_rej = sample_pair(tgt[s + k - 1], dr[r * gamma + k - 1], T,
-                                        int(drafts[r, k - 1]), int(ra[r, k - 1]),
-                                        int(rs[r, k - 1]), V)
-                if not ok:
-                    c, tok = k - 1, t_rej
-                    break
+                p = softmax64(tgt[s + k - 1], T)
+                q = softmax64(dr[r * gamma + k - 1], T)
+                d = int(drafts[r, k - 1])
+                if 0 <= d < V and accepts(p[d], q[d], uniform(ra[r, k - 1])):
+                    continue
+                R = residual(p, q)
+                c, tok = k - 1, draw(R if R.sum() > 0 else p, uniform(rs[r, k - 1]))
+                break
             if tok is None:
-                tok = draw(weights(tgt[s + l - 1], T), int(rs[r, l - 1]))
+                tok = draw(softmax64(tgt[s + l - 1], T), uniform(rs[r, l - 1]))
         correct[r] = c
         bonus[r] = tok
         commit[r] = c + 1
@@ -242,3 +188,198 @@ def accept_sampling(B, gamma, target_rows, draft_rows, dtype, cu_seqlens, drafts
         out[r, c] = tok
     return {"num_correct": correct, "bonus": bonus, "commit": commit,
             "new_seq": (prefix + commit).astype(np.int32), "out_tokens": out, "status": status}
+
+
+# ---------------------------------------------------------------- validation
+
+
+def prob_error_bound(V: int, eps_w: float = EPS_W):
+    """(eps_p, eta_p) with |p'(i) - p(i)| <= eps_p * p(i) + eta_p for every
+    token of a V-token row, when p' = W / sum W is formed from weights
+    W_i = W*_i (1 + e_i) + a_i, |e_i| <= eps_w and |a_i| <= 1/2 + 1e-5 (a
+    rounding to integers, the cut-off tokens included), around exact
+    weights W*_i = 2^31 exp((x_i - m) / T) whose sum is at least 2^31 (the
+    maximum's own weight).
+
+    With the normaliser's relative error zeta = eps_w + a * V / 2^31:
+    p'/p - 1 = (1 + e_i) / (1 + zeta_Z) - 1 - ..., so
+    eps_p = (eps_w + zeta) / (1 - zeta) and eta_p = a / (2^31 (1 - zeta))."""
+    a = 0.5 + 1e-5
+    zeta = eps_w + a * V / 2.0**31
+    return (eps_w + zeta) / (1.0 - zeta), a / (2.0**31 * (1.0 - zeta))
+
+
+def _draw_check(w, U, g, delta, n):
+    """Is token g a valid draw for U when every CDF value may be off by delta?
+    Returns (float64 token k, U within delta of a boundary of k's CDF step,
+    ok)."""
+    c = np.cumsum(np.asarray(w, dtype=np.float64))
+    S = c[-1]
+    k = int(np.searchsorted(c, U * S, side="right"))
+    near = U - (c[k - 1] / S if k > 0 else 0.0) <= delta or c[k] / S - U <= delta
+    if g == k:
+        return k, near, True
+    if not (0 <= g < n):
+        return k, near, False
+    lo = (c[g - 1] / S if g > 0 else 0.0) - delta
+    hi = c[g] / S + delta
+    slack = 1e-12
+    ok = lo - slack <= U <= hi + slack
+    return k, near, ok
+
+
+def validate(B, gamma, target_rows, draft_rows, dtype, cu_seqlens, drafts, temps, rand_accept,
+             rand_sample, got, prefix_lens=None, max_rows=None, reqs=None, eps_w=EPS_W):
+    """Check an implementation's outputs ``got`` (num_correct, bonus, commit,
+    new_seq, out_tokens as arrays over all B requests) against the float64
+    definition, request by request (all, or those listed in ``reqs``).
+
+    Greedy, malformed and out-of-domain requests must match exactly. For a
+    sampling request the chain is walked in float64 along the
+    implementation's own decisions:
+
+    * accept test of draft d with U: the margin g = U q(d) - p(d) decides
+      (accept iff g < 0). With p', q' within the bound of
+      ``prob_error_bound``, the implementation's margin differs from g by at
+      most band = eps_p (p(d) + U q(d)) + 2 eta_p, so its decision must
+      equal the float64 one when |g| > band; otherwise the case is counted
+      as a band case and either decision is valid;
+    * the draw: the implementation's token must be the float64 inverse-CDF
+      token unless U lies within delta of a CDF boundary, where delta =
+      eps_p + V eta_p for a draw from p; for the residual, whose total R
+      (= TV) and partial sums each move by at most E = 2 eps_p + 2 V eta_p,
+      delta = 2 E / (R - E) (every token of positive weight is valid when
+      R <= E). The token must still fall inside its own widened CDF step.
+
+    Returns a dict of counts (accept tests and draws; of each, how many had
+    U inside the band and how many of those the implementation decided
+    differently from float64: the flips) and a list of failure strings
+    (empty when valid)."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    drafts = np.asarray(drafts, dtype=np.int64).reshape(B, gamma)
+    temps = np.asarray(temps, dtype=np.float32).reshape(B)
+    ra = np.asarray(rand_accept, dtype=np.uint32).reshape(B, gamma)
+    rs = np.asarray(rand_sample, dtype=np.uint32).reshape(B, gamma + 1)
+    prefix = np.zeros(B, np.int64) if prefix_lens is None else np.asarray(prefix_lens, np.int64)
+    tgt = as_f32_rows(target_rows, dtype)
+    dr = as_f32_rows(draft_rows, dtype)
+    V = tgt.shape[1]
+    eps_p, eta_p = prob_error_bound(V, eps_w)
+    total = int(cu[B]) if B > 0 else 0
+    limit = min(total, tgt.shape[0] if max_rows is None else max_rows)
+    g_nc = np.asarray(got["num_correct"])
+    g_bo = np.asarray(got["bonus"])
+    g_cm = np.asarray(got["commit"])
+    g_ns = np.asarray(got["new_seq"])
+    g_out = np.asarray(got["out_tokens"]).reshape(-1, gamma + 1)
+    stats = {"requests": 0, "sampling_requests": 0, "accept_tests": 0, "accept_band": 0,
+             "accept_band_flips": 0, "draws_p": 0, "draws_p_band": 0, "draws_p_flips": 0,
+             "draws_residual": 0, "draws_residual_band": 0, "draws_residual_flips": 0,
+             "accept_min_rel_margin": math.inf}
+    fails = []
+
+    def expect(r, c, tok):
+        want_out = np.array(drafts[r].tolist() + [-1], np.int64)
+        if tok is not None:
+            want_out[c] = tok
+        if not (g_nc[r] == c and g_bo[r] == tok and g_cm[r] == c + 1
+                and g_ns[r] == prefix[r] + c + 1 and np.array_equal(g_out[r], want_out)):
+            fails.append(f"r={r}: outputs ({g_nc[r]}, {g_bo[r]}, {g_cm[r]}, {g_ns[r]}) "
+                         f"!= expected ({c}, {tok}, {c + 1}, {prefix[r] + c + 1}) or out_tokens")
+
+    def expect_bad(r):
+        if not (g_nc[r] == 0 and g_bo[r] == -1 and g_cm[r] == 0 and g_ns[r] == prefix[r]
+                and np.all(g_out[r] == -1)):
+            fails.append(f"r={r}: expected the malformed-request outputs")
+
+    for r in (range(B) if reqs is None else reqs):
+        r = int(r)
+        stats["requests"] += 1
+        s, e = int(cu[r]), int(cu[r + 1])
+        l = e - s
+        if not (1 <= l <= gamma + 1 and 0 <= s and e <= limit):
+            expect_bad(r)
+            continue
+        T = float(temps[r])
+        if T == 0.0:
+            am = row_argmax(tgt[s:e])
+            c = 0
+            while c < l - 1 and drafts[r, c] == am[c]:
+                c += 1
+            expect(r, c, int(am[c]))
+            continue
+        rows = [tgt[s + j] for j in range(l)] + [dr[r * gamma + k] for k in range(l - 1)]
+        if not temp_ok(T) or any(row_is_bad(x) for x in rows):
+            expect_bad(r)
+            continue
+        stats["sampling_requests"] += 1
+        gc = int(g_nc[r])
+        if not 0 <= gc <= l - 1:
+            fails.append(f"r={r}: num_correct {gc} outside [0, {l - 1}]")
+            continue
+        chain_ok = True
+        for k in range(1, gc + 2 if gc < l - 1 else l):
+            p = softmax64(tgt[s + k - 1], T)
+            q = softmax64(dr[r * gamma + k - 1], T)
+            d = int(drafts[r, k - 1])
+            U = uniform(ra[r, k - 1])
+            gpu_acc = k <= gc
+            stats["accept_tests"] += 1
+            if not 0 <= d < V:
+                if gpu_acc:
+                    fails.append(f"r={r} k={k}: draft {d} outside the vocabulary accepted")
+                    chain_ok = False
+                    break
+                f64_acc = False
+                band = False
+            else:
+                marg = U * q[d] - p[d]
+                width = eps_p * (p[d] + U * q[d]) + 2.0 * eta_p
+                f64_acc = marg < 0.0
+                band = abs(marg) <= width
+                if p[d] + U * q[d] > 0:
+                    stats["accept_min_rel_margin"] = min(stats["accept_min_rel_margin"],
+                                                         abs(marg) / (p[d] + U * q[d]))
+            if band:
+                stats["accept_band"] += 1
+                stats["accept_band_flips"] += int(gpu_acc != f64_acc)
+            elif gpu_acc != f64_acc:
+                fails.append(f"r={r} k={k}: accept {gpu_acc} but float64 says {f64_acc} "
+                             f"(U={U:.9f}, p={p[d] if 0 <= d < V else 0:.6g}, "
+                             f"q={q[d] if 0 <= d < V else 0:.6g})")
+                chain_ok = False
+                break
+            if not gpu_acc:  # the chain ends with a residual draw
+                R = residual(p, q)
+                Rs = float(R.sum())
+                E = 2.0 * eps_p + 2.0 * V * eta_p
+                Us = uniform(rs[r, k - 1])
+                stats["draws_residual"] += 1
+                if Rs == 0.0:
+                    ex_tok, near, ok = _draw_check(p, Us, int(g_bo[r]), eps_p + V * eta_p, V)
+                elif Rs <= E:  # any token the residual or p could hold
+                    ex_tok, near, ok = draw(R, Us), True, 0 <= int(g_bo[r]) < V
+                else:
+                    ex_tok, near, ok = _draw_check(R, Us, int(g_bo[r]), 2.0 * E / (Rs - E), V)
+                stats["draws_residual_band"] += int(near)
+                stats["draws_residual_flips"] += int(ok and ex_tok != int(g_bo[r]))
+                if not ok:
+                    fails.append(f"r={r} k={k}: residual draw {int(g_bo[r])}, float64 gives "
+                                 f"{ex_tok} (U={Us:.9f}, TV={Rs:.6g})")
+                    chain_ok = False
+                break
+        if not chain_ok:
+            continue
+        if gc == l - 1:  # every draft passed: the bonus is drawn from p of row l-1
+            p = softmax64(tgt[s + l - 1], T)
+            Us = uniform(rs[r, l - 1])
+            ex_tok, near, ok = _draw_check(p, Us, int(g_bo[r]), eps_p + V * eta_p, V)
+            stats["draws_p"] += 1
+            stats["draws_p_band"] += int(near)
+            stats["draws_p_flips"] += int(ok and ex_tok != int(g_bo[r]))
+            if not ok:
+                fails.append(f"r={r}: bonus draw {int(g_bo[r])}, float64 gives {ex_tok} "
+                             f"(U={Us:.9f})")
+                continue
+        expect(r, gc, int(g_bo[r]))
+    return {"stats": stats, "failures": fails}

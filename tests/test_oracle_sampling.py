@@ -1,23 +1,27 @@
-"""Pins for the chain speculative-sampling accept oracle.
+"""Pins for the float64 chain speculative-sampling accept oracle
+(``oracle.sampling``), the definition the GPU results are checked against.
 
 Fixed by:
-* the exp2 table against an independent 80-bit long-double evaluation, and
-  K against a 50-digit decimal 2^16 / ln 2;
-* the fixed-resolution probabilities against the float64 softmax (closed
-  form), the value 2^31 at the maximum, table entries hit exactly,
-  monotonicity and the power-of-two scaling invariance of x / T;
+* the softmax against closed forms: a uniform row gives 1/V, the pair
+  [0, -T ln 3] gives [3/4, 1/4], ratios p_i / p_j = exp((x_i - x_j) / T),
+  translation invariance, and the sum 1;
 * the theorem of speculative sampling: one chain step outputs a token
   distributed exactly as p (to the 2^-24 resolution of the random words),
   whatever q is, and its acceptance rate is sum min(p, q) = 1 - TV, the
-  pages' identity; both computed by exhaustive counting over all 2^24
-  values of each random word, with the oracle's own decision functions;
+  pages' identity; both counted exhaustively over all 2^24 values of each
+  random word with the oracle's own decision functions;
 * closed cases: p == q always accepts, disjoint one-hot rows always reject
-  and resample the target token, a draft outside the vocabulary is rejected;
+  and resample the target token, a draft outside the vocabulary is
+  rejected, zero probability is never drawn or accepted;
 * the greedy path (temperature 0) equal to the greedy accept oracle;
 * compaction invariance: compact accept with length l agrees with the
   full-width (static) accept under the same random words wherever the
-  static chain stops before l - 1 ([CSSD], compact vs static).
+  static chain stops before l - 1 ([CSSD], compact vs static);
+* the validator: the oracle's own outputs pass it with no band case, and
+  outputs with a planted wrong decision or draw fail it.
 """
+
+import math
 
 import numpy as np
 import pytest
@@ -26,76 +30,42 @@ import oracle
 from oracle import sampling as S
 
 
-def test_exp_table_against_long_double():
-    Bt = S.exp_table()
-    ld = np.longdouble
-    assert np.finfo(ld).eps < 1e-18  # 80-bit extended on this host
-    assert len(Bt) == S.B_LEN == 257
-    for i, v in enumerate(Bt):
-        ref = ld(2) ** (31 - ld(i) / 256)
-        assert abs(ld(v) - ref) <= 0.5 + ref * 1e-17, (i, v, ref)
-    assert Bt[0] == 2**31 and Bt[256] == 2**30
-    # K is the float32 nearest to 2^16 log2(e)
-    from decimal import Decimal, getcontext
-    getcontext().prec = 50
-    k = Decimal(65536) / Decimal(2).ln()
-    below = np.nextafter(S.K_LOG2E_16, np.float32(0))
-    above = np.nextafter(S.K_LOG2E_16, np.float32(1e9))
-    d0 = abs(Decimal(float(S.K_LOG2E_16)) - k)
-    assert d0 < abs(Decimal(float(below)) - k) and d0 < abs(Decimal(float(above)) - k)
-
-
-@pytest.mark.parametrize("T", [0.05, 0.6, 1.0, 1.7, 8.0])
-def test_weights_match_softmax(T):
-    rng = np.random.default_rng(int(T * 100))
-    x = rng.normal(0.0, 3.0, 5000).astype(np.float32)
-    W = S.weights(x, T)
-    assert W.max() == 2**31 and W[np.argmax(x)] == 2**31
-    p = W.astype(np.float64) / float(W.sum())
-    y = (x.astype(np.float64) - x.max()) / np.float64(np.float32(T))
-    q = np.exp(y) / np.exp(y).sum()
-    big = q > 1e-3 * q.max()  # W above 2^21: the 2^-31 grid is below 5e-7 relative
-    assert np.max(np.abs(p - q)[big] / q[big]) < 1.5e-5
-    assert 0.5 * np.abs(p - q).sum() < 1e-5
-    # monotone in the logit (up to one unit of the interpolation's rounding)
-    order = np.argsort(x, kind="stable")
-    Wo = W[order]
-    assert np.all(np.diff(Wo) >= -1)
-    assert np.all(np.diff(Wo)[Wo[:-1] > 2**16] >= 0)
-
-
-def test_weights_scaling_invariance_and_special_values():
-    rng = np.random.default_rng(2)
-    x = rng.normal(0.0, 4.0, 3000).astype(np.float32)
+def test_softmax_closed_forms():
+    x = np.zeros(37, np.float32)
+    assert np.allclose(S.softmax64(x, 0.7), 1.0 / 37, rtol=0, atol=1e-17)
+    T = np.float32(1.3)
+    x2 = np.array([0.0, -np.float64(T) * math.log(3.0)], np.float32)
+    p = S.softmax64(x2, T)
+    assert abs(p[0] - 0.75) < 1e-7 and abs(p[1] - 0.25) < 1e-7  # x2 rounded to float32
+    rng = np.random.default_rng(1)
+    # 1/256 steps: adding 8 below is exact in float32
+    x = (np.round(rng.normal(0, 3, 2000) * 256) / 256).astype(np.float32)
     for T in (0.3, 1.0, 2.5):
-        assert np.array_equal(S.weights(x, T), S.weights(x * 4, T * 4))
-        assert np.array_equal(S.weights(x, T), S.weights(x / 8, T / 8))
-    # -inf has weight 0; a logit 30 below the max at T = 1 is below 2^-32
-    z = np.array([0.0, -np.inf, -30.0, -1.0, -22.0], np.float32)
-    W = S.weights(z, 1.0)
-    assert W[0] == 2**31 and W[1] == 0 and W[2] == 0
-    assert abs(int(W[3]) - 2**31 * np.exp(-1.0)) < 2**31 * 1e-5
-    assert abs(int(W[4]) - 2**31 * np.exp(-22.0)) <= 1
-    # j = 256 i lands on table entries, shifted by the octave: W = round(B[i % 256] / 2^n)
-    Bt = S.exp_table()
-    for i in (1, 7, 100, 4000):
-        x = np.array([0.0, -np.float32(i * 256) / np.float32(S.K_LOG2E_16)], np.float32)
-        u = (x[0] - x[1]) * S.K_LOG2E_16
-        if np.rint(u) == i * 256:
-            n = i >> 8
-            assert S.weights(x, 1.0)[1] == (Bt[i & 255] + ((1 << n) >> 1)) >> n
+        p = S.softmax64(x, T)
+        assert abs(p.sum() - 1.0) < 1e-13
+        i, j = np.argmax(x), 17
+        assert abs(p[j] / p[i] - math.exp((float(x[j]) - float(x[i])) / float(np.float32(T)))) \
+            < 1e-13
+        assert np.allclose(S.softmax64(x + np.float32(8.0), T), p, rtol=1e-12, atol=0)
+    y = np.array([1.0, -np.inf, 0.0], np.float32)
+    assert S.softmax64(y, 1.0)[1] == 0.0
 
 
-def _count_accept(Wp_d, Zp, Wq_d, Zq):
+def test_uniform_word():
+    assert S.uniform(0) == 0.0 and S.uniform(255) == 0.0
+    assert S.uniform(256) == 2.0**-24 and S.uniform(0xFFFFFFFF) == 1.0 - 2.0**-24
+
+
+def _count_accept(p_d, q_d):
     """#u in [0, 2^24) accepted: the test is monotone in u, so bisect."""
-    lo, hi = 0, 1 << 24  # accepts(lo - 1) true, accepts(hi) false
-    if not S.accepts(Wp_d, Zp, Wq_d, Zq, 0):
+    if not S.accepts(p_d, q_d, 0.0):
         return 0
-    if S.accepts(Wp_d, Zp, Wq_d, Zq, ((1 << 24) - 1) << 8):
+    if S.accepts(p_d, q_d, 1.0 - 2.0**-24):
         return 1 << 24
+    lo, hi = 0, 1 << 24  # accepts(lo) true, accepts(hi) false
     while hi - lo > 1:
         mid = (lo + hi) // 2
-        if S.accepts(Wp_d, Zp, Wq_d, Zq, mid << 8):
+        if S.accepts(p_d, q_d, mid / 2.0**24):
             lo = mid
         else:
             hi = mid
@@ -103,15 +73,15 @@ def _count_accept(Wp_d, Zp, Wq_d, Zq):
 
 
 def _draw_counts(w):
-    """#v in [0, 2^24) drawing each index: draw is monotone in v, so bisect
-    for the first v of each index."""
+    """#u in [0, 2^24) drawing each index: draw is monotone in u, so bisect
+    for the first u of each index."""
     n = len(w)
     first = []
     for i in range(n + 1):
         lo, hi = 0, 1 << 24
-        while lo < hi:  # first v with draw(v) >= i
+        while lo < hi:  # first u with draw(u) >= i
             mid = (lo + hi) // 2
-            if S.draw(w, mid << 8) >= i:
+            if S.draw(w, mid / 2.0**24) >= i:
                 hi = mid
             else:
                 lo = mid + 1
@@ -129,24 +99,19 @@ def test_one_chain_step_outputs_the_target_distribution(seed):
     if seed == 5:
         q_row[2] = -np.inf  # the draft never proposes token 2
     T = [1.0, 0.5, 2.0, 1.0, 0.8, 1.0][seed]
-    Wp, Wq = S.weights(p_row, T), S.weights(q_row, T)
-    Zp, Zq = int(Wp.sum()), int(Wq.sum())
-    p = np.array([int(v) for v in Wp], dtype=object)
-    R = S.residual(Wp, Zp, Wq, Zq)
-    rho = _draw_counts(R if int(np.sum(R)) else Wp)
+    p, q = S.softmax64(p_row, T), S.softmax64(q_row, T)
+    R = S.residual(p, q)
+    rho = _draw_counts(R if R.sum() > 0 else p)
     out = np.zeros(V)
     acc_rate = 0.0
     for d in range(V):
-        qd = int(Wq[d]) / Zq
-        a = _count_accept(int(Wp[d]), Zp, int(Wq[d]), Zq) / 2**24
-        acc_rate += qd * a
-        out[d] += qd * a
-        out += qd * (1 - a) * rho / 2**24
-    target = np.array([float(v) for v in p]) / Zp
-    assert np.max(np.abs(out - target)) < 2 * 2.0**-24, (out, target)
-    ptrue, qtrue = Wp.astype(np.float64) / Zp, Wq.astype(np.float64) / Zq
-    assert abs(acc_rate - np.minimum(ptrue, qtrue).sum()) < 2 * 2.0**-24
-    assert abs(acc_rate - (1 - 0.5 * np.abs(ptrue - qtrue).sum())) < 2 * 2.0**-24
+        a = _count_accept(p[d], q[d]) / 2**24
+        acc_rate += q[d] * a
+        out[d] += q[d] * a
+        out += q[d] * (1 - a) * rho / 2**24
+    assert np.max(np.abs(out - p)) < 2 * 2.0**-24, (out, p)
+    assert abs(acc_rate - np.minimum(p, q).sum()) < 2 * 2.0**-24
+    assert abs(acc_rate - (1 - 0.5 * np.abs(p - q).sum())) < 2 * 2.0**-24
 
 
 def _batch(rng, B, gamma, V, lens, dtype="f32"):
@@ -167,6 +132,7 @@ def test_identical_rows_always_accept_and_disjoint_rows_always_reject():
     for r in range(B):
         for k in range(1, lens[r]):
             drf[r * gamma + k - 1] = tgt[cu[r] + k - 1]
+    ra[:] = 0xFFFFFFFF  # the largest U still passes when p == q
     res = S.accept_sampling(B, gamma, tgt, drf, "f32", cu, drafts, np.ones(B), ra, rs)
     assert res["num_correct"].tolist() == (lens - 1).tolist()
     # disjoint one-hots: q proposes token 3, p puts all mass on token 7
@@ -175,9 +141,9 @@ def test_identical_rows_always_accept_and_disjoint_rows_always_reject():
     drf[:] = -np.inf
     drf[:, 3] = 0.0
     drafts[:] = 3
+    ra[:] = 0
     res = S.accept_sampling(B, gamma, tgt, drf, "f32", cu, drafts, np.ones(B), ra, rs)
-    expect_bonus = [7 if l > 1 else 7 for l in lens]
-    assert res["num_correct"].tolist() == [0] * B and res["bonus"].tolist() == expect_bonus
+    assert res["num_correct"].tolist() == [0] * B and res["bonus"].tolist() == [7] * B
     assert res["status"] == 0
     # a draft outside the vocabulary is rejected even when p == q
     drf[:] = tgt[0]
@@ -224,8 +190,8 @@ def test_compact_agrees_with_static_under_the_same_random_words(seed):
     stops = static["num_correct"] < lens - 1
     assert np.array_equal(comp["bonus"][stops], static["bonus"][stops])
     for r in np.flatnonzero(~stops):  # capped: the bonus is drawn from p of row l - 1
-        W = S.weights(tgt_c[cu_c[r] + lens[r] - 1], temps[r])
-        assert comp["bonus"][r] == S.draw(W, rs[r, lens[r] - 1])
+        p = S.softmax64(tgt_c[cu_c[r] + lens[r] - 1], temps[r])
+        assert comp["bonus"][r] == S.draw(p, S.uniform(rs[r, lens[r] - 1]))
     assert stops.any() and (~stops).any()
 
 
@@ -235,11 +201,8 @@ def test_bad_data_falls_back():
     lens = np.array([4, 2, 3, 1, 4])
     cu, tgt, drf, drafts, ra, rs = _batch(rng, B, gamma, V, lens)
     temps = np.array([1.0, -1.0, 1.0, np.nan, 0.0], np.float32)
-    # a scale K / T that overflows float32 is out of domain too; just above
-    # it, the row's maximum keeps the full weight
-    tiny = np.float32(1e-34)
-    assert not np.isfinite(S.temp_scale(tiny)) and np.isfinite(S.temp_scale(np.float32(3e-34)))
-    assert S.weights(np.array([0.0, -1e-30], np.float32), np.float32(3e-34))[0] == 2**31
+    tiny = np.float32(1e-34)  # below the domain (94548.46 / T overflows float32)
+    assert not S.temp_ok(tiny) and S.temp_ok(np.float32(3e-34)) and not S.temp_ok(np.inf)
     tgt[cu[2] + 1, 3] = np.inf  # request 2's second row
     tgt[cu[4], 5] = np.nan  # greedy request: NaN is an ordinary (largest) value
     res = S.accept_sampling(B, gamma, tgt, drf, "f32", cu, drafts, temps, ra, rs,
@@ -275,19 +238,19 @@ def test_bf16_rows_widen_exactly():
 
 
 def test_zero_probability_is_never_drawn_or_accepted():
-    # counts over all 2^24 values of the word are exactly the integer shares
-    w = np.array([0, 3, 0, 5, 0], dtype=object)
+    # counts over all 2^24 values of U are the weight shares, rounded up
+    w = np.array([0.0, 3.0, 0.0, 5.0, 0.0])
     counts = _draw_counts(w)
     assert counts[0] == 0 and counts[2] == 0 and counts[4] == 0
     assert counts.sum() == 2**24 and abs(counts[1] - 3 * 2**24 / 8) <= 1
-    assert S.draw(w, 0) == 1 and S.draw(w, 0xFFFFFFFF) == 3
+    assert S.draw(w, 0.0) == 1 and S.draw(w, 1.0 - 2.0**-24) == 3
     # min(1, p/q) is 0 when p(d) = 0, whatever q(d) is
-    Z = 5 * 2**31
-    assert _count_accept(0, Z, 2**31, Z) == 0
-    assert _count_accept(0, Z, 0, Z) == 0
-    # and 1 when p(d) >= q(d) > 0
-    assert _count_accept(2**31, Z, 2**31, Z) == 2**24
-    assert _count_accept(2**30, Z, 2**31, Z) == 2**23
+    assert _count_accept(0.0, 0.4) == 0 and _count_accept(0.0, 0.0) == 0
+    # and 1 when p(d) >= q(d) > 0; half the words when p = q / 2
+    assert _count_accept(0.4, 0.4) == 2**24 and _count_accept(0.5, 0.25) == 2**24
+    assert _count_accept(0.125, 0.25) == 2**23
+    # q(d) = 0 < p(d): always accepted
+    assert _count_accept(0.1, 0.0) == 2**24
 
 
 def test_each_output_column_draws_with_its_own_word():
@@ -316,23 +279,100 @@ def test_each_output_column_draws_with_its_own_word():
         assert res["out_tokens"][0].tolist() == [9, 9, 9, expect]
 
 
-@pytest.mark.parametrize("T", [0.7, 1.0, 2.0])
-def test_weights_are_unbiased(T):
-    # nearest rounding of j leaves no systematic error: the mean signed
-    # relative error of W against 2^31 exp((x - m) / T) is about 0, while a
-    # floor (or any one-sided rounding) biases it by about 2^-17 ln 2 = 5e-6
-    rng = np.random.default_rng(31)
-    x = (rng.uniform(-22.0, 0.0, 200000) * T).astype(np.float32)
-    x[0] = 0.0
-    W = S.weights(x, T)
-    ref = 2.0**31 * np.exp(x.astype(np.float64) / np.float64(np.float32(T)))
-    big = W > 2**20
-    rel = W[big] / ref[big] - 1.0
-    assert abs(rel.mean()) < 1e-6, rel.mean()
-    assert np.max(np.abs(rel)) < 1.2e-5
-    # small weights: the interpolation rounds to nearest too (mean error in
-    # units of 2^-31 about 0, not the +1/2 of a truncating interpolation)
-    small = (W > 2**8) & (W < 2**14)
-    assert small.sum() > 5000
-    err = W[small] - ref[small]
-    assert abs(err.mean()) < 0.1, err.mean()
+def test_accept_probability_at_a_known_ratio():
+    # p(d) / q(d) = 0.6 exactly in the softmaxes: rows [0, ln a] at T = 1
+    # for target and draft; words just below and above 0.6 * 2^24 decide
+    a_p, a_q = 3.0, 1.0  # p = [1/4, 3/4], q = [1/2, 1/2]: p(1)/q(1) = 1.5, p(0)/q(0) = 0.5
+    tgt = np.array([[0.0, math.log(a_p)]], np.float32)
+    drf = np.array([[0.0, math.log(a_q)]], np.float32)
+    p, q = S.softmax64(tgt[0], 1.0), S.softmax64(drf[0], 1.0)
+    ratio = p[0] / q[0]
+    assert abs(ratio - 0.5) < 1e-7
+    u_hi = int(ratio * 2**24)  # U = u_hi / 2^24 just below the ratio
+    assert S.accepts(p[0], q[0], u_hi / 2**24) and not S.accepts(p[0], q[0], (u_hi + 2) / 2**24)
+    assert S.accepts(p[1], q[1], 1.0 - 2.0**-24)
+
+
+def _rand_inputs(seed, B=20, gamma=5, V=400):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, gamma + 2, B)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tgt = rng.normal(0, 2.0, (int(cu[-1]), V)).astype(np.float32)
+    drf = np.empty((B * gamma, V), np.float32)
+    for r in range(B):
+        for k in range(gamma):
+            src = tgt[cu[r] + k] if k < lens[r] else rng.normal(0, 2.0, V)
+            drf[r * gamma + k] = src + rng.normal(0, 0.6, V)
+    drafts = np.argmax(drf, axis=1).reshape(B, gamma).astype(np.int32)
+    temps = rng.uniform(0.5, 1.5, B).astype(np.float32)
+    temps[0] = 0.0
+    ra = rng.integers(0, 2**32, (B, gamma), dtype=np.uint64).astype(np.uint32)
+    rs = rng.integers(0, 2**32, (B, gamma + 1), dtype=np.uint64).astype(np.uint32)
+    return dict(B=B, gamma=gamma, target_rows=tgt, draft_rows=drf, dtype="f32",
+                cu_seqlens=cu, drafts=drafts, temps=temps, rand_accept=ra, rand_sample=rs,
+                prefix_lens=rng.integers(1, 100, B))
+
+
+def test_validator_accepts_the_definition_and_rejects_planted_mistakes():
+    args = _rand_inputs(41)
+    ref = S.accept_sampling(**args)
+    rep = S.validate(**args, got=ref)
+    assert rep["failures"] == []
+    st = rep["stats"]
+    assert st["sampling_requests"] == args["B"] - 1 and st["accept_tests"] > 20
+    assert st["accept_band_flips"] == 0
+    assert st["draws_p_flips"] == 0 and st["draws_residual_flips"] == 0
+    B, gamma = args["B"], args["gamma"]
+    cu = args["cu_seqlens"]
+
+    def planted(mut):
+        g = {k: np.array(v, copy=True) for k, v in ref.items() if k != "status"}
+        mut(g)
+        return S.validate(**args, got=g)["failures"]
+
+    # one more (or one fewer) accepted draft than the definition gives, where
+    # the decision is far from its threshold
+    r_rej = next(r for r in range(1, B) if ref["num_correct"][r] < cu[r + 1] - cu[r] - 1)
+    def accept_more(g, r=r_rej):
+        c = int(g["num_correct"][r]) + 1
+        g["num_correct"][r], g["commit"][r] = c, c + 1
+        g["new_seq"][r] += 1
+        g["out_tokens"][r, :gamma] = args["drafts"][r]
+        g["out_tokens"][r, gamma] = -1
+        g["out_tokens"][r, c] = g["bonus"][r]
+    assert planted(accept_more)
+    # a bonus token other than the inverse-CDF one
+    def other_bonus(g, r=r_rej):
+        b = (int(g["bonus"][r]) + 1) % args["target_rows"].shape[1]
+        g["bonus"][r] = b
+        g["out_tokens"][r, g["num_correct"][r]] = b
+    assert planted(other_bonus)
+    # a wrong commit length or new sequence length
+    assert planted(lambda g: g["commit"].__setitem__(3, g["commit"][3] + 1))
+    assert planted(lambda g: g["new_seq"].__setitem__(4, g["new_seq"][4] - 1))
+    # the greedy request (temperature 0) must match exactly
+    assert planted(lambda g: g["bonus"].__setitem__(0, g["bonus"][0] + 1))
+
+
+def test_validator_band_accepts_a_flip_only_near_the_threshold():
+    # one request, one draft, p(d) / q(d) = 1/2: a word at U just below 1/2
+    # accepts; the validator tolerates the reject decision only while U lies
+    # within the band of the threshold
+    V = 2
+    tgt = np.array([[0.0, math.log(3.0)], [0.0, 0.0]], np.float32)
+    drf = np.array([[0.0, 0.0]], np.float32)
+    p, q = S.softmax64(tgt[0], 1.0), S.softmax64(drf[0], 1.0)
+    eps_p, eta_p = S.prob_error_bound(V)
+    base = dict(B=1, gamma=1, target_rows=tgt, draft_rows=drf, dtype="f32",
+                cu_seqlens=np.array([0, 2], np.int32), drafts=np.array([[0]], np.int32),
+                temps=np.ones(1, np.float32), rand_sample=np.zeros((1, 2), np.uint32))
+    rej = {"num_correct": np.array([0]), "bonus": np.array([1]), "commit": np.array([1]),
+           "new_seq": np.array([1]), "out_tokens": np.array([[1, -1]])}
+    for U, tolerated in ((p[0] / q[0] - 1e-9, True), (p[0] / q[0] - 1e-3, False)):
+        w = np.array([[int(U * 2**24) << 8]], np.uint32)
+        assert S.accepts(p[0], q[0], S.uniform(w[0, 0]))
+        rep = S.validate(**base, rand_accept=w, got=rej)
+        assert (rep["failures"] == []) == tolerated, rep
+        if tolerated:
+            assert rep["stats"]["accept_band"] == 1
+    assert eps_p < 1e-4
