@@ -27,7 +27,7 @@ from ._lib import (
 
 __all__ = [
     "load", "dspark_plan", "dspark_pack", "dspark_plan_pack", "dspark_plan_pack_ex",
-    "dspark_accept", "dspark_tv_accept", "COST_ADDITIVE", "COST_SPS1D",
+    "dspark_accept", "dspark_accept_noalloc", "dspark_tv_accept", "COST_ADDITIVE", "COST_SPS1D",
     "dspark_cap_accept", "dspark_scatter_to_strided", "dspark_accept_workspace_size",
     "alloc_plan_outputs", "alloc_pack_outputs", "alloc_accept_outputs",
     "alloc_cap_accept_outputs", "dspark_sts_fit", "dspark_sts_workspace_size", "DsparkError", "F32", "BF16", "IN_CONF_LOGITS", "IN_COND",
@@ -321,6 +321,37 @@ def dspark_accept(B: int, gamma: int, V: int, dt: int, packed_logits: torch.Tens
         _stream(stream),
     )
     _lib.check("dspark_accept", _lib.lib().dspark_accept(*args))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 1 << 20  # DSPARK_NOALLOC_SCRATCH_BYTES
+
+
+def dspark_accept_noalloc(B: int, gamma: int, V: int, dt: int, packed_logits: torch.Tensor,
+                          ld: int, max_rows: int, cu_seqlens: torch.Tensor,
+                          draft_tokens: torch.Tensor, prefix_lens, out: AcceptOutputs,
+                          stream=None) -> AcceptOutputs:
+    """dspark_accept with the library's own scratch array instead of a
+    workspace (out.workspace is not used); allocates nothing."""
+    i32 = torch.int32
+    args = (
+        B, gamma, V, dt,
+        _ptr(packed_logits, "packed_logits", _logit_dtype(dt), max_rows * ld if max_rows else 0),
+        ld, max_rows,
+        _ptr(cu_seqlens, "cu_seqlens", i32, B + 1),
+        _ptr(draft_tokens, "draft_tokens", i32, B * gamma),
+        _ptr(prefix_lens, "prefix_lens", i32, B, required=False),
+        _ptr(out.row_argmax, "row_argmax", i32, max_rows),
+        _ptr(out.num_correct, "num_correct", i32, B),
+        _ptr(out.bonus, "bonus", i32, B),
+        _ptr(out.commit_lens, "commit_lens", i32, B),
+        _ptr(out.out_tokens, "out_tokens", i32, B * (gamma + 1)),
+        _ptr(out.new_seq_lens, "new_seq_lens", i32, B, required=False),
+        _ptr(out.prefix_mask, "prefix_mask", torch.uint8, B * gamma, required=False),
+        _ptr(out.accept_meta, "accept_meta", i32, 2),
+        _stream(stream),
+    )
+    _lib.check("dspark_accept_noalloc", _lib.lib().dspark_accept_noalloc(*args))
     return out
 
 

@@ -54,6 +54,10 @@ SIGNATURES = {
         c_int32, c_int32, c_int32, c_int, c_void_p, c_int64, c_int32, c_void_p, c_void_p,
         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
         c_void_p, c_void_p, c_size_t, c_void_p]),
+    "dspark_accept_noalloc": (c_int, [
+        c_int32, c_int32, c_int32, c_int, c_void_p, c_int64, c_int32, c_void_p, c_void_p,
+        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+        c_void_p, c_void_p]),
     "dspark_cap_accept": (c_int, [
         c_int32, c_int32, c_int32, c_int, c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -112,6 +112,32 @@ size_t ws_bytes(int max_rows, int chunks) {
   return b > 256 ? b : 256;
 }
 
+// The partials of dspark_accept_noalloc: a device array the library holds on
+// every GPU it runs on until the process ends, so that call allocates nothing.
+// In host code `scratch` only names the symbol: its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only that
+// address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[DSPARK_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    // threads that race here store the same address
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
 
 namespace dspark {
@@ -545,46 +571,61 @@ size_t dspark_accept_workspace_size(int32_t max_rows, int32_t V, dspark_dtype dt
   return ws_bytes(max_rows, row_geom(V, dt).chunks);
 }
 
-dspark_status dspark_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,
-                            const void* packed_logits, int64_t ld, int32_t max_rows,
-                            const int32_t* cu_seqlens, const int32_t* draft_tokens,
-                            const int32_t* prefix_lens, int32_t* row_argmax,
-                            int32_t* num_correct, int32_t* bonus, int32_t* commit_lens,
-                            int32_t* out_tokens, int32_t* new_seq_lens, uint8_t* prefix_mask,
-                            int32_t* accept_meta, void* workspace, size_t workspace_bytes,
-                            void* stream) {
-  if (B < 0) return fail(DSPARK_E_INVALID, "dspark_accept: B = %d < 0", B);
+namespace {
+
+// The body of dspark_accept, with the partials in `workspace` (null: the
+// no-allocation variant, whose partials go to the library's own array).
+dspark_status accept_call(const char* fn, int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,
+                          const void* packed_logits, int64_t ld, int32_t max_rows,
+                          const int32_t* cu_seqlens, const int32_t* draft_tokens,
+                          const int32_t* prefix_lens, int32_t* row_argmax, int32_t* num_correct,
+                          int32_t* bonus, int32_t* commit_lens, int32_t* out_tokens,
+                          int32_t* new_seq_lens, uint8_t* prefix_mask, int32_t* accept_meta,
+                          void* workspace, size_t workspace_bytes, bool own_scratch,
+                          void* stream) {
+  if (B < 0) return fail(DSPARK_E_INVALID, "%s: B = %d < 0", fn, B);
   if (gamma < 1 || gamma > DSPARK_MAX_GAMMA)
-    return fail(DSPARK_E_INVALID, "dspark_accept: gamma = %d outside [1, %d]", gamma,
+    return fail(DSPARK_E_INVALID, "%s: gamma = %d outside [1, %d]", fn, gamma,
                 DSPARK_MAX_GAMMA);
   if (dt != DSPARK_F32 && dt != DSPARK_BF16)
-    return fail(DSPARK_E_UNSUPPORTED, "dspark_accept: unsupported dtype %d", (int)dt);
+    return fail(DSPARK_E_UNSUPPORTED, "%s: unsupported dtype %d", fn, (int)dt);
   if (V < 1 || V > DSPARK_MAX_VOCAB)
     return fail(V < 1 ? DSPARK_E_INVALID : DSPARK_E_UNSUPPORTED,
-                "dspark_accept: V = %d outside [1, %d]", V, DSPARK_MAX_VOCAB);
-  if (max_rows < 0) return fail(DSPARK_E_INVALID, "dspark_accept: max_rows = %d < 0", max_rows);
-  if (ld < V) return fail(DSPARK_E_INVALID, "dspark_accept: ld = %lld < V = %d", (long long)ld, V);
+                "%s: V = %d outside [1, %d]", fn, V, DSPARK_MAX_VOCAB);
+  if (max_rows < 0) return fail(DSPARK_E_INVALID, "%s: max_rows = %d < 0", fn, max_rows);
+  if (ld < V) return fail(DSPARK_E_INVALID, "%s: ld = %lld < V = %d", fn, (long long)ld, V);
   const size_t es = elem_size(dt);
   if ((ld * (int64_t)es) % 16 != 0)
-    return fail(DSPARK_E_INVALID, "dspark_accept: row stride %lld bytes is not a multiple of 16",
+    return fail(DSPARK_E_INVALID, "%s: row stride %lld bytes is not a multiple of 16", fn,
                 (long long)(ld * (int64_t)es));
   if (max_rows > 0 && (!packed_logits || !aligned16(packed_logits)))
-    return fail(DSPARK_E_INVALID, "dspark_accept: packed_logits NULL or not 16-byte aligned");
+    return fail(DSPARK_E_INVALID, "%s: packed_logits NULL or not 16-byte aligned", fn);
   if (!cu_seqlens || !accept_meta)
-    return fail(DSPARK_E_INVALID, "dspark_accept: cu_seqlens or accept_meta is NULL");
+    return fail(DSPARK_E_INVALID, "%s: cu_seqlens or accept_meta is NULL", fn);
   if (B > 0 && (!draft_tokens || !num_correct || !bonus || !commit_lens || !out_tokens))
-    return fail(DSPARK_E_INVALID, "dspark_accept: a required per-request pointer is NULL");
+    return fail(DSPARK_E_INVALID, "%s: a required per-request pointer is NULL", fn);
   if (max_rows > 0 && !row_argmax)
-    return fail(DSPARK_E_INVALID, "dspark_accept: row_argmax is NULL");
+    return fail(DSPARK_E_INVALID, "%s: row_argmax is NULL", fn);
   if (new_seq_lens && !prefix_lens)
-    return fail(DSPARK_E_INVALID, "dspark_accept: new_seq_lens needs prefix_lens");
+    return fail(DSPARK_E_INVALID, "%s: new_seq_lens needs prefix_lens", fn);
   const RowGeom g = row_geom(V, dt);
   if ((int64_t)max_rows * g.chunks > 0x7fffffffLL)
-    return fail(DSPARK_E_UNSUPPORTED, "dspark_accept: max_rows * chunks overflows int32");
+    return fail(DSPARK_E_UNSUPPORTED, "%s: max_rows * chunks overflows int32", fn);
   const size_t need = ws_bytes(max_rows, g.chunks);
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
-    return fail(DSPARK_E_WORKSPACE, "dspark_accept: workspace needs %zu bytes, 256-byte aligned",
-                need);
+  if (own_scratch) {
+    if (need > DSPARK_NOALLOC_SCRATCH_BYTES)
+      return fail(DSPARK_E_WORKSPACE,
+                  "%s: max_rows = %d at V = %d needs %zu bytes of partials, above the %d-byte "
+                  "array of the no-allocation entry point; use dspark_accept with a workspace",
+                  fn, max_rows, V, need, DSPARK_NOALLOC_SCRATCH_BYTES);
+    const hipError_t e = noalloc_scratch(&workspace);
+    if (e != hipSuccess)
+      return fail(DSPARK_E_LAUNCH, "%s: resolving the scratch array on this device: %s", fn,
+                  hipGetErrorString(e));
+  } else if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+             workspace_bytes < need) {
+    return fail(DSPARK_E_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned", fn, need);
+  }
 
   dspark::AcceptArgs a;
   a.logits = static_cast<const unsigned char*>(packed_logits);
@@ -616,7 +657,36 @@ dspark_status dspark_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt
   // kernel reads the actual total on the device and idle workgroups exit
   const int64_t units_max = (int64_t)max_rows * g.chunks;
   const int grid = units_max > 0 ? (int)units_max : 1;
-  return launched(dspark::launch_accept(a, dt, grid, (hipStream_t)stream), "dspark_accept");
+  return launched(dspark::launch_accept(a, dt, grid, (hipStream_t)stream), fn);
+}
+
+}  // namespace
+
+dspark_status dspark_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,
+                            const void* packed_logits, int64_t ld, int32_t max_rows,
+                            const int32_t* cu_seqlens, const int32_t* draft_tokens,
+                            const int32_t* prefix_lens, int32_t* row_argmax,
+                            int32_t* num_correct, int32_t* bonus, int32_t* commit_lens,
+                            int32_t* out_tokens, int32_t* new_seq_lens, uint8_t* prefix_mask,
+                            int32_t* accept_meta, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return accept_call("dspark_accept", B, gamma, V, dt, packed_logits, ld, max_rows, cu_seqlens,
+                     draft_tokens, prefix_lens, row_argmax, num_correct, bonus, commit_lens,
+                     out_tokens, new_seq_lens, prefix_mask, accept_meta, workspace,
+                     workspace_bytes, false, stream);
+}
+
+dspark_status dspark_accept_noalloc(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,
+                                    const void* packed_logits, int64_t ld, int32_t max_rows,
+                                    const int32_t* cu_seqlens, const int32_t* draft_tokens,
+                                    const int32_t* prefix_lens, int32_t* row_argmax,
+                                    int32_t* num_correct, int32_t* bonus, int32_t* commit_lens,
+                                    int32_t* out_tokens, int32_t* new_seq_lens,
+                                    uint8_t* prefix_mask, int32_t* accept_meta, void* stream) {
+  return accept_call("dspark_accept_noalloc", B, gamma, V, dt, packed_logits, ld, max_rows,
+                     cu_seqlens, draft_tokens, prefix_lens, row_argmax, num_correct, bonus,
+                     commit_lens, out_tokens, new_seq_lens, prefix_mask, accept_meta, nullptr, 0,
+                     true, stream);
 }
 
 size_t dspark_accept_sampling_workspace_size(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt) {

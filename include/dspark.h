@@ -337,6 +337,37 @@ dspark_status dspark_accept(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt
                             void* stream);
 
 /*
+ * dspark_accept_noalloc - dspark_accept without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, outputs, data errors and stream behaviour are those of
+ * dspark_accept, without workspace and workspace_bytes. The per-unit partials
+ * live in a device array of DSPARK_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every GPU it runs on until the process ends; the call allocates and frees
+ * nothing. It accepts max_rows while dspark_accept_workspace_size(max_rows, V,
+ * dt) <= DSPARK_NOALLOC_SCRATCH_BYTES (max_rows <= 16384 at V = 129280 bf16,
+ * 4096 at V = 262144 f32); beyond that it returns DSPARK_E_WORKSPACE without
+ * launching anything. The first call on a device looks up the array's address
+ * on that device (the device current at the call); a failure there returns
+ * DSPARK_E_LAUNCH.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * partials: calls that overlap in time on one GPU (on different streams, or
+ * from different host threads without ordering) race on it and give undefined
+ * results. Calls ordered on one stream are safe. Nothing needs clearing: each
+ * call rewrites every partial it reads.
+ */
+#define DSPARK_NOALLOC_SCRATCH_BYTES (1 << 20)
+dspark_status dspark_accept_noalloc(int32_t B, int32_t gamma, int32_t V, dspark_dtype dt,
+                                    const void* packed_logits, int64_t ld, int32_t max_rows,
+                                    const int32_t* cu_seqlens, const int32_t* draft_tokens,
+                                    const int32_t* prefix_lens, int32_t* row_argmax,
+                                    int32_t* num_correct, int32_t* bonus, int32_t* commit_lens,
+                                    int32_t* out_tokens, int32_t* new_seq_lens,
+                                    uint8_t* prefix_mask, int32_t* accept_meta, void* stream);
+
+/*
  * dspark_cap_accept - greedy accept in cap-accept mode.
  *
  * Defined by [SGLang] "三种 verify mode" and "可观测性" (cap-accept verifies

@@ -363,3 +363,27 @@ def test_accept_sampling_argument_errors():
     assert size(0, 3, 100, _lib.F32) == 256  # one job slot, no partials
     assert size(-1, 3, 100, _lib.F32) == 0 and size(4, 65, 100, _lib.F32) == 0
     assert size(4, 3, 0, _lib.F32) == 0 and size(4, 3, 100, 7) == 0
+
+
+def test_accept_noalloc_argument_errors():
+    call = _lib.lib().dspark_accept_noalloc
+    ok = dict(B=2, gamma=4, V=1024, dt=_lib.BF16, logits=FAKE, ld=1024, max_rows=10, cu=FAKE,
+              drafts=FAKE, prefix=FAKE, am=FAKE, nc=FAKE, bonus=FAKE, commit=FAKE, out=FAKE,
+              newseq=FAKE, mask=NULL, meta=FAKE, stream=NULL)
+
+    def run(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return call(*d.values())
+
+    assert run(V=0) == _lib.E_INVALID
+    assert run(cu=NULL) == _lib.E_INVALID
+    assert run(logits=ctypes.c_void_p(0x1008)) == _lib.E_INVALID
+    # partials beyond the 1 MiB array are refused before any launch: at V =
+    # 129280 bf16 (8 units per row) that is max_rows > 16384; at V = 262144
+    # float32 (32 units) max_rows > 4096
+    assert run(V=129280, ld=129280, max_rows=16385) == _lib.E_WORKSPACE
+    assert run(V=262144, ld=262144, dt=_lib.F32, max_rows=4097) == _lib.E_WORKSPACE
+    assert b"1048576" in _lib.lib().dspark_last_error()
+    f = _lib.lib().dspark_accept_workspace_size
+    assert f(16384, 129280, _lib.BF16) == 1 << 20 and f(4096, 262144, _lib.F32) == 1 << 20
