@@ -59,11 +59,45 @@ def _run(cmd, verbose):
         raise RuntimeError(f"build failed: {cmd[-1]}")
 
 
+def check_m0_use(asm: str) -> None:
+    """The soft accept-rate kernels copy global memory straight into LDS with
+    inline assembly that sets M0 (the LDS address) itself, out of the
+    compiler's sight. That is sound only while nothing else in the code uses
+    M0: raise unless every line of the gfx950 assembly that names m0 is one of
+    those inline-assembly statements (an `s_mov_b32 m0, sN` directly followed
+    by `s_nop 0` and `global_load_lds_dwordx4`, between the compiler's
+    ;;#ASMSTART / ;;#ASMEND markers)."""
+    lines = asm.splitlines()
+    inside = False
+    for i, line in enumerate(lines):
+        t = line.strip()
+        if t.startswith(";;#ASMSTART"):
+            inside = True
+            continue
+        if t.startswith(";;#ASMEND"):
+            inside = False
+            continue
+        if t.startswith((";", ".")) or "m0" not in t.replace(",", " ").split():
+            continue
+        ok = (inside and t.startswith("s_mov_b32 m0, s") and i + 2 < len(lines)
+              and lines[i + 1].strip() == "s_nop 0"
+              and lines[i + 2].strip().startswith("global_load_lds_dwordx4"))
+        if not ok:
+            raise RuntimeError(f"tv.hip: unexpected use of M0 in the generated code: {t!r}")
+
+
 def build(verbose: bool = False) -> Path:
     """Compile libdspark.so and libdspark_hostcheck.so next to this file."""
     hipcc = _hipcc()
     tmp = LIB.with_suffix(".so.tmp")
     _run([hipcc, *COMMON_FLAGS, "-o", tmp, *[CSRC / s for s in LIB_SOURCES]], verbose)
+    asm = LIB.with_suffix(".tv.s")
+    flags = [f for f in COMMON_FLAGS if f not in ("-shared", "-fPIC")]
+    _run([hipcc, *flags, "-S", "--cuda-device-only", "-o", asm, CSRC / "tv.hip"], verbose)
+    try:
+        check_m0_use(asm.read_text())
+    finally:
+        asm.unlink()
     os.replace(tmp, LIB)
     tmp = HOSTCHECK.with_suffix(".so.tmp")
     _run([hipcc, *COMMON_FLAGS, "-o", tmp, CSRC / "hostcheck.hip"], verbose)

@@ -387,3 +387,16 @@ def test_accept_noalloc_argument_errors():
     assert b"1048576" in _lib.lib().dspark_last_error()
     f = _lib.lib().dspark_accept_workspace_size
     assert f(16384, 129280, _lib.BF16) == 1 << 20 and f(4096, 262144, _lib.F32) == 1 << 20
+
+
+def test_m0_check_of_the_build():
+    from dspark_verify_scheduling_amd.build import check_m0_use
+
+    good = "\t;;#ASMSTART\n\ts_mov_b32 m0, s14\n\ts_nop 0\n\tglobal_load_lds_dwordx4 v1, s[42:43]\n\t;;#ASMEND\n"
+    check_m0_use(good)
+    for bad in ("\ts_mov_b32 m0, -1\n\tds_read_b32 v0, v1\n",
+                good + "\ts_mov_b32 m0, s3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 v1, s[4:5]\n",
+                "\t;;#ASMSTART\n\ts_mov_b32 m0, s14\n\ts_add_u32 s1, s1, 1\n\tglobal_load_lds_dwordx4 v1, s[2:3]\n\t;;#ASMEND\n",
+                "\tv_readlane_b32 s0, v1, m0\n"):
+        with pytest.raises(RuntimeError):
+            check_m0_use(bad)
