@@ -200,9 +200,13 @@ __device__ inline float exp_sum_vec(const u32x4& d, float off) {
   constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
   float x[kEpv];
   widen<DT>(d, x);
-  float s0 = 0.0f, s1 = 0.0f;
+  // the partial sums start at their first term, not at 0 + that term (the
+  // same value: exponentials are >= +0), which the compiler would keep as an
+  // add
+  float s0 = exp2_raw(__fmaf_rn(x[0], kLog2e, -off));
+  float s1 = exp2_raw(__fmaf_rn(x[1], kLog2e, -off));
 #pragma unroll
-  for (int i = 0; i < kEpv; i += 2) {
+  for (int i = 2; i < kEpv; i += 2) {
     s0 += exp2_raw(__fmaf_rn(x[i], kLog2e, -off));
     s1 += exp2_raw(__fmaf_rn(x[i + 1], kLog2e, -off));
   }
@@ -234,9 +238,11 @@ __device__ inline float min_sum_pair(const u32x4& dq, const u32x4& dp, float aq,
   float x[kEpv], y[kEpv];
   widen<DT>(dq, x);
   widen<DT>(dp, y);
-  float s0 = 0.0f, s1 = 0.0f;
+  // started at the first terms, as in exp_sum_vec
+  float s0 = exp2_raw(fminf(__fmaf_rn(x[0], kLog2e, -aq), __fmaf_rn(y[0], kLog2e, -ap)));
+  float s1 = exp2_raw(fminf(__fmaf_rn(x[1], kLog2e, -aq), __fmaf_rn(y[1], kLog2e, -ap)));
 #pragma unroll
-  for (int i = 0; i < kEpv; i += 2) {
+  for (int i = 2; i < kEpv; i += 2) {
     s0 += exp2_raw(fminf(__fmaf_rn(x[i], kLog2e, -aq), __fmaf_rn(y[i], kLog2e, -ap)));
     s1 += exp2_raw(fminf(__fmaf_rn(x[i + 1], kLog2e, -aq), __fmaf_rn(y[i + 1], kLog2e, -ap)));
   }
