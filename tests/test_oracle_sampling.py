@@ -376,3 +376,35 @@ def test_validator_band_accepts_a_flip_only_near_the_threshold():
         if tolerated:
             assert rep["stats"]["accept_band"] == 1
     assert eps_p < 1e-4
+
+
+def test_rejection_draws_from_the_residual_not_from_p():
+    # p = [1/2, 1/2], q = [9/10, 1/10]; draft 0 passes with probability 5/9.
+    # Rejected, the token comes from max(0, p - q) = [0, 2/5]: always token 1,
+    # where a draw from p with the same word (U = 0) would give token 0.
+    tgt = np.array([[0.0, 0.0], [0.0, 0.0]], np.float32)
+    drf = np.array([[math.log(9.0), 0.0]], np.float32)
+    cu = np.array([0, 2], np.int32)
+    for w_acc, expect_c in ((np.uint32(0xFFFFFFFF), 0), (np.uint32(0), 1)):
+        res = S.accept_sampling(1, 1, tgt, drf, "f32", cu, np.array([[0]], np.int32),
+                                np.ones(1, np.float32), np.array([[w_acc]], np.uint32),
+                                np.zeros((1, 2), np.uint32))
+        assert res["num_correct"][0] == expect_c
+        if expect_c == 0:
+            assert res["bonus"][0] == 1
+        else:  # both passed: the bonus is drawn from p of row 1 with U = 0
+            assert res["bonus"][0] == 0
+
+
+def test_each_draft_is_tested_with_its_own_word():
+    # two drafts with p(d) / q(d) = 1/2 each: word 0 (U = 0) passes, the
+    # largest word rejects; the first rejected draft names the word used
+    tgt = np.array([[0.0, 0.0]] * 3, np.float32)  # p = [1/2, 1/2]
+    drf = np.array([[0.0, -np.inf]] * 2, np.float32)  # q = [1, 0]: p(0) / q(0) = 1/2
+    cu = np.array([0, 3], np.int32)
+    drafts = np.array([[0, 0]], np.int32)
+    hi = np.uint32(0xFFFFFFFF)
+    for ra, expect in (([0, hi], 1), ([hi, 0], 0), ([0, 0], 2)):
+        res = S.accept_sampling(1, 2, tgt, drf, "f32", cu, drafts, np.ones(1, np.float32),
+                                np.array([ra], np.uint32), np.zeros((1, 3), np.uint32))
+        assert res["num_correct"][0] == expect
