@@ -277,6 +277,22 @@ __device__ inline T block_excl_scan(T v, T* wsum, T* total) {
   return before + incl - v;
 }
 
+// block_excl_scan without its closing barrier, for callers that pass another
+// barrier before anything writes `wsum` again.
+template <typename T, int NTHREADS>
+__device__ inline T block_excl_scan_open(T v, T* wsum, T* total) {
+  constexpr int kWaves = NTHREADS / kWave;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const T incl = wave_incl_scan_op(v, T(0), OpAdd{});
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  const T t = lane < kWaves ? wsum[lane] : T(0);
+  const T tincl = wave_incl_scan_op(t, T(0), OpAdd{});
+  const T before = wave > 0 ? read_lane(tincl, wave - 1) : T(0);
+  *total = read_lane(tincl, kWaves - 1);
+  return before + incl - v;
+}
+
 // Reduction over the block with `op` (identity `ident`), result in every
 // thread. `wsum` needs one slot per wave.
 template <typename T, int NTHREADS, typename Op>

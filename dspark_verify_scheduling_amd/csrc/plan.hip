@@ -25,7 +25,7 @@
 //      the unique keys. A bucket sort on the survival bits over the observed
 //      range [min, max] (about one key per bucket) places every key with one
 //      LDS atomic, a scan of the bucket counts and an exact rank among its
-//      bucket's few members: four barriers and O(n) work. If a bucket holds
+//      bucket's few members: three or four barriers and O(n) work. If a bucket holds
 //      more than 32 keys (many equal survivals), the keys are instead merged
 //      from the per-request runs, which are already descending, pairwise in
 //      ceil(log2 B) rounds of merge path. Both give the same order.
@@ -255,6 +255,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     conf_c[idx] = c;
   }
   __syncthreads();
+  // The bucket counts of the sort lie past the confidences when B * gamma
+  // floats fit in the key buffer's bytes: then they are cleared here, and the
+  // reduction's barrier below orders the clear before the counting.
+  const bool early_clear = (size_t)B * G * sizeof(float) <= (size_t)n_keys * sizeof(uint64_t);
+  if (early_clear) {
+    for (int i = tid; i <= kMaxBuckets; i += kPlanThreads) bucket[i] = 0;
+  }
 
   // ---- 1b. survival, forced terms, candidate keys: one thread per
   // (request, position). Thread (r, k) forms c_1 * ... * c_k itself, left to
@@ -333,7 +340,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
                      kWave - 1);
     smax = read_lane(wave_incl_scan_op(mine ? wmax[lane] : 0u, 0u, umax), kWave - 1);
     bad = read_lane(wave_incl_scan_op(mine ? wbad[lane] : 0, 0, ior), kWave - 1);
-    __syncthreads();
+    // no closing barrier: w32 is written again only after the counting
+    // barrier of the sort (or the fallback's barrier); the others never
   }
   if (bad) {
     fallback<PACK>(a, p, (bad & 1) ? DSPARK_DATA_BAD_CONF : DSPARK_DATA_BAD_COST, lds, w32,
@@ -350,8 +358,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     while (nb < n_el && nb < kMaxBuckets) nb <<= 1;
     int shift = 0;
     while ((range >> shift) >= (unsigned int)nb) ++shift;
-    for (int i = tid; i <= nb; i += kPlanThreads) bucket[i] = 0;
-    __syncthreads();
+    if (!early_clear) {
+      for (int i = tid; i <= nb; i += kPlanThreads) bucket[i] = 0;
+      __syncthreads();
+    }
     uint64_t mk[kMaxItems];
     int mb[kMaxItems], ms[kMaxItems];
 #pragma unroll
@@ -378,7 +388,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     }
     if (big > kMaxBucketFill) atomicMax(&s_maxb, big);
     int total_cnt;
-    int run = block_excl_scan<int, kPlanThreads>(cnt_local, w32, &total_cnt);
+    // the barrier after the offsets below closes the scan
+    int run = block_excl_scan_open<int, kPlanThreads>(cnt_local, w32, &total_cnt);
     for (int q = 0; q < per; ++q) {
       const int i = tid * per + q;
       if (i < nb) {
@@ -424,8 +435,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     local += fxv[e];
   }
   long long total_fx;
-  const long long offset = block_excl_scan<long long, kPlanThreads>(local, w64, &total_fx);
+  // w64 is not written again: no closing barrier
+  const long long offset = block_excl_scan_open<long long, kPlanThreads>(local, w64, &total_fx);
   const long long base = (long long)B * (1ll << 40) + forced;
+  // every thread has read its sorted keys (the scan's barrier), so the key
+  // buffer is free: start the per-request counts of verify_lens in it; the
+  // argmax barrier below orders these stores before the counting
+  int32_t* cnt = reinterpret_cast<int32_t*>(lds);
+  for (int r = tid; r < B; r += kPlanThreads) cnt[r] = lmin;
 
   const int lo_b = min(max(a.b_lo, 0), n_el);
   const int hi_b = a.b_hi < 0 ? n_el : min(a.b_hi, n_el);
@@ -540,9 +557,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   }
 
   // ---- 4. verify_lens = L_min + #(first b_exec keys of each request)
-  int32_t* cnt = reinterpret_cast<int32_t*>(lds);  // the keys now live in registers
-  for (int r = tid; r < B; r += kPlanThreads) cnt[r] = lmin;
-  __syncthreads();
 #pragma unroll
   for (int e = 0; e < kMaxItems; ++e) {
     if (e < ipt && base_i + e < bexec) atomicAdd(&cnt[key_r(x[e])], 1);
