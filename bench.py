@@ -221,19 +221,24 @@ def schedule_record(po, ao, total, tier):
             "committed": committed, "committed_minus_tau": committed - tau}
 
 
+SCHED_SHIFTS = (-1.5, 0.0, 1.5, 4.0)  # confidence-logit mean shifts of the seeded steps
+
+
 def schedule_stats(dv, torch, dev, stream, n):
     """The step on n seeded B=256, gamma=8, V=129280 workloads (metadata seeds
-    50000..50000+n-1): each plans and packs on the GPU, its packed rows are
-    filled on the GPU with N(0, 3) clipped to +-15 (a seeded torch generator)
-    and the planted maximum 16 at each row's planted id (no planted ties),
-    then the accept runs. Records are bucketed by the tier the step used."""
+    50000..50000+n-1, the confidence-logit mean shifted by SCHED_SHIFTS in
+    turn so that the steps use different tiers): each plans and packs on the
+    GPU, its packed rows are filled on the GPU with N(0, 3) clipped to +-15 (a
+    seeded torch generator) and the planted maximum 16 at each row's planted
+    id (no planted ties), then the accept runs. Records are bucketed by the
+    tier the step used."""
     from workloads import make
 
     gen = torch.Generator(device=dev)
     gen.manual_seed(20260611)
     recs = []
     for i in range(n):
-        w = make(3, seed=50000 + i, logits=False)
+        w = make(3, seed=50000 + i, logits=False, conf_shift=SCHED_SHIFTS[i % len(SCHED_SHIFTS)])
         B, G, V = w.B, w.gamma, w.V
         tiers = [int(x) for x in w.tiers]
 
@@ -280,7 +285,7 @@ def schedule_stats(dv, torch, dev, stream, n):
             "mean_committed_minus_tau": statistics.mean(r["committed_minus_tau"] for r in rs),
         }
     torch.cuda.empty_cache()
-    return {"steps": n, "by_tier": out}
+    return {"steps": n, "conf_shifts": list(SCHED_SHIFTS), "by_tier": out}
 
 
 def cpu_baseline(w, lens_ref, packed_host, total, budget_s):

@@ -225,9 +225,12 @@ def _draft_logits(spec, ss, target, d_ids, sig_r):
     return out.reshape(B, g, V)
 
 
-def make(cfg: int, seed: Optional[int] = None, *, logits: bool = True) -> Workload:
+def make(cfg: int, seed: Optional[int] = None, *, logits: bool = True,
+         conf_shift: float = 0.0) -> Workload:
     """Draw workload ``cfg`` (0-4). ``logits=False`` skips the big logit arrays
-    (every other array is unchanged by that choice)."""
+    (every other array is unchanged by that choice). ``conf_shift`` moves the
+    mean of the confidence logits of configs 1-3 (the planted draft matches
+    follow the shifted logits)."""
     spec = CONFIGS[cfg]
     seed = 1000 * (cfg + 1) if seed is None else int(seed)
     ss_meta, ss_target, ss_draft = np.random.SeedSequence(seed).spawn(3)
@@ -242,14 +245,14 @@ def make(cfg: int, seed: Optional[int] = None, *, logits: bool = True) -> Worklo
         conf = np.log(c / (1.0 - c)).astype(np.float32)
         temps = np.ones(g, dtype=np.float32)
     elif cfg == 1:
-        conf = (rng.normal(1.5, 1.0, size=(B, g)) - 0.25 * k).astype(np.float32)
+        conf = (rng.normal(1.5 + conf_shift, 1.0, size=(B, g)) - 0.25 * k).astype(np.float32)
         temps = rng.uniform(0.8, 1.5, size=g).astype(np.float32)
     elif cfg == 2:
         mu = rng.choice(np.array([2.5, 1.0, -0.5]), size=B)
-        conf = (rng.normal(0.0, 1.0, size=(B, g)) + mu[:, None] - 0.25 * k).astype(np.float32)
+        conf = (rng.normal(conf_shift, 1.0, size=(B, g)) + mu[:, None] - 0.25 * k).astype(np.float32)
         temps = rng.uniform(0.8, 1.5, size=g).astype(np.float32)
     elif cfg == 3:
-        conf = (rng.normal(1.2, 1.2, size=(B, g)) - 0.3 * k).astype(np.float32)
+        conf = (rng.normal(1.2 + conf_shift, 1.2, size=(B, g)) - 0.3 * k).astype(np.float32)
         temps = rng.uniform(0.7, 2.0, size=g).astype(np.float32)
     else:
         temps = np.ones(g, dtype=np.float32)
