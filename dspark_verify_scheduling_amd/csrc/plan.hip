@@ -73,6 +73,35 @@ __device__ inline bool better(double r1, int b1, double r2, int b2) {
   return r1 > r2 || (r1 == r2 && b1 < b2);
 }
 
+// The cross-wave steps below read one per-wave partial per lane of a 16-lane
+// row (lane l takes wave l & 15's), so every row holds all of them and four
+// row shifts combine them.
+static_assert(kWaves == 16, "one per-wave partial per lane of a 16-lane row");
+
+// Inclusive scan inside each 16-lane row.
+template <typename T, typename Op>
+__device__ inline T row_incl_scan(T x, T ident, Op op) {
+  x = op(x, dpp_t<0x111>(x, ident));
+  x = op(x, dpp_t<0x112>(x, ident));
+  x = op(x, dpp_t<0x114>(x, ident));
+  x = op(x, dpp_t<0x118>(x, ident));
+  return x;
+}
+
+// Exclusive block scan of v (sums), one barrier and no closing one: the
+// per-wave totals go to wsum, and every wave scans all 16 of them.
+template <typename T>
+__device__ inline T plan_excl_scan_open(T v, T* wsum, T* total) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const T incl = wave_incl_scan_op(v, T(0), OpAdd{});
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  const T t = row_incl_scan(wsum[lane & 15], T(0), OpAdd{});
+  const T before = wave > 0 ? read_lane(t, wave - 1) : T(0);
+  *total = read_lane(t, 15);
+  return before + incl - v;
+}
+
 // (ratio desc, b asc) maximum over the wave, left in lane 63. "None" is
 // (-1, INT_MAX): every real ratio is >= 0.
 __device__ inline void wave_argmax(double& r, int& b) {
@@ -92,6 +121,20 @@ __device__ inline void wave_argmax(double& r, int& b) {
   step({dpp_t<0x118>(r, -1.0), dpp_t<0x118>(b, 0x7fffffff)});
   step({dpp_t<0x142, 0xA>(r, -1.0), dpp_t<0x142, 0xA>(b, 0x7fffffff)});
   step({dpp_t<0x143, 0xC>(r, -1.0), dpp_t<0x143, 0xC>(b, 0x7fffffff)});
+}
+
+// The same maximum inside each 16-lane row, left in the row's last lane.
+__device__ inline void row_argmax(double& r, int& b) {
+  auto step = [&](double r2, int b2) {
+    if (better(r2, b2, r, b)) {
+      r = r2;
+      b = b2;
+    }
+  };
+  step(dpp_t<0x111>(r, -1.0), dpp_t<0x111>(b, 0x7fffffff));
+  step(dpp_t<0x112>(r, -1.0), dpp_t<0x112>(b, 0x7fffffff));
+  step(dpp_t<0x114>(r, -1.0), dpp_t<0x114>(b, 0x7fffffff));
+  step(dpp_t<0x118>(r, -1.0), dpp_t<0x118>(b, 0x7fffffff));
 }
 
 
@@ -314,7 +357,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     }
   }
   // one block reduction for the five quantities: per-wave DPP reductions,
-  // then lane w of every wave combines wave w's partials
+  // then every wave combines the 16 per-wave partials
   {
     const int lane = lane_id(), wave = tid / kWave;
     auto umin = [](unsigned int x, unsigned int y) { return min(x, y); };
@@ -333,13 +376,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
       wbad[wave] = bad;
     }
     __syncthreads();
-    const bool mine = lane < kWaves;
-    forced = read_lane(wave_incl_scan_op(mine ? w64[lane] : 0ll, 0ll, OpAdd{}), kWave - 1);
-    n_el = read_lane(wave_incl_scan_op(mine ? w32[lane] : 0, 0, OpAdd{}), kWave - 1);
-    smin = read_lane(wave_incl_scan_op(mine ? wmin[lane] : 0xFFFFFFFFu, 0xFFFFFFFFu, umin),
-                     kWave - 1);
-    smax = read_lane(wave_incl_scan_op(mine ? wmax[lane] : 0u, 0u, umax), kWave - 1);
-    bad = read_lane(wave_incl_scan_op(mine ? wbad[lane] : 0, 0, ior), kWave - 1);
+    const int l = lane & 15;
+    const long long f2 = w64[l];
+    const int n2 = w32[l], b2 = wbad[l];
+    const unsigned int mn2 = wmin[l], mx2 = wmax[l];
+    forced = read_lane(row_incl_scan(f2, 0ll, OpAdd{}), 15);
+    n_el = read_lane(row_incl_scan(n2, 0, OpAdd{}), 15);
+    smin = read_lane(row_incl_scan(mn2, 0xFFFFFFFFu, umin), 15);
+    smax = read_lane(row_incl_scan(mx2, 0u, umax), 15);
+    bad = read_lane(row_incl_scan(b2, 0, ior), 15);
     // no closing barrier: w32 is written again only after the counting
     // barrier of the sort (or the fallback's barrier); the others never
   }
@@ -389,7 +434,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     if (big > kMaxBucketFill) atomicMax(&s_maxb, big);
     int total_cnt;
     // the barrier after the offsets below closes the scan
-    int run = block_excl_scan_open<int, kPlanThreads>(cnt_local, w32, &total_cnt);
+    int run = plan_excl_scan_open<int>(cnt_local, w32, &total_cnt);
     for (int q = 0; q < per; ++q) {
       const int i = tid * per + q;
       if (i < nb) {
@@ -436,7 +481,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   }
   long long total_fx;
   // w64 is not written again: no closing barrier
-  const long long offset = block_excl_scan_open<long long, kPlanThreads>(local, w64, &total_fx);
+  const long long offset = plan_excl_scan_open<long long>(local, w64, &total_fx);
   const long long base = (long long)B * (1ll << 40) + forced;
   // every thread has read its sorted keys (the scan's barrier), so the key
   // buffer is free: start the per-request counts of verify_lens in it; the
@@ -516,11 +561,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     fallback<PACK>(a, p, s_flags, lds, w32, &s_tier, &pre);
     return;
   }
-  double br = lane < kWaves ? wratio[lane] : -1.0;
-  int bstar = lane < kWaves ? wb[lane] : 0x7fffffff;
-  wave_argmax(br, bstar);
-  br = read_lane(br, kWave - 1);
-  bstar = read_lane(bstar, kWave - 1);
+  double br = wratio[lane & 15];
+  int bstar = wb[lane & 15];
+  row_argmax(br, bstar);
+  br = read_lane(br, 15);
+  bstar = read_lane(bstar, 15);
 
 #pragma unroll
   for (int t = 0; t <= kMaxItems; ++t) {
