@@ -1,6 +1,8 @@
 // Internal declarations shared by the HIP kernels of libdspark (gfx950 only).
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -258,27 +260,22 @@ struct OpAdd {
   __device__ T operator()(T a, T b) const { return a + b; }
 };
 
-// Exclusive scan over the block. `wsum` needs one slot per wave. Returns the
-// exclusive prefix of this thread's value; *total receives the block total.
-// Lane w of every wave reads wave w's total (one LDS read per lane), and the
-// wave offsets come from a DPP scan over those lanes.
-template <typename T, int NTHREADS>
-__device__ inline T block_excl_scan(T v, T* wsum, T* total) {
-  constexpr int kWaves = NTHREADS / kWave;
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const T incl = wave_incl_scan_op(v, T(0), OpAdd{});
-  if (lane == kWave - 1) wsum[wave] = incl;
-  __syncthreads();
-  const T t = lane < kWaves ? wsum[lane] : T(0);
-  const T tincl = wave_incl_scan_op(t, T(0), OpAdd{});
-  const T before = wave > 0 ? read_lane(tincl, wave - 1) : T(0);
-  *total = read_lane(tincl, kWaves - 1);
-  __syncthreads();  // wsum may be reused right after
-  return before + incl - v;
+// Inclusive scan inside each 16-lane row.
+template <typename T, typename Op>
+__device__ inline T row_incl_scan(T x, T ident, Op op) {
+  x = op(x, dpp_t<0x111>(x, ident));
+  x = op(x, dpp_t<0x112>(x, ident));
+  x = op(x, dpp_t<0x114>(x, ident));
+  x = op(x, dpp_t<0x118>(x, ident));
+  return x;
 }
 
-// block_excl_scan without its closing barrier, for callers that pass another
-// barrier before anything writes `wsum` again.
+// Exclusive scan over the block, without a closing barrier: for callers that
+// pass another barrier before anything writes `wsum` (one slot per wave)
+// again. Returns the exclusive prefix of this thread's value; *total receives
+// the block total. With 16 waves and integer sums, every 16-lane row reads all
+// 16 wave totals (lane l takes wave l & 15's) and scans them with four row
+// shifts.
 template <typename T, int NTHREADS>
 __device__ inline T block_excl_scan_open(T v, T* wsum, T* total) {
   constexpr int kWaves = NTHREADS / kWave;
@@ -286,11 +283,25 @@ __device__ inline T block_excl_scan_open(T v, T* wsum, T* total) {
   const T incl = wave_incl_scan_op(v, T(0), OpAdd{});
   if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
-  const T t = lane < kWaves ? wsum[lane] : T(0);
-  const T tincl = wave_incl_scan_op(t, T(0), OpAdd{});
-  const T before = wave > 0 ? read_lane(tincl, wave - 1) : T(0);
-  *total = read_lane(tincl, kWaves - 1);
-  return before + incl - v;
+  if constexpr (kWaves == 16 && std::is_integral_v<T>) {
+    const T t = row_incl_scan(wsum[lane & 15], T(0), OpAdd{});
+    *total = read_lane(t, 15);
+    return (wave > 0 ? read_lane(t, wave - 1) : T(0)) + incl - v;
+  } else {
+    const T t = lane < kWaves ? wsum[lane] : T(0);
+    const T tincl = wave_incl_scan_op(t, T(0), OpAdd{});
+    *total = read_lane(tincl, kWaves - 1);
+    return (wave > 0 ? read_lane(tincl, wave - 1) : T(0)) + incl - v;
+  }
+}
+
+// Exclusive scan over the block (block_excl_scan_open, then a barrier so that
+// `wsum` may be reused right after).
+template <typename T, int NTHREADS>
+__device__ inline T block_excl_scan(T v, T* wsum, T* total) {
+  const T r = block_excl_scan_open<T, NTHREADS>(v, wsum, total);
+  __syncthreads();
+  return r;
 }
 
 // Reduction over the block with `op` (identity `ident`), result in every

@@ -15,8 +15,8 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(PackArgs a) {
   extern __shared__ int32_t sh[];  // lens[B], cu[B + 1]
   __shared__ int w32[kWaves + 1];
   __shared__ int s_flags;
-  __shared__ int s_tier;
   const int tid = threadIdx.x;
+  const int tier_lane = load_tier_lane(a);
   int32_t* lens = sh;
   int32_t* cu = sh + a.B;
   if (tid == 0) s_flags = 0;
@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(PackArgs a) {
   }
   if (bad) atomicOr(&s_flags, DSPARK_DATA_BAD_LENS);
   __syncthreads();
-  pack_block<kPackThreads>(a, lens, cu, w32, &s_tier, s_flags);
+  pack_block<kPackThreads>(a, lens, cu, w32, tier_lane, s_flags);
 }
 
 }  // namespace

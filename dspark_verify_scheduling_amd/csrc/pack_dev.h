@@ -42,14 +42,31 @@ struct PackPrefetch {
   }
 };
 
+// The tier table one entry per lane (lane l < ntiers holds tiers[l]), loaded
+// at kernel start so that picking the tier needs no load.
+__device__ inline int load_tier_lane(const PackArgs& a) {
+  const int l = lane_id();
+  return a.tiers[l < a.ntiers ? l : 0];
+}
+
+// The first tier >= total, else the last tier (tiers ascend), from the
+// per-lane table; wave-uniform, called by every lane of the wave.
+__device__ inline int pick_tier(int tier_lane, int ntiers, int total) {
+  const int l = lane_id();
+  const unsigned long long m = __ballot(l < ntiers && tier_lane >= total);
+  const int i = m ? (int)__builtin_ctzll(m) : ntiers - 1;
+  return __builtin_amdgcn_readlane(tier_lane, i);
+}
+
 // Packs B requests whose (already clamped) lengths sit in LDS `lens`,
 // writing cu_seqlens into LDS `cu` (B + 1 entries) and to global memory.
 // Block-wide: every thread of the NTHREADS-thread workgroup must call it.
-// `status` is OR-ed into meta[2] by thread 0 at the end. `pre` holds the
-// inputs of this thread's first NPRE slots (see PackPrefetch).
+// `status` is OR-ed into meta[2] by thread 0 at the end. `tier_lane` is
+// load_tier_lane's value; `pre` holds the inputs of this thread's first NPRE
+// slots (see PackPrefetch).
 template <int NTHREADS, int NPRE = 0>
 __device__ void pack_block(const PackArgs& a, const int32_t* lens, int32_t* cu, int* wsum,
-                           int* s_tier, int status,
+                           int tier_lane, int status,
                            const PackPrefetch<NTHREADS, NPRE>* pre = nullptr) {
   const int tid = threadIdx.x;
   const int B = a.B, G = a.gamma;
@@ -60,7 +77,8 @@ __device__ void pack_block(const PackArgs& a, const int32_t* lens, int32_t* cu, 
     if (r0 + t < B) local += lens[r0 + t];
   }
   int total;
-  int run = block_excl_scan<int, NTHREADS>(local, wsum, &total);
+  // wsum is not written again: no closing barrier
+  int run = block_excl_scan_open<int, NTHREADS>(local, wsum, &total);
   for (int t = 0; t < ipt; ++t) {
     const int r = r0 + t;
     if (r < B) {
@@ -72,15 +90,8 @@ __device__ void pack_block(const PackArgs& a, const int32_t* lens, int32_t* cu, 
   if (tid == 0) {
     cu[B] = total;
     a.cu[B] = total;
-    int tier = a.tiers[a.ntiers - 1];
-    for (int i = 0; i < a.ntiers; ++i) {
-      if (a.tiers[i] >= total) {
-        tier = a.tiers[i];
-        break;
-      }
-    }
-    *s_tier = tier;
   }
+  const int tier = pick_tier(tier_lane, a.ntiers, total);
   __syncthreads();
   const int rows = B * (G + 1);
 #pragma unroll
@@ -107,7 +118,6 @@ __device__ void pack_block(const PackArgs& a, const int32_t* lens, int32_t* cu, 
       if (a.pos) a.pos[i] = (a.prefix ? a.prefix[r] : 0) + j;
     }
   }
-  const int tier = *s_tier;
   for (int i = total + tid; i < tier; i += NTHREADS) {
     a.ids[i] = 0;
     if (a.req) a.req[i] = -1;

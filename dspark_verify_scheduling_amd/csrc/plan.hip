@@ -78,30 +78,6 @@ __device__ inline bool better(double r1, int b1, double r2, int b2) {
 // row shifts combine them.
 static_assert(kWaves == 16, "one per-wave partial per lane of a 16-lane row");
 
-// Inclusive scan inside each 16-lane row.
-template <typename T, typename Op>
-__device__ inline T row_incl_scan(T x, T ident, Op op) {
-  x = op(x, dpp_t<0x111>(x, ident));
-  x = op(x, dpp_t<0x112>(x, ident));
-  x = op(x, dpp_t<0x114>(x, ident));
-  x = op(x, dpp_t<0x118>(x, ident));
-  return x;
-}
-
-// Exclusive block scan of v (sums), one barrier and no closing one: the
-// per-wave totals go to wsum, and every wave scans all 16 of them.
-template <typename T>
-__device__ inline T plan_excl_scan_open(T v, T* wsum, T* total) {
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const T incl = wave_incl_scan_op(v, T(0), OpAdd{});
-  if (lane == kWave - 1) wsum[wave] = incl;
-  __syncthreads();
-  const T t = row_incl_scan(wsum[lane & 15], T(0), OpAdd{});
-  const T before = wave > 0 ? read_lane(t, wave - 1) : T(0);
-  *total = read_lane(t, 15);
-  return before + incl - v;
-}
-
 // (ratio desc, b asc) maximum over the wave, left in lane 63. "None" is
 // (-1, INT_MAX): every real ratio is >= 0.
 __device__ inline void wave_argmax(double& r, int& b) {
@@ -208,13 +184,13 @@ using PlanPrefetch = PackPrefetch<kPlanThreads, kPackPrefetch>;
 
 template <bool PACK>
 __device__ void fallback(const PlanArgs& a, const PackArgs& p, int flags, uint64_t* lds, int* w32,
-                         int* s_tier, const PlanPrefetch* pre) {
+                         int tier_lane, const PlanPrefetch* pre) {
   write_fallback(a, flags);
   if (PACK) {
     int32_t* lens = reinterpret_cast<int32_t*>(lds);
     for (int r = threadIdx.x; r < a.B; r += kPlanThreads) lens[r] = a.lmax;
     __syncthreads();
-    pack_block<kPlanThreads, kPackPrefetch>(p, lens, lens + a.B, w32, s_tier, 0, pre);
+    pack_block<kPlanThreads, kPackPrefetch>(p, lens, lens + a.B, w32, tier_lane, 0, pre);
   }
 }
 
@@ -238,7 +214,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   __shared__ double wratio[kWaves];
   __shared__ int wb[kWaves];
   __shared__ int s_flags;
-  __shared__ int s_tier;
   __shared__ unsigned int wmin[kWaves], wmax[kWaves];
   __shared__ int wbad[kWaves];
   __shared__ int s_maxb;
@@ -262,7 +237,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   }
 
   PlanPrefetch pre;
-  if (PACK) pre.load(p);
+  int tier_lane = 0;
+  if (PACK) {
+    pre.load(p);
+    tier_lane = load_tier_lane(p);
+  }
   // cost entries of the budgets this thread will evaluate: b = base_i + e + 1
   const bool sps_mode = a.cost_mode == DSPARK_COST_SPS1D;
   float th[kMaxItems];
@@ -390,7 +369,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   }
   if (bad) {
     fallback<PACK>(a, p, (bad & 1) ? DSPARK_DATA_BAD_CONF : DSPARK_DATA_BAD_COST, lds, w32,
-                   &s_tier, &pre);
+                   tier_lane, &pre);
     return;
   }
 
@@ -434,7 +413,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     if (big > kMaxBucketFill) atomicMax(&s_maxb, big);
     int total_cnt;
     // the barrier after the offsets below closes the scan
-    int run = plan_excl_scan_open<int>(cnt_local, w32, &total_cnt);
+    int run = block_excl_scan_open<int, kPlanThreads>(cnt_local, w32, &total_cnt);
     for (int q = 0; q < per; ++q) {
       const int i = tid * per + q;
       if (i < nb) {
@@ -481,7 +460,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   }
   long long total_fx;
   // w64 is not written again: no closing barrier
-  const long long offset = plan_excl_scan_open<long long>(local, w64, &total_fx);
+  const long long offset = block_excl_scan_open<long long, kPlanThreads>(local, w64, &total_fx);
   const long long base = (long long)B * (1ll << 40) + forced;
   // every thread has read its sorted keys (the scan's barrier), so the key
   // buffer is free: start the per-request counts of verify_lens in it; the
@@ -558,7 +537,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   }
   __syncthreads();
   if (s_flags) {
-    fallback<PACK>(a, p, s_flags, lds, w32, &s_tier, &pre);
+    fallback<PACK>(a, p, s_flags, lds, w32, tier_lane, &pre);
     return;
   }
   double br = wratio[lane & 15];
@@ -591,13 +570,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   int bexec = bstar;
   if (PACK && a.align) {
     const int total = m0 + bstar;
-    int tier = p.tiers[p.ntiers - 1];
-    for (int i = 0; i < p.ntiers; ++i) {
-      if (p.tiers[i] >= total) {
-        tier = p.tiers[i];
-        break;
-      }
-    }
+    const int tier = pick_tier(tier_lane, p.ntiers, total);
     bexec = min(bstar + (tier - total), n_el);
   }
 
@@ -614,7 +587,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     a.meta[2] = 0;
     a.meta[3] = m0 + bexec;
   }
-  if (PACK) pack_block<kPlanThreads, kPackPrefetch>(p, cnt, cnt + B, w32, &s_tier, 0, &pre);
+  if (PACK) pack_block<kPlanThreads, kPackPrefetch>(p, cnt, cnt + B, w32, tier_lane, 0, &pre);
 }
 
 }  // namespace
