@@ -200,6 +200,19 @@ __device__ inline T wave_sum(T v) {
   return v;
 }
 
+// n / d for 0 <= n < 2^15 and 1 <= d <= 65 with one float32 multiply and a
+// truncation, exact: with inv = RN32((1 + 2^-22) / d) = (1 + e) / d,
+// e in [2^-22 - 2^-23.9, 2^-22 + 2^-23.9], and n = q d + f (0 <= f < d), the
+// product RN32(n * inv) = (n / d)(1 + e)(1 + h), |h| <= 2^-24, is at least
+// n / d >= q and at most n / d + (n / d) 2^-21 < q + (d - 1) / d + 2^-6 / d
+// < q + 1, so it truncates to q.
+struct SmallDiv {
+  float inv;
+  int d;
+  __device__ explicit SmallDiv(int d_) : inv(__fdiv_rn(1.0f + 0x1p-22f, (float)d_)), d(d_) {}
+  __device__ int quo(int n) const { return (int)__fmul_rn((float)n, inv); }
+};
+
 // ---- wave primitives on DPP (data-parallel primitives): lane exchanges
 // inside the VALU, no LDS round trip. Encodings of the gfx9-family DPP
 // controls used here: row_shr:n = 0x110 + n, row_bcast:15 = 0x142,

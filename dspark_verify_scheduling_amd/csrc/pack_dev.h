@@ -27,13 +27,14 @@ struct PackPrefetch {
   int prefix[NPRE > 0 ? NPRE : 1];
   __device__ void load(const PackArgs& a) {
     const int G = a.gamma, rows = a.B * (G + 1);
+    const SmallDiv per_req(G + 1);  // rows < 2^15
 #pragma unroll
     for (int q = 0; q < NPRE; ++q) {
       const int f = threadIdx.x + q * NTHREADS;
       id[q] = 0;
       prefix[q] = 0;
       if (f < rows) {
-        const int r = f / (G + 1);
+        const int r = per_req.quo(f);
         const int j = f - r * (G + 1);
         id[q] = j ? a.drafts[(size_t)r * G + (j - 1)] : a.anchors[r];
         prefix[q] = a.prefix ? a.prefix[r] : 0;
@@ -93,12 +94,13 @@ __device__ void pack_block(const PackArgs& a, const int32_t* lens, int32_t* cu, 
   }
   const int tier = pick_tier(tier_lane, a.ntiers, total);
   __syncthreads();
-  const int rows = B * (G + 1);
+  const int rows = B * (G + 1);  // < 2^15
+  const SmallDiv per_req(G + 1);
 #pragma unroll
   for (int q = 0; q < NPRE; ++q) {
     const int f = tid + q * NTHREADS;
     if (f < rows) {
-      const int r = f / (G + 1);
+      const int r = per_req.quo(f);
       const int j = f - r * (G + 1);
       if (j < lens[r]) {
         const int i = cu[r] + j;
@@ -109,7 +111,7 @@ __device__ void pack_block(const PackArgs& a, const int32_t* lens, int32_t* cu, 
     }
   }
   for (int f = tid + NPRE * NTHREADS; f < rows; f += NTHREADS) {
-    const int r = f / (G + 1);
+    const int r = per_req.quo(f);
     const int j = f - r * (G + 1);
     if (j < lens[r]) {
       const int i = cu[r] + j;

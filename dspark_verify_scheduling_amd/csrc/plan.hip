@@ -265,11 +265,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
 
   // ---- 1a. calibrated confidence of every (request, position), in parallel
   int bad = 0;
+  const SmallDiv per_req(G);  // B * gamma <= 8192
   for (int idx = tid; idx < B * G; idx += kPlanThreads) {
     const float v = a.conf[idx];
     float c = v;
     if (a.kind == DSPARK_IN_CONF_LOGITS) {
-      const float T = a.temps[idx % G];
+      const float T = a.temps[idx - per_req.quo(idx) * G];
       if (!(T > 0.0f && T <= FLT_MAX)) bad = 1;
       c = sigmoid_cr(__fdiv_rn(v, T));
     }
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   int n_el = 0;
   unsigned int smin = 0xFFFFFFFFu, smax = 0u;
   for (int idx = tid; idx < B * G; idx += kPlanThreads) {
-    const int r = idx / G;
+    const int r = per_req.quo(idx);
     const int k = idx - r * G + 1;
     const float* cr = conf_c + r * G;
     float s = cr[0];
