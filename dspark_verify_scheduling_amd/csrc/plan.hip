@@ -55,8 +55,8 @@ namespace {
 
 constexpr int kWaves = kPlanThreads / kWave;
 constexpr int kMaxItems = DSPARK_MAX_CANDIDATES / kPlanThreads;  // keys per thread, at most
-constexpr int kMinBuckets = 64;
-constexpr int kMaxBuckets = 4096;
+constexpr int kLgMinBuckets = 6, kLgMaxBuckets = 12;
+constexpr int kMaxBuckets = 1 << kLgMaxBuckets;
 constexpr int kMaxBucketFill = 32;  // beyond this the bucket rank loop gives way to merging
 
 __device__ inline uint64_t make_key(float s, int k, int r) {
@@ -236,6 +236,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     s_maxb = 0;
   }
 
+  // this thread's confidences (and their temperatures) first: the
+  // calibration waits for them, not for the loads issued after them
+  const SmallDiv per_req(G);  // B * gamma <= 8192
+  const bool logits = a.kind == DSPARK_IN_CONF_LOGITS;
+  float cin[kMaxItems], tin[kMaxItems];
+#pragma unroll
+  for (int e = 0; e < kMaxItems; ++e) {
+    const int idx = tid + e * kPlanThreads;
+    cin[e] = 0.0f;
+    tin[e] = 1.0f;
+    if (idx < B * G) {
+      cin[e] = a.conf[idx];
+      if (logits) tin[e] = a.temps[idx - per_req.quo(idx) * G];
+    }
+  }
+
   PlanPrefetch pre;
   int tier_lane = 0;
   if (PACK) {
@@ -265,17 +281,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
 
   // ---- 1a. calibrated confidence of every (request, position), in parallel
   int bad = 0;
-  const SmallDiv per_req(G);  // B * gamma <= 8192
-  for (int idx = tid; idx < B * G; idx += kPlanThreads) {
-    const float v = a.conf[idx];
-    float c = v;
-    if (a.kind == DSPARK_IN_CONF_LOGITS) {
-      const float T = a.temps[idx - per_req.quo(idx) * G];
-      if (!(T > 0.0f && T <= FLT_MAX)) bad = 1;
-      c = sigmoid_cr(__fdiv_rn(v, T));
+#pragma unroll
+  for (int e = 0; e < kMaxItems; ++e) {
+    const int idx = tid + e * kPlanThreads;
+    if (idx < B * G) {
+      const float v = cin[e];
+      float c = v;
+      if (logits) {
+        const float T = tin[e];
+        if (!(T > 0.0f && T <= FLT_MAX)) bad = 1;
+        c = sigmoid_cr(__fdiv_rn(v, T));
+      }
+      if (!(c >= 0.0f && c <= 1.0f)) bad = 1;
+      conf_c[idx] = c;
     }
-    if (!(c >= 0.0f && c <= 1.0f)) bad = 1;
-    conf_c[idx] = c;
   }
   __syncthreads();
   // The bucket counts of the sort lie past the confidences when B * gamma
@@ -379,10 +398,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   const uint64_t* sorted = keys;
   if (n_el > 0) {
     const unsigned int hi = smax, range = smax - smin;
-    int nb = kMinBuckets;
-    while (nb < n_el && nb < kMaxBuckets) nb <<= 1;
-    int shift = 0;
-    while ((range >> shift) >= (unsigned int)nb) ++shift;
+    // nb = the power of two in [64, 4096] nearest above n_el; shift = the
+    // least s with (range >> s) < nb
+    const int lg_nb = min(max(32 - __clz(n_el - 1), kLgMinBuckets), kLgMaxBuckets);
+    const int nb = 1 << lg_nb;
+    const int shift = range < (unsigned int)nb ? 0 : (31 - __clz((int)range)) - lg_nb + 1;
     if (!early_clear) {
       for (int i = tid; i <= nb; i += kPlanThreads) bucket[i] = 0;
       __syncthreads();
