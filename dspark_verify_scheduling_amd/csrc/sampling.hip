@@ -273,7 +273,9 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
   __shared__ unsigned int s_idx[kWaves];  // apart from s_key: waves may still read the key
   __shared__ int s_flag[kWaves];
   __shared__ unsigned long long s_z[kWaves][kChunks];
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  // the wave index as a scalar: the per-wave LDS addresses need no registers
+  const int tid = threadIdx.x, lane = lane_id(),
+            wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int nvec = a.nvec;
   load_table(s_B);
 
@@ -331,6 +333,10 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
   const int last_chunk = (nvec - 1) / kSampChunkVecs;
 
   for (int k = 0; k < n_rows; ++k) {
+    // the row length through an opaque copy, so that the per-slot bounds
+    // are formed where they are used rather than kept live across the loop
+    int nvk = nvec;
+    asm volatile("" : "+s"(nvk));
     const int slot = s_list[k];
     const float xt = tid < a.tail ? xr : -INFINITY;
 
@@ -338,7 +344,7 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
     // a slot stores it back with -inf in the lanes past the row end (no
     // maximum, zero weight); later uses read r[i] as it is.
     auto slot_vec = [&](int i) -> u32x4 {
-      r[i] = i * kRsThreads + tid < nvec ? r[i] : fill;
+      r[i] = i * kRsThreads + tid < nvk ? r[i] : fill;
       return r[i];
     };
     unsigned int key;
@@ -349,7 +355,7 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
       argmax::u16x2 mu = (argmax::u16x2){0, 0};
 #pragma unroll
       for (int i = 0; i < SLOTS; ++i) {
-        if (i * kRsThreads < nvec) {
+        if (i * kRsThreads < nvk) {
           const u32x4 d = slot_vec(i);
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
@@ -376,7 +382,7 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
         unsigned int kk = 0;
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
-          if (i * kRsThreads < nvec) {
+          if (i * kRsThreads < nvk) {
             const u32x4 d = r[i];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
@@ -398,7 +404,7 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
       unsigned int kk = 0;
 #pragma unroll
       for (int i = 0; i < SLOTS; ++i) {
-        if (i * kRsThreads < nvec) {
+        if (i * kRsThreads < nvk) {
           const u32x4 d = slot_vec(i);
 #pragma unroll
           for (int w = 0; w < 4; ++w) kk = max(kk, argmax::f32_key(d[w]));
@@ -423,11 +429,11 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
         const unsigned int kt = DT == DSPARK_BF16
                                     ? (argmax::bf16x2_keys(__float_as_uint(xt) >> 16) & 0xFFFFu)
                                     : argmax::f32_key(__float_as_uint(xt));
-        if (kt == key) cand = (unsigned int)(nvec * kEpv + tid);
+        if (kt == key) cand = (unsigned int)(nvk * kEpv + tid);
       }
 #pragma unroll
       for (int i = SLOTS - 1; i >= 0; --i) {
-        if (i * kRsThreads < nvec) {
+        if (i * kRsThreads < nvk) {
           const u32x4 d = r[i];
           const unsigned int base = (unsigned int)(i * kRsThreads + tid) * kEpv;
 #pragma unroll
