@@ -99,6 +99,39 @@ __device__ inline unsigned int weight(float x, float m, float c, const uint2* Bt
   return (y + ((1u << n) >> 1)) >> n;
 }
 
+// weight(x[e], m[e], c, Bt) for e < N, the N table reads issued before the
+// first is used (one wait for all of them).
+template <int N>
+__device__ inline void weights(const float (&x)[N], const float (&m)[N], float c,
+                               const uint2* Bt, unsigned int (&w)[N]) {
+  unsigned int bits[N], h[N];
+  uint2 bd[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const float u = __fmul_rn(__fsub_rn(m[e], x[e]), c);
+    bits[e] = __float_as_uint(__fadd_rn(u, 12582912.0f));
+    h[e] = u < kUcut ? __builtin_amdgcn_ubfe(bits[e], 8, 8) : 256u;
+  }
+#pragma unroll
+  for (int e = 0; e < N; ++e) bd[e] = Bt[h[e]];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const unsigned int n = __builtin_amdgcn_ubfe(bits[e], 16, 5);
+    const unsigned int r = bits[e] & 255u;
+    const unsigned int y = bd[e].x - (((unsigned int)__umul24(bd[e].y, r) + 128u) >> 8);
+    w[e] = (y + ((1u << n) >> 1)) >> n;
+  }
+}
+
+// The weights of x[0] and x[1] in a row with maximum m, summed.
+__device__ inline unsigned long long weight_sum2(const float* x, float m, float c, const uint2* Bt) {
+  const float xs[2] = {x[0], x[1]}, ms[2] = {m, m};
+  unsigned int w[2];
+  weights<2>(xs, ms, c, Bt, w);
+  return (unsigned long long)w[0] + w[1];
+}
+
 // The weight table in LDS: kExp2Len - 1 interpolation pairs, then the zero
 // pair.
 __device__ inline void load_table(uint2* Bt) {
@@ -237,7 +270,7 @@ __global__ __launch_bounds__(kSampThreads) void samp_z_kernel(SampArgs a) {
       float x[kEpv];
       widen<DT>(d[i], x);
 #pragma unroll
-      for (int e = 0; e < kEpv; ++e) z += weight(x[e], m, c, s_B);
+      for (int e = 0; e < kEpv; e += 2) z += weight_sum2(x + e, m, c, s_B);
     }
   }
   z = wave_sum_u64(z);
@@ -478,7 +511,7 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
         float x[kEpv];
         widen<DT>(d, x);
 #pragma unroll
-        for (int e = 0; e < kEpv; ++e) zc += weight(x[e], m, c, s_B);
+        for (int e = 0; e < kEpv; e += 2) zc += weight_sum2(x + e, m, c, s_B);
       }
       // both slots of a chunk are summed before either is reloaded (the
       // reload's address depends on an opaque copy of the thread index tied
