@@ -76,6 +76,22 @@ def test_plan_parity(cfg, seed):
     _check_plan(got, ref)
 
 
+@pytest.mark.parametrize("shift", [-3.0, -1.5, 1.5, 4.0, 6.0])
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_plan_parity_confidence_shifts(cfg, shift):
+    """Low to very high confidence (the confidence-logit mean moved by
+    `shift`): survivals spread far below eps, or crowd just under 1, which
+    moves the bucket occupancy, the chosen budget and the tier."""
+    w = make(cfg, seed=int(1000 + 10 * shift), logits=False, conf_shift=shift)
+    got, ref = _plan_both(w)
+    _check_plan(got, ref)
+    args = (w.B, w.gamma, oracle.IN_CONF_LOGITS, w.conf, w.temps, w.min_len, w.max_len, w.eps,
+            w.b_lo, w.b_hi, w.bias, w.alpha, w.theta)
+    gp, gk = plan_pack(*args, w.anchors, w.drafts, w.tiers, w.prefix_lens,
+                       tag=f"cfg{cfg} shift {shift}")
+    _check_plan_pack(w, args, gp, gk)
+
+
 def test_plan_pages_examples():
     bias, alpha, theta = np.float32(0), np.zeros(3, np.float32), np.ones(7, np.float32)
     cond = np.array([[0.9, 0.8], [0.6, 0.5]], np.float32)
