@@ -89,27 +89,61 @@ constexpr double kLn2_3 = 0x1.cc01f97b57a08p-87;
 constexpr double kLog2e = 0x1.71547652b82fep+0;
 constexpr double kBand = 0x1p-45;
 
-// e^t for |t| < 120 in fp64, relative error < 2^-50.
-DSPARK_HD double exp_fast(double t) {
+// A coefficient passed through a scalar register pair on the device: the
+// three-operand v_fma_f64 takes no 64-bit literal, and a literal addend costs
+// two v_mov_b32 ahead of a v_fmac_f64 per Horner step; from a scalar pair the
+// step is one v_fma_f64. The value is unchanged.
+__host__ inline double scalar_const(double c) { return c; }
+__device__ inline double scalar_const(double c) {
+  asm volatile("" : "+s"(c));
+  return c;
+}
+
+// On the device, a point the instruction scheduler does not move code across:
+// it keeps the steps of several interleaved dependency chains together (the
+// scheduler would otherwise run the chains one after the other).
+__host__ inline void sched_fence() {}
+__device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// e^t for |t| < 120 in fp64, relative error < 2^-50, for N independent
+// arguments: each step is taken for all N before the next, so that their
+// dependency chains interleave. Every argument gets the same operations.
+template <int N>
+DSPARK_HD void exp_fast_n(const double (&t)[N], double (&out)[N]) {
 #pragma clang fp contract(off)
-  double n = __builtin_rint(t * kLog2e);
-  double r = t - n * kLn2_1;            // exact
-  r = __builtin_fma(-n, kLn2_2, r);     // one rounding
-  double p = 0x1.6124613a86d09p-33;     // 1/13!
-  p = __builtin_fma(p, r, 0x1.1eed8eff8d898p-29);  // 1/12!
-  p = __builtin_fma(p, r, 0x1.ae64567f544e4p-26);  // 1/11!
-  p = __builtin_fma(p, r, 0x1.27e4fb7789f5cp-22);  // 1/10!
-  p = __builtin_fma(p, r, 0x1.71de3a556c734p-19);  // 1/9!
-  p = __builtin_fma(p, r, 0x1.a01a01a01a01ap-16);  // 1/8!
-  p = __builtin_fma(p, r, 0x1.a01a01a01a01ap-13);  // 1/7!
-  p = __builtin_fma(p, r, 0x1.6c16c16c16c17p-10);  // 1/6!
-  p = __builtin_fma(p, r, 0x1.1111111111111p-7);   // 1/5!
-  p = __builtin_fma(p, r, 0x1.5555555555555p-5);   // 1/4!
-  p = __builtin_fma(p, r, 0x1.5555555555555p-3);   // 1/3!
-  p = __builtin_fma(p, r, 0x1p-1);                 // 1/2!
-  p = __builtin_fma(p, r, 1.0);
-  p = __builtin_fma(p, r, 1.0);
-  return __builtin_ldexp(p, (int)n);
+  double n[N], r[N], p[N];
+  for (int i = 0; i < N; ++i) n[i] = __builtin_rint(t[i] * kLog2e);
+  for (int i = 0; i < N; ++i) r[i] = t[i] - n[i] * kLn2_1;                // exact
+  for (int i = 0; i < N; ++i) r[i] = __builtin_fma(-n[i], kLn2_2, r[i]);  // one rounding
+  for (int i = 0; i < N; ++i) p[i] = 0x1.6124613a86d09p-33;                // 1/13!
+  const double c[11] = {
+      scalar_const(0x1.1eed8eff8d898p-29),  // 1/12!
+      scalar_const(0x1.ae64567f544e4p-26),  // 1/11!
+      scalar_const(0x1.27e4fb7789f5cp-22),  // 1/10!
+      scalar_const(0x1.71de3a556c734p-19),  // 1/9!
+      scalar_const(0x1.a01a01a01a01ap-16),  // 1/8!
+      scalar_const(0x1.a01a01a01a01ap-13),  // 1/7!
+      scalar_const(0x1.6c16c16c16c17p-10),  // 1/6!
+      scalar_const(0x1.1111111111111p-7),   // 1/5!
+      scalar_const(0x1.5555555555555p-5),   // 1/4!
+      scalar_const(0x1.5555555555555p-3),   // 1/3!
+      0x1p-1,                               // 1/2!
+  };
+  for (int k = 0; k < 11; ++k) {
+    for (int i = 0; i < N; ++i) p[i] = __builtin_fma(p[i], r[i], c[k]);
+    if (N > 1) sched_fence();
+  }
+  for (int i = 0; i < N; ++i) p[i] = __builtin_fma(p[i], r[i], 1.0);
+  if (N > 1) sched_fence();
+  for (int i = 0; i < N; ++i) p[i] = __builtin_fma(p[i], r[i], 1.0);
+  for (int i = 0; i < N; ++i) out[i] = __builtin_ldexp(p[i], (int)n[i]);
+}
+
+DSPARK_HD double exp_fast(double t) {
+  const double a[1] = {t};
+  double e[1];
+  exp_fast_n<1>(a, e);
+  return e[0];
 }
 
 // e^t for |t| < 120 in double-double, about 100 correct bits.
@@ -168,21 +202,52 @@ DSPARK_HD float sigmoid_slow(float x) {
   return dd_to_f32(y);
 }
 
+// The fast path alone, branch-free, for N independent inputs: y[i], and
+// through ok[i] whether it is the correctly rounded sigmoid (false: take
+// sigmoid_slow). Inputs at or past the saturation points and NaN are settled
+// by selects; the N exponentials interleave (exp_fast_n).
+template <int N>
+DSPARK_HD void sigmoid_fast_n(const float (&x)[N], float (&y)[N], bool (&ok)[N]) {
+#pragma clang fp contract(off)
+  double t[N], e[N];
+  for (int i = 0; i < N; ++i) {
+    // clamped into the fast path's range (NaN becomes -104); the selects
+    // below settle every input that was clamped
+    t[i] = -(double)__builtin_fminf(__builtin_fmaxf(x[i], -104.0f), 17.5f);
+  }
+  exp_fast_n<N>(t, e);
+  for (int i = 0; i < N; ++i) {
+    const double yd = 1.0 / (1.0 + e[i]);
+    const float lo = (float)(yd * (1.0 - kBand));
+    const float hi = (float)(yd * (1.0 + kBand));
+    float r = lo;
+    bool k = lo == hi;
+    if (x[i] >= 17.5f) {  // 1 - sigmoid < e^-x < 2^-25: rounds to 1
+      r = 1.0f;
+      k = true;
+    }
+    if (x[i] <= -104.0f) {  // sigmoid < e^x < 2^-150: rounds to +0
+      r = 0.0f;
+      k = true;
+    }
+    if (x[i] != x[i]) {
+      r = x[i];
+      k = true;
+    }
+    y[i] = r;
+    ok[i] = k;
+  }
+}
+
 // Returns the correctly rounded sigmoid and, through *slow, whether the
 // double-double path ran.
 DSPARK_HD float sigmoid_cr(float x, bool* slow = nullptr) {
-#pragma clang fp contract(off)
-  if (slow) *slow = false;
-  if (x != x) return x;
-  if (x >= 17.5f) return 1.0f;    // 1 - sigmoid < e^-x < 2^-25: rounds to 1
-  if (x <= -104.0f) return 0.0f;  // sigmoid < e^x < 2^-150: rounds to +0
-  double e = exp_fast(-(double)x);
-  double y = 1.0 / (1.0 + e);
-  float lo = (float)(y * (1.0 - kBand));
-  float hi = (float)(y * (1.0 + kBand));
-  if (lo == hi) return lo;
-  if (slow) *slow = true;
-  return sigmoid_slow(x);
+  const float xs[1] = {x};
+  float r[1];
+  bool ok[1];
+  sigmoid_fast_n<1>(xs, r, ok);
+  if (slow) *slow = !ok[0];
+  return ok[0] ? r[0] : sigmoid_slow(x);
 }
 
 }  // namespace dspark

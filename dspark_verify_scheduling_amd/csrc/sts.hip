@@ -138,6 +138,8 @@ __device__ inline float div_by_rcp(double z, double rcp_t) {
   return __double2float_rn(__dmul_rn(z, rcp_t));
 }
 
+constexpr int kStsIlp = 2;  // candidates per step of the bin loop (4 was no faster)
+
 __global__ __launch_bounds__(kStsBinThreads) void sts_bin_kernel(StsArgs a, int k) {
   extern __shared__ long long hist[];  // [nT][2 * nbins + 1]: labels, survival sums, Brier
   __shared__ double s_rcp[DSPARK_STS_MAX_GRID];  // RN64(1 / T) per candidate
@@ -168,18 +170,50 @@ __global__ __launch_bounds__(kStsBinThreads) void sts_bin_kernel(StsArgs a, int 
     const float sp = advance_survival(a, k, n, t_prev, phase == 0);
     const double zk = (double)a.z[(size_t)n * a.gamma + k];
     const unsigned long long y = a.labels[(size_t)n * a.gamma + k] ? 1ull : 0ull;
-    for (int j = phase, t = t0; j < nT; j += kStsPhases) {
-      const float s = __fmul_rn(sp, sigmoid_cr(div_by_rcp(zk, s_rcp[t])));
-      const double sd = s == s ? (double)s : 0.0;  // a NaN survival counts as 0
-      int b = (int)floor(sd * nb);
-      b = b < nb ? b : nb - 1;
-      unsigned long long* h = reinterpret_cast<unsigned long long*>(hist + t * stride);
-      if (y) atomicAdd(h + b, 1ull);
-      atomicAdd(h + nb + b, (unsigned long long)fx40(sd));
-      const double d = sd - (double)y;  // d and d * d each rounded to float64
-      atomicAdd(h + 2 * nb, (unsigned long long)fx40(d * d));
-      t += kStsPhases;
-      if (t >= nT) t -= nT;  // once past the end only when nT > 4: then t < nT again
+    // kStsIlp candidates (j, j + 4, ...) per step: their sigmoids' fast
+    // paths interleave, and one branch on all the results takes any exact
+    // path. Candidate i of a step is used while j + 4 i < nT; past that it
+    // repeats the step's first candidate and is dropped.
+    for (int j = phase, t = t0; j < nT; j += kStsIlp * kStsPhases) {
+      int tc[kStsIlp];
+      float x[kStsIlp], c[kStsIlp];
+      bool ok[kStsIlp];
+#pragma unroll
+      for (int i = 0, ti = t; i < kStsIlp; ++i) {
+        // t + 4 i (mod nT), kept below nT by one subtraction per step: a
+        // candidate past the first is in use only when nT > 4
+        tc[i] = j + i * kStsPhases < nT ? ti : t;
+        x[i] = div_by_rcp(zk, s_rcp[tc[i]]);
+        ti += kStsPhases;
+        if (ti >= nT) ti -= nT;
+      }
+      sigmoid_fast_n<kStsIlp>(x, c, ok);
+      bool all_ok = true;
+#pragma unroll
+      for (int i = 0; i < kStsIlp; ++i) all_ok = all_ok && ok[i];
+      if (!all_ok) {
+        for (int i = 0; i < kStsIlp; ++i) {
+          if (!ok[i]) c[i] = sigmoid_slow(x[i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kStsIlp; ++i) {
+        if (j + i * kStsPhases >= nT) break;
+        const float s = __fmul_rn(sp, c[i]);
+        const double sd = s == s ? (double)s : 0.0;  // a NaN survival counts as 0
+        int b = (int)floor(sd * nb);
+        b = b < nb ? b : nb - 1;
+        unsigned long long* h = reinterpret_cast<unsigned long long*>(hist + tc[i] * stride);
+        if (y) atomicAdd(h + b, 1ull);
+        atomicAdd(h + nb + b, (unsigned long long)fx40(sd));
+        const double d = sd - (double)y;  // d and d * d each rounded to float64
+        atomicAdd(h + 2 * nb, (unsigned long long)fx40(d * d));
+      }
+#pragma unroll
+      for (int i = 0; i < kStsIlp; ++i) {
+        t += kStsPhases;
+        if (t >= nT) t -= nT;
+      }
     }
   }
   __syncthreads();
