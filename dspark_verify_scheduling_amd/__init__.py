@@ -55,7 +55,7 @@ def _ptr(t: Optional[torch.Tensor], name: str, dtype, numel: int, required: bool
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:  # (cheaper than t.device.type)
         raise ValueError(f"{name} must be a CUDA tensor, got {t.device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
