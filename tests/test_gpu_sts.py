@@ -81,6 +81,17 @@ def test_sts_fit_edge_cases():
     _fit_both(np.zeros((0, 3), np.float32), np.zeros((0, 3), np.uint8), GRID, 15, "no records")
 
 
+@pytest.mark.parametrize("n_t", [2, 3, 4, 5, 7, 9, 63])
+def test_sts_fit_grid_sizes(n_t):
+    """Candidate counts around the four threads per record and the two
+    candidates a thread takes per step: fewer candidates than threads, an odd
+    count per thread, and counts that leave a thread's last step half used."""
+    rng = np.random.default_rng(100 + n_t)
+    z, y = _records(rng, 2000, 3, np.array([0.9, 1.3, 1.7]))
+    grid = np.exp(np.linspace(np.log(0.5), np.log(2.5), n_t)).astype(np.float32)
+    _fit_both(z, y, grid, 12, f"n_t={n_t}")
+
+
 def test_sts_fit_reuses_a_dirty_workspace():
     """The workspace's contents on entry do not matter: a garbage-filled
     workspace, then a second, smaller fit on the same one (its histogram
