@@ -10,15 +10,18 @@
 // 目标分布" (accept, reject and the residual resample follow the speculative
 // algorithm; random numbers keep their meaning under compaction).
 //
-// Probabilities at fixed resolution. A row x at temperature T > 0 with
-// maximum m gets integer weights, every float step one IEEE float32 operation:
-//   c = K / T (K = 94548.4609375f, the float32 nearest to 2^16 log2 e),
-//   u = (m - x) * c, j = nearest integer to u (ties to even), W = 0 unless
-//   j < 2^21; else n = j >> 16, h = (j >> 8) & 255, r = j & 255,
-//   Y = B[h] - (((B[h] - B[h+1]) * r + 128) >> 8),  W = (Y + (2^n >> 1)) >> n
-// with B[i] the nearest integer to 2^31 * 2^(-i/256) (exp_tables.h), so
-// W ~ 2^31 exp((x - m) / T) and p = W / Z, Z = sum W < 2^49. Every decision
-// below is then an exact integer comparison, the same in any summation order:
+// Probabilities as integer weights. A row x at temperature T > 0 with
+// maximum m gets, per element:
+//   c = K / T (K = 94548.4609375f, the float32 nearest to 2^16 log2 e; the
+//     temperature is in the domain while c is finite),
+//   t = RN32((x - m) * (c * 2^-16) + 31), one fused multiply-add,
+//   W = 2^t rounded to the nearest integer (ties to even), 2^t from the
+//     hardware base-2 exponential (v_exp_f32, within 0.8 of a float32 unit
+//     in the last place on gfx950),
+// so W is 2^31 exp((x - m) / T) within a relative 4e-6 plus half a unit, the
+// maximum's own weight is 2^31, and p = W / Z with Z = sum W <= V 2^31.
+// Every decision below is then an exact integer comparison, the same in any
+// summation order:
 //   accept draft d  iff  (w >> 8) * Wq[d] * Zp < 2^24 * Wp[d] * Zq
 //   draw with word w from integer weights v (total S): the smallest i whose
 //   running sum exceeds floor((w >> 8) * S / 2^24)
@@ -54,7 +57,6 @@
 
 #include "argmax_unit.h"
 #include "common.h"
-#include "exp_tables.h"
 
 #pragma clang fp contract(off)
 
@@ -66,78 +68,22 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned __int128 u128;
 
 constexpr float kLog2e16 = 94548.4609375f;  // float32 nearest to 2^16 log2(e)
-constexpr unsigned int kJmax = 1u << 21;     // from here on the weight is 0
-constexpr float kUcut = kJmax - 0.5f;         // j = RNE(u) < kJmax iff u < kUcut
 constexpr int kRedWaves = kSampThreads / kWave;
 static_assert(kSampThreads == kAccThreads && kSampVecsPerThread == kAccVecsPerThread,
               "the max kernel runs the greedy accept's unit argmax");
 
+// c = K / T of the file header (a temperature is in the domain while it is
+// finite).
 __device__ inline float temp_coef(float T) { return __fdiv_rn(kLog2e16, T); }
 
-// The integer weight of x in a row with maximum m (x <= m); Bt holds the
-// pairs (B[h], B[h] - B[h+1]) for h < 256 and a zero pair at 256, in LDS.
-// Branch-free:
-// - adding 1.5 * 2^23 rounds u in [0, 2^22) to the nearest integer (ties to
-//   even) and leaves it in the low 22 mantissa bits: j = bits & 0x3FFFFF, so
-//   n = j >> 16 (five bits suffice below the cutoff), h = (j >> 8) & 255 and
-//   r = j & 255;
-// - j = RNE(u) < 2^21 exactly when u < 2^21 - 1/2 (a tie there rounds up, to
-//   even); past that (or for u = +inf) h is the zero pair, so y = 0 and the
-//   rounding shift gives 0 whatever n the bits hold.
-// W of the file header for x in a row with maximum m, c = K / T.
-__device__ inline unsigned int weight(float x, float m, float c, const uint2* Bt) {
-  const float u = __fmul_rn(__fsub_rn(m, x), c);  // >= 0, or +inf
-  // adding 1.5 * 2^23 rounds u in [0, 2^22) to the nearest integer j (ties to
-  // even) and leaves j in the low 22 mantissa bits
-  const unsigned int bits = __float_as_uint(__fadd_rn(u, 12582912.0f));
-  const unsigned int n = __builtin_amdgcn_ubfe(bits, 16, 5);  // j >> 16 while j < 2^21
-  // past the cut-off the zero pair at index 256 gives W = 0, whatever n is
-  const unsigned int h = u < kUcut ? __builtin_amdgcn_ubfe(bits, 8, 8) : 256u;
-  const unsigned int r = bits & 255u;
-  const uint2 bd = Bt[h];  // (B[h], B[h] - B[h + 1])
-  const unsigned int y = bd.x - (((unsigned int)__umul24(bd.y, r) + 128u) >> 8);
-  return (y + ((1u << n) >> 1)) >> n;
-}
-
-// weight(x[e], m[e], c, Bt) for e < N, the N table reads issued before the
-// first is used (one wait for all of them).
-template <int N>
-__device__ inline void weights(const float (&x)[N], const float (&m)[N], float c,
-                               const uint2* Bt, unsigned int (&w)[N]) {
-  unsigned int bits[N], h[N];
-  uint2 bd[N];
-#pragma unroll
-  for (int e = 0; e < N; ++e) {
-    const float u = __fmul_rn(__fsub_rn(m[e], x[e]), c);
-    bits[e] = __float_as_uint(__fadd_rn(u, 12582912.0f));
-    h[e] = u < kUcut ? __builtin_amdgcn_ubfe(bits[e], 8, 8) : 256u;
-  }
-#pragma unroll
-  for (int e = 0; e < N; ++e) bd[e] = Bt[h[e]];
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int e = 0; e < N; ++e) {
-    const unsigned int n = __builtin_amdgcn_ubfe(bits[e], 16, 5);
-    const unsigned int r = bits[e] & 255u;
-    const unsigned int y = bd[e].x - (((unsigned int)__umul24(bd[e].y, r) + 128u) >> 8);
-    w[e] = (y + ((1u << n) >> 1)) >> n;
-  }
-}
-
-// The weights of x[0] and x[1] in a row with maximum m, summed.
-__device__ inline unsigned long long weight_sum2(const float* x, float m, float c, const uint2* Bt) {
-  const float xs[2] = {x[0], x[1]}, ms[2] = {m, m};
-  unsigned int w[2];
-  weights<2>(xs, ms, c, Bt, w);
-  return (unsigned long long)w[0] + w[1];
-}
-
-// The weight table in LDS: kExp2Len - 1 interpolation pairs, then the zero
-// pair.
-__device__ inline void load_table(uint2* Bt) {
-  for (int i = threadIdx.x; i < kExp2Len; i += blockDim.x) {
-    Bt[i] = i < kExp2Len - 1 ? make_uint2(kExp2B[i], kExp2B[i] - kExp2B[i + 1]) : make_uint2(0u, 0u);
-  }
+// W of the file header for x in a row with maximum m (x <= m), c = K / T:
+// t = RN32((x - m) * (c * 2^-16) + 31) in one fused multiply-add (c * 2^-16
+// is exact), the hardware base-2 exponential of t (v_exp_f32), then the
+// nearest integer (ties to even). x = -inf gives t = -inf and W = 0; the row
+// maximum gives t = 31 and W = 2^31.
+__device__ inline unsigned int weight(float x, float m, float c) {
+  const float t = __fmaf_rn(__fsub_rn(x, m), __fmul_rn(c, 0x1p-16f), 31.0f);
+  return __float2uint_rz(__builtin_rintf(__builtin_amdgcn_exp2f(t)));
 }
 
 template <dspark_dtype DT>
@@ -234,7 +180,6 @@ __global__ __launch_bounds__(kSampThreads) void samp_max_kernel(SampArgs a) {
 
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kSampThreads) void samp_z_kernel(SampArgs a) {
-  __shared__ uint2 s_B[kExp2Len];
   __shared__ unsigned long long s_red[kRedWaves];
   constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -250,19 +195,17 @@ __global__ __launch_bounds__(kSampThreads) void samp_z_kernel(SampArgs a) {
     const int v = v0 + i * kSampThreads + tid;
     d[i] = v < v1 ? __builtin_nontemporal_load(rv + v) : (u32x4){0, 0, 0, 0};
   }
-  load_table(s_B);
   unsigned long long best = 0;
   const unsigned long long* kp = a.kpart + (size_t)slot * a.chunks;
 #pragma unroll 8
   for (int c = 0; c < a.chunks; ++c) best = kp[c] > best ? kp[c] : best;
-  __syncthreads();  // the table
   if (argmax::best_bad<DT>(best)) {
     if (tid == 0) a.zpart[(size_t)slot * a.chunks + ch] = 0;
     return;
   }
   const float m = argmax::best_value<DT>(best), c = temp_coef(s.T);
   unsigned long long z = 0;
-  if (ch == a.chunks - 1 && tid < a.tail) z = weight(elem<DT>(s.row, a.nvec * kEpv + tid), m, c, s_B);
+  if (ch == a.chunks - 1 && tid < a.tail) z = weight(elem<DT>(s.row, a.nvec * kEpv + tid), m, c);
 #pragma unroll
   for (int i = 0; i < kSampVecsPerThread; ++i) {
     const int v = v0 + i * kSampThreads + tid;
@@ -270,7 +213,7 @@ __global__ __launch_bounds__(kSampThreads) void samp_z_kernel(SampArgs a) {
       float x[kEpv];
       widen<DT>(d[i], x);
 #pragma unroll
-      for (int e = 0; e < kEpv; e += 2) z += weight_sum2(x + e, m, c, s_B);
+      for (int e = 0; e < kEpv; ++e) z += weight(x[e], m, c);
     }
   }
   z = wave_sum_u64(z);
@@ -299,7 +242,6 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
   constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
   constexpr int kWaves = kRsThreads / kWave;
   constexpr int kChunks = (SLOTS + 1) / 2;
-  __shared__ uint2 s_B[kExp2Len];
   __shared__ int s_list[kRsMaxList];
   __shared__ int s_scan[kWaves];
   __shared__ unsigned int s_key[kWaves];
@@ -310,7 +252,6 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
   const int tid = threadIdx.x, lane = lane_id(),
             wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int nvec = a.nvec;
-  load_table(s_B);
 
   if (blockIdx.x == 0 && tid == 0) {
     a.meta[0] = a.cu[a.B];
@@ -511,7 +452,7 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
         float x[kEpv];
         widen<DT>(d, x);
 #pragma unroll
-        for (int e = 0; e < kEpv; e += 2) zc += weight_sum2(x + e, m, c, s_B);
+        for (int e = 0; e < kEpv; ++e) zc += weight(x[e], m, c);
       }
       // both slots of a chunk are summed before either is reloaded (the
       // reload's address depends on an opaque copy of the thread index tied
@@ -526,7 +467,7 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
       }
       if ((i & 1) || i == SLOTS - 1) {
         const int ch = i >> 1;
-        if (ch == last_chunk && cur.samp && !bad && tid < a.tail) zc += weight(xt, m, c, s_B);
+        if (ch == last_chunk && cur.samp && !bad && tid < a.tail) zc += weight(xt, m, c);
         zc = wave_sum_u64(zc);
         if (lane == 0) s_z[wave][ch] = zc;
         zc = 0;
@@ -550,9 +491,6 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
 // One wave per request.
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kWave) void samp_decide_kernel(SampArgs a) {
-  __shared__ uint2 s_B[kExp2Len];
-  load_table(s_B);
-  __syncthreads();
   const int r = blockIdx.x, lane = threadIdx.x, G = a.gamma;
   const int total = a.cu[a.B];
   const int total_eff = min(max(total, 0), a.max_rows);
@@ -647,8 +585,8 @@ __global__ __launch_bounds__(kWave) void samp_decide_kernel(SampArgs a) {
       const float mq = argmax::best_value<DT>(kd);
       const float xp = elem<DT>(a.tgt + (size_t)(c0 + lane) * a.ld_t, dr);
       const float xq = elem<DT>(a.drf + ((size_t)r * G + lane) * a.ld_q, dr);
-      const unsigned long long wp = weight(xp, mp, cT, s_B);
-      const unsigned long long wq = weight(xq, mq, cT, s_B);
+      const unsigned long long wp = weight(xp, mp, cT);
+      const unsigned long long wq = weight(xq, mq, cT);
       const unsigned int u = a.ra[(size_t)r * G + lane] >> 8;
       // u * wq < 2^55 and wp * Zq < 2^80: both sides below 2^104
       const u128 lhs = (u128)((unsigned long long)u * wq) * zt;
@@ -722,9 +660,9 @@ __device__ inline u128 run_value(const DrawCtx& c, Pair s) {
 }
 
 template <dspark_dtype DT>
-__device__ inline void add_elem(const DrawCtx& c, int i, const uint2* Bt, Pair& s) {
-  const unsigned int wp = weight(elem<DT>(c.p, i), c.mp, c.cT, Bt);
-  const unsigned int wq = c.resid ? weight(elem<DT>(c.q, i), c.mq, c.cT, Bt) : 0u;
+__device__ inline void add_elem(const DrawCtx& c, int i, Pair& s) {
+  const unsigned int wp = weight(elem<DT>(c.p, i), c.mp, c.cT);
+  const unsigned int wq = c.resid ? weight(elem<DT>(c.q, i), c.mq, c.cT) : 0u;
   if (member(c, wp, wq)) {
     s.a += wp;
     s.b += wq;
@@ -753,7 +691,6 @@ __device__ inline DrawCtx draw_ctx(const SampArgs& a, const SampJob& job, int r)
 // Per (request, chunk) of a residual draw: the member sums of Wp and Wq.
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kSampThreads) void samp_rsum_kernel(SampArgs a) {
-  __shared__ uint2 s_B[kExp2Len];
   __shared__ Pair s_red[kRedWaves];
   constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -771,10 +708,8 @@ __global__ __launch_bounds__(kSampThreads) void samp_rsum_kernel(SampArgs a) {
     dp[i] = v < v1 ? __builtin_nontemporal_load(pv + v) : (u32x4){0, 0, 0, 0};
     dq[i] = v < v1 ? __builtin_nontemporal_load(qv + v) : (u32x4){0, 0, 0, 0};
   }
-  load_table(s_B);
-  __syncthreads();
   Pair s{0, 0};
-  if (ch == a.chunks - 1 && tid < a.tail) add_elem<DT>(c, a.nvec * kEpv + tid, s_B, s);
+  if (ch == a.chunks - 1 && tid < a.tail) add_elem<DT>(c, a.nvec * kEpv + tid, s);
 #pragma unroll
   for (int i = 0; i < kSampVecsPerThread; ++i) {
     if (v0 + i * kSampThreads + tid < v1) {
@@ -783,8 +718,8 @@ __global__ __launch_bounds__(kSampThreads) void samp_rsum_kernel(SampArgs a) {
       widen<DT>(dq[i], y);
 #pragma unroll
       for (int e = 0; e < kEpv; ++e) {
-        const unsigned int wp = weight(x[e], c.mp, c.cT, s_B);
-        const unsigned int wq = weight(y[e], c.mq, c.cT, s_B);
+        const unsigned int wp = weight(x[e], c.mp, c.cT);
+        const unsigned int wq = weight(y[e], c.mq, c.cT);
         if (member(c, wp, wq)) {
           s.a += wp;
           s.b += wq;
@@ -814,7 +749,6 @@ __global__ __launch_bounds__(kSampThreads) void samp_rsum_kernel(SampArgs a) {
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kSampDrawThreads) void samp_draw_kernel(SampArgs a) {
   constexpr int kWaves = kSampDrawThreads / kWave;
-  __shared__ uint2 s_B[kExp2Len];
   __shared__ unsigned long long s_scan[kWaves];
   __shared__ int s_ctl[2];  // residual flag; crossing chunk
   __shared__ u128 s_t;      // threshold left at the start of the crossing chunk
@@ -825,7 +759,6 @@ __global__ __launch_bounds__(kSampDrawThreads) void samp_draw_kernel(SampArgs a)
   const int r = blockIdx.x, C = a.chunks;
   const SampJob job = a.jobs[r];
   if (job.mode == 0) return;
-  load_table(s_B);
   DrawCtx c = draw_ctx(a, job, r);
   if (tid < C) {  // one load per thread, not a chain of them in one thread
     s_zs[tid] = a.zpart[((size_t)r * (a.gamma + 1) + job.col) * C + tid];
@@ -895,8 +828,8 @@ __global__ __launch_bounds__(kSampDrawThreads) void samp_draw_kernel(SampArgs a)
       widen<DT>(dq[k], y);
 #pragma unroll
       for (int e = 0; e < kEpv; ++e) {
-        const unsigned int wp = weight(x[e], c.mp, c.cT, s_B);
-        const unsigned int wq = c.resid ? weight(y[e], c.mq, c.cT, s_B) : 0u;
+        const unsigned int wp = weight(x[e], c.mp, c.cT);
+        const unsigned int wq = c.resid ? weight(y[e], c.mq, c.cT) : 0u;
         if (member(c, wp, wq)) {
           mine.a += wp;
           mine.b += wq;
@@ -905,7 +838,7 @@ __global__ __launch_bounds__(kSampDrawThreads) void samp_draw_kernel(SampArgs a)
     }
   }
   if (has_tail) {
-    for (int i = t0; i < a.V; ++i) add_elem<DT>(c, i, s_B, mine);
+    for (int i = t0; i < a.V; ++i) add_elem<DT>(c, i, mine);
   }
   unsigned long long tot_a, tot_b;
   const unsigned long long ea =
@@ -926,8 +859,8 @@ __global__ __launch_bounds__(kSampDrawThreads) void samp_draw_kernel(SampArgs a)
   // level 3: one element per lane (at most 2 vectors plus the tail: < 64)
   const int i = s_ctl[0] + tid;
   const bool in = i < s_ctl[1];
-  const unsigned int wp = in ? weight(elem<DT>(c.p, i), c.mp, c.cT, s_B) : 0u;
-  const unsigned int wq = in && c.resid ? weight(elem<DT>(c.q, i), c.mq, c.cT, s_B) : 0u;
+  const unsigned int wp = in ? weight(elem<DT>(c.p, i), c.mp, c.cT) : 0u;
+  const unsigned int wq = in && c.resid ? weight(elem<DT>(c.q, i), c.mq, c.cT) : 0u;
   const bool mem = in && member(c, wp, wq);
   const unsigned long long ia = wave_incl_scan_op(mem ? (unsigned long long)wp : 0ull, 0ull, OpAdd{});
   const unsigned long long ib = wave_incl_scan_op(mem ? (unsigned long long)wq : 0ull, 0ull, OpAdd{});

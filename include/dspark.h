@@ -465,14 +465,12 @@ size_t dspark_accept_workspace_size(int32_t max_rows, int32_t V, dspark_dtype dt
  *            chain with num_correct = k - 1 and the token of column k - 1
  *            drawn from the residual max(0, p - q) of that pair; if all pass,
  *            column l - 1 gets a token drawn from p of target row l - 1.
- * Probabilities at fixed resolution, so every decision is exact: for a row x
- * with maximum m, every float step one IEEE float32 operation, u = (m - x) *
- * (K / T) with K = 94548.4609375 (the float32 nearest to 2^16 log2 e); j = u
- * rounded to the nearest integer; W = 0 unless j < 2^21, else with
- * n = j >> 16, h = (j >> 8) & 255, r = j & 255:
- * Y = B[h] - (((B[h] - B[h+1]) * r + 128) >> 8) and W = (Y + (2^n >> 1)) >> n,
- * where B[i] is the nearest integer to 2^31 * 2^(-i/256). p = W / sum W,
- * within about 6e-6 relative of the softmax of x / T.
+ * Probabilities as integer weights, so every decision is an exact integer
+ * comparison: for a row x with maximum m, t = RN32((x - m) * c + 31) in one
+ * fused multiply-add with c = RN32(K / T) * 2^-16 and K = 94548.4609375 (the
+ * float32 nearest to 2^16 log2 e), and W = 2^t from the hardware base-2
+ * exponential, rounded to the nearest integer. p = W / sum W, each weight
+ * within 4e-6 relative plus half a unit of 2^31 exp((x - m) / T).
  *   accept draft d  iff  (rand_accept >> 8) * Wq[d] * Zp < 2^24 * Wp[d] * Zq
  *   draw from integer weights w (total S) with word v: the smallest index
  *   whose running sum exceeds floor((v >> 8) * S / 2^24); residual weights

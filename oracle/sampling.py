@@ -40,8 +40,8 @@ in float64 in the pages' terms. For request r with verify length l (rows
   takes the smallest index i with cumsum(w)_i > U * sum(w) (inverse CDF).
 * Temperature 0 marks a greedy request: the greedy rule of
   ``oracle.accept`` applies. A temperature that is negative, NaN or
-  infinite, or below the domain the fixed-resolution kernels accept (the
-  float32 quotient 94548.4609375 / T overflows, T below about 2.8e-34),
+  infinite, or below the domain the kernels accept (the float32 quotient
+  94548.4609375 / T overflows, T below about 2.8e-34),
   sets DATA_BAD_CONF; a NaN or +inf logit, or no finite element, in a row
   a sampling request reads sets DATA_BAD_LOGITS. Either way the request
   gets the malformed-layout outputs of ``oracle.accept`` (correct 0, bonus
@@ -70,10 +70,19 @@ from .plan import DATA_BAD_CONF
 DATA_BAD_LOGITS = 8
 WORD_SHIFT = 8  # a word w stands for U = (w >> 8) / 2^24
 U_SCALE = float(1 << 24)
-# the largest relative error of one unnormalised weight in the kernels' fixed
-# resolution (j = RNE(u) at 2^-16 of a base-2 unit, float32 rounding of u,
-# the 8-bit interpolation of 2^-x): 1.06e-5 + 9.3e-7, rounded up
-EPS_W = 1.2e-5
+# The largest relative error of one unnormalised weight of the kernels, before
+# its rounding to an integer. The kernels form t = RN32((x - m) c' + 31) with
+# c' = RN32(K / T) 2^-16 and K = RN32(2^16 log2 e) in one fused multiply-add,
+# and 2^t with the hardware exponential; the exact exponent is
+# t* = 31 + (x - m) log2(e) / T. For every weight of at least 1/2
+# (|t* - 31| <= 32):
+#   |t - t*| <= 32 (2^-24 [x - m] + 2^-24 [K / T] + 1.34e-8 [K]) + 2^-20
+#             = 5.20e-6 (in base-2 units), a relative 3.61e-6 on 2^t;
+#   the exponential itself: within one float32 unit, 2^-23 = 1.19e-7
+#   relative (0.79 units measured on gfx950);
+# together 3.73e-6, rounded up. Smaller weights are within their own size
+# of 0, inside the absolute term of ``prob_error_bound``.
+EPS_W = 4.0e-6
 
 
 def uniform(word) -> float:
@@ -197,7 +206,7 @@ def prob_error_bound(V: int, eps_w: float = EPS_W):
     """(eps_p, eta_p) with |p'(i) - p(i)| <= eps_p * p(i) + eta_p for every
     token of a V-token row, when p' = W / sum W is formed from weights
     W_i = W*_i (1 + e_i) + a_i, |e_i| <= eps_w and |a_i| <= 1/2 + 1e-5 (a
-    rounding to integers, the cut-off tokens included), around exact
+    rounding to the nearest integer, the weights below 1/2 included), around exact
     weights W*_i = 2^31 exp((x_i - m) / T) whose sum is at least 2^31 (the
     maximum's own weight).
 

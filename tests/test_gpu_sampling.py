@@ -1,19 +1,22 @@
-"""GPU parity of dspark_accept_sampling against the CPU oracles, through the C ABI.
+"""GPU parity of dspark_accept_sampling against the CPU oracle, through the C ABI.
 
-Two bars, on every case:
+The bars:
 
 * the definition (``oracle.sampling``, float64 softmaxes, accept iff
-  U < p(d) / q(d), the normalised residual max(0, p - q)): every GPU decision
-  equals the float64 one unless the random number lies inside the error band
-  of the kernels' fixed resolution, where either decision is valid and the
-  check follows the GPU's; greedy, malformed and out-of-domain requests
-  match exactly. Band cases are counted and reported;
-* the white-box form (``oracle.sampling_fixed``, the kernels' integer
-  weights): bit-exact. num_correct, bonus, commit, new_seq, out_tokens and
-  the status word match exactly.
+  U < p(d) / q(d), the normalised residual max(0, p - q)), on every case:
+  every GPU decision equals the float64 one unless the random number lies
+  inside the error band the kernels' weights allow (``prob_error_bound``),
+  where either decision is valid and the check follows the GPU's; greedy,
+  malformed and out-of-domain requests match exactly, and so does the status
+  word. Band cases are counted and reported;
+* the kernels' weights themselves against 2^31 exp((x - m) / T) in float64:
+  single weights isolated in crafted rows, and every slot's weight sum, each
+  within the per-weight bound (EPS_W relative plus half a unit) the band is
+  built on.
 """
 
 import json
+import math
 import os
 from pathlib import Path
 
@@ -24,7 +27,6 @@ import torch
 import dspark_verify_scheduling_amd as dv
 import oracle
 from oracle import sampling as F64
-from oracle import sampling_fixed as S
 from oracle.accept import as_f32_rows
 from workloads import gen
 from _gpu import DEV, logits_up, say, up
@@ -67,15 +69,9 @@ def run_gpu(B, gamma, V, dt, tgt, drf, cu, drafts, temps, ra, rs, prefix=None, m
             "out_tokens": out.out_tokens.cpu().numpy(), "meta": out.accept_meta.cpu().numpy()}
 
 
-def check(got, ref, total, reqs=None):
-    sel = slice(None) if reqs is None else reqs
-    for k in ("num_correct", "bonus", "commit", "new_seq", "out_tokens"):
-        a, b = got[k][sel], ref[k]
-        assert np.array_equal(a, b), (k, np.argwhere(a != b)[:5].tolist(),
-                                      a[np.any(a != b, axis=-1) if a.ndim > 1 else a != b][:3],
-                                      b[np.any(a != b, axis=-1) if b.ndim > 1 else a != b][:3])
-    if reqs is None:
-        assert got["meta"][0] == total and got["meta"][1] == ref["status"], (got["meta"], ref["status"])
+def check_status(got, ref, total):
+    """accept_meta = [total, status], the status as the float64 oracle's."""
+    assert got["meta"][0] == total and got["meta"][1] == ref["status"], (got["meta"], ref["status"])
 
 
 def rand_case(seed, B, gamma, V, dt, greedy_frac=0.2, q_noise=0.5):
@@ -124,10 +120,10 @@ def both(c, tag, max_rows=None):
     got = run_gpu(c["B"], c["gamma"], c["V"], c["dt"], c["tgt"], c["drf"], c["cu"], c["drafts"],
                   c["temps"], c["ra"], c["rs"], c["prefix"], max_rows=max_rows, tag=tag)
     dtype = "bf16" if c["dt"] == dv.BF16 else "f32"
-    ref = S.accept_sampling(c["B"], c["gamma"], c["tgt"], c["drf"], dtype, c["cu"], c["drafts"],
-                            c["temps"], c["ra"], c["rs"], prefix_lens=c["prefix"],
-                            max_rows=max_rows)
-    check(got, ref, int(c["cu"][-1]))
+    ref = F64.accept_sampling(c["B"], c["gamma"], c["tgt"], c["drf"], dtype, c["cu"],
+                              c["drafts"], c["temps"], c["ra"], c["rs"], prefix_lens=c["prefix"],
+                              max_rows=max_rows)
+    check_status(got, ref, int(c["cu"][-1]))
     check_f64(got, c["B"], c["gamma"], c["tgt"], c["drf"], dtype, c["cu"], c["drafts"],
               c["temps"], c["ra"], c["rs"], c["prefix"], max_rows=max_rows, tag=tag)
     return got, ref
@@ -180,7 +176,7 @@ def test_sampling_edge_cases():
     c["drafts"][6, 0] = c["V"] + 3        # outside the vocabulary
     c["drafts"][7, 1] = -1
     got, ref = both(c, "bad data")
-    assert ref["status"] == S.DATA_BAD_LOGITS | oracle.DATA_BAD_CONF
+    assert ref["status"] == F64.DATA_BAD_LOGITS | oracle.DATA_BAD_CONF
     # identical p and q rows: every draft in the support passes
     c = rand_case(12, 6, 5, 640, dv.BF16, greedy_frac=0.0)
     for r in range(c["B"]):
@@ -258,7 +254,7 @@ def test_sampling_rowstat_special_rows():
     c["tgt"][cu[6]] = 0xFF80                                     # -inf row
     c["tgt"][cu[7], 100] = 0xFFC1                                # negative NaN
     got, ref = both(c, "rowstat special rows")
-    assert ref["status"] & S.DATA_BAD_LOGITS
+    assert ref["status"] & F64.DATA_BAD_LOGITS
 
 
 def test_sampling_rowstat_greedy_special_rows():
@@ -287,7 +283,7 @@ def test_sampling_rowstat_greedy_special_rows():
 def test_sampling_many_slots_two_read_path():
     """More than 64 slots per CU (B = 1000, gamma = 8: 17,000 slots) with rows
     the row-statistics kernel could hold (V = 8192 bf16): the batch keeps the
-    two-read kernels. 40 requests are checked against the oracle."""
+    two-read kernels. Every request is checked against the float64 definition."""
     B, G, V = 1000, 8, 8192
     rng = np.random.default_rng(41)
     lens = rng.integers(1, G + 2, B)
@@ -303,13 +299,6 @@ def test_sampling_many_slots_two_read_path():
     prefix = rng.integers(5, 500, B).astype(np.int32)
     got = run_gpu(B, G, V, dv.BF16, tgt, drf, cu, drafts, temps, ra, rs, prefix, tag="17000 slots")
     assert got["meta"].tolist() == [total, 0]
-    reqs = np.sort(rng.choice(B, 40, replace=False))
-    sub_cu = np.concatenate([[0], np.cumsum(lens[reqs])]).astype(np.int32)
-    sub_tgt = np.concatenate([tgt[cu[r]:cu[r + 1]] for r in reqs])
-    sub_drf = np.concatenate([drf[r * G:(r + 1) * G] for r in reqs])
-    ref = S.accept_sampling(len(reqs), G, sub_tgt, sub_drf, "bf16", sub_cu, drafts[reqs],
-                            temps[reqs], ra[reqs], rs[reqs], prefix_lens=prefix[reqs])
-    check(got, ref, None, reqs=reqs)
     check_f64(got, B, G, tgt, drf, "bf16", cu, drafts, temps, ra, rs, prefix,
               tag="17000 slots, all 1000 requests")
 
@@ -327,16 +316,14 @@ def _record(name, rec):
     SUMMARY.write_text(json.dumps(data, indent=1, sort_keys=True))
 
 
-@pytest.mark.parametrize("cfg,greedy_frac,n_white", [(3, 0.0, 48), (2, 0.1, 16), (1, 0.1, 8),
-                                                     (4, 0.1, 16)])
-def test_sampling_full_size_every_request(cfg, greedy_frac, n_white):
+@pytest.mark.parametrize("cfg,greedy_frac", [(3, 0.0), (2, 0.1), (1, 0.1), (4, 0.1)])
+def test_sampling_full_size_every_request(cfg, greedy_frac):
     """Full-size workloads (cfg1: B = 8, V = 32000 f32; cfg2: B = 64, V =
     151936 bf16; cfg3: B = 256, gamma = 8, V = 129280 bf16, the benchmark's
     own sampling inputs; cfg4: gamma = 16 with its own draft logits and a
     spread of verify lengths). cfg1-3 run on their planned layouts in the
     launch configuration the benchmark times (max_rows = the tier). Every
-    request is checked against the float64 definition; n_white of them are
-    compared bit for bit with the fixed-resolution form."""
+    request is checked against the float64 definition."""
     w = gen.make(cfg)
     if cfg == 4:
         lens = np.random.default_rng(4).integers(1, w.gamma + 2, w.B)
@@ -360,17 +347,6 @@ def test_sampling_full_size_every_request(cfg, greedy_frac, n_white):
                    ex.rand_accept, ex.rand_sample, w.prefix_lens, max_rows=max_rows,
                    tag=f"cfg{cfg} all {w.B} requests")
     assert st["requests"] == w.B and st["sampling_requests"] == int(np.sum(ex.temps != 0))
-    # bit for bit against the fixed-resolution form on a sample of requests
-    rng = np.random.default_rng(cfg)
-    reqs = np.sort(rng.choice(w.B, min(n_white, w.B), replace=False))
-    sub_cu = np.concatenate([[0], np.cumsum(lens[reqs])]).astype(np.int32)
-    sub_tgt = np.concatenate([tgt[cu[r]:cu[r + 1]] for r in reqs])
-    sub_drf = np.concatenate([drf[r * w.gamma:(r + 1) * w.gamma] for r in reqs])
-    ref = S.accept_sampling(len(reqs), w.gamma, sub_tgt, sub_drf, w.dtype, sub_cu,
-                            w.drafts[reqs], ex.temps[reqs], ex.rand_accept[reqs],
-                            ex.rand_sample[reqs], prefix_lens=w.prefix_lens[reqs])
-    check(got, ref, None, reqs=reqs)
-    assert ref["status"] == 0
     say(f"cfg{cfg}: mean correct {got['num_correct'].mean():.3f} over {w.B} requests, "
         f"{total} rows")
     if cfg == 3:  # a second call on the same inputs is identical (no state in the workspace)
@@ -379,8 +355,7 @@ def test_sampling_full_size_every_request(cfg, greedy_frac, n_white):
         for k in ("num_correct", "bonus", "out_tokens"):
             assert np.array_equal(got[k], again[k])
     _record(f"cfg{cfg}", {"B": w.B, "gamma": w.gamma, "V": w.V, "dtype": w.dtype,
-                          "rows": total, "max_rows": max_rows, "greedy_frac": greedy_frac,
-                          "white_box_requests": len(reqs), **st})
+                          "rows": total, "max_rows": max_rows, "greedy_frac": greedy_frac, **st})
 
 
 def test_sampling_graph_replay_matches_eager():
@@ -442,49 +417,121 @@ def test_sampling_graph_replay_matches_eager():
     assert any(not torch.equal(expect[0][1], e[1]) for e in expect[1:])
 
 
-# White-box pin of the weights themselves: the per-chunk weight sums the
-# kernels leave in the workspace, added up per slot, must equal the oracle's
-# Z = sum W exactly. (Decisions agree even when a few weights are off by one
-# step, so the outputs alone would not show it.) The layout read here is the
-# library's internal one: per (slot, chunk) 64-bit maxima, then 64-bit weight
-# sums, slots = B (gamma + 1) target slots then B gamma draft slots, chunks of
-# 2048 16-byte vectors, each part padded to 256 bytes.
+# The weights themselves. The kernels leave per-chunk weight sums in the
+# workspace; the layout read here is the library's internal one: per (slot,
+# chunk) 64-bit maxima, then 64-bit weight sums, slots = B (gamma + 1) target
+# slots then B gamma draft slots, chunks of 2048 16-byte vectors, each part
+# padded to 256 bytes.
+def _slot_sums(out, B, gamma, V, dt):
+    esize = 2 if dt == dv.BF16 else 4
+    chunks = max(1, -(-(V * esize // 16) // 2048))
+    slots = B * (2 * gamma + 1)
+    part_bytes = -(-(slots * chunks * 8) // 256) * 256
+    ws = out.workspace.cpu().numpy()
+    z = ws[part_bytes:part_bytes + slots * chunks * 8].view(np.uint64).reshape(slots, chunks)
+    return [int(v) for v in z.astype(object).sum(axis=1)]
+
+
+def _exact_weights(x, T):
+    """2^31 exp((x - m) / T) in float64, m the row maximum (float32 values)."""
+    x = np.asarray(x, np.float32).astype(np.float64)
+    return 2.0**31 * np.exp((x - np.max(x)) / np.float64(np.float32(T)))
+
+
+@pytest.mark.parametrize("V,dt", [(1024, dv.F32), (4096, dv.F32)])
+def test_sampling_single_weights_within_bound(V, dt):
+    """Rows with the maximum at 0, one other finite element x and -inf
+    elsewhere: a slot's weight sum is W(0) + W(x), so each call isolates one
+    weight per slot. Over x from the maximum down past the last nonzero
+    weight and temperatures from 0.05 to 4: W(max) = 2^31 exactly, and every
+    W(x) within EPS_W relative plus half a unit of 2^31 exp(x / T). (V = 1024
+    f32 takes the two-read kernels, V = 4096 the row-statistics kernel.)"""
+    B, G = 32, 4
+    rng = np.random.default_rng(V)
+    lens = np.full(B, G + 1)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    slots = B * (2 * G + 1)
+    worst, n = 0.0, 0
+    for it in range(6):
+        temps = np.exp(rng.uniform(np.log(0.05), np.log(4.0), B)).astype(np.float32)
+        # t* = 31 + x log2(e) / T spread over [-2, 31]
+        frac = rng.uniform(-2.0, 31.0, slots)
+        tgt = np.full((B * (G + 1), V), -np.inf, np.float32)
+        drf = np.full((B * G, V), -np.inf, np.float32)
+        xs = np.empty(slots, np.float32)
+        for r in range(B):
+            T = float(temps[r])
+            for j in range(G + 1):
+                sl = r * (G + 1) + j
+                xs[sl] = np.float32((frac[sl] - 31.0) * T / math.log2(math.e))
+                tgt[cu[r] + j, 0], tgt[cu[r] + j, 1 + sl % (V - 1)] = 0.0, min(xs[sl], 0.0)
+            for k in range(G):
+                sl = B * (G + 1) + r * G + k
+                xs[sl] = np.float32((frac[sl] - 31.0) * T / math.log2(math.e))
+                drf[r * G + k, 0], drf[r * G + k, 1 + sl % (V - 1)] = 0.0, min(xs[sl], 0.0)
+        if it == 0:  # rows holding only the maximum
+            tgt[cu[0], 1:] = -np.inf
+            xs[0] = -np.inf
+        drafts = np.zeros((B, G), np.int32)
+        out = dv.alloc_sampling_outputs(B, G, V, dt, DEV)
+        say(f"single weights V={V} call {it}")
+        dv.dspark_accept_sampling(
+            B, G, V, dt, logits_up(tgt, dt), V, tgt.shape[0], up(cu), logits_up(drf, dt), V,
+            up(drafts), up(temps), up(np.zeros((B, G), np.int32)),
+            up(np.zeros((B, G + 1), np.int32)), up(np.zeros(B, np.int32)), out)
+        torch.cuda.synchronize()
+        z = _slot_sums(out, B, G, V, dt)
+        for sl in range(slots):
+            r = sl // (G + 1) if sl < B * (G + 1) else (sl - B * (G + 1)) // G
+            T = np.float64(temps[r])
+            w = z[sl] - 2**31
+            assert w >= 0, (sl, z[sl])
+            x = np.float64(min(xs[sl], np.float32(0.0)))
+            ws = 2.0**31 * math.exp(x / T) if np.isfinite(x) else 0.0
+            bound = F64.EPS_W * ws + 0.5 + 1e-5
+            assert abs(w - ws) <= bound, (sl, float(x), float(T), w, ws)
+            if ws > 1e3:
+                worst = max(worst, abs(w - ws) / ws)
+            n += 1
+    say(f"{n} single weights within the bound; largest relative error {worst:.3g} "
+        f"(EPS_W = {F64.EPS_W:g})")
+
+
 @pytest.mark.parametrize("seed,B,gamma,V,dt,t_lo,t_hi", [
     (21, 6, 4, 129280, dv.BF16, 0.3, 2.0),
-    (22, 5, 3, 32000, dv.F32, 0.05, 1.5),   # small T: u near the 2^21 cutoff
+    (22, 5, 3, 32000, dv.F32, 0.05, 1.5),   # small T: most weights near 0
     (23, 4, 5, 4099, dv.BF16, 0.5, 4.0),
 ])
-def test_sampling_weight_sums_exact(seed, B, gamma, V, dt, t_lo, t_hi):
+def test_sampling_weight_sums_within_bound(seed, B, gamma, V, dt, t_lo, t_hi):
+    """Every slot's weight sum Z against the float64 sum of 2^31 exp((x - m) /
+    T): within the sum of the per-weight bounds."""
     c = rand_case(seed, B, gamma, V, dt, greedy_frac=0.0)
     rng = np.random.default_rng(seed + 100)
     c["temps"] = rng.uniform(t_lo, t_hi, B).astype(np.float32)
     esize = 2 if dt == dv.BF16 else 4
-    nvec = V * esize // 16
-    chunks = max(1, -(-nvec // 2048))
-    slots = B * (2 * gamma + 1)
-    part_bytes = -(-(slots * chunks * 8) // 256) * 256
     ld = V if (V * esize) % 16 == 0 else (V + 16 // esize - 1) // (16 // esize) * (16 // esize)
     pad = (lambda x: np.pad(x, ((0, 0), (0, ld - V)))) if ld != V else (lambda x: x)
     out = dv.alloc_sampling_outputs(B, gamma, V, dt, DEV)
-    say(f"weight sums seed={seed} V={V} dt={dt} chunks={chunks}")
+    say(f"weight sums seed={seed} V={V} dt={dt}")
     dv.dspark_accept_sampling(
         B, gamma, V, dt, logits_up(pad(c["tgt"]), dt), ld, c["tgt"].shape[0],
         up(np.asarray(c["cu"], np.int32)), logits_up(pad(c["drf"]), dt), ld,
         up(c["drafts"].reshape(B, gamma)), up(c["temps"]), up(_bits(c["ra"]).reshape(B, gamma)),
         up(_bits(c["rs"]).reshape(B, gamma + 1)), up(c["prefix"]), out)
     torch.cuda.synchronize()
-    ws = out.workspace.cpu().numpy()
-    z = ws[part_bytes:part_bytes + slots * chunks * 8].view(np.uint64).reshape(slots, chunks)
+    z = _slot_sums(out, B, gamma, V, dt)
     tgt = as_f32_rows(c["tgt"], "bf16" if dt == dv.BF16 else "f32")
     drf = as_f32_rows(c["drf"], "bf16" if dt == dv.BF16 else "f32")
-    cu, checked = c["cu"], 0
+    cu, checked, worst = c["cu"], 0, 0.0
     for r in range(B):
         l, T = int(cu[r + 1] - cu[r]), float(c["temps"][r])
         rows = [(r * (gamma + 1) + j, tgt[cu[r] + j]) for j in range(l)]
         rows += [(B * (gamma + 1) + r * gamma + k, drf[r * gamma + k]) for k in range(l - 1)]
         for slot, x in rows:
-            want = int(S.weights(x, T).sum())
-            got = int(z[slot].astype(object).sum())
-            assert got == want, (r, slot, T, got, want)
+            ws = _exact_weights(x, T)
+            want = float(np.sum(ws))
+            bound = float(np.sum(F64.EPS_W * ws + 0.5 + 1e-5)) + 1e-9 * want
+            assert abs(z[slot] - want) <= bound, (r, slot, T, z[slot], want, bound)
+            worst = max(worst, abs(z[slot] - want) / want)
             checked += 1
-    say(f"{checked} slot weight sums exact")
+    say(f"{checked} slot weight sums within the bound; largest relative error {worst:.3g}")

@@ -18,7 +18,10 @@ Fixed by:
   full-width (static) accept under the same random words wherever the
   static chain stops before l - 1 ([CSSD], compact vs static);
 * the validator: the oracle's own outputs pass it with no band case, and
-  outputs with a planted wrong decision or draw fail it.
+  outputs with a planted wrong decision or draw fail it;
+* the error bounds the validator's band is built from: EPS_W against the
+  kernels' stated weight arithmetic taken exactly in rationals, and
+  prob_error_bound against weights pushed to the edges of their error.
 """
 
 import math
@@ -408,3 +411,101 @@ def test_each_draft_is_tested_with_its_own_word():
         res = S.accept_sampling(1, 2, tgt, drf, "f32", cu, drafts, np.ones(1, np.float32),
                                 np.array([ra], np.uint32), np.zeros((1, 3), np.uint32))
         assert res["num_correct"][0] == expect
+
+
+# ---- the per-weight bound EPS_W against the kernels' stated weight arithmetic
+
+
+def _round_f32(fr):
+    """The float32 nearest to the rational fr (ties to even), as a Fraction;
+    normal range only."""
+    from fractions import Fraction
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    # 24 significant bits: a = m * 2^(e - 23), m in [2^23, 2^24)
+    scale = Fraction(2) ** (23 - e)
+    m = a * scale
+    q, rem = divmod(m.numerator, m.denominator)
+    half = Fraction(rem, m.denominator)
+    if half > Fraction(1, 2) or (half == Fraction(1, 2) and q % 2 == 1):
+        q += 1
+    return sign * Fraction(q) / scale
+
+
+def test_eps_w_covers_the_kernels_weight_arithmetic():
+    """W = nearest integer to 2^t, t = RN32((x - m) c' + 31) in one fused
+    multiply-add, c' = RN32(K / T) 2^-16, K = RN32(2^16 log2 e), with 2^t off
+    by up to one float32 unit either way: |W - W*| <= EPS_W W* + 1/2 + 1e-5
+    for W* = 2^31 exp((x - m) / T), over random rows, temperatures and float32
+    or bfloat16 values (the fused multiply-add and every rounding taken
+    exactly, in rationals)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(77)
+    K = Fraction(float(np.float32(94548.4609375)))
+    worst = 0.0
+    for _ in range(3000):
+        T = np.float32(np.exp(rng.uniform(np.log(0.02), np.log(8.0))))
+        m = np.float32(rng.normal(0, 20))
+        # t* spread over [-2, 31]
+        ts = rng.uniform(-2.0, 31.0)
+        x = np.float32(m + (ts - 31.0) * float(T) / math.log2(math.e))
+        if rng.random() < 0.5:  # bfloat16 values
+            x = np.float32(np.frombuffer((np.float32(x).view(np.uint32) & 0xFFFF0000).tobytes(),
+                                         np.float32)[0])
+            m = np.float32(np.frombuffer((np.float32(m).view(np.uint32) & 0xFFFF0000).tobytes(),
+                                         np.float32)[0])
+        if x > m:
+            x, m = m, x
+        c = _round_f32(K / Fraction(float(T))) / 2**16
+        d = _round_f32(Fraction(float(x)) - Fraction(float(m)))
+        t = float(_round_f32(d * c + 31))
+        y = 2.0 ** t
+        ws = 2.0**31 * math.exp((float(x) - float(m)) / float(T))
+        ulp = 2.0 ** (math.frexp(y)[1] - 24)
+        for yh in (y - ulp, y, y + ulp):
+            W = float(np.rint(yh))
+            assert abs(W - ws) <= S.EPS_W * ws + 0.5 + 1e-5, (float(x), float(m), float(T), W, ws)
+            if ws > 1e6:  # the relative part, net of the half unit
+                worst = max(worst, (abs(W - ws) - 0.5) / ws)
+    # random rows reach a fair part of the worst case (about a quarter)
+    assert worst > 0.1 * S.EPS_W, worst
+
+
+@pytest.mark.parametrize("V", [7, 1000, 32000, 151936])
+def test_prob_error_bound_covers_weights_at_the_edges_of_their_error(V):
+    """prob_error_bound against weights W = W* (1 + e) + a pushed to the edges
+    of the per-weight model (|e| = EPS_W, |a| = 1/2, W >= 0): the token under
+    test pushed up or down and every other weight the other way. Every token's
+    probability stays within eps_p p + eta_p of the float64 softmax, on
+    workload-like rows and on rows built to make the bound tight (one maximum
+    and V - 1 weights of 1 to 3 units, so the half units add up in the
+    normaliser); there the worst case reaches over 90% of the bound, so a term
+    dropped from it fails."""
+    rng = np.random.default_rng(V)
+    eps_p, eta_p = S.prob_error_bound(V)
+    a = 0.5
+    rows = [rng.normal(0.0, 3.0, V), rng.standard_cauchy(V).clip(-60, 60)]
+    tight = np.log(rng.uniform(1.0, 3.0, V) / 2.0**31)
+    tight[rng.integers(V)] = 0.0
+    rows.append(tight)
+    worst = 0.0
+    for k, x in enumerate(rows):
+        ws = 2.0**31 * np.exp(x - x.max())
+        p = ws / ws.sum()
+        for i in {int(np.argmax(x)), int(rng.integers(V)), int(np.argmin(x))}:
+            for sgn in (1.0, -1.0):
+                e = np.full(V, -sgn * S.EPS_W)
+                off = np.full(V, -sgn * a)
+                e[i], off[i] = sgn * S.EPS_W, sgn * a
+                W = np.maximum(ws * (1.0 + e) + off, 0.0)
+                pp = W / W.sum()
+                ratio = np.abs(pp - p) / (eps_p * p + eta_p)
+                assert ratio.max() <= 1.0, (k, i, sgn, float(ratio.max()))
+                if k == 2:
+                    worst = max(worst, float(ratio[i]))
+    assert worst > 0.9, worst
