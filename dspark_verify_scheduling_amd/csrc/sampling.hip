@@ -81,9 +81,15 @@ __device__ inline float temp_coef(float T) { return __fdiv_rn(kLog2e16, T); }
 // is exact), the hardware base-2 exponential of t (v_exp_f32), then the
 // nearest integer (ties to even). x = -inf gives t = -inf and W = 0; the row
 // maximum gives t = 31 and W = 2^31.
-__device__ inline unsigned int weight(float x, float m, float c) {
+__device__ inline float weight_f(float x, float m, float c) {
   const float t = __fmaf_rn(__fsub_rn(x, m), __fmul_rn(c, 0x1p-16f), 31.0f);
-  return __float2uint_rz(__builtin_rintf(__builtin_amdgcn_exp2f(t)));
+  return __builtin_rintf(__builtin_amdgcn_exp2f(t));
+}
+
+// The same weight as an integer (the float above is integer-valued and at
+// most 2^31, so the conversion is exact).
+__device__ inline unsigned int weight(float x, float m, float c) {
+  return __float2uint_rz(weight_f(x, m, c));
 }
 
 template <dspark_dtype DT>
@@ -247,7 +253,8 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
   __shared__ unsigned int s_key[kWaves];
   __shared__ unsigned int s_idx[kWaves];  // apart from s_key: waves may still read the key
   __shared__ int s_flag[kWaves];
-  __shared__ unsigned long long s_z[kWaves][kChunks];
+  // per-thread chunk sums of the weight pass: [chunk][thread]
+  __shared__ unsigned long long s_zl[kChunks][kRsThreads];
   // the wave index as a scalar: the per-wave LDS addresses need no registers
   const int tid = threadIdx.x, lane = lane_id(),
             wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -315,10 +322,10 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
     const float xt = tid < a.tail ? xr : -INFINITY;
 
     // ---- pass 1: the maximum key, slots in arrival order. The first use of
-    // a slot stores it back with -inf in the lanes past the row end (no
-    // maximum, zero weight); later uses read r[i] as it is.
+    // the row's last, partial slot stores it back with -inf in the lanes past
+    // the row end (no maximum, zero weight); later uses read r[i] as it is.
     auto slot_vec = [&](int i) -> u32x4 {
-      r[i] = i * kRsThreads + tid < nvk ? r[i] : fill;
+      if ((i + 1) * kRsThreads > nvk) r[i] = i * kRsThreads + tid < nvk ? r[i] : fill;
       return r[i];
     };
     unsigned int key;
@@ -468,20 +475,25 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
       if ((i & 1) || i == SLOTS - 1) {
         const int ch = i >> 1;
         if (ch == last_chunk && cur.samp && !bad && tid < a.tail) zc += weight(xt, m, c);
-        zc = wave_sum_u64(zc);
-        if (lane == 0) s_z[wave][ch] = zc;
+        s_zl[ch][tid] = zc;
         zc = 0;
       }
     }
+    // wave w < chunks adds up chunk w's 1024 thread sums and stores the
+    // chunk's partials; the next row writes s_zl only after its pass-1
+    // barrier, which every wave reaches after these reads
     __syncthreads();
-    if (tid < a.chunks) {
+    if (wave < a.chunks) {
       unsigned long long t = 0;
-      if (tid < kChunks) {
+      if (wave < kChunks) {
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) t += s_z[w][tid];
+        for (int j = 0; j < kWaves; ++j) t += s_zl[wave][j * kWave + lane];
+        t = wave_sum_u64(t);
       }
-      a.zpart[(size_t)slot * a.chunks + tid] = bad || !cur.samp ? 0ull : t;
-      a.kpart[(size_t)slot * a.chunks + tid] = tid == 0 ? best : 0ull;
+      if (lane == 0) {
+        a.zpart[(size_t)slot * a.chunks + wave] = bad || !cur.samp ? 0ull : t;
+        a.kpart[(size_t)slot * a.chunks + wave] = wave == 0 ? best : 0ull;
+      }
     }
     cur = nxt;
     xr = xr_next;
@@ -710,6 +722,10 @@ __global__ __launch_bounds__(kSampThreads) void samp_rsum_kernel(SampArgs a) {
   }
   Pair s{0, 0};
   if (ch == a.chunks - 1 && tid < a.tail) add_elem<DT>(c, a.nvec * kEpv + tid, s);
+  // member() without branches: the float32 screen decides every element it
+  // can, and the few near equality (flagged) are decided exactly afterwards,
+  // in a second walk that only a wave holding one takes
+  bool near = false;
 #pragma unroll
   for (int i = 0; i < kSampVecsPerThread; ++i) {
     if (v0 + i * kSampThreads + tid < v1) {
@@ -718,11 +734,31 @@ __global__ __launch_bounds__(kSampThreads) void samp_rsum_kernel(SampArgs a) {
       widen<DT>(dq[i], y);
 #pragma unroll
       for (int e = 0; e < kEpv; ++e) {
-        const unsigned int wp = weight(x[e], c.mp, c.cT);
-        const unsigned int wq = weight(y[e], c.mq, c.cT);
-        if (member(c, wp, wq)) {
-          s.a += wp;
-          s.b += wq;
+        const float fp = weight_f(x[e], c.mp, c.cT), fq = weight_f(y[e], c.mq, c.cT);
+        const float xs = fp * c.zqf, ys = fq * c.zpf;
+        const bool hi = xs > ys * (1.0f + 0x1p-20f), lo = xs < ys * (1.0f - 0x1p-20f);
+        s.a += hi ? __float2uint_rz(fp) : 0u;
+        s.b += hi ? __float2uint_rz(fq) : 0u;
+        near |= !hi && !lo && fp != 0.0f;
+      }
+    }
+  }
+  if (__ballot(near)) {
+#pragma unroll
+    for (int i = 0; i < kSampVecsPerThread; ++i) {
+      if (near && v0 + i * kSampThreads + tid < v1) {
+        float x[kEpv], y[kEpv];
+        widen<DT>(dp[i], x);
+        widen<DT>(dq[i], y);
+        for (int e = 0; e < kEpv; ++e) {
+          const float fp = weight_f(x[e], c.mp, c.cT), fq = weight_f(y[e], c.mq, c.cT);
+          const float xs = fp * c.zqf, ys = fq * c.zpf;
+          const bool hi = xs > ys * (1.0f + 0x1p-20f), lo = xs < ys * (1.0f - 0x1p-20f);
+          const unsigned int wp = __float2uint_rz(fp), wq = __float2uint_rz(fq);
+          if (!hi && !lo && wp != 0 && member(c, wp, wq)) {
+            s.a += wp;
+            s.b += wq;
+          }
         }
       }
     }
