@@ -134,26 +134,43 @@ struct Slot {
   float T;
 };
 
+// A slot's request r and its index in the request's target or draft slots.
+struct SlotIdx {
+  int r, idx;
+  bool target;
+};
+
+__device__ inline SlotIdx slot_index(const SampArgs& a, int slot) {
+  const int G = a.gamma, nt = a.B * (G + 1);
+  SlotIdx x;
+  x.target = slot < nt;
+  x.r = x.target ? slot / (G + 1) : (slot - nt) / G;
+  x.idx = x.target ? slot - x.r * (G + 1) : slot - nt - x.r * G;
+  return x;
+}
+
+// Whether a request reads the slot, from its request's cu[r], cu[r + 1] and
+// temperature (total_eff = the packed total clamped to [0, max_rows]).
+__device__ inline bool slot_live(const SampArgs& a, const SlotIdx& x, int total_eff, int c0, int c1,
+                                 float T) {
+  const int G = a.gamma, len = c1 - c0;
+  const bool ok = c0 >= 0 && len >= 1 && len <= G + 1 && c0 + len <= total_eff;
+  const bool samp = is_sampling_temp(T);
+  if (!ok || !(samp || T == 0.0f)) return false;
+  return x.target ? x.idx < len : samp && x.idx < len - 1;
+}
+
 __device__ inline Slot resolve_slot(const SampArgs& a, int slot) {
   Slot s{nullptr, false, false, 0.0f};
-  const int G = a.gamma, nt = a.B * (G + 1);
-  const bool target = slot < nt;
-  const int r = target ? slot / (G + 1) : (slot - nt) / G;
-  const int idx = target ? slot - r * (G + 1) : slot - nt - r * G;
+  const SlotIdx x = slot_index(a, slot);
   const int total_eff = min(max(a.cu[a.B], 0), a.max_rows);
-  const int c0 = a.cu[r], len = a.cu[r + 1] - c0;
-  const bool ok = c0 >= 0 && len >= 1 && len <= G + 1 && c0 + len <= total_eff;
-  s.T = a.temps[r];
-  const bool samp = is_sampling_temp(s.T);
-  if (!ok || !(samp || s.T == 0.0f)) return s;
-  if (target) {
-    s.live = idx < len;
-    s.row = a.tgt + (size_t)(c0 + idx) * a.ld_t;
-  } else {
-    s.live = samp && idx < len - 1;
-    s.row = a.drf + (size_t)(slot - nt) * a.ld_q;
-  }
-  s.samp = s.live && samp;
+  const int c0 = a.cu[x.r];
+  s.T = a.temps[x.r];
+  s.live = slot_live(a, x, total_eff, c0, a.cu[x.r + 1], s.T);
+  if (!s.live) return s;
+  s.row = x.target ? a.tgt + (size_t)(c0 + x.idx) * a.ld_t
+                   : a.drf + (size_t)(slot - a.B * (a.gamma + 1)) * a.ld_q;
+  s.samp = is_sampling_temp(s.T);
   return s;
 }
 
@@ -265,26 +282,37 @@ __global__ __launch_bounds__(kRsThreads) void samp_rowstat_kernel(SampArgs a) {
     a.meta[1] = 0;
   }
   // ---- this workgroup's rows: thread t looks at slots [t k, t k + k)
+  // (k <= 64, which the host ensures), eight at a time so that a group's
+  // loads are all in flight together, and keeps their liveness as bits
   const int nslots = a.B * (2 * a.gamma + 1);
   const int per = (nslots + kRsThreads - 1) / kRsThreads;
   const int s0 = tid * per;
-  int cnt = 0;
-  for (int j = 0; j < per; ++j) {
-    const int slot = s0 + j;
-    if (slot < nslots && resolve_slot(a, slot).live) ++cnt;
+  const int total_eff = min(max(a.cu[a.B], 0), a.max_rows);
+  unsigned long long live = 0;
+  for (int j0 = 0; j0 < per; j0 += 8) {
+    SlotIdx x[8];
+    int c0[8], c1[8];
+    float T[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // loads at in-range indices, all issued first
+      x[j] = slot_index(a, min(s0 + j0 + j, nslots - 1));
+      c0[j] = a.cu[x[j].r];
+      c1[j] = a.cu[x[j].r + 1];
+      T[j] = a.temps[x[j].r];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = j0 + j;
+      if (k < per && s0 + k < nslots && slot_live(a, x[j], total_eff, c0[j], c1[j], T[j]))
+        live |= 1ull << k;
+    }
   }
   int total = 0;
-  int rank = block_excl_scan<int, kRsThreads>(cnt, s_scan, &total);
-  if (cnt) {
-    for (int j = 0; j < per; ++j) {
-      const int slot = s0 + j;
-      if (slot < nslots && resolve_slot(a, slot).live) {
-        if (rank % (int)gridDim.x == (int)blockIdx.x) {
-          const int i = rank / (int)gridDim.x;
-          if (i < kRsMaxList) s_list[i] = slot;
-        }
-        ++rank;
-      }
+  int rank = block_excl_scan<int, kRsThreads>(__popcll(live), s_scan, &total);
+  for (unsigned long long m = live; m; m &= m - 1, ++rank) {
+    if (rank % (int)gridDim.x == (int)blockIdx.x) {
+      const int i = rank / (int)gridDim.x;
+      if (i < kRsMaxList) s_list[i] = s0 + __builtin_ctzll(m);
     }
   }
   __syncthreads();
@@ -937,7 +965,8 @@ hipError_t launch_dt(SampArgs a, hipStream_t s) {
     if (e != hipSuccess) return e;
     const long long slots = (long long)a.B * (2 * a.gamma + 1);
     const int g = (int)std::min<long long>(cus, slots);
-    if (slots <= (long long)kRsMaxList * g) grid = g;
+    // each thread keeps the liveness of at most 64 slots as bits
+    if (slots <= (long long)kRsMaxList * g && slots <= 64LL * kRsThreads) grid = g;
   }
   a.rowstat = grid > 0;
   hipError_t e;
