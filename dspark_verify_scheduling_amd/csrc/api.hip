@@ -82,7 +82,7 @@ StsGeom sts_geom(int N, int n_t, int n_bins) {
 
 // Workspace of dspark_accept_sampling: a maximum key and a weight sum per
 // (slot, chunk), slots B * (2 * gamma + 1); two residual sums per (request,
-// chunk); one draw job per request.
+// chunk, part of the chunk); one draw job per request.
 struct SampGeom {
   int chunks, chunk_vecs;
   size_t part_bytes, rpart_bytes, bytes;
@@ -100,7 +100,8 @@ SampGeom samp_geom(int B, int gamma, int V, dspark_dtype dt) {
                     dspark::kSampMaxChunks,
                 "the draw kernel holds the chunk sums of the longest row in LDS");
   g.part_bytes = align256((size_t)B * (2 * gamma + 1) * g.chunks * sizeof(unsigned long long));
-  g.rpart_bytes = align256((size_t)B * g.chunks * 2 * sizeof(unsigned long long));
+  g.rpart_bytes =
+      align256((size_t)B * g.chunks * dspark::kRsumParts * 2 * sizeof(unsigned long long));
   g.bytes = 2 * g.part_bytes + g.rpart_bytes +
             align256((size_t)(B > 0 ? B : 1) * sizeof(dspark::SampJob));
   return g;

@@ -173,13 +173,14 @@ struct SampArgs {
   int rowstat;                // the row statistics come from samp_rowstat_kernel
   unsigned long long* kpart;  // maximum key with its index
   unsigned long long* zpart;  // weight sum
-  unsigned long long* rpart;  // [B, chunks, 2]: residual member sums of Wp, Wq
+  unsigned long long* rpart;  // [B, chunks, kRsumParts, 2]: residual member sums of Wp, Wq
   SampJob* jobs;              // [B]
 };
 constexpr int kSampThreads = 256;       // max and weight-sum kernels
 constexpr int kSampVecsPerThread = 8;
 constexpr int kSampChunkVecs = kSampThreads * kSampVecsPerThread;
 constexpr int kSampDrawThreads = 1024;  // draw kernel
+constexpr int kRsumParts = 2;           // residual-sum workgroups per chunk
 constexpr int kSampMaxChunks = 32;      // chunks of a DSPARK_MAX_VOCAB float32 row
 constexpr int kRsThreads = 1024;        // row-statistics kernel
 constexpr int kRsMaxSlots = 16;         // 16-byte register slots per thread, at most

@@ -45,8 +45,8 @@
 //   samp_decide_kernel: one wave per request: the chain tests, lane k on
 //     draft k + 1, the first rejection by ballot, every output except the
 //     drawn token; a draw job for sampling requests.
-//   samp_rsum_kernel: per (request, chunk) of a residual draw, the sums of
-//     Wp and Wq over the tokens where the residual is positive.
+//   samp_rsum_kernel: per (request, chunk, half chunk) of a residual draw,
+//     the sums of Wp and Wq over the tokens where the residual is positive.
 //   samp_draw_kernel: one workgroup per draw job: the crossing chunk from the
 //     chunk sums (the weight sums for a plain draw), then that chunk split
 //     over all 1024 threads (a few elements each) and scanned; the thread
@@ -728,34 +728,41 @@ __device__ inline DrawCtx draw_ctx(const SampArgs& a, const SampJob& job, int r)
   return c;
 }
 
-// Per (request, chunk) of a residual draw: the member sums of Wp and Wq.
+// Per (request, chunk, part) of a residual draw: the member sums of Wp and
+// Wq over part `part` of the chunk (kRsumParts equal parts; smaller
+// workgroups keep more of them on a CU, loading while others sum).
+constexpr int kRsumVecs = kSampVecsPerThread / kRsumParts;  // per thread
+static_assert(kRsumVecs * kRsumParts == kSampVecsPerThread, "parts split a chunk evenly");
+
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kSampThreads) void samp_rsum_kernel(SampArgs a) {
   __shared__ Pair s_red[kRedWaves];
   constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int r = blockIdx.x / a.chunks, ch = blockIdx.x - r * a.chunks;
+  const int part = blockIdx.x % kRsumParts, u = blockIdx.x / kRsumParts;
+  const int r = u / a.chunks, ch = u - r * a.chunks;
   const SampJob job = a.jobs[r];
   if (job.mode != 2) return;
   const DrawCtx c = draw_ctx(a, job, r);
   const u32x4* pv = reinterpret_cast<const u32x4*>(c.p);
   const u32x4* qv = reinterpret_cast<const u32x4*>(c.q);
-  const int v0 = ch * a.chunk_vecs, v1 = min(v0 + a.chunk_vecs, a.nvec);
-  u32x4 dp[kSampVecsPerThread], dq[kSampVecsPerThread];
+  const int v0 = ch * a.chunk_vecs + part * (kRsumVecs * kSampThreads);
+  const int v1 = min(v0 + kRsumVecs * kSampThreads, min(ch * a.chunk_vecs + a.chunk_vecs, a.nvec));
+  u32x4 dp[kRsumVecs], dq[kRsumVecs];
 #pragma unroll
-  for (int i = 0; i < kSampVecsPerThread; ++i) {
+  for (int i = 0; i < kRsumVecs; ++i) {
     const int v = v0 + i * kSampThreads + tid;
     dp[i] = v < v1 ? __builtin_nontemporal_load(pv + v) : (u32x4){0, 0, 0, 0};
     dq[i] = v < v1 ? __builtin_nontemporal_load(qv + v) : (u32x4){0, 0, 0, 0};
   }
   Pair s{0, 0};
-  if (ch == a.chunks - 1 && tid < a.tail) add_elem<DT>(c, a.nvec * kEpv + tid, s);
+  if (part == 0 && ch == a.chunks - 1 && tid < a.tail) add_elem<DT>(c, a.nvec * kEpv + tid, s);
   // member() without branches: the float32 screen decides every element it
   // can, and the few near equality (flagged) are decided exactly afterwards,
   // in a second walk that only a wave holding one takes
   bool near = false;
 #pragma unroll
-  for (int i = 0; i < kSampVecsPerThread; ++i) {
+  for (int i = 0; i < kRsumVecs; ++i) {
     if (v0 + i * kSampThreads + tid < v1) {
       float x[kEpv], y[kEpv];
       widen<DT>(dp[i], x);
@@ -773,7 +780,7 @@ __global__ __launch_bounds__(kSampThreads) void samp_rsum_kernel(SampArgs a) {
   }
   if (__ballot(near)) {
 #pragma unroll
-    for (int i = 0; i < kSampVecsPerThread; ++i) {
+    for (int i = 0; i < kRsumVecs; ++i) {
       if (near && v0 + i * kSampThreads + tid < v1) {
         float x[kEpv], y[kEpv];
         widen<DT>(dp[i], x);
@@ -801,8 +808,8 @@ __global__ __launch_bounds__(kSampThreads) void samp_rsum_kernel(SampArgs a) {
       t.a += s_red[w].a;
       t.b += s_red[w].b;
     }
-    a.rpart[((size_t)r * a.chunks + ch) * 2] = t.a;
-    a.rpart[((size_t)r * a.chunks + ch) * 2 + 1] = t.b;
+    a.rpart[((size_t)u * kRsumParts + part) * 2] = t.a;
+    a.rpart[((size_t)u * kRsumParts + part) * 2 + 1] = t.b;
   }
 }
 
@@ -826,9 +833,15 @@ __global__ __launch_bounds__(kSampDrawThreads) void samp_draw_kernel(SampArgs a)
   DrawCtx c = draw_ctx(a, job, r);
   if (tid < C) {  // one load per thread, not a chain of them in one thread
     s_zs[tid] = a.zpart[((size_t)r * (a.gamma + 1) + job.col) * C + tid];
-    if (job.mode == 2) {
-      s_rs[tid].a = a.rpart[((size_t)r * C + tid) * 2];
-      s_rs[tid].b = a.rpart[((size_t)r * C + tid) * 2 + 1];
+    if (job.mode == 2) {  // the chunk's parts added up
+      const unsigned long long* rp = a.rpart + ((size_t)r * C + tid) * kRsumParts * 2;
+      Pair t{0, 0};
+#pragma unroll
+      for (int q = 0; q < kRsumParts; ++q) {
+        t.a += rp[2 * q];
+        t.b += rp[2 * q + 1];
+      }
+      s_rs[tid] = t;
     }
   }
   __syncthreads();
@@ -984,8 +997,8 @@ hipError_t launch_dt(SampArgs a, hipStream_t s) {
   hipLaunchKernelGGL(samp_decide_kernel<DT>, dim3(a.B), dim3(kWave), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(samp_rsum_kernel<DT>, dim3((unsigned)(a.B * a.chunks)), dim3(kSampThreads), 0,
-                     s, a);
+  hipLaunchKernelGGL(samp_rsum_kernel<DT>, dim3((unsigned)(a.B * a.chunks * kRsumParts)),
+                     dim3(kSampThreads), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(samp_draw_kernel<DT>, dim3(a.B), dim3(kSampDrawThreads), 0, s, a);

@@ -356,10 +356,11 @@ def test_accept_sampling_argument_errors():
     assert run() == _lib.E_WORKSPACE
     size = _lib.lib().dspark_accept_sampling_workspace_size
     # 9 + 12 slots, one chunk of 125 vectors: 21 keys and 21 sums, 4 requests
-    # of 2 residual sums, 4 jobs of 48 bytes
+    # of 2 x 2 residual sums, 4 jobs of 48 bytes
     assert size(4, 3, 1000, _lib.BF16) == 256 + 256 + 256 + 256
-    # V = 129280 bf16: 16160 vectors in 8 chunks; 4 * 17 slots
-    assert size(4, 8, 129280, _lib.BF16) == 2 * (4 * 17 * 8 * 8) + 512 + 256  # 4352 = 17 * 256
+    # V = 129280 bf16: 16160 vectors in 8 chunks; 4 * 17 slots; residual sums
+    # per (request, chunk, half chunk)
+    assert size(4, 8, 129280, _lib.BF16) == 2 * (4 * 17 * 8 * 8) + 1024 + 256  # 4352 = 17 * 256
     assert size(0, 3, 100, _lib.F32) == 256  # one job slot, no partials
     assert size(-1, 3, 100, _lib.F32) == 0 and size(4, 65, 100, _lib.F32) == 0
     assert size(4, 3, 0, _lib.F32) == 0 and size(4, 3, 100, 7) == 0
