@@ -709,6 +709,68 @@ __device__ inline void add_elem(const DrawCtx& c, int i, Pair& s) {
   }
 }
 
+// member() summed over the valid vectors of dp (p) and dq (q) without
+// branches: the float32 screen decides every element it can, and the few near
+// equality (flagged) are decided exactly afterwards, in a second walk that
+// only a wave holding one takes. A plain draw (not c.resid) sums Wp alone.
+template <dspark_dtype DT, int N>
+__device__ inline Pair member_sums(const DrawCtx& c, const u32x4 (&dp)[N], const u32x4 (&dq)[N],
+                                   const bool (&valid)[N]) {
+  constexpr int kEpv = DT == DSPARK_BF16 ? 8 : 4;
+  Pair s{0, 0};
+  if (!c.resid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (valid[i]) {
+        float x[kEpv];
+        widen<DT>(dp[i], x);
+#pragma unroll
+        for (int e = 0; e < kEpv; ++e) s.a += weight(x[e], c.mp, c.cT);
+      }
+    }
+    return s;
+  }
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (valid[i]) {
+      float x[kEpv], y[kEpv];
+      widen<DT>(dp[i], x);
+      widen<DT>(dq[i], y);
+#pragma unroll
+      for (int e = 0; e < kEpv; ++e) {
+        const float fp = weight_f(x[e], c.mp, c.cT), fq = weight_f(y[e], c.mq, c.cT);
+        const float xs = fp * c.zqf, ys = fq * c.zpf;
+        const bool hi = xs > ys * (1.0f + 0x1p-20f), lo = xs < ys * (1.0f - 0x1p-20f);
+        s.a += hi ? __float2uint_rz(fp) : 0u;
+        s.b += hi ? __float2uint_rz(fq) : 0u;
+        near |= !hi && !lo && fp != 0.0f;
+      }
+    }
+  }
+  if (__ballot(near)) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (near && valid[i]) {
+        float x[kEpv], y[kEpv];
+        widen<DT>(dp[i], x);
+        widen<DT>(dq[i], y);
+        for (int e = 0; e < kEpv; ++e) {
+          const float fp = weight_f(x[e], c.mp, c.cT), fq = weight_f(y[e], c.mq, c.cT);
+          const float xs = fp * c.zqf, ys = fq * c.zpf;
+          const bool hi = xs > ys * (1.0f + 0x1p-20f), lo = xs < ys * (1.0f - 0x1p-20f);
+          const unsigned int wp = __float2uint_rz(fp), wq = __float2uint_rz(fq);
+          if (!hi && !lo && wp != 0 && member(c, wp, wq)) {
+            s.a += wp;
+            s.b += wq;
+          }
+        }
+      }
+    }
+  }
+  return s;
+}
+
 __device__ inline void set_mode(DrawCtx& c, const SampJob& job, bool resid) {
   c.resid = resid;
   c.zp = resid ? job.zp : 0ull;
@@ -755,49 +817,11 @@ __global__ __launch_bounds__(kSampThreads) void samp_rsum_kernel(SampArgs a) {
     dp[i] = v < v1 ? __builtin_nontemporal_load(pv + v) : (u32x4){0, 0, 0, 0};
     dq[i] = v < v1 ? __builtin_nontemporal_load(qv + v) : (u32x4){0, 0, 0, 0};
   }
-  Pair s{0, 0};
+  bool valid[kRsumVecs];
+#pragma unroll
+  for (int i = 0; i < kRsumVecs; ++i) valid[i] = v0 + i * kSampThreads + tid < v1;
+  Pair s = member_sums<DT, kRsumVecs>(c, dp, dq, valid);
   if (part == 0 && ch == a.chunks - 1 && tid < a.tail) add_elem<DT>(c, a.nvec * kEpv + tid, s);
-  // member() without branches: the float32 screen decides every element it
-  // can, and the few near equality (flagged) are decided exactly afterwards,
-  // in a second walk that only a wave holding one takes
-  bool near = false;
-#pragma unroll
-  for (int i = 0; i < kRsumVecs; ++i) {
-    if (v0 + i * kSampThreads + tid < v1) {
-      float x[kEpv], y[kEpv];
-      widen<DT>(dp[i], x);
-      widen<DT>(dq[i], y);
-#pragma unroll
-      for (int e = 0; e < kEpv; ++e) {
-        const float fp = weight_f(x[e], c.mp, c.cT), fq = weight_f(y[e], c.mq, c.cT);
-        const float xs = fp * c.zqf, ys = fq * c.zpf;
-        const bool hi = xs > ys * (1.0f + 0x1p-20f), lo = xs < ys * (1.0f - 0x1p-20f);
-        s.a += hi ? __float2uint_rz(fp) : 0u;
-        s.b += hi ? __float2uint_rz(fq) : 0u;
-        near |= !hi && !lo && fp != 0.0f;
-      }
-    }
-  }
-  if (__ballot(near)) {
-#pragma unroll
-    for (int i = 0; i < kRsumVecs; ++i) {
-      if (near && v0 + i * kSampThreads + tid < v1) {
-        float x[kEpv], y[kEpv];
-        widen<DT>(dp[i], x);
-        widen<DT>(dq[i], y);
-        for (int e = 0; e < kEpv; ++e) {
-          const float fp = weight_f(x[e], c.mp, c.cT), fq = weight_f(y[e], c.mq, c.cT);
-          const float xs = fp * c.zqf, ys = fq * c.zpf;
-          const bool hi = xs > ys * (1.0f + 0x1p-20f), lo = xs < ys * (1.0f - 0x1p-20f);
-          const unsigned int wp = __float2uint_rz(fp), wq = __float2uint_rz(fq);
-          if (!hi && !lo && wp != 0 && member(c, wp, wq)) {
-            s.a += wp;
-            s.b += wq;
-          }
-        }
-      }
-    }
-  }
   s.a = wave_sum_u64(s.a);
   s.b = wave_sum_u64(s.b);
   if (lane == 0) s_red[wave] = s;
@@ -820,7 +844,7 @@ __global__ __launch_bounds__(kSampThreads) void samp_rsum_kernel(SampArgs a) {
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kSampDrawThreads) void samp_draw_kernel(SampArgs a) {
   constexpr int kWaves = kSampDrawThreads / kWave;
-  __shared__ unsigned long long s_scan[kWaves];
+  __shared__ unsigned long long s_scan[kWaves], s_scan_b[kWaves];
   __shared__ int s_ctl[2];  // residual flag; crossing chunk
   __shared__ u128 s_t;      // threshold left at the start of the crossing chunk
   __shared__ Pair s_rs[kSampMaxChunks];            // residual chunk sums
@@ -896,32 +920,17 @@ __global__ __launch_bounds__(kSampDrawThreads) void samp_draw_kernel(SampArgs a)
   const bool last = tid == kSampDrawThreads - 1;
   const int t0 = a.nvec * kEpv;  // first tail element
   const bool has_tail = last && ch == C - 1 && a.tail > 0;
-  Pair mine{0, 0};
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    if (my0 + k < my1) {
-      float x[kEpv], y[kEpv];
-      widen<DT>(dp[k], x);
-      widen<DT>(dq[k], y);
-#pragma unroll
-      for (int e = 0; e < kEpv; ++e) {
-        const unsigned int wp = weight(x[e], c.mp, c.cT);
-        const unsigned int wq = c.resid ? weight(y[e], c.mq, c.cT) : 0u;
-        if (member(c, wp, wq)) {
-          mine.a += wp;
-          mine.b += wq;
-        }
-      }
-    }
-  }
+  const bool valid[2] = {my0 < my1, my0 + 1 < my1};
+  Pair mine = member_sums<DT, 2>(c, dp, dq, valid);
   if (has_tail) {
     for (int i = t0; i < a.V; ++i) add_elem<DT>(c, i, mine);
   }
+  // both exclusive scans with one barrier (each has its own partials)
   unsigned long long tot_a, tot_b;
   const unsigned long long ea =
-      block_excl_scan<unsigned long long, kSampDrawThreads>(mine.a, s_scan, &tot_a);
+      block_excl_scan_open<unsigned long long, kSampDrawThreads>(mine.a, s_scan, &tot_a);
   const unsigned long long eb =
-      block_excl_scan<unsigned long long, kSampDrawThreads>(mine.b, s_scan, &tot_b);
+      block_excl_scan_open<unsigned long long, kSampDrawThreads>(mine.b, s_scan_b, &tot_b);
   const u128 before = run_value(c, Pair{ea, eb});
   const u128 after = run_value(c, Pair{ea + mine.a, eb + mine.b});
   // exactly one thread has before <= t < after: it hands its element range
