@@ -535,3 +535,65 @@ def test_sampling_weight_sums_within_bound(seed, B, gamma, V, dt, t_lo, t_hi):
             worst = max(worst, abs(z[slot] - want) / want)
             checked += 1
     say(f"{checked} slot weight sums within the bound; largest relative error {worst:.3g}")
+
+
+@pytest.mark.parametrize("V,dt", [(20000, dv.BF16), (6000, dv.F32), (3000, dv.BF16)])
+def test_sampling_residual_near_equality(V, dt):
+    """q equal to p except at one token d of tiny probability, whose q weight
+    is e^5 times p's. The draft d is rejected (large accept words), and every
+    other token has Wp Zq and Wq Zp within 2^-20 of each other (Zq - Zp is
+    below 2^-20 Zp, checked on the kernels' own sums), so the residual sums and
+    the draw decide membership on the exact path. With identical logits and
+    maxima the residual is p's weight times Zq - Zp on every token but d, so
+    the drawn token must be the inverse-CDF draw from p without d, within the
+    band of a draw from p."""
+    B, G = 8, 1
+    rng = np.random.default_rng(V)
+    temps = rng.uniform(0.7, 1.4, B).astype(np.float32)
+    cu = np.arange(0, 2 * B + 1, 2, dtype=np.int32)
+    rows = rng.normal(0, 2.5, (2 * B, V)).astype(np.float32)
+    if dt == dv.BF16:
+        rows = as_f32_rows(gen.f32_to_bf16_bits(rows), "bf16")
+    drf = np.empty((B, V), np.float32)
+    drafts = np.empty((B, G), np.int32)
+    for r in range(B):
+        p, T = rows[2 * r], float(temps[r])
+        d = int(np.argmin(p))
+        p[d] = p.max() - 18.5 * T  # a weight of about 20 units of 2^31
+        q = p.copy()
+        q[d] = p[d] + 5.0 * T
+        if dt == dv.BF16:
+            p[:] = as_f32_rows(gen.f32_to_bf16_bits(p[None]), "bf16")[0]
+            q = as_f32_rows(gen.f32_to_bf16_bits(q[None]), "bf16")[0]
+        drf[r] = q
+        drafts[r, 0] = d
+    ra = rng.integers(2**31, 2**32, (B, G), dtype=np.uint64).astype(np.uint32)
+    rs = rng.integers(0, 2**32, (B, G + 1), dtype=np.uint64).astype(np.uint32)
+    prefix = np.zeros(B, np.int32)
+    tgt_in = gen.f32_to_bf16_bits(rows) if dt == dv.BF16 else rows
+    drf_in = gen.f32_to_bf16_bits(drf) if dt == dv.BF16 else drf
+    esize = 2 if dt == dv.BF16 else 4
+    ld = V if (V * esize) % 16 == 0 else (V + 16 // esize - 1) // (16 // esize) * (16 // esize)
+    pad = (lambda x: np.pad(x, ((0, 0), (0, ld - V)))) if ld != V else (lambda x: x)
+    out = dv.alloc_sampling_outputs(B, G, V, dt, DEV)
+    say(f"near equality V={V} dt={dt}")
+    dv.dspark_accept_sampling(
+        B, G, V, dt, logits_up(pad(tgt_in), dt), ld, 2 * B, up(cu), logits_up(pad(drf_in), dt), ld,
+        up(drafts), up(temps), up(_bits(ra)), up(_bits(rs)), up(prefix), out)
+    torch.cuda.synchronize()
+    z = _slot_sums(out, B, G, V, dt)
+    got = {"num_correct": out.num_correct.cpu().numpy(), "bonus": out.bonus.cpu().numpy(),
+           "commit": out.commit_lens.cpu().numpy(), "new_seq": out.new_seq_lens.cpu().numpy(),
+           "out_tokens": out.out_tokens.cpu().numpy(), "meta": out.accept_meta.cpu().numpy()}
+    dtype = "bf16" if dt == dv.BF16 else "f32"
+    check_f64(got, B, G, tgt_in, drf_in, dtype, cu, drafts, temps, ra, rs, prefix, tag="near")
+    eps_p, eta_p = F64.prob_error_bound(V)
+    for r in range(B):
+        zp, zq = z[r * (G + 1)], z[B * (G + 1) + r * G]
+        assert 0 < zq - zp < zp / 2**20, (r, zp, zq)  # the premise: every other token near
+        assert got["num_correct"][r] == 0, r          # the draft is rejected
+        w = F64.softmax64(rows[2 * r], float(temps[r]))
+        w[drafts[r, 0]] = 0.0
+        k, _, ok = F64._draw_check(w, F64.uniform(rs[r, 0]), int(got["bonus"][r]),
+                                   eps_p + V * eta_p, V)
+        assert ok and got["bonus"][r] != drafts[r, 0], (r, k, got["bonus"][r])
