@@ -50,7 +50,8 @@
 //   samp_draw_kernel: one workgroup per draw job: the crossing chunk from the
 //     chunk sums (the weight sums for a plain draw), then that chunk split
 //     over all 1024 threads (a few elements each) and scanned; the thread
-//     holding the crossing point walks its elements in order.
+//     holding the crossing point hands its elements to one wave, which scans
+//     them one per lane.
 #include <float.h>
 
 #include <algorithm>
@@ -838,9 +839,10 @@ __global__ __launch_bounds__(kSampThreads) void samp_rsum_kernel(SampArgs a) {
 }
 
 // One workgroup per request with a draw job: the crossing chunk from the
-// per-chunk sums (residual: samp_rsum_kernel; plain: the weight sums of the
-// target slot), then the chunk's elements split over the threads, scanned,
-// and walked by the thread holding the crossing point.
+// per-chunk sums (residual: samp_rsum_kernel's halves added; plain: the
+// weight sums of the target slot), then the chunk's elements split over the
+// threads and scanned, then the crossing thread's elements one per lane of
+// wave 0.
 template <dspark_dtype DT>
 __global__ __launch_bounds__(kSampDrawThreads) void samp_draw_kernel(SampArgs a) {
   constexpr int kWaves = kSampDrawThreads / kWave;
