@@ -10,7 +10,8 @@ would have produced, is resident in HBM before the timed region. Three
 copies of the packed logits rotate (about 0.56 GB of live rows), so the
 256 MB Infinity Cache cannot serve repeated reads.
 
-Prints one JSON line. ``value`` is steps/s (eager launches). ``roofline`` is
+Prints one JSON line. ``value`` is steps/s (eager launches: K steps between
+one HIP event pair, nothing else on the stream). ``roofline`` is
 the accept call's achieved HBM bandwidth: algorithmic bytes per launch over
 its average launch duration, 100 dedicated accept launches back to back
 between one HIP event pair on the stream they run on, whatever ``--steps``
@@ -42,7 +43,8 @@ sys.path.insert(0, str(ROOT))
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "plan+accept steps/s and logit-pass HBM GB/s (% peak) at B=256,γ=8,V=129280"
-ACC_EVERY = 4  # timed steps whose accept call is bracketed by HIP events
+ACC_EVERY = 4  # of the in-step accept measurement's steps, one in ACC_EVERY is bracketed
+N_IN_STEP = 50  # bracketed accept calls inside steps
 N_ACC = 100  # dedicated accept launches behind the roofline figure
 N_SCHED = 16  # seeded steps behind the scheduling statistics
 TRAFFIC_FILE = ROOT / "profiles" / "accept_b256_g8_v129280_bf16_traffic.json"
@@ -422,29 +424,38 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # ---- timed: K eager steps. Events bracket the accept call of every
-    # ACC_EVERY-th step, on its stream: a pair of event records costs about
-    # 3 us per step, so the other steps run without them.
-    sampled = list(range(0, args.steps, ACC_EVERY))
-    ev_a0 = {i: torch.cuda.Event(enable_timing=True) for i in sampled}
-    ev_a1 = {i: torch.cuda.Event(enable_timing=True) for i in sampled}
+    # ---- timed: K eager steps, nothing else on the stream between the two
+    # events
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
         plan_pack(stream)
-        if i in ev_a0:
-            ev_a0[i].record(stream)
         dv.dspark_accept(B, G, V, dt, packed[i % n_rot], V, tier, ko.cu_seqlens, drafts_t,
                          prefix_t, ao, stream)
-        if i in ev_a1:
-            ev_a1[i].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(stop) / args.steps
-    acc_us = [1e3 * ev_a0[i].elapsed_time(ev_a1[i]) for i in sampled]
+
+    # ---- the accept call inside a step: further steps (after the timed
+    # ones) whose accept call every ACC_EVERY-th step is bracketed by an event
+    # pair (a pair costs about 3 us, so the other steps run without one)
+    n_in = ACC_EVERY * N_IN_STEP
+    ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(N_IN_STEP)]
+    ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(N_IN_STEP)]
+    torch.cuda.synchronize()
+    for i in range(n_in):
+        plan_pack(stream)
+        if i % ACC_EVERY == 0:
+            ev_a0[i // ACC_EVERY].record(stream)
+        dv.dspark_accept(B, G, V, dt, packed[i % n_rot], V, tier, ko.cu_seqlens, drafts_t,
+                         prefix_t, ao, stream)
+        if i % ACC_EVERY == 0:
+            ev_a1[i // ACC_EVERY].record(stream)
+    torch.cuda.synchronize()
+    acc_us = [1e3 * ev_a0[j].elapsed_time(ev_a1[j]) for j in range(N_IN_STEP)]
     acc_mean_us = statistics.mean(acc_us)
 
     # results of the timed steps must be the planned ones
