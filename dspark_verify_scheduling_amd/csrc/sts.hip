@@ -46,7 +46,13 @@ namespace {
 
 constexpr double kFx = 0x1p40;
 
-__device__ inline long long fx40(double v) { return __double2ll_rn(v * kFx); }
+// RN(v * 2^40) as an integer (ties to even), for v in [0, 1] (every value
+// binned here is): v * 2^40 + 2^52 in one fused multiply-add is that integer
+// plus 2^52, since the doubles in [2^52, 2^53) are exactly the integers, and
+// its bits minus those of 2^52 are the integer.
+__device__ inline long long fx40(double v) {
+  return __double_as_longlong(__fma_rn(v, kFx, 0x1p52)) - __double_as_longlong(0x1p52);
+}
 
 // Shared memory of the candidate choice.
 struct SelectSmem {
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(kStsBinThreads) void sts_bin_kernel(StsArgs a, int 
         if (j + i * kStsPhases >= nT) break;
         const float s = __fmul_rn(sp, c[i]);
         const double sd = s == s ? (double)s : 0.0;  // a NaN survival counts as 0
-        int b = (int)floor(sd * nb);
+        int b = (int)(sd * nb);  // sd >= 0 and sd * nb exact: truncation is the floor
         b = b < nb ? b : nb - 1;
         unsigned long long* h = reinterpret_cast<unsigned long long*>(hist + tc[i] * stride);
         if (y) atomicAdd(h + b, 1ull);
