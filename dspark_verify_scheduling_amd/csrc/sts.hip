@@ -63,25 +63,39 @@ struct SelectSmem {
 
 // Picks the temperature of position kk from its summed histograms h
 // ([n_t][2 * nbins + 1]): n * ECE = sum over bins of |labels * 2^40 - survival
-// sum|; the smallest wins, the first candidate on ties. Block-wide, one
-// (candidate, bin) pair per thread and round (a single round for up to
-// blockDim.x pairs); every thread returns the choice. With `record`, the
-// position's results are stored.
+// sum|; the smallest wins, the first candidate on ties. Block-wide: with at
+// most 16 bins and 16 * n_t threads, thread 16c + b takes bin b of candidate
+// c and each 16-lane row sums its candidate; otherwise one (candidate, bin)
+// pair per thread and round, summed with LDS atomics. Every thread returns
+// the choice. With `record`, the position's results are stored.
 __device__ int select_candidate(const StsArgs& a, const long long* h, int kk, bool record,
                                 SelectSmem& sm) {
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int nT = a.n_t, nb = a.nbins, stride = 2 * nb + 1;
-  for (int c = tid; c < nT; c += nthr) {
-    sm.err[c] = 0;
-    sm.brier[c] = h[(size_t)c * stride + 2 * nb];
-  }
-  __syncthreads();
-  for (int i = tid; i < nT * nb; i += nthr) {
-    const int c = i / nb, b = i - c * nb;
-    const long long d = h[(size_t)c * stride + b] * (1ll << 40) - h[(size_t)c * stride + nb + b];
-    if (d != 0) {
-      atomicAdd(reinterpret_cast<unsigned long long*>(&sm.err[c]),
-                (unsigned long long)(d < 0 ? -d : d));
+  if (nb <= 16 && nT * 16 <= nthr) {
+    // one (candidate, bin) per thread, the 16 lanes of a DPP row on one
+    // candidate: every load in one round, the row sum by four row shifts
+    const int c = tid >> 4, b = tid & 15;
+    const bool in = c < nT && b < nb;
+    const long long* hc = h + (size_t)(c < nT ? c : 0) * stride;
+    const long long lab = in ? hc[b] : 0, sum = in ? hc[nb + b] : 0;
+    if (c < nT && b == 0) sm.brier[c] = hc[2 * nb];
+    const long long d = lab * (1ll << 40) - sum;
+    const long long e = row_incl_scan(d < 0 ? -d : d, 0ll, OpAdd{});
+    if (c < nT && b == 15) sm.err[c] = e;
+  } else {
+    for (int c = tid; c < nT; c += nthr) {
+      sm.err[c] = 0;
+      sm.brier[c] = h[(size_t)c * stride + 2 * nb];
+    }
+    __syncthreads();
+    for (int i = tid; i < nT * nb; i += nthr) {
+      const int c = i / nb, b = i - c * nb;
+      const long long d = h[(size_t)c * stride + b] * (1ll << 40) - h[(size_t)c * stride + nb + b];
+      if (d != 0) {
+        atomicAdd(reinterpret_cast<unsigned long long*>(&sm.err[c]),
+                  (unsigned long long)(d < 0 ? -d : d));
+      }
     }
   }
   __syncthreads();
