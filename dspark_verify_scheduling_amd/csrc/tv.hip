@@ -16,7 +16,9 @@
 // Rows that fit on one CU (bf16 V up to 130055) take tv_resident_kernel: one
 // persistent workgroup per CU keeps each pair in registers and LDS between
 // the passes, so every logit is read from HBM once, and loads the next pair
-// while it finishes the current one. Longer rows take tv_kernel, one
+// while it finishes the current one. The same kernel takes rows of up to
+// 4096 vectors more (bf16 V up to 162823) and reads only those vectors twice.
+// Longer rows take tv_kernel, one
 // workgroup per pair, which streams them twice (pass 1 with ordinary loads,
 // pass 2 with nontemporal ones); the pair's rows are then mostly gone from the
 // XCD's 4 MB L2 when pass 2 comes back to them.
@@ -250,16 +252,15 @@ __device__ inline float min_sum_pair(const u32x4& dq, const u32x4& dp, float aq,
 }
 
 // Direct global-to-LDS copy of one wave's 64 x 16 bytes: lane l's vector
-// src[l] lands at dst[l], without passing through registers. src and dst are
-// wave-uniform (SGPR base address, the lane's byte offset in a VGPR); M0 holds
-// dst's LDS byte address (one wait state before the load reads it; nothing
-// else in these kernels uses M0, so it is not saved). Written
+// src[l] lands at LDS byte address lds_addr + 16 l, without passing through
+// registers. src and lds_addr are wave-uniform (SGPR base address, the lane's
+// byte offset in a VGPR); M0 holds lds_addr (one wait state before the load
+// reads it; nothing else in these kernels uses M0, so it is not saved). Written
 // as inline assembly so that the compiler's wait-count bookkeeping does not
 // see it: its waits for the register loads stay exact positions in the load
 // queue (the copies only make them more conservative), and the callers wait
 // for the copies themselves (vmcnt(0) and a barrier) before reading the LDS.
-__device__ inline void lds_dma16(const u32x4* src, u32x4* dst, unsigned int lane_bytes) {
-  const unsigned int lds_addr = (unsigned int)(size_t)(__attribute__((address_space(3))) void*)dst;
+__device__ inline void lds_dma16(const u32x4* src, unsigned int lds_addr, unsigned int lane_bytes) {
   const unsigned long long g = (unsigned long long)src;
   const unsigned long long g_uniform =
       ((unsigned long long)(unsigned int)__builtin_amdgcn_readfirstlane((int)(g >> 32)) << 32) |
@@ -314,22 +315,28 @@ __device__ inline void block_stat2(Stat& sq, Stat& sp, float4* ws) {
 //   in registers of thread v % 1024 (slot v / 1024) for v < 11 * 1024, and
 //   in LDS for the rest (q at i, p at n_lds + i, i = v - 11 * 1024),
 // which holds rows of up to 11 * 1024 + 4992 vectors (bf16 V <= 130055):
-// 88 VGPRs and up to 156 KB of LDS. The next pair's loads are issued while
-// pass 2 of the current one runs: each register slot is reloaded as soon as
-// pass 2 has consumed it, and the LDS part is copied straight from HBM into
-// LDS (no registers) once every wave has read the current one. Pass 1 of the
-// next pair then consumes the slots in the order they arrive.
+// 88 VGPRs and up to 156 KB of LDS. Up to kResMaxOverflow vectors past those
+// are read from memory twice: in pass 1 after the LDS part, and in pass 2
+// before the register slots (so that waiting for them never waits for the
+// next pair's reloads). The next pair's loads are issued while pass 2 of the
+// current one runs: each register slot is reloaded as soon as pass 2 has
+// consumed it, and the LDS part is copied straight from HBM into LDS (no
+// registers) once every wave has read the current one. Pass 1 of the next
+// pair then consumes the slots in the order they arrive.
 //
 // FULL (rows of at least 11 * 1024 vectors) issues every register-slot load
 // unconditionally, so the compiler can wait for each slot by its position in
 // the load queue instead of for the whole queue; after the last pair the
 // reloads read the current row's first 1 KB again (cached), and are unused.
-// Shorter rows fill the slots past the row end with -inf instead. Longer rows
-// take the two-pass streaming kernel above.
+// Shorter rows fill the slots past the row end with -inf instead. Rows past
+// the overflow limit take the two-pass streaming kernel above.
 constexpr int kResRegSlots = 11;
 constexpr int kResLdsSlots = 5;
 constexpr int kResRegSpan = kResRegSlots * kTvThreads;
 constexpr int kResLdsMaxPairs = 4992;  // 2 * 4992 * 16 B = 156 KB
+// vectors past the register slots and the LDS part (read twice, from memory):
+// rows of up to 11 * 1024 + 4992 + 4096 vectors (bf16 V <= 162823)
+constexpr int kResMaxOverflow = 4 * kTvThreads;
 
 template <dspark_dtype DT, bool FULL>
 __global__ __launch_bounds__(kTvThreads) void tv_resident_kernel(TvArgs a) {
@@ -343,9 +350,19 @@ __global__ __launch_bounds__(kTvThreads) void tv_resident_kernel(TvArgs a) {
   const int wave_off = __builtin_amdgcn_readfirstlane(tid & ~(kWave - 1));
   const unsigned int lane_bytes = (unsigned int)(tid & (kWave - 1)) * sizeof(u32x4);
   const int nvec = a.nvec;
-  const int n_lds = FULL ? nvec - kResRegSpan : 0;
+  const int n_lds = FULL ? min(nvec - kResRegSpan, kResLdsMaxPairs) : 0;
+  // The overflow vectors [x0, nvec), read twice. Thread tid takes those
+  // congruent to tid modulo the workgroup size, starting at xs, as in the
+  // register slots and the LDS part: the rare exact re-sum of pass 1 sweeps
+  // v = tid, tid + 1024, ... and so covers the same vectors.
+  const int x0 = kResRegSpan + n_lds;
+  const int xs = x0 + ((tid - x0) & (kTvThreads - 1));
   u32x4* lq = lds_pairs;
   u32x4* lp = lds_pairs + n_lds;
+  // LDS byte addresses of the two parts (uniform), for the copies
+  const unsigned int lq_addr = (unsigned int)__builtin_amdgcn_readfirstlane(
+      (int)(unsigned int)(size_t)(__attribute__((address_space(3))) void*)lds_pairs);
+  const unsigned int lp_addr = lq_addr + (unsigned int)n_lds * 16u;
   const u32x4 fill = (u32x4){kNegInf, kNegInf, kNegInf, kNegInf};
 
   int pair = blockIdx.x;
@@ -375,8 +392,8 @@ __global__ __launch_bounds__(kTvThreads) void tv_resident_kernel(TvArgs a) {
       const int i = c * kTvThreads + tid;
       if (i < n_lds) {
         const int w0 = c * kTvThreads + wave_off;
-        lds_dma16(qv + kResRegSpan + w0, lq + w0, lane_bytes);
-        lds_dma16(pv + kResRegSpan + w0, lp + w0, lane_bytes);
+        lds_dma16(qv + kResRegSpan + w0, lq_addr + w0 * 16u, lane_bytes);
+        lds_dma16(pv + kResRegSpan + w0, lp_addr + w0 * 16u, lane_bytes);
       }
     }
   }
@@ -425,6 +442,11 @@ __global__ __launch_bounds__(kTvThreads) void tv_resident_kernel(TvArgs a) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       lds_sums(oq, op, fq, fp);
+#pragma unroll 1
+      for (int v = xs; v < nvec; v += kTvThreads) {  // overflow, first read
+        fq += exp_sum_vec<DT>(qv[v], oq);
+        fp += exp_sum_vec<DT>(pv[v], op);
+      }
     }
     if (!(fq <= FLT_MAX && fp <= FLT_MAX)) {
       // rare: two sweeps over this thread's vectors, read again from memory
@@ -463,10 +485,11 @@ __global__ __launch_bounds__(kTvThreads) void tv_resident_kernel(TvArgs a) {
     const float aq = sq.mL + log2f(sq.s);  // base-2 log-partitions
     const float ap = sp.mL + log2f(sp.s);
 
-    // pass 2: the tail first (its loads are then not queued behind the
-    // reloads), then the register slots, each reloaded with the next pair once
-    // consumed, then the LDS part. The empty asm makes the raw words opaque, so
-    // pass 2 widens them again instead of keeping pass 1's fp32 copies alive.
+    // pass 2: the tail and any overflow vectors first (their loads are then
+    // not queued behind the reloads), then the register slots, each reloaded
+    // with the next pair once consumed, then the LDS part. The empty asm
+    // makes the raw words opaque, so pass 2 widens them again instead of
+    // keeping pass 1's fp32 copies alive.
     float acc = 0.0f;
     if (tid == 0) {
       for (int t = 0; t < a.tail; ++t) {
@@ -474,6 +497,11 @@ __global__ __launch_bounds__(kTvThreads) void tv_resident_kernel(TvArgs a) {
         acc += exp2_raw(fminf(__fmaf_rn(elem<DT>(qrow, i), kLog2e, -aq),
                               __fmaf_rn(elem<DT>(prow, i), kLog2e, -ap)));
       }
+    }
+    if (FULL) {
+#pragma unroll 1
+      for (int v = xs; v < nvec; v += kTvThreads)  // overflow, second read
+        acc += min_sum_pair<DT>(qv[v], pv[v], aq, ap);
     }
     const int next = pair + gridDim.x;
     const bool more = next < pairs;
@@ -515,13 +543,20 @@ __global__ __launch_bounds__(kTvThreads) void tv_resident_kernel(TvArgs a) {
     // after this barrier no wave reads the LDS part any more
     __syncthreads();
     if (FULL && more) {
+      // opaque copies of the wave offset and the LDS addresses: the compiler
+      // would otherwise share the per-slot offsets with the first copies
+      // before the loop, where they are defined under the lane condition and
+      // so are kept in VGPRs
+      unsigned int qa = lq_addr, pa = lp_addr;
+      int wo = wave_off;
+      asm volatile("" : "+s"(qa), "+s"(pa), "+s"(wo));
 #pragma unroll
       for (int c = 0; c < kResLdsSlots; ++c) {
         const int i = c * kTvThreads + tid;
         if (i < n_lds) {
-          const int w0 = c * kTvThreads + wave_off;
-          lds_dma16(nqv + kResRegSpan + w0, lq + w0, lane_bytes);
-          lds_dma16(npv + kResRegSpan + w0, lp + w0, lane_bytes);
+          const int w0 = c * kTvThreads + wo;
+          lds_dma16(nqv + kResRegSpan + w0, qa + w0 * 16u, lane_bytes);
+          lds_dma16(npv + kResRegSpan + w0, pa + w0 * 16u, lane_bytes);
         }
       }
     }
@@ -554,8 +589,9 @@ __global__ void tv_cumprod_kernel(const float* a_in, float* s_out, int B, int G)
 hipError_t launch_tv(const TvArgs& a, dspark_dtype dt, hipStream_t s) {
   const int pairs = a.B * a.gamma;
   if (pairs > 0) {
-    const int n_lds = a.nvec > kResRegSpan ? a.nvec - kResRegSpan : 0;
-    if (n_lds <= kResLdsMaxPairs) {
+    const int n_rest = a.nvec > kResRegSpan ? a.nvec - kResRegSpan : 0;
+    const int n_lds = n_rest < kResLdsMaxPairs ? n_rest : kResLdsMaxPairs;
+    if (n_rest - n_lds <= kResMaxOverflow) {
       // one persistent workgroup per CU (the registers hold one per CU)
       int cus = 1;
       hipError_t e = current_cu_count(&cus);

@@ -73,13 +73,19 @@ def _rand_logits(rng, shape, sigma, dt):
 
 # Row sizes around the kernel's layout limits: pairs of 16-byte vectors up to
 # 11 * 1024 stay in registers, up to 4992 more in LDS (16256 vectors: bf16
-# V <= 130055 is resident), longer rows take the two-pass streaming kernel.
+# V <= 130055 is fully resident), up to 4096 more are read from memory twice
+# (20352 vectors: bf16 V <= 162823, fp32 V <= 81411), longer rows take the
+# two-pass streaming kernel.
 @pytest.mark.parametrize("V,pad,dt", [(257, 0, 1), (257, 7, 1), (1000, 0, 0), (1001, 3, 0),
                                       (4096, 8, 1), (32000, 0, 1), (3, 1, 0),
                                       (90121, 5, 1),    # registers + 1 LDS pair, ragged tail
-                                      (130055, 0, 1),   # the largest resident bf16 row
-                                      (130056, 0, 1),   # one vector more: streaming
-                                      (70001, 3, 0)])   # fp32, streaming, ragged tail
+                                      (130055, 0, 1),   # the largest fully resident bf16 row
+                                      (130056, 0, 1),   # one vector more: 1 read twice
+                                      (151936, 0, 1),   # 2736 read twice, no tail
+                                      (162823, 0, 1),   # the largest such bf16 row
+                                      (162824, 0, 1),   # one element more: streaming
+                                      (70001, 3, 0),    # fp32, 1244 read twice, ragged tail
+                                      (81412, 0, 0)])   # fp32, streaming
 def test_tv_small(V, pad, dt):
     rng = np.random.default_rng(V * 7 + pad + dt)
     B, G = 3, 4
@@ -114,6 +120,7 @@ def test_tv_small(V, pad, dt):
 # LDS part of one pair, and pair counts that do not divide by the CU count.
 @pytest.mark.parametrize("V,pad,dt,B,G", [(90121, 5, 1, 37, 9),   # 333 pairs, 1 LDS pair
                                           (130055, 0, 1, 33, 8),  # 264 pairs, full LDS
+                                          (151936, 3, 1, 20, 16),  # 320 pairs, 2736 read twice
                                           (98304, 0, 1, 20, 26),  # 520 pairs, 3 per CU at most
                                           (32000, 0, 0, 40, 8),   # fp32, registers only
                                           (45056, 0, 0, 35, 8),   # fp32, exactly 11 * 1024 vectors
@@ -144,7 +151,9 @@ def test_tv_many_pairs(V, pad, dt, B, G):
 # vector; a thread whose sums overflow (an element about 2^7 base-2 units
 # above that, or a first vector of -inf only) sums again against its exact
 # maximum. Spikes far above the rest and -inf blocks take that path.
-@pytest.mark.parametrize("V,dt", [(129280, 1), (98304, 1), (32000, 0), (45056, 0)])
+@pytest.mark.parametrize("V,dt", [(129280, 1), (98304, 1), (32000, 0), (45056, 0),
+                                  (151936, 1),   # vectors past the LDS part, read twice
+                                  (81408, 0)])   # the same in fp32, the longest such row
 def test_tv_overflow_fallback(V, dt):
     rng = np.random.default_rng(V + 5)
     B, G = 6, 4
@@ -158,6 +167,7 @@ def test_tv_overflow_fallback(V, dt):
     p32[2, 2, :] = -60.0               # flat row, its maximum in thread 0's first
     p32[2, 2, 7] = 200.0               # vector: offsets 375 units apart, no fallback
     q32[3, 0, -1] = 300.0              # the last element (tail or last vector)
+    p32[4, 3, V - 3 * epv] = 160.0     # a vector near the end
     q = f32_to_bf16_bits(q32) if dt == 1 else q32
     p = f32_to_bf16_bits(p32) if dt == 1 else p32
     a, S = tv(B, G, V, dt, logits_up(q.reshape(B * G, V), dt), V,
