@@ -303,7 +303,8 @@ def test_sampling_many_slots_two_read_path():
               tag="17000 slots, all 1000 requests")
 
 
-SUMMARY = Path(__file__).resolve().parents[1] / "gpurun_out" / "sampling_f64_validation.json"
+# the error summary is written only when DSPARK_SUMMARY_DIR names an existing folder
+SUMMARY = Path(os.environ.get("DSPARK_SUMMARY_DIR", "/nonexistent")) / "sampling_f64_validation.json"
 
 
 def _record(name, rec):

@@ -36,9 +36,11 @@ def _assert_tv(a, S, ref_a, ref_S):
     assert np.all(np.abs(S - ref_S) <= REL * k * np.abs(ref_S) + FLOOR)
 
 import json
+import os
 from pathlib import Path
 
-SUMMARY = Path(__file__).resolve().parents[1] / "gpurun_out" / "tv_errors.json"
+# the error summary is written only when DSPARK_SUMMARY_DIR names an existing folder
+SUMMARY = Path(os.environ.get("DSPARK_SUMMARY_DIR", "/nonexistent")) / "tv_errors.json"
 
 
 def _record_err(tag, a, S, ref_a, ref_S):
