@@ -147,6 +147,9 @@ def test_sampling_parity_long_rows():
     # rows beyond the register-resident part: bf16 V > 131072, f32 V > 65536
     both(rand_case(7, 3, 3, 200003, dv.BF16, greedy_frac=0.0), "bf16 long rows")
     both(rand_case(8, 3, 3, 70001, dv.F32, greedy_frac=0.0), "f32 long rows")
+    # the largest vocabulary the library takes
+    both(rand_case(9, 2, 2, 262144, dv.BF16, greedy_frac=0.0), "bf16 rows of the maximum V")
+    both(rand_case(10, 2, 2, 262144, dv.F32, greedy_frac=0.5), "f32 rows of the maximum V")
 
 
 def test_all_greedy_equals_dspark_accept():

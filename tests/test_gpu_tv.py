@@ -87,7 +87,9 @@ def _rand_logits(rng, shape, sigma, dt):
                                       (162823, 0, 1),   # the largest such bf16 row
                                       (162824, 0, 1),   # one element more: streaming
                                       (70001, 3, 0),    # fp32, 1244 read twice, ragged tail
-                                      (81412, 0, 0)])   # fp32, streaming
+                                      (81412, 0, 0),    # fp32, streaming
+                                      (262144, 0, 1),   # the largest V the library takes
+                                      (262144, 0, 0)])
 def test_tv_small(V, pad, dt):
     rng = np.random.default_rng(V * 7 + pad + dt)
     B, G = 3, 4
