@@ -48,11 +48,18 @@ N_IN_STEP = 50  # bracketed accept calls inside steps
 QUEUE_AHEAD_CYCLES = 200_000  # about 85 us of GPU spin before a timed region
 
 
-def queue_ahead(torch):
+def queue_ahead(torch, cycles=QUEUE_AHEAD_CYCLES):
     """A spin kernel on the current stream just before a timed region's start
     event: while the GPU runs it, the host queues the first timed launches, so
     the region measures the GPU's time and not the host's first enqueue."""
-    torch.cuda._sleep(QUEUE_AHEAD_CYCLES)
+    torch.cuda._sleep(cycles)
+
+
+# Regions of launches shorter than the host's enqueue of one call (the
+# planner's 14 us, the pack's 4 us) are queued whole behind one longer spin:
+# about 40 us of spin per launch (a ctypes call and its launch take 10-25 us
+# of host time), so the timed launches run back to back on the GPU.
+SPIN_CYCLES_PER_LAUNCH = 95_000
 N_ACC = 100  # dedicated accept launches behind the roofline figure
 N_SCHED = 16  # seeded steps behind the scheduling statistics
 TRAFFIC_FILE = ROOT / "profiles" / "accept_b256_g8_v129280_bf16_traffic.json"
@@ -509,24 +516,24 @@ def main():
     assert int(ao.accept_meta[1].item()) == 0
 
     # ---- plan+pack, plan and pack alone (events), and one step as a HIP graph replay
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     reps = 50
-    queue_ahead(torch)
-    ev[3].record(stream)
-    for _ in range(reps):
-        plan_pack(stream)
-    ev[0].record(stream)
-    for _ in range(reps):
-        dv.dspark_plan(B, G, dv.IN_CONF_LOGITS, conf_t, temps_t, w.min_len, w.max_len, w.eps,
-                       w.b_lo, w.b_hi, float(w.bias), alpha_t, theta_t, po, stream)
-    ev[1].record(stream)
-    for _ in range(reps):
-        dv.dspark_pack(B, G, po.verify_lens, anchors_t, drafts_t, tiers, prefix_t, ko, stream)
-    ev[2].record(stream)
+    regions = [lambda: plan_pack(stream),
+               lambda: dv.dspark_plan(B, G, dv.IN_CONF_LOGITS, conf_t, temps_t, w.min_len,
+                                      w.max_len, w.eps, w.b_lo, w.b_hi, float(w.bias), alpha_t,
+                                      theta_t, po, stream),
+               lambda: dv.dspark_pack(B, G, po.verify_lens, anchors_t, drafts_t, tiers, prefix_t,
+                                      ko, stream)]
+    for j, launch in enumerate(regions):
+        torch.cuda.synchronize()
+        queue_ahead(torch, reps * SPIN_CYCLES_PER_LAUNCH)
+        ev[2 * j].record(stream)
+        for _ in range(reps):
+            launch()
+        ev[2 * j + 1].record(stream)
     torch.cuda.synchronize()
-    plan_pack_us = 1e3 * ev[3].elapsed_time(ev[0]) / reps
-    plan_us = 1e3 * ev[0].elapsed_time(ev[1]) / reps
-    pack_us = 1e3 * ev[1].elapsed_time(ev[2]) / reps
+    plan_pack_us, plan_us, pack_us = (1e3 * ev[2 * j].elapsed_time(ev[2 * j + 1]) / reps
+                                      for j in range(3))
 
     # launch floor of the latency-bound planner: one event pair around a single
     # launch, the queue drained before each, for plan+pack and for the smallest
