@@ -78,41 +78,25 @@ __device__ inline bool better(double r1, int b1, double r2, int b2) {
 // row shifts combine them.
 static_assert(kWaves == 16, "one per-wave partial per lane of a 16-lane row");
 
-// (ratio desc, b asc) maximum over the wave, left in lane 63. "None" is
-// (-1, INT_MAX): every real ratio is >= 0.
-__device__ inline void wave_argmax(double& r, int& b) {
-  struct RB {
-    double r;
-    int b;
-  };
-  auto step = [&](RB o) {
-    if (better(o.r, o.b, r, b)) {
-      r = o.r;
-      b = o.b;
-    }
-  };
-  step({dpp_t<0x111>(r, -1.0), dpp_t<0x111>(b, 0x7fffffff)});
-  step({dpp_t<0x112>(r, -1.0), dpp_t<0x112>(b, 0x7fffffff)});
-  step({dpp_t<0x114>(r, -1.0), dpp_t<0x114>(b, 0x7fffffff)});
-  step({dpp_t<0x118>(r, -1.0), dpp_t<0x118>(b, 0x7fffffff)});
-  step({dpp_t<0x142, 0xA>(r, -1.0), dpp_t<0x142, 0xA>(b, 0x7fffffff)});
-  step({dpp_t<0x143, 0xC>(r, -1.0), dpp_t<0x143, 0xC>(b, 0x7fffffff)});
-}
+struct OpMaxD {
+  __device__ double operator()(double x, double y) const { return __builtin_fmax(x, y); }
+};
 
-// The same maximum inside each 16-lane row, left in the row's last lane.
-__device__ inline void row_argmax(double& r, int& b) {
-  auto step = [&](double r2, int b2) {
-    if (better(r2, b2, r, b)) {
-      r = r2;
-      b = b2;
-    }
-  };
-  step(dpp_t<0x111>(r, -1.0), dpp_t<0x111>(b, 0x7fffffff));
-  step(dpp_t<0x112>(r, -1.0), dpp_t<0x112>(b, 0x7fffffff));
-  step(dpp_t<0x114>(r, -1.0), dpp_t<0x114>(b, 0x7fffffff));
-  step(dpp_t<0x118>(r, -1.0), dpp_t<0x118>(b, 0x7fffffff));
+// The (ratio desc, b asc) maximum of one value per lane over the lanes whose
+// bit is set in `lanes`, where the lane order is the order of b (each lane's
+// budgets lie below the next lane's): the maximum ratio by DPP steps, then
+// the b of the lowest lane holding it, which is the smallest b among equal
+// ratios. A lane's "none" is (-1, INT_MAX); every real ratio is >= 0 and
+// none is NaN, so the maximum is one of the lanes' values, bit for bit.
+// Wave-uniform results.
+template <bool ROW>
+__device__ inline void lane_argmax(double r, int b, unsigned long long lanes, double& best_r,
+                                   int& best_b) {
+  best_r = ROW ? read_lane(row_incl_scan(r, -1.0, OpMaxD{}), 15)
+               : read_lane(wave_incl_scan_op(r, -1.0, OpMaxD{}), kWave - 1);
+  const unsigned long long hit = __ballot(r == best_r) & lanes;
+  best_b = __builtin_amdgcn_readlane(b, (int)__builtin_ctzll(hit));
 }
-
 
 // Number of keys in the descending run d[0, len) greater than `key`
 // (strict = true) or greater than or equal to it (strict = false).
@@ -550,22 +534,25 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     }
   }
   if (cost_bad) atomicOr(&s_flags, DSPARK_DATA_BAD_COST);
-  wave_argmax(best_r, best_b);
   const int lane = lane_id(), wave = tid / kWave;
-  if (lane == kWave - 1) {
-    wratio[wave] = best_r;
-    wb[wave] = best_b;
+  {
+    double wr;
+    int wbst;
+    lane_argmax<false>(best_r, best_b, ~0ull, wr, wbst);
+    if (lane == 0) {
+      wratio[wave] = wr;
+      wb[wave] = wbst;
+    }
   }
   __syncthreads();
   if (s_flags) {
     fallback<PACK>(a, p, s_flags, lds, w32, tier_lane, &pre);
     return;
   }
-  double br = wratio[lane & 15];
-  int bstar = wb[lane & 15];
-  row_argmax(br, bstar);
-  br = read_lane(br, 15);
-  bstar = read_lane(bstar, 15);
+  // lane l of each 16-lane row holds wave l's pair; waves ascend in b
+  double br;
+  int bstar;
+  lane_argmax<true>(wratio[lane & 15], wb[lane & 15], 0xFFFFull, br, bstar);
 
 #pragma unroll
   for (int t = 0; t <= kMaxItems; ++t) {
