@@ -55,6 +55,7 @@ namespace {
 
 constexpr int kWaves = kPlanThreads / kWave;
 constexpr int kMaxItems = DSPARK_MAX_CANDIDATES / kPlanThreads;  // keys per thread, at most
+static_assert(kMaxItems == 8, "item counts 1, 2, 4, 8 cover every B * gamma");
 constexpr int kLgMinBuckets = 6, kLgMaxBuckets = 12;
 constexpr int kMaxBuckets = 1 << kLgMaxBuckets;
 constexpr int kMaxBucketFill = 32;  // beyond this the bucket rank loop gives way to merging
@@ -190,7 +191,10 @@ __host__ __device__ inline size_t plan_x_bytes(int B, int gamma, int n_keys) {
   return c > k ? c : k;
 }
 
-template <bool PACK>
+// ITEMS = the items (confidences, keys, sorted positions) each thread holds
+// at most: a power of two >= B * gamma / 1024, so that the per-item loops
+// are unrolled over live items only.
+template <bool PACK, int ITEMS>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs p) {
   extern __shared__ uint64_t lds[];
   __shared__ long long w64[kWaves + 1];
@@ -224,9 +228,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   // calibration waits for them, not for the loads issued after them
   const SmallDiv per_req(G);  // B * gamma <= 8192
   const bool logits = a.kind == DSPARK_IN_CONF_LOGITS;
-  float cin[kMaxItems], tin[kMaxItems];
+  float cin[ITEMS], tin[ITEMS];
 #pragma unroll
-  for (int e = 0; e < kMaxItems; ++e) {
+  for (int e = 0; e < ITEMS; ++e) {
     const int idx = tid + e * kPlanThreads;
     cin[e] = 0.0f;
     tin[e] = 1.0f;
@@ -244,7 +248,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   }
   // cost entries of the budgets this thread will evaluate: b = base_i + e + 1
   const bool sps_mode = a.cost_mode == DSPARK_COST_SPS1D;
-  float th[kMaxItems];
+  float th[ITEMS];
   float th0 = 0.0f, alpha_b = 0.0f;
   if (sps_mode) {
     for (int i = tid; i < a.sps_len; i += kPlanThreads) {
@@ -252,10 +256,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
       s_ps[i] = a.sps[i];
     }
 #pragma unroll
-    for (int e = 0; e < kMaxItems; ++e) th[e] = 0.0f;
+    for (int e = 0; e < ITEMS; ++e) th[e] = 0.0f;
   } else {
 #pragma unroll
-    for (int e = 0; e < kMaxItems; ++e) {
+    for (int e = 0; e < ITEMS; ++e) {
       const int m = m0 + base_i + e + 1;
       th[e] = (e < ipt && base_i + e < n_keys && m < a.theta_len) ? a.theta[m] : 0.0f;
     }
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   // ---- 1a. calibrated confidence of every (request, position), in parallel
   int bad = 0;
 #pragma unroll
-  for (int e = 0; e < kMaxItems; ++e) {
+  for (int e = 0; e < ITEMS; ++e) {
     const int idx = tid + e * kPlanThreads;
     if (idx < B * G) {
       const float v = cin[e];
@@ -391,10 +395,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
       for (int i = tid; i <= nb; i += kPlanThreads) bucket[i] = 0;
       __syncthreads();
     }
-    uint64_t mk[kMaxItems];
-    int mb[kMaxItems], ms[kMaxItems];
+    uint64_t mk[ITEMS];
+    int mb[ITEMS], ms[ITEMS];
 #pragma unroll
-    for (int e = 0; e < kMaxItems; ++e) {
+    for (int e = 0; e < ITEMS; ++e) {
       const int g = tid + e * kPlanThreads;
       mk[e] = (g < n_keys) ? keys[g] : 0ull;
       mb[e] = 0;
@@ -435,12 +439,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
       sorted = merge_runs(keys, aux, n_keys, span);
     } else {
 #pragma unroll
-      for (int e = 0; e < kMaxItems; ++e) {
+      for (int e = 0; e < ITEMS; ++e) {
         if (mk[e]) aux[bucket[mb[e]] + ms[e]] = mk[e];
       }
       __syncthreads();
 #pragma unroll
-      for (int e = 0; e < kMaxItems; ++e) {
+      for (int e = 0; e < ITEMS; ++e) {
         if (mk[e]) {
           const int b0 = bucket[mb[e]], b1 = bucket[mb[e] + 1];
           int rank = 0;
@@ -453,11 +457,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   }
 
   // ---- 3. exact tau scan, ratio sweep, argmax
-  uint64_t x[kMaxItems];
-  long long fxv[kMaxItems];
+  uint64_t x[ITEMS];
+  long long fxv[ITEMS];
   long long local = 0;
 #pragma unroll
-  for (int e = 0; e < kMaxItems; ++e) {
+  for (int e = 0; e < ITEMS; ++e) {
     const bool in = e < ipt && base_i + e < n_el;
     x[e] = in ? sorted[base_i + e] : 0ull;
     fxv[e] = in ? fx40(key_s(x[e])) : 0;
@@ -477,7 +481,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   const int hi_b = a.b_hi < 0 ? n_el : min(a.b_hi, n_el);
   const double t_fixed = __dadd_rn((double)a.bias, (double)alpha_b);
 
-  double tau_v[kMaxItems + 1], ratio_v[kMaxItems + 1];
+  double tau_v[ITEMS + 1], ratio_v[ITEMS + 1];
   double best_r = -1.0;
   int best_b = 0x7fffffff;
   int cost_bad = 0;
@@ -497,7 +501,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   }
   // slot 0 of thread 0 is b = 0; slot t >= 1 is b = base_i + t
 #pragma unroll
-  for (int t = 0; t <= kMaxItems; ++t) {
+  for (int t = 0; t <= ITEMS; ++t) {
     int b;
     if (t == 0) {
       b = (tid == 0) ? 0 : -1;
@@ -555,7 +559,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   lane_argmax<true>(wratio[lane & 15], wb[lane & 15], 0xFFFFull, br, bstar);
 
 #pragma unroll
-  for (int t = 0; t <= kMaxItems; ++t) {
+  for (int t = 0; t <= ITEMS; ++t) {
     const int b = (t == 0) ? (tid == 0 ? 0 : -1) : ((t <= ipt && base_i + t <= n_el) ? base_i + t : -1);
     if (b < 0) continue;
     if (a.sweep) {
@@ -584,7 +588,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
 
   // ---- 4. verify_lens = L_min + #(first b_exec keys of each request)
 #pragma unroll
-  for (int e = 0; e < kMaxItems; ++e) {
+  for (int e = 0; e < ITEMS; ++e) {
     if (e < ipt && base_i + e < bexec) atomicAdd(&cnt[key_r(x[e])], 1);
   }
   __syncthreads();
@@ -606,13 +610,31 @@ size_t plan_lds_bytes(int B, int gamma, int n_keys) {
   return main > pk ? main : pk;
 }
 
+namespace {
+
+template <bool PACK>
+void launch_plan_items(const PlanArgs& a, const PackArgs& p, size_t lds, hipStream_t s) {
+  const int items = (a.B * a.gamma + kPlanThreads - 1) / kPlanThreads;  // <= kMaxItems
+  if (items <= 1) {
+    hipLaunchKernelGGL((plan_kernel<PACK, 1>), dim3(1), dim3(kPlanThreads), lds, s, a, p);
+  } else if (items <= 2) {
+    hipLaunchKernelGGL((plan_kernel<PACK, 2>), dim3(1), dim3(kPlanThreads), lds, s, a, p);
+  } else if (items <= 4) {
+    hipLaunchKernelGGL((plan_kernel<PACK, 4>), dim3(1), dim3(kPlanThreads), lds, s, a, p);
+  } else {
+    hipLaunchKernelGGL((plan_kernel<PACK, kMaxItems>), dim3(1), dim3(kPlanThreads), lds, s, a, p);
+  }
+}
+
+}  // namespace
+
 hipError_t launch_plan(const PlanArgs& a, const PackArgs* p, hipStream_t s) {
   const size_t lds = plan_lds_bytes(a.B, a.gamma, a.B * (a.lmax - a.lmin));
   if (p) {
-    hipLaunchKernelGGL(plan_kernel<true>, dim3(1), dim3(kPlanThreads), lds, s, a, *p);
+    launch_plan_items<true>(a, *p, lds, s);
   } else {
     PackArgs none{};
-    hipLaunchKernelGGL(plan_kernel<false>, dim3(1), dim3(kPlanThreads), lds, s, a, none);
+    launch_plan_items<false>(a, none, lds, s);
   }
   return hipGetLastError();
 }

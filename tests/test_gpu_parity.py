@@ -133,6 +133,21 @@ def test_plan_edge_cases():
                   rng.uniform(0.5, 2, 64).astype(np.float32), 1, 65, 1e-4, 0, -1))
     cases.append((128, 64, oracle.IN_CONF_LOGITS, rng.normal(2, 2, (128, 64)).astype(np.float32),
                   rng.uniform(0.5, 2, 64).astype(np.float32), 1, 65, 1e-3, 0, -1))
+    # gamma 4, 16 and 32 (requests aligned with the waves' lanes); a request
+    # whose given survival increases
+    s4 = np.sort(rng.random((70, 4)).astype(np.float32), axis=1)[:, ::-1].copy()
+    cases.append((70, 4, oracle.IN_SURVIVAL, s4, None, 1, 5, 0.05, 0, -1))
+    s4b = s4.copy()
+    s4b[33] = [0.5, 0.4, 0.45, 0.1]
+    cases.append((70, 4, oracle.IN_SURVIVAL, s4b, None, 1, 5, 0.05, 0, -1))
+    c16 = rng.uniform(0.5, 1.0, (40, 16)).astype(np.float32)
+    cases.append((40, 16, oracle.IN_COND, c16, None, 1, 17, 1e-3, 0, -1))
+    c32 = rng.uniform(0.7, 1.0, (33, 32)).astype(np.float32)
+    cases.append((33, 32, oracle.IN_COND, c32, None, 2, 30, 1e-4, 0, -1))
+    # 2048 < B * gamma <= 4096: four items per thread
+    z12 = rng.normal(1.5, 1.5, (300, 12)).astype(np.float32)
+    cases.append((300, 12, oracle.IN_CONF_LOGITS, z12, rng.uniform(0.5, 2, 12).astype(np.float32),
+                  1, 13, 1e-4, 0, -1))
     # -0 confidences and survivals rank with +0 (by value, then position, then request)
     cz = np.array([[0.5, -0.0], [0.9, 0.8]], np.float32)
     cases.append((2, 2, oracle.IN_COND, cz, None, 1, 3, 0.0, 0, -1))
