@@ -67,8 +67,15 @@ __device__ inline uint64_t make_key(float s, int k, int r) {
 __device__ inline float key_s(uint64_t key) { return __uint_as_float((uint32_t)(key >> 32)); }
 __device__ inline int key_r(uint64_t key) { return 0xFFFFFF - (int)(key & 0xFFFFFF); }
 
-// survival at the 2^-40 resolution of tau: nearest, ties to even
-__device__ inline long long fx40(float s) { return __double2ll_rn((double)s * 0x1p40); }
+// survival at the 2^-40 resolution of tau: nearest, ties to even, for s in
+// [0, 1] (any other value sends the planner to its fallback, which discards
+// it). s * 2^40 + 2^52 in one fused multiply-add is that integer plus 2^52,
+// since the doubles in [2^52, 2^53) are exactly the integers; its bits minus
+// those of 2^52 are the integer.
+__device__ inline long long fx40(float s) {
+  return __double_as_longlong(__fma_rn((double)s, 0x1p40, 0x1p52)) -
+         __double_as_longlong(0x1p52);
+}
 
 __device__ inline bool better(double r1, int b1, double r2, int b2) {
   return r1 > r2 || (r1 == r2 && b1 < b2);
@@ -344,34 +351,37 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
     }
   }
   // one block reduction for the five quantities: per-wave DPP reductions,
-  // then every wave combines the 16 per-wave partials
+  // then every wave combines the 16 per-wave partials. The flags go through
+  // ballots, and the forced sum is reduced only when positions are forced.
   {
     const int lane = lane_id(), wave = tid / kWave;
     auto umin = [](unsigned int x, unsigned int y) { return min(x, y); };
     auto umax = [](unsigned int x, unsigned int y) { return max(x, y); };
-    auto ior = [](int x, int y) { return x | y; };
-    forced = wave_incl_scan_op(forced, 0ll, OpAdd{});
+    auto flags_of = [](int v) {
+      return (__ballot((v & 1) != 0) ? 1 : 0) | (__ballot((v & 2) != 0) ? 2 : 0);
+    };
+    const bool any_forced = lmin > 1;
+    if (any_forced) forced = wave_incl_scan_op(forced, 0ll, OpAdd{});
     n_el = wave_incl_scan_op(n_el, 0, OpAdd{});
     smin = wave_incl_scan_op(smin, 0xFFFFFFFFu, umin);
     smax = wave_incl_scan_op(smax, 0u, umax);
-    bad = wave_incl_scan_op(bad, 0, ior);
+    const int wflags = flags_of(bad);
     if (lane == kWave - 1) {
       w64[wave] = forced;
       w32[wave] = n_el;
       wmin[wave] = smin;
       wmax[wave] = smax;
-      wbad[wave] = bad;
+      wbad[wave] = wflags;
     }
     __syncthreads();
     const int l = lane & 15;
-    const long long f2 = w64[l];
     const int n2 = w32[l], b2 = wbad[l];
     const unsigned int mn2 = wmin[l], mx2 = wmax[l];
-    forced = read_lane(row_incl_scan(f2, 0ll, OpAdd{}), 15);
+    if (any_forced) forced = read_lane(row_incl_scan(w64[l], 0ll, OpAdd{}), 15);
     n_el = read_lane(row_incl_scan(n2, 0, OpAdd{}), 15);
     smin = read_lane(row_incl_scan(mn2, 0xFFFFFFFFu, umin), 15);
     smax = read_lane(row_incl_scan(mx2, 0u, umax), 15);
-    bad = read_lane(row_incl_scan(b2, 0, ior), 15);
+    bad = flags_of(b2);  // every row holds all 16 waves' flags
     // no closing barrier: w32 is written again only after the counting
     // barrier of the sort (or the fallback's barrier); the others never
   }
