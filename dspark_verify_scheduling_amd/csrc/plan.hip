@@ -307,26 +307,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
   long long forced = 0;
   int n_el = 0;
   unsigned int smin = 0xFFFFFFFFu, smax = 0u;
-  for (int idx = tid; idx < B * G; idx += kPlanThreads) {
-    const int r = per_req.quo(idx);
-    const int k = idx - r * G + 1;
-    const float* cr = conf_c + r * G;
-    float s = cr[0];
-    if (a.kind == DSPARK_IN_SURVIVAL) {
-      s = cr[k - 1];
-      if (k > 1 && s > cr[k - 2]) bad = 1;
-    } else {
-      // factors 1 .. k-1 in batches of 8, each batch's LDS reads issued before
-      // its first multiply; a read past the request's last position is never
-      // multiplied, so the product keeps its left-to-right order
-      for (int i0 = 1; i0 < k; i0 += 8) {
-        float f[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) f[j] = cr[min(i0 + j, G - 1)];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) s = i0 + j < k ? __fmul_rn(s, f[j]) : s;
-      }
-    }
+  auto emit = [&](int idx, int r, int k, float s) {
     if (a.surv_out) a.surv_out[idx] = s;
     if (k < lmin) {
       forced += fx40(s);
@@ -341,6 +322,58 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, PackArgs
         smin = min(smin, sb);
         smax = max(smax, sb);
       }
+    }
+  };
+  if (a.kind != DSPARK_IN_SURVIVAL && G <= 9 && ITEMS <= 4) {
+    // at most 8 factors after the first: every item's reads (clamped to the
+    // request's last position; an item past B * gamma reads request 0 and is
+    // dropped) are issued before the first multiply, and a factor past the
+    // item's own position is never multiplied, so each product keeps its
+    // left-to-right order
+    float f[ITEMS][9];
+    int kk[ITEMS], rr[ITEMS];
+#pragma unroll
+    for (int e = 0; e < ITEMS; ++e) {
+      const int idx = tid + e * kPlanThreads;
+      const int r = idx < B * G ? per_req.quo(idx) : 0;
+      rr[e] = r;
+      kk[e] = idx - r * G + 1;
+      const float* cr = conf_c + r * G;
+#pragma unroll
+      for (int j = 0; j < 9; ++j) f[e][j] = cr[min(j, G - 1)];
+    }
+#pragma unroll
+    for (int e = 0; e < ITEMS; ++e) {
+      const int idx = tid + e * kPlanThreads;
+      if (idx < B * G) {
+        float s = f[e][0];
+#pragma unroll
+        for (int j = 1; j < 9; ++j) s = j < kk[e] ? __fmul_rn(s, f[e][j]) : s;
+        emit(idx, rr[e], kk[e], s);
+      }
+    }
+  } else {
+    for (int idx = tid; idx < B * G; idx += kPlanThreads) {
+      const int r = per_req.quo(idx);
+      const int k = idx - r * G + 1;
+      const float* cr = conf_c + r * G;
+      float s = cr[0];
+      if (a.kind == DSPARK_IN_SURVIVAL) {
+        s = cr[k - 1];
+        if (k > 1 && s > cr[k - 2]) bad = 1;
+      } else {
+        // factors 1 .. k-1 in batches of 8, each batch's LDS reads issued
+        // before its first multiply; a read past the request's last position
+        // is never multiplied, so the product keeps its left-to-right order
+        for (int i0 = 1; i0 < k; i0 += 8) {
+          float f[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) f[j] = cr[min(i0 + j, G - 1)];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) s = i0 + j < k ? __fmul_rn(s, f[j]) : s;
+        }
+      }
+      emit(idx, r, k, s);
     }
   }
   // SPS probes must be strictly ascending (bit 1 of `bad`: a cost error,
